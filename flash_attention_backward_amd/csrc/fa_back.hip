@@ -1,0 +1,308 @@
+// Host side of the flash-attention backward library: descriptor validation, output layout,
+// workspace sizing, the plan, and the launch sequence. Device code is in fab_kernels.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "fa_back.h"
+#include "fab_kernels.h"
+
+using namespace fab;
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+int64_t elem_size(int type) {
+    switch (type) {
+        case FA_BACK_F32: return 4;
+        case FA_BACK_F16: return 2;
+        case FA_BACK_BF16: return 2;
+        case FA_BACK_Q8_0: return 34;   // one 32-value block
+        default: return 0;
+    }
+}
+
+// Everything derived from a valid descriptor: shapes, plan choices, offsets.
+struct Geometry {
+    int D, Dv, H, Hkv, G, N, M, Hm;
+    int R, RB, RT, KT, splits, tiles_per_split, KVT;
+    int npart, nbound;
+    fa_back_layout layout;
+    // workspace offsets (bytes)
+    uint64_t ws_absmax, ws_scal, ws_qf, ws_df, ws_qt, ws_dt;
+    uint64_t ws_pm, ws_pl, ws_pd, ws_pb, ws_lse2, ws_dlt, ws_bound, ws_dqp;
+};
+
+bool tensor_nonneg(const fa_back_tensor& t) {
+    return t.ne[0] >= 0 && t.ne[1] >= 0 && t.ne[2] >= 0;
+}
+
+int check_strides(const fa_back_tensor& t, bool rows16) {
+    const int64_t es = elem_size(t.type);
+    if (t.nb[0] != es) return FA_BACK_ESTRIDE;
+    if (t.nb[1] <= 0 || t.nb[2] <= 0) return FA_BACK_ESTRIDE;
+    const int64_t a = rows16 ? 16 : (t.type == FA_BACK_Q8_0 ? 2 : es);
+    if (t.nb[1] % a || t.nb[2] % a) return FA_BACK_ESTRIDE;
+    return FA_BACK_OK;
+}
+
+int validate(const fa_back_desc* d, Geometry* g) {
+    if (!d) return FA_BACK_EINVAL;
+    const fa_back_tensor &q = d->q, &k = d->k, &v = d->v, &dd = d->d, &m = d->mask;
+    // types
+    auto is_act = [](int t) { return t == FA_BACK_F32 || t == FA_BACK_F16 || t == FA_BACK_BF16; };
+    auto is_kv = [&](int t) { return is_act(t) || t == FA_BACK_Q8_0; };
+    if (!is_act(q.type) || !is_act(dd.type) || !is_kv(k.type) || !is_kv(v.type)) return FA_BACK_EUNSUPPORTED;
+    const bool has_mask = m.type != FA_BACK_NONE;
+    if (has_mask && m.type != FA_BACK_F32 && m.type != FA_BACK_F16) return FA_BACK_EUNSUPPORTED;
+    if (!std::isfinite(d->scale)) return FA_BACK_EINVAL;
+    if (!tensor_nonneg(q) || !tensor_nonneg(k) || !tensor_nonneg(v) || !tensor_nonneg(dd) ||
+        (has_mask && !tensor_nonneg(m)))
+        return FA_BACK_EINVAL;
+    const int64_t D = q.ne[0], N = q.ne[1], H = q.ne[2];
+    const int64_t M = k.ne[1], Hkv = k.ne[2], Dv = v.ne[0];
+    if (D == 0 || H == 0 || Hkv == 0 || Dv == 0) return FA_BACK_EINVAL;
+    // shapes
+    if (k.ne[0] != D) return FA_BACK_ESHAPE;
+    if (v.ne[1] != M || v.ne[2] != Hkv) return FA_BACK_ESHAPE;
+    if (dd.ne[0] != Dv || dd.ne[1] != H || dd.ne[2] != N) return FA_BACK_ESHAPE;
+    if (H % Hkv) return FA_BACK_ESHAPE;
+    if (k.type == FA_BACK_Q8_0 && D % 32) return FA_BACK_ESHAPE;
+    if (v.type == FA_BACK_Q8_0 && Dv % 32) return FA_BACK_ESHAPE;
+    int64_t Hm = 0;
+    if (has_mask) {
+        if (m.ne[0] != M || m.ne[1] != N) return FA_BACK_ESHAPE;
+        Hm = m.ne[2];
+        if (Hm != 1 && Hm != H) return FA_BACK_ESHAPE;
+    }
+    // strides: rows contiguous; F32/F16/BF16 cache rows are read with 16-byte loads
+    int rc;
+    if ((rc = check_strides(q, false)) || (rc = check_strides(dd, false))) return rc;
+    if ((rc = check_strides(k, k.type != FA_BACK_Q8_0)) || (rc = check_strides(v, v.type != FA_BACK_Q8_0)))
+        return rc;
+    if (has_mask && (rc = check_strides(m, false))) return rc;
+    // supported sizes
+    if (D != Dv || (D != 64 && D != 128 && D != 256)) return FA_BACK_EUNSUPPORTED;
+    const int64_t G = H / Hkv;
+    if (N * H >= (int64_t)1 << 30 || M * Hkv >= (int64_t)1 << 30 || G * N >= (int64_t)1 << 30 || H > 65535)
+        return FA_BACK_EUNSUPPORTED;
+
+    g->D = (int)D; g->Dv = (int)Dv; g->H = (int)H; g->Hkv = (int)Hkv; g->G = (int)G;
+    g->N = (int)N; g->M = (int)M; g->Hm = (int)Hm;
+    g->R = (int)(G * N);
+    g->RB = (g->R + 31) / 32;
+    g->RT = (g->RB + kWaves - 1) / kWaves;
+    g->KT = (g->M + kQTileKeys - 1) / kQTileKeys;
+    g->KVT = (g->M + kKVKeys - 1) / kKVKeys;
+    // key-range splits of the query-side passes: aim for >= 512 workgroups (two per CU on
+    // 256 CUs) but keep >= 4 key tiles per split so the dQ partials stay small
+    {
+        const int base = g->RT * g->Hkv;
+        int splits = base > 0 ? (512 + base - 1) / base : 1;
+        const int max_splits = g->KT >= 4 ? g->KT / 4 : 1;
+        if (splits > max_splits) splits = max_splits;
+        if (splits < 1) splits = 1;
+        const int tps = g->KT > 0 ? (g->KT + splits - 1) / splits : 1;
+        g->tiles_per_split = tps;
+        g->splits = g->KT > 0 ? (g->KT + tps - 1) / tps : 1;
+    }
+    g->npart = (int)std::min<int64_t>(512, std::max<int64_t>(1, N * H / 8));
+    const int64_t total_rows = (int64_t)g->Hkv * g->RB * 32;
+    g->nbound = (int)std::min<int64_t>(256, std::max<int64_t>(1, (total_rows + kThreads - 1) / kThreads));
+
+    // packed output
+    fa_back_layout& L = g->layout;
+    L.off_dq = 0;
+    L.off_dk = align_up(L.off_dq + 4ull * D * N * H, kAlign);
+    L.off_dv = align_up(L.off_dk + 4ull * D * M * Hkv, kAlign);
+    L.off_lse = align_up(L.off_dv + 4ull * Dv * M * Hkv, kAlign);
+    L.off_delta = L.off_lse + 4ull * N * H;
+    L.out_bytes = std::max<uint64_t>(align_up(L.off_delta + 4ull * N * H, kAlign), kAlign);
+    // workspace
+    uint64_t o = 0;
+    auto take = [&](uint64_t bytes) { const uint64_t at = o; o = align_up(o + bytes, kAlign); return at; };
+    const uint64_t frag = 2ull * total_rows * D;
+    const uint64_t prow = (uint64_t)g->splits * total_rows;
+    g->ws_absmax = take(8ull * g->npart);
+    g->ws_scal = take(64);
+    g->ws_qf = take(frag);
+    g->ws_df = take(frag);
+    g->ws_qt = take(frag);
+    g->ws_dt = take(frag);
+    g->ws_pm = take(4 * prow);
+    g->ws_pl = take(8 * prow);
+    g->ws_pd = take(8 * prow);
+    g->ws_pb = take(4 * prow);
+    g->ws_lse2 = take(4ull * total_rows);
+    g->ws_dlt = take(4ull * total_rows);
+    g->ws_bound = take(4ull * g->nbound);
+    g->ws_dqp = take(g->splits > 1 ? 4ull * g->splits * total_rows * D : 0);
+    L.workspace_bytes = std::max<uint64_t>(o, kAlign);
+    return FA_BACK_OK;
+}
+
+template <int D>
+int launch_all(const Geometry& g, Params& P, hipStream_t st) {
+    if (g.N == 0 || g.M == 0) {
+        // degenerate: zero dK, dV (N == 0) or every row fully masked (M == 0)
+        const int64_t nk = (int64_t)g.D * g.M * g.Hkv;
+        if (nk) hipLaunchKernelGGL(fill_kernel, dim3(256), dim3(kThreads), 0, st, P.dk, nk, 0.0f);
+        if (nk) hipLaunchKernelGGL(fill_kernel, dim3(256), dim3(kThreads), 0, st, P.dv, nk, 0.0f);
+        const int64_t nq = (int64_t)g.D * g.N * g.H;
+        if (nq) hipLaunchKernelGGL(fill_kernel, dim3(256), dim3(kThreads), 0, st, P.dq, nq, 0.0f);
+        const int64_t nr = (int64_t)g.N * g.H;
+        if (nr) hipLaunchKernelGGL(fill_kernel, dim3(64), dim3(kThreads), 0, st, P.lse, nr, -INFINITY);
+        if (nr) hipLaunchKernelGGL(fill_kernel, dim3(64), dim3(kThreads), 0, st, P.delta, nr, 0.0f);
+        return hipGetLastError() == hipSuccess ? FA_BACK_OK : FA_BACK_EHIP;
+    }
+    hipLaunchKernelGGL(absmax_kernel, dim3(g.npart), dim3(kThreads), 0, st, P);
+    hipLaunchKernelGGL(prep_kernel<D>, dim3(g.Hkv * g.RB), dim3(kThreads), 0, st, P);
+    hipLaunchKernelGGL((qpass_kernel<D, false>), dim3(g.RT * g.Hkv, g.splits), dim3(kThreads), 0, st, P);
+    hipLaunchKernelGGL(merge_kernel, dim3(g.nbound), dim3(kThreads), 0, st, P);
+    hipLaunchKernelGGL((qpass_kernel<D, true>), dim3(g.RT * g.Hkv, g.splits), dim3(kThreads), 0, st, P);
+    if (g.splits > 1) {
+        const int64_t n4 = (int64_t)g.Hkv * g.RB * 32 * (D / 4);
+        const int blocks = (int)std::min<int64_t>(4096, (n4 + kThreads - 1) / kThreads);
+        hipLaunchKernelGGL(dqreduce_kernel<D>, dim3(blocks), dim3(kThreads), 0, st, P);
+    }
+    hipLaunchKernelGGL(kvpass_kernel<D>, dim3(g.KVT * g.Hkv), dim3(kThreads), 0, st, P);
+    return hipGetLastError() == hipSuccess ? FA_BACK_OK : FA_BACK_EHIP;
+}
+
+}  // namespace
+
+struct fa_back_plan {
+    fa_back_desc desc;
+    Geometry geo;
+    int device;
+};
+
+extern "C" {
+
+const char* fa_back_status_string(int s) {
+    switch (s) {
+        case FA_BACK_OK: return "ok";
+        case FA_BACK_EINVAL: return "invalid argument";
+        case FA_BACK_ESHAPE: return "inconsistent shapes";
+        case FA_BACK_ESTRIDE: return "unsupported strides";
+        case FA_BACK_EUNSUPPORTED: return "unsupported type, size or device";
+        case FA_BACK_EHIP: return "HIP runtime error";
+        case FA_BACK_EALIGN: return "misaligned device pointer";
+        default: return "unknown status";
+    }
+}
+
+int fa_back_layout_query(const fa_back_desc* desc, fa_back_layout* layout) {
+    if (!layout) return FA_BACK_EINVAL;
+    Geometry g;
+    const int rc = validate(desc, &g);
+    if (rc == FA_BACK_OK) *layout = g.layout;
+    return rc;
+}
+
+int fa_back_create(const fa_back_desc* desc, int device, fa_back_plan** plan, fa_back_layout* layout) {
+    if (!plan) return FA_BACK_EINVAL;
+    *plan = nullptr;
+    Geometry g;
+    int rc = validate(desc, &g);
+    if (rc != FA_BACK_OK) return rc;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return FA_BACK_EUNSUPPORTED;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return FA_BACK_EHIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return FA_BACK_EUNSUPPORTED;
+    fa_back_plan* p = new (std::nothrow) fa_back_plan;
+    if (!p) return FA_BACK_EINVAL;
+    p->desc = *desc;
+    p->geo = g;
+    p->device = device;
+    *plan = p;
+    if (layout) *layout = g.layout;
+    return FA_BACK_OK;
+}
+
+void fa_back_destroy(fa_back_plan* plan) { delete plan; }
+
+int fa_back_run(const fa_back_plan* plan, const void* q, const void* k, const void* v, const void* d,
+                const void* mask, void* out, void* workspace, void* stream) {
+    if (!plan || !out || !workspace) return FA_BACK_EINVAL;
+    const fa_back_desc& ds = plan->desc;
+    const Geometry& g = plan->geo;
+    // a tensor without elements may be passed as NULL
+    const bool q_empty = (int64_t)g.N * g.H == 0, kv_empty = (int64_t)g.M == 0;
+    if ((!q && !q_empty) || (!d && !q_empty) || (!k && !kv_empty) || (!v && !kv_empty)) return FA_BACK_EINVAL;
+    const bool has_mask = ds.mask.type != FA_BACK_NONE;
+    if (!has_mask && mask) return FA_BACK_EINVAL;
+    if (has_mask && !mask && (int64_t)g.M * g.N != 0) return FA_BACK_EINVAL;
+    auto misaligned = [](const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) != 0; };
+    auto kv_align = [](int t) -> uintptr_t { return t == FA_BACK_Q8_0 ? 2 : 16; };
+    if (misaligned(q, elem_size(ds.q.type)) || misaligned(d, elem_size(ds.d.type)) ||
+        misaligned(k, kv_align(ds.k.type)) || misaligned(v, kv_align(ds.v.type)) ||
+        (has_mask && misaligned(mask, elem_size(ds.mask.type))) || misaligned(out, kAlign) ||
+        misaligned(workspace, kAlign))
+        return FA_BACK_EALIGN;
+
+    int old = -1;
+    if (hipGetDevice(&old) != hipSuccess) return FA_BACK_EHIP;
+    if (old != plan->device && hipSetDevice(plan->device) != hipSuccess) return FA_BACK_EHIP;
+    (void)hipGetLastError();   // clear a stale error so the check below sees only ours
+
+    Params P;
+    std::memset(&P, 0, sizeof(P));
+    P.q = (const char*)q; P.k = (const char*)k; P.v = (const char*)v; P.d = (const char*)d;
+    P.mask = (const char*)mask;
+    P.q_nb0 = ds.q.nb[0]; P.q_nb1 = ds.q.nb[1]; P.q_nb2 = ds.q.nb[2];
+    P.d_nb0 = ds.d.nb[0]; P.d_nb1 = ds.d.nb[1]; P.d_nb2 = ds.d.nb[2];
+    P.k_nb1 = ds.k.nb[1]; P.k_nb2 = ds.k.nb[2];
+    P.v_nb1 = ds.v.nb[1]; P.v_nb2 = ds.v.nb[2];
+    P.m_nb0 = ds.mask.nb[0]; P.m_nb1 = ds.mask.nb[1]; P.m_nb2 = ds.mask.nb[2];
+    P.q_type = ds.q.type; P.d_type = ds.d.type; P.k_type = ds.k.type; P.v_type = ds.v.type;
+    P.m_type = ds.mask.type;
+    P.D = g.D; P.H = g.H; P.Hkv = g.Hkv; P.G = g.G; P.N = g.N; P.M = g.M; P.Hm = g.Hm;
+    P.R = g.R; P.RB = g.RB; P.RT = g.RT; P.KT = g.KT; P.splits = g.splits;
+    P.tiles_per_split = g.tiles_per_split; P.KVT = g.KVT;
+    P.scale = ds.scale;
+    char* o = (char*)out;
+    P.dq = (float*)(o + g.layout.off_dq);
+    P.dk = (float*)(o + g.layout.off_dk);
+    P.dv = (float*)(o + g.layout.off_dv);
+    P.lse = (float*)(o + g.layout.off_lse);
+    P.delta = (float*)(o + g.layout.off_delta);
+    char* w = (char*)workspace;
+    P.absmax_part = (float*)(w + g.ws_absmax);
+    P.npart = g.npart;
+    P.scal = (int*)(w + g.ws_scal);
+    P.qf = (_Float16*)(w + g.ws_qf);
+    P.df = (_Float16*)(w + g.ws_df);
+    P.qt = (_Float16*)(w + g.ws_qt);
+    P.dt = (_Float16*)(w + g.ws_dt);
+    P.part_m = (float*)(w + g.ws_pm);
+    P.part_l = (double*)(w + g.ws_pl);
+    P.part_d = (double*)(w + g.ws_pd);
+    P.part_b = (float*)(w + g.ws_pb);
+    P.row_lse2 = (float*)(w + g.ws_lse2);
+    P.row_dlt = (float*)(w + g.ws_dlt);
+    P.bound_part = (float*)(w + g.ws_bound);
+    P.nbound = g.nbound;
+    P.dq_part = (float*)(w + g.ws_dqp);
+
+    hipStream_t st = (hipStream_t)stream;
+    int rc;
+    switch (g.D) {
+        case 64: rc = launch_all<64>(g, P, st); break;
+        case 128: rc = launch_all<128>(g, P, st); break;
+        case 256: rc = launch_all<256>(g, P, st); break;
+        default: rc = FA_BACK_EUNSUPPORTED;
+    }
+    if (old != plan->device) (void)hipSetDevice(old);
+    return rc;
+}
+
+}  // extern "C"

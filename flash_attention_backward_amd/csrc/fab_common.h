@@ -1,0 +1,121 @@
+// Shared device definitions for the flash-attention backward kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_back.h"
+
+#define FAB_DEV __device__ __forceinline__
+
+namespace fab {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kRowBlock = 32;     // rows per MFMA block (the 32 of a 32x32x16 product)
+constexpr int kQTileKeys = 64;    // keys per tile in the query-side passes
+constexpr int kKVKeys = 128;      // keys owned by one key-side workgroup (32 per wave)
+constexpr int kPScaleLog2 = 15;   // P is rounded to fp16 as p * 2^15 (p <= 1)
+constexpr int kNegInfBits = 0xff800000;
+
+// Everything the kernels need, passed by value.
+struct Params {
+    const char* q;
+    const char* k;
+    const char* v;
+    const char* d;
+    const char* mask;
+    int64_t q_nb0, q_nb1, q_nb2;   // (c, i, h)
+    int64_t d_nb0, d_nb1, d_nb2;   // (c, h, i)
+    int64_t k_nb1, k_nb2;          // (row j, head hk)
+    int64_t v_nb1, v_nb2;
+    int64_t m_nb0, m_nb1, m_nb2;   // (j, i, hm)
+    int q_type, d_type, k_type, v_type, m_type;
+    int D, H, Hkv, G, N, M, Hm;
+    int R;            // query rows per KV head: G * N, row r = i*G + g  (h = hk*G + g)
+    int RB;           // 32-row blocks per KV head
+    int RT;           // query-side row tiles (kWaves row blocks each) per KV head
+    int KT;           // 64-key tiles
+    int splits;       // key-range splits of the query-side passes
+    int tiles_per_split;
+    int KVT;          // 128-key tiles of the key-side pass
+    float scale;
+    // outputs (packed)
+    float* dq;
+    float* dk;
+    float* dv;
+    float* lse;
+    float* delta;
+    // workspace
+    float* absmax_part;   // [2][npart]
+    int npart;
+    int* scal;            // [0] = e_q, [1] = e_do (power-of-two exponents)
+    _Float16* qf;         // [Hkv][RB][32*D]  q rows, fragments for contraction over d
+    _Float16* df;         // [Hkv][RB][32*D]  dO rows, same
+    _Float16* qt;         // [Hkv][RB][32*D]  q, fragments for contraction over rows
+    _Float16* dt;         // [Hkv][RB][32*D]  dO, same
+    float* part_m;        // [splits][Hkv*RB*32]  running max (log2 units)
+    double* part_l;       // softmax sum at part_m
+    double* part_d;       // sum of e * dp at part_m (dp in 2^e_do units)
+    float* part_b;        // max |dp| over visible keys
+    float* row_lse2;      // [Hkv*RB*32]  lse in log2 units, -inf for dead or padding rows
+    float* row_dlt;       // [Hkv*RB*32]  delta in 2^e_do units
+    float* bound_part;    // [nbound] per-block max of max|dp| + |delta|
+    int nbound;
+    float* dq_part;       // [splits][Hkv*RB*32][D] when splits > 1
+};
+
+// Row of the 32x32 product held in accumulator register v by a lane of half g (= lane/32);
+// the column is lane % 32.
+FAB_DEV int crow(int v, int g) { return 8 * (v >> 2) + 4 * g + (v & 3); }
+
+FAB_DEV f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+FAB_DEV float neg_inf() { return __int_as_float(kNegInfBits); }
+
+FAB_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+FAB_DEV float bf16_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
+
+FAB_DEV float load_scalar(const char* p, int type) {
+    if (type == FA_BACK_F32) return *(const float*)p;
+    if (type == FA_BACK_F16) return (float)*(const _Float16*)p;
+    return bf16_to_f32(*(const unsigned short*)p);
+}
+
+FAB_DEV float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+
+// Power-of-two exponent s so that amax * 2^s lies in [2^14, 2^15) (0 for an all-zero or
+// non-finite input), clamped to [-64, 64].
+FAB_DEV int prescale_exponent(float amax) {
+    if (!(amax > 0.0f) || !(amax < 3.0e38f)) return 0;
+    int e;
+    frexpf(amax, &e);   // amax = m * 2^e, m in [0.5, 1)
+    int s = 15 - e;
+    return s < -64 ? -64 : (s > 64 ? 64 : s);
+}
+
+// Exponent ks so that values bounded by b scaled by 2^-ks stay below 2^15.
+FAB_DEV int ds_exponent(float b) {
+    if (!(b > 0.0f) || !(b < 3.0e38f)) return 0;
+    int e;
+    frexpf(b, &e);      // b < 2^e
+    int ks = e - 15;
+    return ks < -100 ? -100 : (ks > 100 ? 100 : ks);
+}
+
+}  // namespace fab

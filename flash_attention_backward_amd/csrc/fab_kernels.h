@@ -1,0 +1,562 @@
+// Kernels of the flash-attention backward (gfx950, wave64, fp16 MFMA with fp32 accumulate).
+//
+// Row order inside a KV head hk: r = i*G + g for query row i of head h = hk*G + g, so the G
+// heads that share a K/V head sit in the same row tiles and share every K/V tile.
+//
+// Launch sequence (all on one stream):
+//   absmax   per-tensor max |q|, max |dO|           -> power-of-two prescale exponents
+//   prep     q, dO -> fp16 MFMA fragments (two layouts each) in the workspace
+//   qpass<0> walk 1 over keys: online softmax max/sum and delta numerator per row
+//   merge    fixed-order merge of the key-range splits -> LSE, delta (packed output)
+//   qpass<1> walk 2 over keys: dS = P (dP - delta), dQ += dS K
+//   dqreduce fixed-order sum of per-split dQ (only when the keys were split)
+//   kvpass   per 128-key tile: dV += P^T dO, dK += dS^T Q over every row of the group
+#pragma once
+
+#include "fab_common.h"
+#include "fab_tiles.h"
+
+namespace fab {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLn2 = 0.6931471805599453;
+
+// ----------------------------------------------------------------------------- absmax
+
+__global__ __launch_bounds__(kThreads) void absmax_kernel(Params p) {
+    __shared__ float red[2][kWaves];
+    float mq = 0.0f, md = 0.0f;
+    const int rows = p.N * p.H;
+    for (int row = blockIdx.x; row < rows; row += gridDim.x) {
+        // q row (i, h) and dO row (h, i) for the same linear index
+        const int i = row / p.H, h = row - (row / p.H) * p.H;
+        for (int c = threadIdx.x; c < p.D; c += kThreads) {
+            const float xq = load_scalar(p.q + c * p.q_nb0 + i * p.q_nb1 + h * p.q_nb2, p.q_type);
+            const float xd = load_scalar(p.d + c * p.d_nb0 + h * p.d_nb1 + i * p.d_nb2, p.d_type);
+            mq = fmaxf(mq, fabsf(xq));
+            md = fmaxf(md, fabsf(xd));
+        }
+    }
+    mq = wave_max(mq);
+    md = wave_max(md);
+    if ((threadIdx.x & 63) == 0) {
+        red[0][threadIdx.x >> 6] = mq;
+        red[1][threadIdx.x >> 6] = md;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float a = red[0][0], b = red[1][0];
+        for (int w = 1; w < kWaves; ++w) {
+            a = fmaxf(a, red[0][w]);
+            b = fmaxf(b, red[1][w]);
+        }
+        p.absmax_part[blockIdx.x] = a;
+        p.absmax_part[p.npart + blockIdx.x] = b;
+    }
+}
+
+// ----------------------------------------------------------------------------- prep
+
+// One workgroup per (hk, 32-row block). Writes, for q and for dO:
+//   *f: element (ks, lane, t) = X[row lane%32][d 16ks + 8(lane/32) + t]    (contraction over d)
+//   *t: element (md, rh, lane, t) = X[row 16rh + crow(t, lane/32)][d 32md + lane%32]
+//       (contraction over rows; crow(t, g) for t < 8 is the row of accumulator t)
+template <int D>
+__global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
+    constexpr int LD = D + 8;
+    __shared__ __attribute__((aligned(16))) _Float16 sQ[32 * LD];
+    __shared__ __attribute__((aligned(16))) _Float16 sD[32 * LD];
+    __shared__ float red[2][kWaves];
+
+    // exponents from the absmax partials (every block reduces them identically)
+    float aq = 0.0f, ad = 0.0f;
+    for (int t = threadIdx.x; t < p.npart; t += kThreads) {
+        aq = fmaxf(aq, p.absmax_part[t]);
+        ad = fmaxf(ad, p.absmax_part[p.npart + t]);
+    }
+    aq = wave_max(aq);
+    ad = wave_max(ad);
+    if ((threadIdx.x & 63) == 0) {
+        red[0][threadIdx.x >> 6] = aq;
+        red[1][threadIdx.x >> 6] = ad;
+    }
+    __syncthreads();
+    aq = red[0][0];
+    ad = red[1][0];
+    for (int w = 1; w < kWaves; ++w) {
+        aq = fmaxf(aq, red[0][w]);
+        ad = fmaxf(ad, red[1][w]);
+    }
+    const int eq = prescale_exponent(aq), edo = prescale_exponent(ad);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        p.scal[0] = eq;
+        p.scal[1] = edo;
+    }
+    const float fq = ldexpf(1.0f, eq), fd = ldexpf(1.0f, edo);
+
+    const int hk = blockIdx.x / p.RB, rb = blockIdx.x - (blockIdx.x / p.RB) * p.RB;
+    for (int idx = threadIdx.x; idx < 32 * D; idx += kThreads) {
+        const int rr = idx / D, c = idx - (idx / D) * D;
+        const int r = rb * 32 + rr;
+        float xq = 0.0f, xd = 0.0f;
+        if (r < p.R) {
+            const int i = r / p.G, g = r - (r / p.G) * p.G;
+            const int h = hk * p.G + g;
+            xq = load_scalar(p.q + c * p.q_nb0 + (int64_t)i * p.q_nb1 + (int64_t)h * p.q_nb2, p.q_type);
+            xd = load_scalar(p.d + c * p.d_nb0 + (int64_t)h * p.d_nb1 + (int64_t)i * p.d_nb2, p.d_type);
+        }
+        sQ[rr * LD + c] = (_Float16)(xq * fq);
+        sD[rr * LD + c] = (_Float16)(xd * fd);
+    }
+    __syncthreads();
+    const int64_t blk = ((int64_t)hk * p.RB + rb) * 32 * D;
+    // contraction-over-d fragments
+    for (int item = threadIdx.x; item < (D / 16) * 64; item += kThreads) {
+        const int ks = item >> 6, lane = item & 63;
+        const int row = lane & 31, d0 = 16 * ks + 8 * (lane >> 5);
+        *(f16x8*)(p.qf + blk + 8 * item) = *(const f16x8*)(sQ + row * LD + d0);
+        *(f16x8*)(p.df + blk + 8 * item) = *(const f16x8*)(sD + row * LD + d0);
+    }
+    // contraction-over-rows fragments
+    for (int item = threadIdx.x; item < (D / 32) * 2 * 64; item += kThreads) {
+        const int md = item >> 7, rh = (item >> 6) & 1, lane = item & 63;
+        const int dcol = 32 * md + (lane & 31), g = lane >> 5;
+        f16x8 a, b;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int row = 16 * rh + crow(t, g);
+            a[t] = sQ[row * LD + dcol];
+            b[t] = sD[row * LD + dcol];
+        }
+        *(f16x8*)(p.qt + blk + 8 * item) = a;
+        *(f16x8*)(p.dt + blk + 8 * item) = b;
+    }
+}
+
+// ----------------------------------------------------------------------------- helpers
+
+FAB_DEV float mask_value(const char* mrow, int type, int j) {
+    if (type == FA_BACK_F16) return (float)*(const _Float16*)(mrow + 2 * (int64_t)j);
+    return *(const float*)(mrow + 4 * (int64_t)j);
+}
+
+// dS exponent: every workgroup of a wave reduces the merge kernel's bound partials.
+FAB_DEV int load_ds_exponent(const Params& p) {
+    float b = 0.0f;
+    for (int t = threadIdx.x & 63; t < p.nbound; t += 64) b = fmaxf(b, p.bound_part[t]);
+    return ds_exponent(wave_max(b));
+}
+
+// ----------------------------------------------------------------------------- query side
+
+// Workgroup: one KV head, kWaves row blocks of 32 rows (one per wave), one key-range split.
+// Each wave keeps its rows' q and dO fragments in registers and walks the split's 64-key
+// tiles; K and V tiles are decoded once into LDS and shared by the four waves.
+// The 32x32 products are computed transposed, S^T = K Q^T, so a lane holds one query row
+// (column lane%32) and 16 keys; the two lanes l and l^32 together hold the row's 32 keys.
+template <int D, bool GRAD>
+__global__ __launch_bounds__(kThreads, 1) void qpass_kernel(Params p) {
+    using L = TileLds<D, kQTileKeys>;
+    constexpr int KS = D / 16;     // 16-deep steps of a contraction over d
+    constexpr int MD = D / 32;     // 32-wide d blocks of dQ
+    __shared__ __attribute__((aligned(16))) _Float16 sK[kQTileKeys * L::kLd];
+    __shared__ __attribute__((aligned(16))) _Float16 sV[kQTileKeys * L::kLd];
+    __shared__ __attribute__((aligned(16))) _Float16 sKT[GRAD ? D * L::kLdT : 8];
+    __shared__ __attribute__((aligned(16))) unsigned char sRawK[L::kRaw];
+    __shared__ __attribute__((aligned(16))) unsigned char sRawV[L::kRaw];
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l32 = lane & 31, g = lane >> 5;
+    const int hk = blockIdx.x % p.Hkv;
+    const int rt = blockIdx.x / p.Hkv;
+    const int split = blockIdx.y;
+    const int rb = rt * kWaves + wave;
+    const bool active = rb < p.RB;
+    const int rowsHK = p.RB * 32;
+    const int r = rb * 32 + l32;
+    const int i = r / p.G, gh = r - (r / p.G) * p.G;
+    const int h = hk * p.G + gh;
+    const bool row_ok = active && r < p.R;
+    const int ridx = hk * rowsHK + r;
+
+    const int eq = p.scal[0], edo = p.scal[1];
+    const float sc2 = p.scale * ldexpf(1.0f, -eq) * kLog2e;
+
+    f16x8 bq[KS], bd[KS];
+    if (active) {
+        const _Float16* fq = p.qf + ((int64_t)hk * p.RB + rb) * 32 * D;
+        const _Float16* fd = p.df + ((int64_t)hk * p.RB + rb) * 32 * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bq[ks] = *(const f16x8*)(fq + (ks * 64 + lane) * 8);
+            bd[ks] = *(const f16x8*)(fd + (ks * 64 + lane) * 8);
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) bq[ks][t] = bd[ks][t] = (_Float16)0.0f;
+    }
+    const bool has_mask = p.m_type != FA_BACK_NONE;
+    const char* mrow = (has_mask && row_ok)
+        ? p.mask + (int64_t)i * p.m_nb1 + (int64_t)(p.Hm == 1 ? 0 : h) * p.m_nb2 : nullptr;
+
+    // walk 1 state
+    float m_run = neg_inf();
+    double l64 = 0.0, d64 = 0.0;
+    float bmax = 0.0f;
+    // walk 2 state
+    float lse2 = neg_inf(), dlt = 0.0f, dsf = 1.0f;
+    int ksx = 0;
+    f32x16 dqacc[GRAD ? MD : 1];
+    if (GRAD) {
+        if (row_ok) {
+            lse2 = p.row_lse2[ridx];
+            dlt = p.row_dlt[ridx];
+        }
+        ksx = load_ds_exponent(p);
+        dsf = ldexpf(1.0f, -ksx);
+#pragma unroll
+        for (int md = 0; md < (GRAD ? MD : 1); ++md)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dqacc[md][v] = 0.0f;
+    }
+    const bool dead = (lse2 == neg_inf());
+
+    const int t0 = split * p.tiles_per_split;
+    const int t1 = min(p.KT, t0 + p.tiles_per_split);
+    for (int t = t0; t < t1; ++t) {
+        const int j0 = t * kQTileKeys;
+        __syncthreads();
+        stage_tile<D, kQTileKeys>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, sRawK);
+        stage_tile<D, kQTileKeys>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, sRawV);
+        __syncthreads();
+        decode_tile<D, kQTileKeys, GRAD>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, sRawK, sK, sKT);
+        decode_tile<D, kQTileKeys, false>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, sRawV, sV, nullptr);
+        __syncthreads();
+        if (!active) continue;
+
+        float s2[GRAD ? 1 : 32], dp[GRAD ? 1 : 32];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 sa, pa;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const f16x8 ak = *(const f16x8*)(sK + (32 * kb + l32) * L::kLd + 16 * ks + 8 * g);
+                const f16x8 av = *(const f16x8*)(sV + (32 * kb + l32) * L::kLd + 16 * ks + 8 * g);
+                sa = mfma32(ak, bq[ks], sa);
+                pa = mfma32(av, bd[ks], pa);
+                if (GRAD && (ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+            f16x8 bs[2];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int key = j0 + 32 * kb + crow(v, g);
+                float sv = sa[v] * sc2;
+                if (!row_ok || key >= p.M) sv = neg_inf();
+                else if (mrow) sv += mask_value(mrow, p.m_type, key) * kLog2e;
+                if (!GRAD) {
+                    s2[16 * kb + v] = sv;
+                    dp[16 * kb + v] = pa[v];
+                } else {
+                    const float pv = dead ? 0.0f : fast_exp2(sv - lse2);
+                    const float dsv = pv * (pa[v] - dlt);
+                    bs[v >> 3][v & 7] = (_Float16)(dsv * dsf);
+                }
+            }
+            if (GRAD) {
+#pragma unroll
+                for (int md = 0; md < MD; ++md) {
+#pragma unroll
+                    for (int rh = 0; rh < 2; ++rh) {
+                        const f16x8 a = *(const f16x8*)(sKT + (32 * md + l32) * L::kLdT + 32 * kb + 16 * rh + 8 * g);
+                        dqacc[md] = mfma32(a, bs[rh], dqacc[md]);
+                    }
+                    if ((md & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+
+        if (!GRAD) {
+            float tmax = neg_inf();
+#pragma unroll
+            for (int v = 0; v < 32; ++v) tmax = fmaxf(tmax, s2[v]);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float mnew = fmaxf(m_run, tmax);
+            if (mnew != neg_inf()) {
+                const float alpha = fast_exp2(m_run - mnew);
+                float ls = 0.0f, ds = 0.0f, bm = 0.0f;
+#pragma unroll
+                for (int v = 0; v < 32; ++v) {
+                    const float e = fast_exp2(s2[v] - mnew);
+                    ls += e;
+                    ds += e * dp[v];
+                    if (s2[v] != neg_inf()) bm = fmaxf(bm, fabsf(dp[v]));
+                }
+                l64 = l64 * (double)alpha + (double)ls;
+                d64 = d64 * (double)alpha + (double)ds;
+                m_run = mnew;
+                bmax = fmaxf(bmax, bm);
+            }
+        }
+    }
+
+    if (!active) return;
+    if (!GRAD) {
+        const double lo = l64 + __shfl_xor(l64, 32);
+        const double dd = d64 + __shfl_xor(d64, 32);
+        const float bb = fmaxf(bmax, __shfl_xor(bmax, 32));
+        if (g == 0) {
+            const int64_t idx = (int64_t)split * p.Hkv * rowsHK + ridx;
+            p.part_m[idx] = m_run;
+            p.part_l[idx] = lo;
+            p.part_d[idx] = dd;
+            p.part_b[idx] = bb;
+        }
+    } else if (row_ok) {
+        if (p.splits == 1) {
+            const float fac = p.scale * ldexpf(1.0f, ksx - edo);
+            float* dst = p.dq + ((int64_t)h * p.N + i) * D;
+#pragma unroll
+            for (int md = 0; md < MD; ++md)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    f32x4 o = {dqacc[md][4 * b] * fac, dqacc[md][4 * b + 1] * fac,
+                               dqacc[md][4 * b + 2] * fac, dqacc[md][4 * b + 3] * fac};
+                    *(f32x4*)(dst + 32 * md + 8 * b + 4 * g) = o;
+                }
+        } else {
+            float* dst = p.dq_part + ((int64_t)split * p.Hkv * rowsHK + ridx) * D;
+#pragma unroll
+            for (int md = 0; md < MD; ++md)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    f32x4 o = {dqacc[md][4 * b], dqacc[md][4 * b + 1], dqacc[md][4 * b + 2],
+                               dqacc[md][4 * b + 3]};
+                    *(f32x4*)(dst + 32 * md + 8 * b + 4 * g) = o;
+                }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------- merge
+
+// One thread per row of every KV head: merge the splits in order, write LSE and delta.
+__global__ __launch_bounds__(kThreads) void merge_kernel(Params p) {
+    __shared__ float red[kWaves];
+    const int rowsHK = p.RB * 32;
+    const int total = p.Hkv * rowsHK;
+    float bmax = 0.0f;
+    for (int ridx = blockIdx.x * kThreads + threadIdx.x; ridx < total; ridx += gridDim.x * kThreads) {
+        float mx = neg_inf();
+        for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.part_m[(int64_t)s * total + ridx]);
+        float lse2 = neg_inf();
+        double dl = 0.0, lnat = 0.0;
+        float b = 0.0f;
+        if (mx != neg_inf()) {
+            double Ls = 0.0, Ds = 0.0;
+            for (int s = 0; s < p.splits; ++s) {
+                const int64_t idx = (int64_t)s * total + ridx;
+                const float m = p.part_m[idx];
+                if (m != neg_inf()) {
+                    const double f = exp2((double)m - (double)mx);
+                    Ls += p.part_l[idx] * f;
+                    Ds += p.part_d[idx] * f;
+                }
+                b = fmaxf(b, p.part_b[idx]);
+            }
+            const double l2 = (double)mx + log2(Ls);
+            lse2 = (float)l2;
+            lnat = l2 * kLn2;
+            dl = Ds / Ls;
+            b += fabsf((float)dl);
+        }
+        p.row_lse2[ridx] = lse2;
+        p.row_dlt[ridx] = (float)dl;
+        bmax = fmaxf(bmax, b);
+        const int hk = ridx / rowsHK, r = ridx - (ridx / rowsHK) * rowsHK;
+        if (r < p.R) {
+            const int i = r / p.G, g = r - (r / p.G) * p.G;
+            const int h = hk * p.G + g;
+            const int edo = p.scal[1];
+            p.lse[(int64_t)h * p.N + i] = (mx == neg_inf()) ? neg_inf() : (float)lnat;
+            p.delta[(int64_t)h * p.N + i] = (float)ldexp(dl, -edo);
+        }
+    }
+    bmax = wave_max(bmax);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = bmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = red[0];
+        for (int w = 1; w < kWaves; ++w) b = fmaxf(b, red[w]);
+        p.bound_part[blockIdx.x] = b;
+    }
+}
+
+// ----------------------------------------------------------------------------- dQ reduce
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void dqreduce_kernel(Params p) {
+    const int rowsHK = p.RB * 32;
+    const int64_t total = (int64_t)p.Hkv * rowsHK;
+    const int ksx = load_ds_exponent(p);
+    const float fac = p.scale * ldexpf(1.0f, ksx - p.scal[1]);
+    const int64_t n4 = total * (D / 4);
+    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n4; e += (int64_t)gridDim.x * kThreads) {
+        const int64_t ridx = e / (D / 4);
+        const int c4 = (int)(e - ridx * (D / 4));
+        const int hk = (int)(ridx / rowsHK), r = (int)(ridx - (ridx / rowsHK) * rowsHK);
+        if (r >= p.R) continue;
+        f32x4 acc = *(const f32x4*)(p.dq_part + ridx * D + 4 * c4);
+        for (int s = 1; s < p.splits; ++s) {
+            const f32x4 x = *(const f32x4*)(p.dq_part + ((int64_t)s * total + ridx) * D + 4 * c4);
+            acc += x;
+        }
+        const int i = r / p.G, g = r - (r / p.G) * p.G;
+        const int h = hk * p.G + g;
+        *(f32x4*)(p.dq + ((int64_t)h * p.N + i) * D + 4 * c4) = acc * fac;
+    }
+}
+
+// ----------------------------------------------------------------------------- key side
+
+// Workgroup: one KV head, 128 keys (32 per wave). Each wave keeps its keys' K and V
+// fragments and its dK^T, dV^T accumulators in registers and walks every 32-row block of the
+// group: S = Q K^T and dP = dO V^T put one key per lane column and 16 rows per lane, which
+// is the layout the second operand of dV^T += dO^T P and dK^T += Q^T dS needs.
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void kvpass_kernel(Params p) {
+    using L = TileLds<D, kQTileKeys>;
+    constexpr int KS = D / 16;
+    constexpr int MD = D / 32;
+    __shared__ __attribute__((aligned(16))) _Float16 sK[kQTileKeys * L::kLd];
+    __shared__ __attribute__((aligned(16))) _Float16 sV[kQTileKeys * L::kLd];
+    __shared__ __attribute__((aligned(16))) unsigned char sRawK[L::kRaw];
+    __shared__ __attribute__((aligned(16))) unsigned char sRawV[L::kRaw];
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l32 = lane & 31, g = lane >> 5;
+    const int hk = blockIdx.x % p.Hkv;
+    const int kvt = blockIdx.x / p.Hkv;
+    const int key0 = kvt * kKVKeys;
+    const int myj = key0 + 32 * wave + l32;
+    const bool key_ok = myj < p.M;
+
+    // K and V fragments: B[d][key] of S = Q K^T, i.e. K[key][16ks + 8g .. +7]
+    f16x8 bk[KS], bv[KS];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int j0 = key0 + half * kQTileKeys;
+        __syncthreads();
+        stage_tile<D, kQTileKeys>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, sRawK);
+        stage_tile<D, kQTileKeys>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, sRawV);
+        __syncthreads();
+        decode_tile<D, kQTileKeys, false>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, sRawK, sK, nullptr);
+        decode_tile<D, kQTileKeys, false>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, sRawV, sV, nullptr);
+        __syncthreads();
+        if ((wave >> 1) == half) {
+            const int lk = 32 * (wave & 1) + l32;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                bk[ks] = *(const f16x8*)(sK + lk * L::kLd + 16 * ks + 8 * g);
+                bv[ks] = *(const f16x8*)(sV + lk * L::kLd + 16 * ks + 8 * g);
+            }
+        }
+    }
+
+    const int eq = p.scal[0], edo = p.scal[1];
+    const float sc2 = p.scale * ldexpf(1.0f, -eq) * kLog2e;
+    const int ksx = load_ds_exponent(p);
+    const float dsf = ldexpf(1.0f, -ksx);
+    const float pf = ldexpf(1.0f, kPScaleLog2);
+    const bool has_mask = p.m_type != FA_BACK_NONE;
+    const int rowsHK = p.RB * 32;
+
+    f32x16 dkacc[MD], dvacc[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dkacc[md][v] = dvacc[md][v] = 0.0f;
+
+    for (int rb = 0; rb < p.RB; ++rb) {
+        const int64_t blk = ((int64_t)hk * p.RB + rb) * 32 * D;
+        const float* lrow = p.row_lse2 + (int64_t)hk * rowsHK + 32 * rb;
+        const float* drow = p.row_dlt + (int64_t)hk * rowsHK + 32 * rb;
+        f32x4 l4[4], d4[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            l4[b] = *(const f32x4*)(lrow + 8 * b + 4 * g);
+            d4[b] = *(const f32x4*)(drow + 8 * b + 4 * g);
+        }
+        f32x16 sa, pa;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const f16x8 aq = *(const f16x8*)(p.qf + blk + (ks * 64 + lane) * 8);
+            const f16x8 ad = *(const f16x8*)(p.df + blk + (ks * 64 + lane) * 8);
+            sa = mfma32(aq, bk[ks], sa);
+            pa = mfma32(ad, bv[ks], pa);
+        }
+        f16x8 bp[2], bs[2];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = 32 * rb + crow(v, g);
+            const float l2 = l4[v >> 2][v & 3];
+            float pv = 0.0f;
+            if (key_ok && l2 != neg_inf()) {
+                float sv = sa[v] * sc2;
+                if (has_mask) {
+                    const int i = r / p.G, gh = r - (r / p.G) * p.G;
+                    const int h = hk * p.G + gh;
+                    const char* mrow = p.mask + (int64_t)i * p.m_nb1 + (int64_t)(p.Hm == 1 ? 0 : h) * p.m_nb2;
+                    sv += mask_value(mrow, p.m_type, myj) * kLog2e;
+                }
+                pv = fast_exp2(sv - l2);
+            }
+            const float dsv = pv * (pa[v] - d4[v >> 2][v & 3]);
+            bp[v >> 3][v & 7] = (_Float16)(pv * pf);
+            bs[v >> 3][v & 7] = (_Float16)(dsv * dsf);
+        }
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+#pragma unroll
+            for (int rh = 0; rh < 2; ++rh) {
+                const int64_t off = blk + ((int64_t)(md * 2 + rh) * 64 + lane) * 8;
+                const f16x8 adt = *(const f16x8*)(p.dt + off);
+                const f16x8 aqt = *(const f16x8*)(p.qt + off);
+                dvacc[md] = mfma32(adt, bp[rh], dvacc[md]);
+                dkacc[md] = mfma32(aqt, bs[rh], dkacc[md]);
+            }
+        }
+    }
+
+    if (!key_ok) return;
+    const float fk = p.scale * ldexpf(1.0f, ksx - eq - edo);
+    const float fv = ldexpf(1.0f, -kPScaleLog2 - edo);
+    float* dkr = p.dk + ((int64_t)hk * p.M + myj) * D;
+    float* dvr = p.dv + ((int64_t)hk * p.M + myj) * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            f32x4 ok = {dkacc[md][4 * b] * fk, dkacc[md][4 * b + 1] * fk, dkacc[md][4 * b + 2] * fk,
+                        dkacc[md][4 * b + 3] * fk};
+            f32x4 ov = {dvacc[md][4 * b] * fv, dvacc[md][4 * b + 1] * fv, dvacc[md][4 * b + 2] * fv,
+                        dvacc[md][4 * b + 3] * fv};
+            *(f32x4*)(dkr + 32 * md + 8 * b + 4 * g) = ok;
+            *(f32x4*)(dvr + 32 * md + 8 * b + 4 * g) = ov;
+        }
+}
+
+// ----------------------------------------------------------------------------- fills
+
+// Degenerate shapes: N == 0 (dK = dV = 0) or M == 0 (every row fully masked).
+__global__ __launch_bounds__(kThreads) void fill_kernel(float* a, int64_t n, float val) {
+    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += (int64_t)gridDim.x * kThreads)
+        a[e] = val;
+}
+
+}  // namespace fab

@@ -1,0 +1,131 @@
+/*
+ * fa_back.h -- flash-attention backward (FLASH_ATTN_BACK) on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "CambrianTech/llama.cpp PR #63", first review, "The math in
+ * fattn_back_q" and "The math in fattn_back_kv"): for query heads h with KV head
+ * hk = h / (H / Hkv), query rows i and keys j,
+ *     s_ij    = scale * q_i . k_j + mask[j, i, h % Hm]          (mask optional)
+ *     lse_i   = log sum_j exp(s_ij)                              (-inf if every s_ij = -inf)
+ *     p_ij    = exp(s_ij - lse_i)                                (0 on a fully masked row)
+ *     dp_ij   = dO_i . v_j
+ *     delta_i = sum_j p_ij dp_ij          ( = rowsum(dO o O), O is never formed )
+ *     dS_ij   = p_ij (dp_ij - delta_i)
+ *     dQ_i    = scale * sum_j dS_ij k_j
+ *     dK_j    = scale * sum_{h in group(hk), i} dS_ij q_i
+ *     dV_j    =         sum_{h in group(hk), i} p_ij dO_i
+ * The N x M score matrix is never stored and the K/V cache is never converted as a whole:
+ * each K/V tile is decoded once per workgroup into on-chip memory.
+ *
+ * Tensors are described ggml-style: ne[] are extents innermost first, nb[] byte strides.
+ *     q    ne = {D,  N, H  }   F32 | F16 | BF16
+ *     k    ne = {D,  M, Hkv}   F32 | F16 | BF16 | Q8_0   (K and V types are independent)
+ *     v    ne = {Dv, M, Hkv}   F32 | F16 | BF16 | Q8_0
+ *     d    ne = {Dv, H, N  }   F32 | F16 | BF16          (dO; note the H, N order, as the
+ *                                                         operator's "Layout and shape" states)
+ *     mask ne = {M,  N, Hm }   F32 | F16, Hm in {1, H}; type FA_BACK_NONE for no mask
+ * nb[0] must equal the element size (34 bytes per 32-value block for Q8_0), i.e. each row
+ * is contiguous; rows and heads may have any positive stride (e.g. a cache view whose heads
+ * are interleaved per cell). A Q8_0 block is a little-endian fp16 scale followed by 32 int8;
+ * its value is scale * int8.
+ *
+ * Output: one packed F32 buffer, laid out as the operator's packed result (first review,
+ * "Layout and shape"; second review, output index):
+ *     dQ    at off_dq    [D,  N, H  ]  element (c, i, h)  at ((h*N + i)*D + c)
+ *     dK    at off_dk    [D,  M, Hkv]  element (c, j, hk) at ((hk*M + j)*D + c)
+ *     dV    at off_dv    [Dv, M, Hkv]  element (c, j, hk) at ((hk*M + j)*Dv + c)
+ *     LSE   at off_lse   N*H floats, row h*N + i (natural log; -inf for a fully masked row)
+ *     delta at off_delta = off_lse + 4*N*H bytes, N*H floats, row h*N + i
+ * Regions start 256-byte aligned (except delta, which directly follows LSE); bytes between
+ * regions are unspecified. Every defined byte is written by every run.
+ *
+ * Numerics: every product runs on fp16 MFMA with fp32 accumulation; Q and dO are scaled by
+ * exact powers of two before rounding to fp16, P by 2^15 and dS by a power of two derived
+ * from the data, and all scaling is undone exactly in fp32. The per-row softmax sums and
+ * delta are carried across key tiles in fp64. K and V values must lie within fp16 range
+ * (|x| < 65504). Inputs holding NaN or +-inf (other than -inf mask entries) give undefined
+ * results. Results are bitwise reproducible for the same inputs and device type: every
+ * output element has exactly one writer and every reduction runs in a fixed order; no
+ * atomics are used.
+ *
+ * Supported: D == Dv in {64, 128, 256}; H % Hkv == 0; N, M >= 0 (N == 0: dK = dV = 0;
+ * M == 0: every row is fully masked); F32/F16/BF16 K or V rows 16-byte aligned (base and
+ * strides); Q8_0 rows 2-byte aligned.
+ */
+#ifndef FA_BACK_H
+#define FA_BACK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define FA_BACK_NONE (-1)
+#define FA_BACK_F32 0
+#define FA_BACK_F16 1
+#define FA_BACK_BF16 2
+#define FA_BACK_Q8_0 8
+
+/* status codes (no entry point aborts or exits) */
+#define FA_BACK_OK 0
+#define FA_BACK_EINVAL (-1)       /* null pointer, negative extent, non-finite scale        */
+#define FA_BACK_ESHAPE (-2)       /* extents disagree (D, Dv, N, M, H % Hkv, Hm, q8_0 width) */
+#define FA_BACK_ESTRIDE (-3)      /* nb[0] != element size, zero stride, misaligned stride  */
+#define FA_BACK_EUNSUPPORTED (-4) /* type combination, D/Dv, size limit, device not gfx950  */
+#define FA_BACK_EHIP (-5)         /* a HIP runtime call or kernel launch failed             */
+#define FA_BACK_EALIGN (-6)       /* a device pointer passed to fa_back_run is misaligned   */
+
+typedef struct {
+    int32_t type;    /* FA_BACK_* element type */
+    int64_t ne[3];   /* extents, innermost first */
+    int64_t nb[3];   /* byte strides */
+} fa_back_tensor;
+
+typedef struct {
+    fa_back_tensor q, k, v, d, mask;   /* mask.type == FA_BACK_NONE: no mask */
+    float scale;                        /* softmax scale, e.g. 1/sqrt(D) */
+} fa_back_desc;
+
+typedef struct {
+    uint64_t off_dq, off_dk, off_dv, off_lse, off_delta;  /* byte offsets in `out` */
+    uint64_t out_bytes;        /* size the caller allocates for `out` */
+    uint64_t workspace_bytes;  /* device scratch the caller allocates for `workspace` */
+} fa_back_layout;
+
+typedef struct fa_back_plan fa_back_plan;
+
+/* Validate a descriptor and compute the output layout and workspace size. Touches no
+ * device, so it runs on a host without a GPU. Returns FA_BACK_OK or an error code;
+ * `layout` is written only on success. */
+int fa_back_layout_query(const fa_back_desc* desc, fa_back_layout* layout);
+
+/* Validate `desc` (before touching the device), check that `device` is a gfx950 GPU with
+ * enough LDS, and build an immutable plan. On success *plan owns host memory only and
+ * `layout` (if non-NULL) receives the same layout as fa_back_layout_query. On failure
+ * *plan is set to NULL. */
+int fa_back_create(const fa_back_desc* desc, int device, fa_back_plan** plan,
+                   fa_back_layout* layout);
+
+/* Enqueue the backward on `stream` (a hipStream_t; NULL = the default stream) of the
+ * plan's device. q, k, v, d, mask are device pointers to the first element of each view
+ * (mask must be NULL iff the plan has no mask); out (layout.out_bytes) and workspace
+ * (layout.workspace_bytes) are device buffers owned by the caller, 256-byte aligned, kept
+ * alive until the stream has finished the work. The call allocates nothing, does not
+ * synchronise, and the plan may be shared by concurrent runs that use distinct out and
+ * workspace buffers. Workspace contents need not be initialised and are clobbered. */
+int fa_back_run(const fa_back_plan* plan, const void* q, const void* k, const void* v,
+                const void* d, const void* mask, void* out, void* workspace, void* stream);
+
+/* Free a plan (NULL is allowed). */
+void fa_back_destroy(fa_back_plan* plan);
+
+/* Static text for a status code. */
+const char* fa_back_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_BACK_H */

@@ -104,7 +104,7 @@ def flash_attn_back(q, k, v, do, mask, scale):
         S = sc * (q[h] @ Kh.T)                     # (N, M)
         if mask is not None:
             S = S + mask[h % Hm]
-        m = S.max(axis=1)
+        m = S.max(axis=1, initial=NEG_INF)         # a row with no keys counts as masked
         dead = ~np.isfinite(m)                     # every entry of the row is -inf
         m_safe = np.where(dead, 0.0, m)
         ssum = np.exp(S - m_safe[:, None]).sum(axis=1)
@@ -136,7 +136,7 @@ def _row_block(q, k, v, do, mask, sc, h, rows, G, Hm):
     S = sc * (q[h, rows] @ k[hk].T)
     if mask is not None:
         S = S + mask[h % Hm][rows]
-    m = S.max(axis=1)
+    m = S.max(axis=1, initial=NEG_INF)
     dead = ~np.isfinite(m)
     m_safe = np.where(dead, 0.0, m)
     ssum = np.exp(S - m_safe[:, None]).sum(axis=1)

@@ -1,0 +1,145 @@
+"""The C ABI on a host without a GPU: the library loads, exports every declared entry point,
+validates descriptors with the documented status codes and computes the packed layout."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import fa_inputs
+import flash_attention_backward_amd as fab
+from flash_attention_backward_amd import fa_back as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "fa_back.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(fa_back_\w+)\s*\(", txt, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("fa_back_create", "fa_back_run", "fa_back_destroy", "fa_back_layout_query",
+              "fa_back_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fab.load_library()
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def _desc(name="c1"):
+    return B.describe(fa_inputs.make(name))
+
+
+@pytest.mark.parametrize("name", ["c0", "c1", "c1_strided", "c2b", "c3"])
+def test_layout(name):
+    p = fa_inputs.make(name)
+    lay = fab.fa_back_layout_query(B.describe(p))
+    assert lay.off_dq == 0
+    assert lay.off_dk % 256 == 0 and lay.off_dv % 256 == 0 and lay.off_lse % 256 == 0
+    assert lay.off_dk >= 4 * p.D * p.N * p.H
+    assert lay.off_dv >= lay.off_dk + 4 * p.D * p.M * p.Hkv
+    assert lay.off_lse >= lay.off_dv + 4 * p.Dv * p.M * p.Hkv
+    assert lay.off_delta == lay.off_lse + 4 * p.N * p.H
+    assert lay.out_bytes >= lay.off_delta + 4 * p.N * p.H and lay.out_bytes % 256 == 0
+    assert lay.workspace_bytes > 0
+
+
+def _expect(rc, mutate, name="c1"):
+    d = _desc(name)
+    mutate(d)
+    lay = B.Layout()
+    got = fab.load_library().fa_back_layout_query(ctypes.byref(d), ctypes.byref(lay))
+    assert got == rc, (got, rc)
+
+
+def test_validation_codes():
+    _expect(B.OK, lambda d: None)
+    _expect(B.EUNSUPPORTED, lambda d: setattr(d.q, "type", B.Q8_0))
+    _expect(B.EUNSUPPORTED, lambda d: setattr(d.mask, "type", B.BF16))
+    _expect(B.EINVAL, lambda d: setattr(d, "scale", float("nan")))
+
+    def neg(d): d.q.ne[1] = -1
+    _expect(B.EINVAL, neg)
+
+    def dmis(d): d.k.ne[0] = 64
+    _expect(B.ESHAPE, dmis)
+
+    def hmis(d):
+        d.k.ne[2] = 3; d.v.ne[2] = 3
+    _expect(B.ESHAPE, hmis)
+
+    def nmis(d): d.d.ne[2] = 63
+    _expect(B.ESHAPE, nmis)
+
+    def nb0(d): d.q.nb[0] = 8
+    _expect(B.ESTRIDE, nb0)
+
+    def zero_stride(d): d.k.nb[1] = 0
+    _expect(B.ESTRIDE, zero_stride)
+
+    def odd_q8(d): d.k.nb[1] = 137
+    _expect(B.ESTRIDE, odd_q8)
+
+    def dv_differs(d):
+        d.v.ne[0] = 64; d.d.ne[0] = 64; d.v.nb[1] = 68; d.v.nb[2] = 68 * d.v.ne[1]
+    _expect(B.EUNSUPPORTED, dv_differs)
+
+    def q8_width(d):
+        for t in (d.q, d.k, d.v, d.d):
+            t.ne[0] = 48
+    _expect(B.ESHAPE, q8_width)
+
+
+def test_validation_mask_and_kv_alignment():
+    def hm3(d): d.mask.ne[2] = 3
+    _expect(B.ESHAPE, hm3, "c1_causal")
+
+    def mask_m(d): d.mask.ne[0] = 100
+    _expect(B.ESHAPE, mask_m, "c1_causal")
+
+    def f16_rows_unaligned(d): d.k.nb[1] = 264
+    _expect(B.ESTRIDE, f16_rows_unaligned, "c1_f16kv")
+
+    def unsupported_d(d):
+        for t in (d.q, d.k, d.v, d.d):
+            t.ne[0] = 96
+        d.q.nb[1] = 4 * 96; d.q.nb[2] = 4 * 96 * 64
+    _expect(B.EUNSUPPORTED, unsupported_d, "c1_f32kv")
+
+
+def test_null_arguments():
+    lib = fab.load_library()
+    lay = B.Layout()
+    assert lib.fa_back_layout_query(None, ctypes.byref(lay)) == B.EINVAL
+    d = _desc()
+    assert lib.fa_back_layout_query(ctypes.byref(d), None) == B.EINVAL
+    assert lib.fa_back_create(ctypes.byref(d), 0, None, None) == B.EINVAL
+    assert lib.fa_back_run(None, *([None] * 8)) == B.EINVAL
+    lib.fa_back_destroy(None)
+
+
+def test_create_without_gpu_reports_unsupported():
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    lib = fab.load_library()
+    d = _desc()
+    plan = ctypes.c_void_p(1234)
+    rc = lib.fa_back_create(ctypes.byref(d), 0, ctypes.byref(plan), None)
+    assert rc == B.EUNSUPPORTED
+    assert not plan.value
+
+
+def test_status_strings():
+    assert fab.status_string(0) == "ok"
+    assert "shape" in fab.status_string(-2)
+    assert fab.status_string(12345) == "unknown status"
