@@ -1,0 +1,157 @@
+#!/usr/bin/env python3
+"""Benchmark of the flash-attention backward on one MI355X.
+
+Workload (default): the long-cache causal-tail case, N=2048 query rows against an M=75520
+cache, H=24 query heads over Hkv=4 KV heads (GQA 6), D=Dv=256, q8_0 K/V, F32 Q/dO drawn
+N(0,1), F16 causal-tail mask (query i sees keys j <= M-N+i), scale 1/16, seed 0.
+
+A step is one fa_back_run (every kernel of the backward) on inputs already resident in HBM.
+W warmup steps, then K timed steps between device synchronisations. Each timed step goes
+through fa_back_run_timed, which records HIP events on the launch stream between the
+library's kernels, so the dominant kernel's average duration is measured live over the
+timed region. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c4n16|c3|...]
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn-backward TFLOP/s + ms/call, q8_0 H24/Hkv4/D256 N2048 M75520"
+PEAK_MFMA_F16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+# matrix-product work per visible (row, key, head) triple, per phase (D = Dv)
+PHASE_FLOPS_PER_PAIR_PER_D = {"walk1": 4, "walk2": 6, "kvpass": 8}
+KERNEL_NAMES = {"walk1": "qpass_kernel<D, false>", "walk2": "qpass_kernel<D, true>",
+                "kvpass": "kvpass_kernel<D>"}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def describe_workload(p):
+    mask = "none" if p.mask is None else f"causal-tail {p.mask_type}"
+    return (f"{p.name}: N{p.N} M{p.M} H{p.H} Hkv{p.Hkv} D{p.D} K {p.k_type} V {p.v_type} "
+            f"Q/dO {p.q_type} mask {mask}")
+
+
+def cpu_baseline(rows: int):
+    """Time the float64 oracle on a bounded sample of the same workload: the last `rows`
+    query rows of every head against the whole cache (same draws, same mask rows)."""
+    import numpy as np
+    import fa_inputs
+    from oracle import fa_back_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    name = {8: "c4n8", 16: "c4n16"}.get(rows)
+    if name:
+        s = fa_inputs.make(name)
+    else:
+        full = fa_inputs.make("c4")
+        s = full
+        s.name = f"c4 last {rows} rows"
+        s.q = np.ascontiguousarray(full.q[:, full.N - rows:, :])
+        s.d = np.ascontiguousarray(full.d[full.N - rows:, :, :])
+        s.mask = np.ascontiguousarray(full.mask[:, full.N - rows:, :])
+        s.N = rows
+    f = fa_inputs.flop_count(s)
+    log(f"cpu baseline: oracle on {s.name} ({f['full'] / 1e9:.1f} GFLOP counted), {threads} BLAS threads")
+    t0 = time.perf_counter()
+    O.run_problem(s)
+    dt = time.perf_counter() - t0
+    log(f"cpu baseline: {dt:.2f} s")
+    return {"value": f["full"] / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"float64 numpy oracle on the last {rows} query rows of all {s.H} heads against "
+                      f"the full M={s.M} cache (same inputs and mask rows); value = that sample's "
+                      f"counted FLOPs / oracle wall time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c4")
+    ap.add_argument("--cpu-rows", type=int, default=64, help="query rows in the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this implementation runs on one GPU; multi-GPU runs are not supported "
+              f"(got --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fa_inputs
+    import flash_attention_backward_amd as fab
+
+    log(f"generating {args.workload} inputs")
+    p = fa_inputs.make(args.workload)
+    flops = fa_inputs.flop_count(p)
+    log(f"{describe_workload(p)}; visible pairs {flops['visible']:,}; {flops['full'] / 1e12:.3f} TFLOP")
+    dev = torch.device("cuda:0")
+    dp = fab.DeviceProblem(p, dev, poison=False)
+    stream = torch.cuda.current_stream(dev)
+    log(f"warmup x{args.warmup}")
+    for _ in range(args.warmup):
+        dp.run()
+    torch.cuda.synchronize()
+    log(f"timing x{args.steps}")
+    phases = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        phases.append(dp.run_timed(stream))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    mean_phase = {n: statistics.fmean(ph[k] for ph in phases) for k, n in enumerate(fab.fa_back.PHASES)}
+    log("phase ms: " + " ".join(f"{k}={v:.3f}" for k, v in mean_phase.items()))
+
+    dom = max(PHASE_FLOPS_PER_PAIR_PER_D, key=lambda n: mean_phase[n])
+    dom_flops = PHASE_FLOPS_PER_PAIR_PER_D[dom] * p.D * flops["visible"]
+    achieved = dom_flops / (mean_phase[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_F16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4), "traffic": None,
+                "kernel": KERNEL_NAMES[dom].replace("D", str(p.D), 1), "phase": dom,
+                "flops_per_launch": dom_flops, "avg_launch_ms": round(mean_phase[dom], 4)}
+    value = flops["full"] / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC if args.workload == "c4" else f"attn-backward TFLOP/s + ms/call, {args.workload}",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": describe_workload(p), "N": p.N, "M": p.M, "H": p.H, "Hkv": p.Hkv,
+                   "D": p.D, "Dv": p.Dv, "q_type": p.q_type, "k_type": p.k_type, "v_type": p.v_type,
+                   "mask": p.mask_type, "seed": p.seed},
+        "flops": {"count": "2*V*(5D+4Dv), V = visible (row, key, head) triples",
+                  "visible": flops["visible"], "full": flops["full"], "five_gemm": flops["five"],
+                  "tflops_five_gemm": round(flops["five"] / (ms * 1e-3) / 1e12, 3)},
+        "phase_ms": {k: round(v, 4) for k, v in mean_phase.items()},
+        "roofline": roofline,
+    }
+    dp.close()
+    del dp
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline and args.workload == "c4":
+        rec["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -148,8 +148,18 @@ int validate(const fa_back_desc* d, Geometry* g) {
     return FA_BACK_OK;
 }
 
+// Records an event after each phase when `ev` is non-NULL (ev[0] is recorded by the caller
+// before the first phase). Phases: absmax, prep, walk 1, merge, walk 2, dQ reduce, key side.
+struct PhaseMarks {
+    hipEvent_t* ev;
+    hipStream_t st;
+    void mark(int phase) const {
+        if (ev) (void)hipEventRecord(ev[phase + 1], st);
+    }
+};
+
 template <int D>
-int launch_all(const Geometry& g, Params& P, hipStream_t st) {
+int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& pm) {
     if (g.N == 0 || g.M == 0) {
         // degenerate: zero dK, dV (N == 0) or every row fully masked (M == 0)
         const int64_t nk = (int64_t)g.D * g.M * g.Hkv;
@@ -160,19 +170,27 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st) {
         const int64_t nr = (int64_t)g.N * g.H;
         if (nr) hipLaunchKernelGGL(fill_kernel, dim3(64), dim3(kThreads), 0, st, P.lse, nr, -INFINITY);
         if (nr) hipLaunchKernelGGL(fill_kernel, dim3(64), dim3(kThreads), 0, st, P.delta, nr, 0.0f);
+        for (int ph = 0; ph < FA_BACK_NUM_PHASES; ++ph) pm.mark(ph);
         return hipGetLastError() == hipSuccess ? FA_BACK_OK : FA_BACK_EHIP;
     }
     hipLaunchKernelGGL(absmax_kernel, dim3(g.npart), dim3(kThreads), 0, st, P);
+    pm.mark(0);
     hipLaunchKernelGGL(prep_kernel<D>, dim3(g.Hkv * g.RB), dim3(kThreads), 0, st, P);
+    pm.mark(1);
     hipLaunchKernelGGL((qpass_kernel<D, false>), dim3(g.RT * g.Hkv, g.splits), dim3(kThreads), 0, st, P);
+    pm.mark(2);
     hipLaunchKernelGGL(merge_kernel, dim3(g.nbound), dim3(kThreads), 0, st, P);
+    pm.mark(3);
     hipLaunchKernelGGL((qpass_kernel<D, true>), dim3(g.RT * g.Hkv, g.splits), dim3(kThreads), 0, st, P);
+    pm.mark(4);
     if (g.splits > 1) {
         const int64_t n4 = (int64_t)g.Hkv * g.RB * 32 * (D / 4);
         const int blocks = (int)std::min<int64_t>(4096, (n4 + kThreads - 1) / kThreads);
         hipLaunchKernelGGL(dqreduce_kernel<D>, dim3(blocks), dim3(kThreads), 0, st, P);
     }
+    pm.mark(5);
     hipLaunchKernelGGL(kvpass_kernel<D>, dim3(g.KVT * g.Hkv), dim3(kThreads), 0, st, P);
+    pm.mark(6);
     return hipGetLastError() == hipSuccess ? FA_BACK_OK : FA_BACK_EHIP;
 }
 
@@ -230,8 +248,9 @@ int fa_back_create(const fa_back_desc* desc, int device, fa_back_plan** plan, fa
 
 void fa_back_destroy(fa_back_plan* plan) { delete plan; }
 
-int fa_back_run(const fa_back_plan* plan, const void* q, const void* k, const void* v, const void* d,
-                const void* mask, void* out, void* workspace, void* stream) {
+static int run_impl(const fa_back_plan* plan, const void* q, const void* k, const void* v,
+                    const void* d, const void* mask, void* out, void* workspace, void* stream,
+                    float* phase_ms) {
     if (!plan || !out || !workspace) return FA_BACK_EINVAL;
     const fa_back_desc& ds = plan->desc;
     const Geometry& g = plan->geo;
@@ -294,15 +313,44 @@ int fa_back_run(const fa_back_plan* plan, const void* q, const void* k, const vo
     P.dq_part = (float*)(w + g.ws_dqp);
 
     hipStream_t st = (hipStream_t)stream;
-    int rc;
-    switch (g.D) {
-        case 64: rc = launch_all<64>(g, P, st); break;
-        case 128: rc = launch_all<128>(g, P, st); break;
-        case 256: rc = launch_all<256>(g, P, st); break;
-        default: rc = FA_BACK_EUNSUPPORTED;
+    hipEvent_t ev[FA_BACK_NUM_PHASES + 1];
+    int nev = 0;
+    PhaseMarks pm{nullptr, st};
+    int rc = FA_BACK_OK;
+    if (phase_ms) {
+        for (; nev <= FA_BACK_NUM_PHASES; ++nev)
+            if (hipEventCreate(&ev[nev]) != hipSuccess) { rc = FA_BACK_EHIP; break; }
+        if (rc == FA_BACK_OK && hipEventRecord(ev[0], st) != hipSuccess) rc = FA_BACK_EHIP;
+        pm.ev = ev;
     }
+    if (rc == FA_BACK_OK) {
+        switch (g.D) {
+            case 64: rc = launch_all<64>(g, P, st, pm); break;
+            case 128: rc = launch_all<128>(g, P, st, pm); break;
+            case 256: rc = launch_all<256>(g, P, st, pm); break;
+            default: rc = FA_BACK_EUNSUPPORTED;
+        }
+    }
+    if (phase_ms && rc == FA_BACK_OK) {
+        if (hipEventSynchronize(ev[FA_BACK_NUM_PHASES]) != hipSuccess) rc = FA_BACK_EHIP;
+        for (int ph = 0; rc == FA_BACK_OK && ph < FA_BACK_NUM_PHASES; ++ph)
+            if (hipEventElapsedTime(&phase_ms[ph], ev[ph], ev[ph + 1]) != hipSuccess) rc = FA_BACK_EHIP;
+    }
+    for (int e = 0; e < nev; ++e) (void)hipEventDestroy(ev[e]);
     if (old != plan->device) (void)hipSetDevice(old);
     return rc;
+}
+
+int fa_back_run(const fa_back_plan* plan, const void* q, const void* k, const void* v, const void* d,
+                const void* mask, void* out, void* workspace, void* stream) {
+    return run_impl(plan, q, k, v, d, mask, out, workspace, stream, nullptr);
+}
+
+int fa_back_run_timed(const fa_back_plan* plan, const void* q, const void* k, const void* v,
+                      const void* d, const void* mask, void* out, void* workspace, void* stream,
+                      float* phase_ms) {
+    if (!phase_ms) return FA_BACK_EINVAL;
+    return run_impl(plan, q, k, v, d, mask, out, workspace, stream, phase_ms);
 }
 
 }  // extern "C"

@@ -62,6 +62,8 @@ def load_library():
     lib.fa_back_create.restype = ctypes.c_int
     lib.fa_back_run.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 8
     lib.fa_back_run.restype = ctypes.c_int
+    lib.fa_back_run_timed.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 8 + [ctypes.POINTER(ctypes.c_float)]
+    lib.fa_back_run_timed.restype = ctypes.c_int
     lib.fa_back_destroy.argtypes = [ctypes.c_void_p]
     lib.fa_back_destroy.restype = None
     lib.fa_back_status_string.argtypes = [ctypes.c_int]
@@ -102,6 +104,21 @@ def fa_back_run(plan, q: int, k: int, v: int, d: int, mask: Optional[int], out: 
     rc = load_library().fa_back_run(plan, q, k, v, d, mask or None, out, workspace, stream or None)
     if rc != OK:
         raise FaBackError(rc, "fa_back_run")
+
+
+NUM_PHASES = 7
+PHASES = ("absmax", "prep", "walk1", "merge", "walk2", "dqreduce", "kvpass")
+
+
+def fa_back_run_timed(plan, q: int, k: int, v: int, d: int, mask: Optional[int], out: int,
+                      workspace: int, stream: int = 0) -> list:
+    """Run once, blocking, and return the elapsed milliseconds of each kernel phase."""
+    ms = (ctypes.c_float * NUM_PHASES)()
+    rc = load_library().fa_back_run_timed(plan, q, k, v, d, mask or None, out, workspace,
+                                          stream or None, ms)
+    if rc != OK:
+        raise FaBackError(rc, "fa_back_run_timed")
+    return list(ms)
 
 
 def fa_back_destroy(plan) -> None:
@@ -201,6 +218,15 @@ class DeviceProblem:
                     self.bufs["v"].data_ptr(), self.bufs["d"].data_ptr(),
                     None if m is None else m.data_ptr(), self.out.data_ptr(), self.ws.data_ptr(),
                     s.cuda_stream)
+
+    def run_timed(self, stream=None) -> list:
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        m = self.bufs["mask"]
+        return fa_back_run_timed(self.plan, self.bufs["q"].data_ptr(), self.bufs["k"].data_ptr(),
+                                 self.bufs["v"].data_ptr(), self.bufs["d"].data_ptr(),
+                                 None if m is None else m.data_ptr(), self.out.data_ptr(),
+                                 self.ws.data_ptr(), s.cuda_stream)
 
     def outputs(self) -> dict:
         return unpack(self.out.cpu().numpy(), self.layout, self.p)

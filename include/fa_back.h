@@ -118,6 +118,20 @@ int fa_back_create(const fa_back_desc* desc, int device, fa_back_plan** plan,
 int fa_back_run(const fa_back_plan* plan, const void* q, const void* k, const void* v,
                 const void* d, const void* mask, void* out, void* workspace, void* stream);
 
+/* Number of kernel phases reported by fa_back_run_timed, in launch order:
+ * 0 absmax of q and dO, 1 q/dO to fp16 fragments, 2 query-side walk 1 (LSE and delta
+ * statistics), 3 merge of key-range splits (writes LSE and delta), 4 query-side walk 2 (dQ),
+ * 5 dQ split reduction (empty when the keys were not split), 6 key-side pass (dK, dV). */
+#define FA_BACK_NUM_PHASES 7
+
+/* fa_back_run plus timing, for profiling: records a HIP event on `stream` before the first
+ * kernel and after each phase, waits for the last one, and writes each phase's elapsed
+ * milliseconds to phase_ms[0 .. FA_BACK_NUM_PHASES-1]. Unlike fa_back_run it blocks the
+ * host until the run has finished; it creates and destroys its own events. */
+int fa_back_run_timed(const fa_back_plan* plan, const void* q, const void* k, const void* v,
+                      const void* d, const void* mask, void* out, void* workspace, void* stream,
+                      float* phase_ms);
+
 /* Free a plan (NULL is allowed). */
 void fa_back_destroy(fa_back_plan* plan);
 
