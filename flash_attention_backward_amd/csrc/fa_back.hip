@@ -36,8 +36,8 @@ struct Geometry {
     int npart, nbound;
     fa_back_layout layout;
     // workspace offsets (bytes)
-    uint64_t ws_absmax, ws_scal, ws_qf, ws_df, ws_qt, ws_dt;
-    uint64_t ws_pm, ws_pl, ws_pd, ws_pb, ws_lse2, ws_dlt, ws_bound, ws_dqp;
+    uint64_t ws_absmax, ws_scal, ws_qr, ws_dr;
+    uint64_t ws_pm, ws_pl, ws_pd, ws_pb, ws_lse2, ws_dlt, ws_bound, ws_dqp, ws_mcls;
 };
 
 bool tensor_nonneg(const fa_back_tensor& t) {
@@ -132,10 +132,8 @@ int validate(const fa_back_desc* d, Geometry* g) {
     const uint64_t prow = (uint64_t)g->splits * total_rows;
     g->ws_absmax = take(8ull * g->npart);
     g->ws_scal = take(64);
-    g->ws_qf = take(frag);
-    g->ws_df = take(frag);
-    g->ws_qt = take(frag);
-    g->ws_dt = take(frag);
+    g->ws_qr = take(frag);
+    g->ws_dr = take(frag);
     g->ws_pm = take(4 * prow);
     g->ws_pl = take(8 * prow);
     g->ws_pd = take(8 * prow);
@@ -144,6 +142,7 @@ int validate(const fa_back_desc* d, Geometry* g) {
     g->ws_dlt = take(4ull * total_rows);
     g->ws_bound = take(4ull * g->nbound);
     g->ws_dqp = take(g->splits > 1 ? 4ull * g->splits * total_rows * D : 0);
+    g->ws_mcls = take(has_mask ? (uint64_t)(Hm == 1 ? 1 : g->Hkv) * g->RB * g->KT : 0);
     L.workspace_bytes = std::max<uint64_t>(o, kAlign);
     return FA_BACK_OK;
 }
@@ -176,6 +175,10 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
     hipLaunchKernelGGL(absmax_kernel, dim3(g.npart), dim3(kThreads), 0, st, P);
     pm.mark(0);
     hipLaunchKernelGGL(prep_kernel<D>, dim3(g.Hkv * g.RB), dim3(kThreads), 0, st, P);
+    if (g.Hm > 0)
+        hipLaunchKernelGGL(maskclass_kernel, dim3((g.Hm == 1 ? 1 : g.Hkv) * g.RB,
+                                                  (g.KT + kClassTilesPerBlock - 1) / kClassTilesPerBlock),
+                           dim3(kThreads), 0, st, P);
     pm.mark(1);
     hipLaunchKernelGGL((qpass_kernel<D, false>), dim3(g.RT * g.Hkv, g.splits), dim3(kThreads), 0, st, P);
     pm.mark(2);
@@ -298,10 +301,8 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     P.absmax_part = (float*)(w + g.ws_absmax);
     P.npart = g.npart;
     P.scal = (int*)(w + g.ws_scal);
-    P.qf = (_Float16*)(w + g.ws_qf);
-    P.df = (_Float16*)(w + g.ws_df);
-    P.qt = (_Float16*)(w + g.ws_qt);
-    P.dt = (_Float16*)(w + g.ws_dt);
+    P.qr = (_Float16*)(w + g.ws_qr);
+    P.dr = (_Float16*)(w + g.ws_dr);
     P.part_m = (float*)(w + g.ws_pm);
     P.part_l = (double*)(w + g.ws_pl);
     P.part_d = (double*)(w + g.ws_pd);
@@ -311,6 +312,7 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     P.bound_part = (float*)(w + g.ws_bound);
     P.nbound = g.nbound;
     P.dq_part = (float*)(w + g.ws_dqp);
+    P.mcls = (unsigned char*)(w + g.ws_mcls);
 
     hipStream_t st = (hipStream_t)stream;
     hipEvent_t ev[FA_BACK_NUM_PHASES + 1];

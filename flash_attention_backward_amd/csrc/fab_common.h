@@ -58,10 +58,8 @@ struct Params {
     float* absmax_part;   // [2][npart]
     int npart;
     int* scal;            // [0] = e_q, [1] = e_do (power-of-two exponents)
-    _Float16* qf;         // [Hkv][RB][32*D]  q rows, fragments for contraction over d
-    _Float16* df;         // [Hkv][RB][32*D]  dO rows, same
-    _Float16* qt;         // [Hkv][RB][32*D]  q, fragments for contraction over rows
-    _Float16* dt;         // [Hkv][RB][32*D]  dO, same
+    _Float16* qr;         // [Hkv][RB*32][D]  q rows scaled by 2^e_q, fp16, row-major
+    _Float16* dr;         // [Hkv][RB*32][D]  dO rows scaled by 2^e_do, fp16, row-major
     float* part_m;        // [splits][Hkv*RB*32]  running max (log2 units)
     double* part_l;       // softmax sum at part_m
     double* part_d;       // sum of e * dp at part_m (dp in 2^e_do units)
@@ -71,7 +69,13 @@ struct Params {
     float* bound_part;    // [nbound] per-block max of max|dp| + |delta|
     int nbound;
     float* dq_part;       // [splits][Hkv*RB*32][D] when splits > 1
+    unsigned char* mcls;  // [Hc][RB][KT] mask class of (row block, 64-key tile); Hc = Hm==1 ? 1 : Hkv
 };
+
+// Mask classes of a (32-row block, 64-key tile): no masking needed, every entry -inf, other.
+constexpr int kMaskZero = 0;
+constexpr int kMaskDead = 1;
+constexpr int kMaskMixed = 2;
 
 // Row of the 32x32 product held in accumulator register v by a lane of half g (= lane/32);
 // the column is lane % 32.

@@ -5,7 +5,8 @@
 //
 // Launch sequence (all on one stream):
 //   absmax   per-tensor max |q|, max |dO|           -> power-of-two prescale exponents
-//   prep     q, dO -> fp16 MFMA fragments (two layouts each) in the workspace
+//   prep     q, dO -> power-of-two-scaled fp16 rows in the workspace
+//   maskcls  class of every (32-row block, 64-key tile) of the mask (only with a mask)
 //   qpass<0> walk 1 over keys: online softmax max/sum and delta numerator per row
 //   merge    fixed-order merge of the key-range splits -> LSE, delta (packed output)
 //   qpass<1> walk 2 over keys: dS = P (dP - delta), dQ += dS K
@@ -57,15 +58,10 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(Params p) {
 
 // ----------------------------------------------------------------------------- prep
 
-// One workgroup per (hk, 32-row block). Writes, for q and for dO:
-//   *f: element (ks, lane, t) = X[row lane%32][d 16ks + 8(lane/32) + t]    (contraction over d)
-//   *t: element (md, rh, lane, t) = X[row 16rh + crow(t, lane/32)][d 32md + lane%32]
-//       (contraction over rows; crow(t, g) for t < 8 is the row of accumulator t)
+// One workgroup per (hk, 32-row block): q and dO rows, scaled by the power-of-two prescale,
+// rounded to fp16 and written row-major in the row order r = i*G + g (padding rows are 0).
 template <int D>
 __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
-    constexpr int LD = D + 8;
-    __shared__ __attribute__((aligned(16))) _Float16 sQ[32 * LD];
-    __shared__ __attribute__((aligned(16))) _Float16 sD[32 * LD];
     __shared__ float red[2][kWaves];
 
     // exponents from the absmax partials (every block reduces them identically)
@@ -95,50 +91,33 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
     const float fq = ldexpf(1.0f, eq), fd = ldexpf(1.0f, edo);
 
     const int hk = blockIdx.x / p.RB, rb = blockIdx.x - (blockIdx.x / p.RB) * p.RB;
-    for (int idx = threadIdx.x; idx < 32 * D; idx += kThreads) {
-        const int rr = idx / D, c = idx - (idx / D) * D;
+    constexpr int GR = D / 8;
+    for (int item = threadIdx.x; item < 32 * GR; item += kThreads) {
+        const int rr = item / GR, grp = item - (item / GR) * GR;
         const int r = rb * 32 + rr;
-        float xq = 0.0f, xd = 0.0f;
+        f16x8 vq, vd;
         if (r < p.R) {
             const int i = r / p.G, g = r - (r / p.G) * p.G;
             const int h = hk * p.G + g;
-            xq = load_scalar(p.q + c * p.q_nb0 + (int64_t)i * p.q_nb1 + (int64_t)h * p.q_nb2, p.q_type);
-            xd = load_scalar(p.d + c * p.d_nb0 + (int64_t)h * p.d_nb1 + (int64_t)i * p.d_nb2, p.d_type);
-        }
-        sQ[rr * LD + c] = (_Float16)(xq * fq);
-        sD[rr * LD + c] = (_Float16)(xd * fd);
-    }
-    __syncthreads();
-    const int64_t blk = ((int64_t)hk * p.RB + rb) * 32 * D;
-    // contraction-over-d fragments
-    for (int item = threadIdx.x; item < (D / 16) * 64; item += kThreads) {
-        const int ks = item >> 6, lane = item & 63;
-        const int row = lane & 31, d0 = 16 * ks + 8 * (lane >> 5);
-        *(f16x8*)(p.qf + blk + 8 * item) = *(const f16x8*)(sQ + row * LD + d0);
-        *(f16x8*)(p.df + blk + 8 * item) = *(const f16x8*)(sD + row * LD + d0);
-    }
-    // contraction-over-rows fragments
-    for (int item = threadIdx.x; item < (D / 32) * 2 * 64; item += kThreads) {
-        const int md = item >> 7, rh = (item >> 6) & 1, lane = item & 63;
-        const int dcol = 32 * md + (lane & 31), g = lane >> 5;
-        f16x8 a, b;
+            const char* qrow = p.q + (int64_t)i * p.q_nb1 + (int64_t)h * p.q_nb2;
+            const char* drow = p.d + (int64_t)h * p.d_nb1 + (int64_t)i * p.d_nb2;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int row = 16 * rh + crow(t, g);
-            a[t] = sQ[row * LD + dcol];
-            b[t] = sD[row * LD + dcol];
+            for (int t = 0; t < 8; ++t) {
+                const int c = 8 * grp + t;
+                vq[t] = (_Float16)(load_scalar(qrow + c * p.q_nb0, p.q_type) * fq);
+                vd[t] = (_Float16)(load_scalar(drow + c * p.d_nb0, p.d_type) * fd);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) vq[t] = vd[t] = (_Float16)0.0f;
         }
-        *(f16x8*)(p.qt + blk + 8 * item) = a;
-        *(f16x8*)(p.dt + blk + 8 * item) = b;
+        const int64_t off = (((int64_t)hk * p.RB + rb) * 32 + rr) * D + 8 * grp;
+        *(f16x8*)(p.qr + off) = vq;
+        *(f16x8*)(p.dr + off) = vd;
     }
 }
 
 // ----------------------------------------------------------------------------- helpers
-
-FAB_DEV float mask_value(const char* mrow, int type, int j) {
-    if (type == FA_BACK_F16) return (float)*(const _Float16*)(mrow + 2 * (int64_t)j);
-    return *(const float*)(mrow + 4 * (int64_t)j);
-}
 
 // dS exponent: every workgroup of a wave reduces the merge kernel's bound partials.
 FAB_DEV int load_ds_exponent(const Params& p) {
@@ -147,23 +126,83 @@ FAB_DEV int load_ds_exponent(const Params& p) {
     return ds_exponent(wave_max(b));
 }
 
+// ----------------------------------------------------------------------------- mask classes
+
+// Class of every (32-row block, 64-key tile) of the mask, so the passes can skip tiles no row
+// sees and skip mask reads where every entry is 0. Rows past N and keys past M are ignored.
+// Grid: x = Hc * RB (Hc = 1 when the mask is shared by all heads), y = tile groups of 16.
+constexpr int kClassTilesPerBlock = 16;
+
+__global__ __launch_bounds__(kThreads) void maskclass_kernel(Params p) {
+    __shared__ int red[2][kWaves];
+    const int hc = blockIdx.x / p.RB, rb = blockIdx.x - (blockIdx.x / p.RB) * p.RB;
+    const int rr = threadIdx.x >> 3, kg = threadIdx.x & 7;
+    const int r = rb * 32 + rr;
+    const bool row_ok = r < p.R;
+    const int i = r / p.G, gh = r - (r / p.G) * p.G;
+    const char* mrow = p.mask + (int64_t)i * p.m_nb1 + (int64_t)(p.Hm == 1 ? 0 : hc * p.G + gh) * p.m_nb2;
+    const int tb = blockIdx.y * kClassTilesPerBlock;
+    const int te = min(p.KT, tb + kClassTilesPerBlock);
+    for (int t = tb; t < te; ++t) {
+        bool all0 = true, allinf = true;
+        if (row_ok) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = t * kQTileKeys + 8 * kg + e;
+                if (j < p.M) {
+                    const float x = p.m_type == FA_BACK_F16 ? (float)*(const _Float16*)(mrow + 2 * (int64_t)j)
+                                                             : *(const float*)(mrow + 4 * (int64_t)j);
+                    all0 = all0 && (x == 0.0f);
+                    allinf = allinf && (x == neg_inf());
+                }
+            }
+        }
+        const bool w0 = __all(all0), winf = __all(allinf);
+        if ((threadIdx.x & 63) == 0) {
+            red[0][threadIdx.x >> 6] = w0;
+            red[1][threadIdx.x >> 6] = winf;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            bool b0 = true, binf = true;
+            for (int w = 0; w < kWaves; ++w) {
+                b0 = b0 && red[0][w];
+                binf = binf && red[1][w];
+            }
+            p.mcls[((int64_t)hc * p.RB + rb) * p.KT + t] =
+                (unsigned char)(binf ? kMaskDead : (b0 ? kMaskZero : kMaskMixed));
+        }
+        __syncthreads();
+    }
+}
+
+FAB_DEV int mask_class(const Params& p, int hk, int rb, int t) {
+    if (p.m_type == FA_BACK_NONE) return kMaskZero;
+    const int hc = p.Hm == 1 ? 0 : hk;
+    return p.mcls[((int64_t)hc * p.RB + rb) * p.KT + t];
+}
+
+FAB_DEV float mask_at(const char* mrow, int type, int j) {
+    return type == FA_BACK_F16 ? (float)*(const _Float16*)(mrow + 2 * (int64_t)j)
+                               : *(const float*)(mrow + 4 * (int64_t)j);
+}
+
 // ----------------------------------------------------------------------------- query side
 
 // Workgroup: one KV head, kWaves row blocks of 32 rows (one per wave), one key-range split.
 // Each wave keeps its rows' q and dO fragments in registers and walks the split's 64-key
-// tiles; K and V tiles are decoded once into LDS and shared by the four waves.
+// tiles; K and V tiles are decoded once per workgroup into LDS and shared by the four
+// waves. The raw q8_0 bytes of tile t+1 are fetched by DMA while tile t is computed.
 // The 32x32 products are computed transposed, S^T = K Q^T, so a lane holds one query row
 // (column lane%32) and 16 keys; the two lanes l and l^32 together hold the row's 32 keys.
 template <int D, bool GRAD>
 __global__ __launch_bounds__(kThreads, 1) void qpass_kernel(Params p) {
-    using L = TileLds<D, kQTileKeys>;
     constexpr int KS = D / 16;     // 16-deep steps of a contraction over d
     constexpr int MD = D / 32;     // 32-wide d blocks of dQ
-    __shared__ __attribute__((aligned(16))) _Float16 sK[kQTileKeys * L::kLd];
-    __shared__ __attribute__((aligned(16))) _Float16 sV[kQTileKeys * L::kLd];
-    __shared__ __attribute__((aligned(16))) _Float16 sKT[GRAD ? D * L::kLdT : 8];
-    __shared__ __attribute__((aligned(16))) unsigned char sRawK[L::kRaw];
-    __shared__ __attribute__((aligned(16))) unsigned char sRawV[L::kRaw];
+    constexpr int RAW = RawTile<D, kQTileKeys>::kBytes;
+    __shared__ __attribute__((aligned(16))) _Float16 sK[kQTileKeys * D];
+    __shared__ __attribute__((aligned(16))) _Float16 sV[kQTileKeys * D];
+    __shared__ __attribute__((aligned(16))) unsigned char sRaw[2][2][RAW];   // [buffer][K, V]
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l32 = lane & 31, g = lane >> 5;
@@ -178,18 +217,19 @@ __global__ __launch_bounds__(kThreads, 1) void qpass_kernel(Params p) {
     const int h = hk * p.G + gh;
     const bool row_ok = active && r < p.R;
     const int ridx = hk * rowsHK + r;
+    const bool kq8 = p.k_type == FA_BACK_Q8_0, vq8 = p.v_type == FA_BACK_Q8_0;
 
     const int eq = p.scal[0], edo = p.scal[1];
     const float sc2 = p.scale * ldexpf(1.0f, -eq) * kLog2e;
 
     f16x8 bq[KS], bd[KS];
     if (active) {
-        const _Float16* fq = p.qf + ((int64_t)hk * p.RB + rb) * 32 * D;
-        const _Float16* fd = p.df + ((int64_t)hk * p.RB + rb) * 32 * D;
+        const _Float16* rq = p.qr + ((int64_t)hk * rowsHK + r) * D;
+        const _Float16* rd = p.dr + ((int64_t)hk * rowsHK + r) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bq[ks] = *(const f16x8*)(fq + (ks * 64 + lane) * 8);
-            bd[ks] = *(const f16x8*)(fd + (ks * 64 + lane) * 8);
+            bq[ks] = *(const f16x8*)(rq + 16 * ks + 8 * g);
+            bd[ks] = *(const f16x8*)(rd + 16 * ks + 8 * g);
         }
     } else {
 #pragma unroll
@@ -225,16 +265,33 @@ __global__ __launch_bounds__(kThreads, 1) void qpass_kernel(Params p) {
 
     const int t0 = split * p.tiles_per_split;
     const int t1 = min(p.KT, t0 + p.tiles_per_split);
+    if (t0 < t1) {
+        if (kq8) dma_raw_tile<D, kQTileKeys>(p.k, p.k_nb1, p.k_nb2, hk, t0 * kQTileKeys, p.M, sRaw[0][0]);
+        if (vq8) dma_raw_tile<D, kQTileKeys>(p.v, p.v_nb1, p.v_nb2, hk, t0 * kQTileKeys, p.M, sRaw[0][1]);
+    }
     for (int t = t0; t < t1; ++t) {
         const int j0 = t * kQTileKeys;
+        const int buf = (t - t0) & 1;
+        wait_all_mem();
+        __syncthreads();   // raw(t) landed everywhere; every wave is done with tile t-1
+        // mask class of this wave's rows; a tile no row of the workgroup sees is skipped whole
+        const int cls = active ? mask_class(p, hk, rb, t) : kMaskDead;
+        bool wg_dead = true;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int rbw = rt * kWaves + w;
+            wg_dead = wg_dead && (rbw >= p.RB || mask_class(p, hk, rbw, t) == kMaskDead);
+        }
+        if (t + 1 < t1) {
+            if (kq8) dma_raw_tile<D, kQTileKeys>(p.k, p.k_nb1, p.k_nb2, hk, j0 + kQTileKeys, p.M, sRaw[buf ^ 1][0]);
+            if (vq8) dma_raw_tile<D, kQTileKeys>(p.v, p.v_nb1, p.v_nb2, hk, j0 + kQTileKeys, p.M, sRaw[buf ^ 1][1]);
+        }
+        if (wg_dead) continue;   // uniform over the workgroup
+        decode_tile<D, kQTileKeys>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, sRaw[buf][0], sK);
+        decode_tile<D, kQTileKeys>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, sRaw[buf][1], sV);
         __syncthreads();
-        stage_tile<D, kQTileKeys>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, sRawK);
-        stage_tile<D, kQTileKeys>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, sRawV);
-        __syncthreads();
-        decode_tile<D, kQTileKeys, GRAD>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, sRawK, sK, sKT);
-        decode_tile<D, kQTileKeys, false>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, sRawV, sV, nullptr);
-        __syncthreads();
-        if (!active) continue;
+        if (cls == kMaskDead) continue;   // uniform over the wave (also covers inactive waves)
+        const Swz z = make_swz<D>(lane);
 
         float s2[GRAD ? 1 : 32], dp[GRAD ? 1 : 32];
 #pragma unroll
@@ -244,11 +301,11 @@ __global__ __launch_bounds__(kThreads, 1) void qpass_kernel(Params p) {
             for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const f16x8 ak = *(const f16x8*)(sK + (32 * kb + l32) * L::kLd + 16 * ks + 8 * g);
-                const f16x8 av = *(const f16x8*)(sV + (32 * kb + l32) * L::kLd + 16 * ks + 8 * g);
+                const f16x8 ak = frag_rows<D>(sK, 32 * kb, ks, lane, z);
+                const f16x8 av = frag_rows<D>(sV, 32 * kb, ks, lane, z);
                 sa = mfma32(ak, bq[ks], sa);
                 pa = mfma32(av, bd[ks], pa);
-                if (GRAD && (ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+                if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the load lookahead
             }
             f16x8 bs[2];
 #pragma unroll
@@ -256,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void qpass_kernel(Params p) {
                 const int key = j0 + 32 * kb + crow(v, g);
                 float sv = sa[v] * sc2;
                 if (!row_ok || key >= p.M) sv = neg_inf();
-                else if (mrow) sv += mask_value(mrow, p.m_type, key) * kLog2e;
+                else if (cls == kMaskMixed) sv += mask_at(mrow, p.m_type, key) * kLog2e;
                 if (!GRAD) {
                     s2[16 * kb + v] = sv;
                     dp[16 * kb + v] = pa[v];
@@ -271,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 1) void qpass_kernel(Params p) {
                 for (int md = 0; md < MD; ++md) {
 #pragma unroll
                     for (int rh = 0; rh < 2; ++rh) {
-                        const f16x8 a = *(const f16x8*)(sKT + (32 * md + l32) * L::kLdT + 32 * kb + 16 * rh + 8 * g);
+                        const f16x8 a = frag_cols<D>(sK, md, 32 * kb + 16 * rh, lane, z);
                         dqacc[md] = mfma32(a, bs[rh], dqacc[md]);
                     }
                     if ((md & 1) == 1) __builtin_amdgcn_sched_barrier(0);
@@ -316,28 +373,18 @@ __global__ __launch_bounds__(kThreads, 1) void qpass_kernel(Params p) {
             p.part_b[idx] = bb;
         }
     } else if (row_ok) {
-        if (p.splits == 1) {
-            const float fac = p.scale * ldexpf(1.0f, ksx - edo);
-            float* dst = p.dq + ((int64_t)h * p.N + i) * D;
+        const bool direct = p.splits == 1;
+        const float fac = direct ? p.scale * ldexpf(1.0f, ksx - edo) : 1.0f;
+        float* dst = direct ? p.dq + ((int64_t)h * p.N + i) * D
+                            : p.dq_part + ((int64_t)split * p.Hkv * rowsHK + ridx) * D;
 #pragma unroll
-            for (int md = 0; md < MD; ++md)
+        for (int md = 0; md < MD; ++md)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    f32x4 o = {dqacc[md][4 * b] * fac, dqacc[md][4 * b + 1] * fac,
-                               dqacc[md][4 * b + 2] * fac, dqacc[md][4 * b + 3] * fac};
-                    *(f32x4*)(dst + 32 * md + 8 * b + 4 * g) = o;
-                }
-        } else {
-            float* dst = p.dq_part + ((int64_t)split * p.Hkv * rowsHK + ridx) * D;
-#pragma unroll
-            for (int md = 0; md < MD; ++md)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    f32x4 o = {dqacc[md][4 * b], dqacc[md][4 * b + 1], dqacc[md][4 * b + 2],
-                               dqacc[md][4 * b + 3]};
-                    *(f32x4*)(dst + 32 * md + 8 * b + 4 * g) = o;
-                }
-        }
+            for (int b = 0; b < 4; ++b) {
+                f32x4 o = {dqacc[md][4 * b] * fac, dqacc[md][4 * b + 1] * fac,
+                           dqacc[md][4 * b + 2] * fac, dqacc[md][4 * b + 3] * fac};
+                *(f32x4*)(dst + 32 * md + 8 * b + 4 * g) = o;
+            }
     }
 }
 
@@ -424,17 +471,25 @@ __global__ __launch_bounds__(kThreads) void dqreduce_kernel(Params p) {
 
 // Workgroup: one KV head, 128 keys (32 per wave). Each wave keeps its keys' K and V
 // fragments and its dK^T, dV^T accumulators in registers and walks every 32-row block of the
-// group: S = Q K^T and dP = dO V^T put one key per lane column and 16 rows per lane, which
-// is the layout the second operand of dV^T += dO^T P and dK^T += Q^T dS needs.
+// group. Each row block of q and dO (fp16, row-major) is copied HBM -> LDS once per
+// workgroup by DMA, double-buffered so block rb+1 arrives while block rb is computed, and
+// read by all four waves. S = Q K^T and dP = dO V^T put one key per lane column and 16 rows
+// per lane, which is the layout the second operand of dV^T += dO^T P and dK^T += Q^T dS
+// needs; the first operands are transpose reads of the same LDS blocks.
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void kvpass_kernel(Params p) {
-    using L = TileLds<D, kQTileKeys>;
     constexpr int KS = D / 16;
     constexpr int MD = D / 32;
-    __shared__ __attribute__((aligned(16))) _Float16 sK[kQTileKeys * L::kLd];
-    __shared__ __attribute__((aligned(16))) _Float16 sV[kQTileKeys * L::kLd];
-    __shared__ __attribute__((aligned(16))) unsigned char sRawK[L::kRaw];
-    __shared__ __attribute__((aligned(16))) unsigned char sRawV[L::kRaw];
+    constexpr int BLK = 32 * D;                                   // halfs per row block
+    constexpr int RAW = RawTile<D, kQTileKeys>::kBytes;
+    constexpr int VT = kKVKeys * D * 2;                           // resident V tile (bytes)
+    constexpr int SETUP = kQTileKeys * D * 2 + 2 * RAW;           // K half-tile decode + raw
+    constexpr int BUFB = 2 * BLK * 2 + 256;                       // q, dO blocks + 32 lse + 32 delta
+    constexpr int LOOP = 2 * BUFB;                                // double-buffered
+    constexpr int LDSB = VT + (SETUP > LOOP ? SETUP : LOOP);
+    __shared__ __attribute__((aligned(16))) unsigned char lds[LDSB];
+    _Float16* sV = (_Float16*)lds;          // [128 keys][D], swizzled, for the whole kernel
+    unsigned char* smem = lds + VT;         // setup scratch, then the row-block buffers
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l32 = lane & 31, g = lane >> 5;
@@ -443,27 +498,34 @@ __global__ __launch_bounds__(kThreads, 1) void kvpass_kernel(Params p) {
     const int key0 = kvt * kKVKeys;
     const int myj = key0 + 32 * wave + l32;
     const bool key_ok = myj < p.M;
+    const int rowsHK = p.RB * 32;
 
-    // K and V fragments: B[d][key] of S = Q K^T, i.e. K[key][16ks + 8g .. +7]
-    f16x8 bk[KS], bv[KS];
+    // K fragments in registers: B[d][key] of S = Q K^T, i.e. K[key][16ks + 8g .. +7];
+    // V stays in LDS and its fragments are read per row block
+    f16x8 bk[KS];
+    {
+        _Float16* sK = (_Float16*)smem;
+        unsigned char* rawK = smem + kQTileKeys * D * 2;
+        unsigned char* rawV = rawK + RAW;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int j0 = key0 + half * kQTileKeys;
-        __syncthreads();
-        stage_tile<D, kQTileKeys>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, sRawK);
-        stage_tile<D, kQTileKeys>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, sRawV);
-        __syncthreads();
-        decode_tile<D, kQTileKeys, false>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, sRawK, sK, nullptr);
-        decode_tile<D, kQTileKeys, false>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, sRawV, sV, nullptr);
-        __syncthreads();
-        if ((wave >> 1) == half) {
-            const int lk = 32 * (wave & 1) + l32;
+        for (int half = 0; half < 2; ++half) {
+            const int j0 = key0 + half * kQTileKeys;
+            __syncthreads();
+            if (p.k_type == FA_BACK_Q8_0) dma_raw_tile<D, kQTileKeys>(p.k, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK);
+            if (p.v_type == FA_BACK_Q8_0) dma_raw_tile<D, kQTileKeys>(p.v, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV);
+            wait_all_mem();
+            __syncthreads();
+            decode_tile<D, kQTileKeys>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, sK);
+            decode_tile<D, kQTileKeys>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV,
+                                       sV + half * kQTileKeys * D);
+            __syncthreads();
+            if ((wave >> 1) == half) {
+                const Swz z = make_swz<D>(lane);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                bk[ks] = *(const f16x8*)(sK + lk * L::kLd + 16 * ks + 8 * g);
-                bv[ks] = *(const f16x8*)(sV + lk * L::kLd + 16 * ks + 8 * g);
+                for (int ks = 0; ks < KS; ++ks) bk[ks] = frag_rows<D>(sK, 32 * (wave & 1), ks, lane, z);
             }
         }
+        __syncthreads();   // the setup region becomes the row-block buffers
     }
 
     const int eq = p.scal[0], edo = p.scal[1];
@@ -471,8 +533,6 @@ __global__ __launch_bounds__(kThreads, 1) void kvpass_kernel(Params p) {
     const int ksx = load_ds_exponent(p);
     const float dsf = ldexpf(1.0f, -ksx);
     const float pf = ldexpf(1.0f, kPScaleLog2);
-    const bool has_mask = p.m_type != FA_BACK_NONE;
-    const int rowsHK = p.RB * 32;
 
     f32x16 dkacc[MD], dvacc[MD];
 #pragma unroll
@@ -480,57 +540,104 @@ __global__ __launch_bounds__(kThreads, 1) void kvpass_kernel(Params p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) dkacc[md][v] = dvacc[md][v] = 0.0f;
 
-    for (int rb = 0; rb < p.RB; ++rb) {
-        const int64_t blk = ((int64_t)hk * p.RB + rb) * 32 * D;
-        const float* lrow = p.row_lse2 + (int64_t)hk * rowsHK + 32 * rb;
-        const float* drow = p.row_dlt + (int64_t)hk * rowsHK + 32 * rb;
-        f32x4 l4[4], d4[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            l4[b] = *(const f32x4*)(lrow + 8 * b + 4 * g);
-            d4[b] = *(const f32x4*)(drow + 8 * b + 4 * g);
+    // DMA of row block rb (q and dO) into buffer b; the LDS copy is swizzled (tile_off)
+    // by choosing each lane's source chunk
+    auto dma_block = [&](int rbx, int b) {
+        constexpr int NI = BLK / 512;                 // 64-lane x 16-byte instructions per tensor
+        unsigned char* base = smem + b * BUFB;
+        _Float16* dstq = (_Float16*)base;
+        for (int ins = wave; ins < 2 * NI; ins += kWaves) {
+            const int ten = ins / NI, ii = ins - (ins / NI) * NI;
+            const int P = ii * 64 + lane;             // physical 16-byte slot in the block
+            const int row = P / (D / 8), pc = P - (P / (D / 8)) * (D / 8);
+            const int c = swz_chunk<D>(row, pc);      // the swizzle is an involution
+            const _Float16* src = (ten ? p.dr : p.qr) + (((int64_t)hk * rowsHK + rbx * 32 + row) * D + 8 * c);
+            dma16(src, dstq + ten * BLK + ii * 512);
         }
-        f32x16 sa, pa;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const f16x8 aq = *(const f16x8*)(p.qf + blk + (ks * 64 + lane) * 8);
-            const f16x8 ad = *(const f16x8*)(p.df + blk + (ks * 64 + lane) * 8);
-            sa = mfma32(aq, bk[ks], sa);
-            pa = mfma32(ad, bv[ks], pa);
+        if (wave == kWaves - 1 && lane < 16) {        // 32 lse then 32 delta values
+            const float* src = (lane < 8 ? p.row_lse2 : p.row_dlt) + (int64_t)hk * rowsHK + rbx * 32 + 4 * (lane & 7);
+            dma16(src, base + 2 * BLK * 2);
         }
-        f16x8 bp[2], bs[2];
+    };
+
+    // class of row block rb for this wave's 64-key half, and whether any wave needs the block
+    const int myt = 2 * kvt + (wave >> 1);
+    auto wave_class = [&](int rbx) -> int {
+        return myt < p.KT ? mask_class(p, hk, rbx, myt) : kMaskDead;
+    };
+    auto block_needed = [&](int rbx) -> bool {
+        const int ta = 2 * kvt, tb = 2 * kvt + 1;
+        return mask_class(p, hk, rbx, ta) != kMaskDead ||
+               (tb < p.KT && mask_class(p, hk, rbx, tb) != kMaskDead);
+    };
+    auto next_needed = [&](int rbx) -> int {
+        while (rbx < p.RB && !block_needed(rbx)) ++rbx;
+        return rbx;
+    };
+
+    int rb = next_needed(0);
+    int buf = 0;
+    if (rb < p.RB) dma_block(rb, 0);
+    while (rb < p.RB) {
+        const int rbn = next_needed(rb + 1);
+        const _Float16* bq = (const _Float16*)(smem + buf * BUFB);
+        const _Float16* bdo = bq + BLK;
+        const float* lrow = (const float*)(smem + buf * BUFB + 2 * BLK * 2);   // lse2 of the block
+        const float* drow = lrow + 32;                                          // delta of the block
+        const int cls = wave_class(rb);
+        wait_all_mem();
+        __syncthreads();   // block rb landed everywhere; every wave is done with the last block
+        if (rbn < p.RB) dma_block(rbn, buf ^ 1);
+
+        if (cls != kMaskDead) {   // uniform over the wave
+            const Swz z = make_swz<D>(lane);
+            f32x16 sa, pa;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = 32 * rb + crow(v, g);
-            const float l2 = l4[v >> 2][v & 3];
-            float pv = 0.0f;
-            if (key_ok && l2 != neg_inf()) {
-                float sv = sa[v] * sc2;
-                if (has_mask) {
-                    const int i = r / p.G, gh = r - (r / p.G) * p.G;
-                    const int h = hk * p.G + gh;
-                    const char* mrow = p.mask + (int64_t)i * p.m_nb1 + (int64_t)(p.Hm == 1 ? 0 : h) * p.m_nb2;
-                    sv += mask_value(mrow, p.m_type, myj) * kLog2e;
+            for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                sa = mfma32(frag_rows<D>(bq, 0, ks, lane, z), bk[ks], sa);
+                pa = mfma32(frag_rows<D>(bdo, 0, ks, lane, z), frag_rows<D>(sV, 32 * wave, ks, lane, z), pa);
+                if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the load lookahead
+            }
+            f32x4 l4[4], d4[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                l4[b] = *(const f32x4*)(lrow + 8 * b + 4 * g);
+                d4[b] = *(const f32x4*)(drow + 8 * b + 4 * g);
+            }
+            f16x8 bp[2], bs[2];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float l2 = l4[v >> 2][v & 3];
+                float pv = 0.0f;
+                if (key_ok && l2 != neg_inf()) {
+                    float sv = sa[v] * sc2;
+                    if (cls == kMaskMixed) {
+                        const int r = 32 * rb + crow(v, g);
+                        const int ii = r / p.G, gh = r - (r / p.G) * p.G;
+                        const char* mrow = p.mask + (int64_t)ii * p.m_nb1 +
+                                           (int64_t)(p.Hm == 1 ? 0 : hk * p.G + gh) * p.m_nb2;
+                        sv += mask_at(mrow, p.m_type, myj) * kLog2e;
+                    }
+                    pv = fast_exp2(sv - l2);
                 }
-                pv = fast_exp2(sv - l2);
+                const float dsv = pv * (pa[v] - d4[v >> 2][v & 3]);
+                bp[v >> 3][v & 7] = (_Float16)(pv * pf);
+                bs[v >> 3][v & 7] = (_Float16)(dsv * dsf);
             }
-            const float dsv = pv * (pa[v] - d4[v >> 2][v & 3]);
-            bp[v >> 3][v & 7] = (_Float16)(pv * pf);
-            bs[v >> 3][v & 7] = (_Float16)(dsv * dsf);
-        }
 #pragma unroll
-        for (int md = 0; md < MD; ++md) {
+            for (int md = 0; md < MD; ++md) {
 #pragma unroll
-            for (int rh = 0; rh < 2; ++rh) {
-                const int64_t off = blk + ((int64_t)(md * 2 + rh) * 64 + lane) * 8;
-                const f16x8 adt = *(const f16x8*)(p.dt + off);
-                const f16x8 aqt = *(const f16x8*)(p.qt + off);
-                dvacc[md] = mfma32(adt, bp[rh], dvacc[md]);
-                dkacc[md] = mfma32(aqt, bs[rh], dkacc[md]);
+                for (int rh = 0; rh < 2; ++rh) {
+                    dvacc[md] = mfma32(frag_cols<D>(bdo, md, 16 * rh, lane, z), bp[rh], dvacc[md]);
+                    dkacc[md] = mfma32(frag_cols<D>(bq, md, 16 * rh, lane, z), bs[rh], dkacc[md]);
+                }
+                if ((md & 1) == 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
+        rb = rbn;
+        buf ^= 1;
     }
 
     if (!key_ok) return;

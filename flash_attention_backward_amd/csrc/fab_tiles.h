@@ -1,10 +1,108 @@
-// K/V tile decoding into LDS: each tile is read from HBM with 16-byte loads and decoded to
-// fp16 exactly once per workgroup. The cache itself is never converted.
+// LDS tiles: K/V tiles decoded once per workgroup from HBM, and the fragment reads of the
+// 32x32x16 products. The cache itself is never converted.
 #pragma once
 
 #include "fab_common.h"
 
 namespace fab {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// ----------------------------------------------------------------------------- layout
+
+// Row-major fp16 tiles [row][D] are stored without padding, 16-byte chunks of a row permuted
+// by an XOR swizzle. It keeps both access patterns free of bank conflicts:
+//   - a 16-lane b128 read of one logical chunk from 16 consecutive rows, and
+//   - a 32-lane transpose read covering 4 consecutive rows x 4 consecutive chunks.
+template <int D>
+FAB_DEV int swz_chunk(int row, int chunk) {
+    constexpr int CM = (D / 8) - 1;   // chunks per row - 1 (8, 16 or 32 chunks)
+    return chunk ^ ((((row & 3) << 2) | ((row >> 2) & 3)) & CM);
+}
+
+// halfs offset of (row, chunk) in a swizzled [rows][D] tile
+template <int D>
+FAB_DEV int tile_off(int row, int chunk) { return row * D + 8 * swz_chunk<D>(row, chunk); }
+
+// Per-lane swizzle terms. Both depend only on the lane (tile row blocks start at multiples of
+// 16 rows); they are passed through an opaque move once per loop iteration so that the
+// compiler computes the per-step LDS addresses in the loop instead of keeping (and
+// spilling) one precomputed address per step.
+struct Swz {
+    int rows;    // XOR term of a frag_rows read: swizzle of row lane%32
+    int col0;    // XOR term of frag_cols read j = 0
+    int col1;    // XOR term of frag_cols read j = 1
+};
+
+FAB_DEV int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+template <int D>
+FAB_DEV Swz make_swz(int lane) {
+    constexpr int CM = (D / 8) - 1;
+    const int g = lane >> 5, s = lane & 15;
+    auto f = [](int row) { return ((row & 3) << 2) | ((row >> 2) & 3); };
+    Swz z;
+    z.rows = opaque(f(lane & 31) & CM);
+    z.col0 = opaque(f(4 * g + (s >> 2)) & CM);
+    z.col1 = opaque(f(8 + 4 * g + (s >> 2)) & CM);
+    return z;
+}
+
+// A operand of a contraction over d: lane l reads row m0 + l%32, d = 16*ks + 8*(l/32) .. +7.
+// m0 must be a multiple of 16.
+template <int D>
+FAB_DEV f16x8 frag_rows(const _Float16* tile, int m0, int ks, int lane, const Swz& z) {
+    const int row = m0 + (lane & 31);
+    return *(const f16x8*)(tile + row * D + 8 * ((2 * ks + (lane >> 5)) ^ z.rows));
+}
+
+// A operand of a contraction over the rows of a swizzled [row][D] tile (rows are the k index,
+// d the m index): lane l gets d = 32*md + l%32 and the 8 rows kbase + crow(t, l/32), t = 0..7
+// (that is kbase + 8*(t/4) + 4*(l/32) + t%4), matching the B operand taken from an
+// accumulator's registers 8*rh + t. Built from two ds_read_b64_tr_b16: in each 16-lane group
+// lane 4a+b receives element b of the 8-byte reads of lanes a, a+4, a+8, a+12.
+// kbase must be a multiple of 16.
+template <int D>
+FAB_DEV f16x8 frag_cols(const _Float16* tile, int md, int kbase, int lane, const Swz& z) {
+    const int g = lane >> 5, h16 = (lane >> 4) & 1, s = lane & 15;
+    const int dcol = 32 * md + 16 * h16 + 4 * (s & 3);     // first of the 4 columns read
+    const int chunk = dcol >> 3, within = dcol & 7;
+    f16x8 r;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = kbase + 8 * j + 4 * g + (s >> 2);
+        const _Float16* p = tile + row * D + 8 * (chunk ^ (j ? z.col1 : z.col0)) + within;
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+        const f16x4 h = __builtin_bit_cast(f16x4, v);
+        r[4 * j + 0] = h[0];
+        r[4 * j + 1] = h[1];
+        r[4 * j + 2] = h[2];
+        r[4 * j + 3] = h[3];
+    }
+    return r;
+}
+
+// ----------------------------------------------------------------------------- DMA
+
+// Asynchronous 16-byte-per-lane copy HBM -> LDS; lane l writes lds_wave_base + 16*l.
+// lds_wave_base must be the same for every lane of the wave.
+FAB_DEV void dma16(const void* gsrc, void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+
+// Wait for this wave's outstanding memory operations (DMA included) and make the compiler
+// assume LDS may have changed.
+FAB_DEV void wait_all_mem() {
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+}
+
+// ----------------------------------------------------------------------------- q8_0 rows
 
 // q8_0 row geometry: D/32 blocks of 34 bytes; a row's bytes are staged in LDS as the
 // 16-byte-aligned chunks that cover it (the row may start at any even address).
@@ -16,56 +114,43 @@ struct Q8Row {
 };
 
 template <int D, int KEYS>
-struct TileLds {
-    static constexpr int kLd = D + 8;            // fp16 row stride of a [key][d] tile
-    static constexpr int kLdT = KEYS + 8;        // fp16 row stride of a [d][key] tile
-    static constexpr int kRaw = KEYS * Q8Row<D>::kSlot + 16;
+struct RawTile {
+    static constexpr int kBytes = KEYS * Q8Row<D>::kSlot + 16;
 };
 
-// Position of key `key` (within a tile) in a transposed [d][key] tile. Inside each group of
-// 16 keys, position 8*g + t holds key 8*(t/4) + 4*g + t%4, so the 8 keys that a lane of half
-// g supplies to a contraction over keys (rows crow(8*rh + t, g) of a 32x32 product) are
-// contiguous.
-FAB_DEV int tpos(int key) {
-    const int k16 = key & 15;
-    return (key & ~15) + 8 * ((k16 >> 2) & 1) + 4 * (k16 >> 3) + (k16 & 3);
-}
-
-// Phase 1: stage the raw bytes of keys [j0, j0+KEYS) of head hk into `raw` (q8_0 only).
+// Issue the DMA of the raw bytes of keys [j0, j0+KEYS) of head hk into `raw` (q8_0 only).
+// Chunk idx = key*kChunks + c lands at raw + 16*idx; chunks outside the row are skipped.
 template <int D, int KEYS>
-FAB_DEV void stage_tile(const char* base, int type, int64_t nb1, int64_t nb2, int hk, int j0,
-                        int M, unsigned char* raw) {
-    if (type != FA_BACK_Q8_0) return;
+FAB_DEV void dma_raw_tile(const char* base, int64_t nb1, int64_t nb2, int hk, int j0, int M,
+                          unsigned char* raw) {
     using R = Q8Row<D>;
     constexpr int NCH = KEYS * R::kChunks;
     constexpr int IT = (NCH + kThreads - 1) / kThreads;
     const char* hbase = base + (int64_t)hk * nb2;
-    u32x4 buf[IT];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const int idx = threadIdx.x + it * kThreads;
-        buf[it] = u32x4{0u, 0u, 0u, 0u};
-        if (idx < NCH) {
-            const int key = idx / R::kChunks;
-            const int c = idx - key * R::kChunks;
-            const int j = j0 + key;
-            if (j < M) {
-                const uintptr_t a = (uintptr_t)(hbase + (int64_t)j * nb1);
-                const uintptr_t a0 = a & ~(uintptr_t)15;
-                // only chunks that hold bytes of this row are read
-                if (a0 + 16u * (uintptr_t)c < a + R::kBytes)
-                    buf[it] = *(const u32x4*)(a0 + 16u * (uintptr_t)c);
-            }
+        const int wbase = it * kThreads + wave * 64;   // first chunk of this wave's instruction
+        if (wbase >= NCH) break;                        // wave-uniform
+        const int idx = wbase + lane;
+        const int key = idx / R::kChunks;
+        const int c = idx - key * R::kChunks;
+        const int j = j0 + key;
+        bool ok = idx < NCH && j < M;
+        uintptr_t src = 0;
+        if (ok) {
+            const uintptr_t a = (uintptr_t)(hbase + (int64_t)j * nb1);
+            const uintptr_t a0 = a & ~(uintptr_t)15;
+            src = a0 + 16u * (uintptr_t)c;
+            ok = src < a + R::kBytes;      // only chunks holding bytes of this row
         }
-    }
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int idx = threadIdx.x + it * kThreads;
-        if (idx < NCH) *(u32x4*)(raw + 16 * idx) = buf[it];
+        if (ok) dma16((const void*)src, raw + 16 * wbase);
     }
 }
 
-// 8 consecutive values of row `key` starting at value 8*grp, decoded to fp16.
+// 8 consecutive values of a row, starting at value 8*grp, decoded to fp16.
+//   q8_0: from the staged raw slot (rawslot, row offset `off` within its first chunk)
+//   F32/F16/BF16: straight from global memory (rows are 16-byte aligned)
 template <int D>
 FAB_DEV f16x8 decode8(const char* rowp, int type, int grp, const unsigned char* rawslot, int off) {
     f16x8 r;
@@ -105,41 +190,27 @@ FAB_DEV f16x8 decode8(const char* rowp, int type, int grp, const unsigned char* 
     return r;
 }
 
-// Phase 2: decode keys [j0, j0+KEYS) into dst ([key][d], stride kLd) and, if TRANS, into
-// dstT ([d][tpos(key)], stride kLdT). Keys >= M become 0. Work item = 4 keys x 8 values.
-template <int D, int KEYS, bool TRANS>
+// Decode keys [j0, j0+KEYS) into the swizzled fp16 tile dst[key][D]. Keys >= M become 0.
+template <int D, int KEYS>
 FAB_DEV void decode_tile(const char* base, int type, int64_t nb1, int64_t nb2, int hk, int j0,
-                         int M, const unsigned char* raw, _Float16* dst, _Float16* dstT) {
-    using L = TileLds<D, KEYS>;
+                         int M, const unsigned char* raw, _Float16* dst) {
     constexpr int GROUPS = D / 8;
-    constexpr int ITEMS = (KEYS / 4) * GROUPS;
+    constexpr int ITEMS = KEYS * GROUPS;
     const char* hbase = base + (int64_t)hk * nb2;
     for (int item = threadIdx.x; item < ITEMS; item += kThreads) {
-        const int kq = item / GROUPS;
-        const int grp = item - kq * GROUPS;
-        f16x8 vals[4];
+        const int key = item / GROUPS;
+        const int grp = item - key * GROUPS;
+        const int j = j0 + key;
+        f16x8 v;
+        if (j < M) {
+            const char* rowp = hbase + (int64_t)j * nb1;
+            const int off = (int)((uintptr_t)rowp & 15);
+            v = decode8<D>(rowp, type, grp, raw + key * Q8Row<D>::kSlot, off);
+        } else {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int key = 4 * kq + kk;
-            const int j = j0 + key;
-            if (j < M) {
-                const char* rowp = hbase + (int64_t)j * nb1;
-                const int off = (int)((uintptr_t)rowp & 15);
-                vals[kk] = decode8<D>(rowp, type, grp, raw + key * Q8Row<D>::kSlot, off);
-            } else {
-#pragma unroll
-                for (int t = 0; t < 8; ++t) vals[kk][t] = (_Float16)0.0f;
-            }
-            *(f16x8*)(dst + key * L::kLd + 8 * grp) = vals[kk];
+            for (int t = 0; t < 8; ++t) v[t] = (_Float16)0.0f;
         }
-        if (TRANS) {
-            const int pos = tpos(4 * kq);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                f16x4 col = {vals[0][t], vals[1][t], vals[2][t], vals[3][t]};
-                *(f16x4*)(dstT + (8 * grp + t) * L::kLdT + pos) = col;
-            }
-        }
+        *(f16x8*)(dst + tile_off<D>(key, grp)) = v;
     }
 }
 
