@@ -192,7 +192,7 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
         hipLaunchKernelGGL(dqreduce_kernel<D>, dim3(blocks), dim3(kThreads), 0, st, P);
     }
     pm.mark(5);
-    hipLaunchKernelGGL(kvpass_kernel<D>, dim3(g.KVT * g.Hkv), dim3(kThreads), 0, st, P);
+    hipLaunchKernelGGL(kvpass_kernel<D>, dim3(g.KVT * g.Hkv), dim3(kKVThreads), 0, st, P);
     pm.mark(6);
     return hipGetLastError() == hipSuccess ? FA_BACK_OK : FA_BACK_EHIP;
 }

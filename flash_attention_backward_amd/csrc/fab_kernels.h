@@ -469,100 +469,87 @@ __global__ __launch_bounds__(kThreads) void dqreduce_kernel(Params p) {
 
 // ----------------------------------------------------------------------------- key side
 
-// Workgroup: one KV head, 128 keys (32 per wave). Each wave keeps its keys' K and V
-// fragments and its dK^T, dV^T accumulators in registers and walks every 32-row block of the
-// group. Each row block of q and dO (fp16, row-major) is copied HBM -> LDS once per
-// workgroup by DMA, double-buffered so block rb+1 arrives while block rb is computed, and
-// read by all four waves. S = Q K^T and dP = dO V^T put one key per lane column and 16 rows
-// per lane, which is the layout the second operand of dV^T += dO^T P and dK^T += Q^T dS
-// needs; the first operands are transpose reads of the same LDS blocks.
+// Workgroup: one KV head, 128 keys in 4 blocks of 32, and 12 waves with one of three roles
+// per key block (wave w: role w/4, key block w%4, so each SIMD runs one wave of each role):
+//   S wave  K fragments in registers, V tile in LDS: S = Q K^T and dP = dO V^T for every
+//           32-row block, then P and dS, handed over through LDS
+//   dK wave dK^T += Q^T dS   (128 accumulator registers)
+//   dV wave dV^T += dO^T P   (128 accumulator registers)
+// Each role runs its own loop over the row blocks with the same two barriers per block, so
+// the compiler keeps only that role's state live and every wave stays within the 170
+// registers that three waves per SIMD allow. The q and dO row blocks (fp16, row-major, with
+// their lse/delta) are copied HBM -> LDS once per workgroup by DMA, double-buffered.
+// S = Q K^T puts one key per lane column and 16 rows per lane, which is the layout the
+// second operand of the dK/dV products needs; their first operands are transpose reads of
+// the same LDS blocks.
+constexpr int kKVWaves = 12;
+constexpr int kKVThreads = kKVWaves * kWave;
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void kvpass_kernel(Params p) {
+struct KVLds {
+    static constexpr int kBlk = 32 * D;                                  // halfs per row block
+    static constexpr int kRaw = RawTile<D, kQTileKeys>::kBytes;
+    static constexpr int kVTile = kKVKeys * D * 2;                       // resident V tile
+    static constexpr int kBuf = 2 * kBlk * 2 + 256;                      // q, dO, 32 lse, 32 delta
+    static constexpr int kExch = 4 * 2 * 2 * 64 * 16;                    // [kb][P,dS][rh][lane] x 16 B
+    static constexpr int kSetup = kQTileKeys * D * 2 + 2 * kRaw;         // K half tile + raw
+    static constexpr int kWork = 2 * kBuf + kExch;
+    static constexpr int kBytes = kVTile + (kSetup > kWork ? kSetup : kWork);
+};
+
+template <int D>
+__global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
+    using L = KVLds<D>;
     constexpr int KS = D / 16;
     constexpr int MD = D / 32;
-    constexpr int BLK = 32 * D;                                   // halfs per row block
-    constexpr int RAW = RawTile<D, kQTileKeys>::kBytes;
-    constexpr int VT = kKVKeys * D * 2;                           // resident V tile (bytes)
-    constexpr int SETUP = kQTileKeys * D * 2 + 2 * RAW;           // K half-tile decode + raw
-    constexpr int BUFB = 2 * BLK * 2 + 256;                       // q, dO blocks + 32 lse + 32 delta
-    constexpr int LOOP = 2 * BUFB;                                // double-buffered
-    constexpr int LDSB = VT + (SETUP > LOOP ? SETUP : LOOP);
-    __shared__ __attribute__((aligned(16))) unsigned char lds[LDSB];
-    _Float16* sV = (_Float16*)lds;          // [128 keys][D], swizzled, for the whole kernel
-    unsigned char* smem = lds + VT;         // setup scratch, then the row-block buffers
+    constexpr int BLK = L::kBlk;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
+    _Float16* sV = (_Float16*)lds;                    // [128 keys][D], swizzled
+    unsigned char* work = lds + L::kVTile;            // setup scratch, then buffers + exchange
+    unsigned char* exch = work + 2 * L::kBuf;
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l32 = lane & 31, g = lane >> 5;
+    const int role = wave >> 2, kb = wave & 3;
     const int hk = blockIdx.x % p.Hkv;
     const int kvt = blockIdx.x / p.Hkv;
     const int key0 = kvt * kKVKeys;
-    const int myj = key0 + 32 * wave + l32;
+    const int myj = key0 + 32 * kb + l32;
     const bool key_ok = myj < p.M;
     const int rowsHK = p.RB * 32;
+    const int myt = 2 * kvt + (kb >> 1);              // 64-key tile of this key block
 
-    // K fragments in registers: B[d][key] of S = Q K^T, i.e. K[key][16ks + 8g .. +7];
-    // V stays in LDS and its fragments are read per row block
+    // ---- setup: V tile resident in LDS; K fragments into the S waves' registers
     f16x8 bk[KS];
     {
-        _Float16* sK = (_Float16*)smem;
-        unsigned char* rawK = smem + kQTileKeys * D * 2;
-        unsigned char* rawV = rawK + RAW;
+        _Float16* sK = (_Float16*)work;
+        unsigned char* rawK = work + kQTileKeys * D * 2;
+        unsigned char* rawV = rawK + L::kRaw;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int j0 = key0 + half * kQTileKeys;
             __syncthreads();
-            if (p.k_type == FA_BACK_Q8_0) dma_raw_tile<D, kQTileKeys>(p.k, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK);
-            if (p.v_type == FA_BACK_Q8_0) dma_raw_tile<D, kQTileKeys>(p.v, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV);
+            if (p.k_type == FA_BACK_Q8_0)
+                dma_raw_tile<D, kQTileKeys, kKVThreads>(p.k, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK);
+            if (p.v_type == FA_BACK_Q8_0)
+                dma_raw_tile<D, kQTileKeys, kKVThreads>(p.v, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV);
             wait_all_mem();
             __syncthreads();
-            decode_tile<D, kQTileKeys>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, sK);
-            decode_tile<D, kQTileKeys>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV,
-                                       sV + half * kQTileKeys * D);
+            decode_tile<D, kQTileKeys, kKVThreads>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, sK);
+            decode_tile<D, kQTileKeys, kKVThreads>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV,
+                                                   sV + half * kQTileKeys * D);
             __syncthreads();
-            if ((wave >> 1) == half) {
+            if (role == 0 && (kb >> 1) == half) {
                 const Swz z = make_swz<D>(lane);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) bk[ks] = frag_rows<D>(sK, 32 * (wave & 1), ks, lane, z);
+                for (int ks = 0; ks < KS; ++ks) bk[ks] = frag_rows<D>(sK, 32 * (kb & 1), ks, lane, z);
             }
         }
         __syncthreads();   // the setup region becomes the row-block buffers
     }
 
-    const int eq = p.scal[0], edo = p.scal[1];
-    const float sc2 = p.scale * ldexpf(1.0f, -eq) * kLog2e;
-    const int ksx = load_ds_exponent(p);
-    const float dsf = ldexpf(1.0f, -ksx);
-    const float pf = ldexpf(1.0f, kPScaleLog2);
-
-    f32x16 dkacc[MD], dvacc[MD];
-#pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) dkacc[md][v] = dvacc[md][v] = 0.0f;
-
-    // DMA of row block rb (q and dO) into buffer b; the LDS copy is swizzled (tile_off)
-    // by choosing each lane's source chunk
-    auto dma_block = [&](int rbx, int b) {
-        constexpr int NI = BLK / 512;                 // 64-lane x 16-byte instructions per tensor
-        unsigned char* base = smem + b * BUFB;
-        _Float16* dstq = (_Float16*)base;
-        for (int ins = wave; ins < 2 * NI; ins += kWaves) {
-            const int ten = ins / NI, ii = ins - (ins / NI) * NI;
-            const int P = ii * 64 + lane;             // physical 16-byte slot in the block
-            const int row = P / (D / 8), pc = P - (P / (D / 8)) * (D / 8);
-            const int c = swz_chunk<D>(row, pc);      // the swizzle is an involution
-            const _Float16* src = (ten ? p.dr : p.qr) + (((int64_t)hk * rowsHK + rbx * 32 + row) * D + 8 * c);
-            dma16(src, dstq + ten * BLK + ii * 512);
-        }
-        if (wave == kWaves - 1 && lane < 16) {        // 32 lse then 32 delta values
-            const float* src = (lane < 8 ? p.row_lse2 : p.row_dlt) + (int64_t)hk * rowsHK + rbx * 32 + 4 * (lane & 7);
-            dma16(src, base + 2 * BLK * 2);
-        }
-    };
-
-    // class of row block rb for this wave's 64-key half, and whether any wave needs the block
-    const int myt = 2 * kvt + (wave >> 1);
-    auto wave_class = [&](int rbx) -> int {
+    // ---- row-block schedule (identical in every role)
+    auto kb_class = [&](int rbx) -> int {
         return myt < p.KT ? mask_class(p, hk, rbx, myt) : kMaskDead;
     };
     auto block_needed = [&](int rbx) -> bool {
@@ -574,87 +561,136 @@ __global__ __launch_bounds__(kThreads, 1) void kvpass_kernel(Params p) {
         while (rbx < p.RB && !block_needed(rbx)) ++rbx;
         return rbx;
     };
+    // DMA of row block rbx (q, dO and their 32 lse / 32 delta values) into buffer b, issued by
+    // the 8 accumulating waves; the LDS copy is swizzled by choosing each lane's source chunk
+    auto dma_block = [&](int rbx, int b) {
+        constexpr int NI = BLK / 512;                 // 64-lane x 16-byte instructions per tensor
+        const int aw = wave - 4;                      // 0..7
+        unsigned char* base = work + b * L::kBuf;
+        for (int ins = aw; ins < 2 * NI; ins += 8) {
+            const int ten = ins / NI, ii = ins - (ins / NI) * NI;
+            const int P = ii * 64 + lane;
+            const int row = P / (D / 8), pc = P - (P / (D / 8)) * (D / 8);
+            const int c = swz_chunk<D>(row, pc);
+            const _Float16* src = (ten ? p.dr : p.qr) + (((int64_t)hk * rowsHK + rbx * 32 + row) * D + 8 * c);
+            dma16(src, base + ten * BLK * 2 + ii * 1024);
+        }
+        if (aw == 7 && lane < 16) {
+            const float* src = (lane < 8 ? p.row_lse2 : p.row_dlt) + (int64_t)hk * rowsHK + rbx * 32 + 4 * (lane & 7);
+            dma16(src, base + 2 * BLK * 2);
+        }
+    };
+    unsigned char* exP = exch + (kb * 2 + 0) * 2048;   // P  B-operand images [rh][lane] x 16 B
+    unsigned char* exS = exch + (kb * 2 + 1) * 2048;   // dS B-operand images
 
-    int rb = next_needed(0);
-    int buf = 0;
-    if (rb < p.RB) dma_block(rb, 0);
-    while (rb < p.RB) {
-        const int rbn = next_needed(rb + 1);
-        const _Float16* bq = (const _Float16*)(smem + buf * BUFB);
-        const _Float16* bdo = bq + BLK;
-        const float* lrow = (const float*)(smem + buf * BUFB + 2 * BLK * 2);   // lse2 of the block
-        const float* drow = lrow + 32;                                          // delta of the block
-        const int cls = wave_class(rb);
-        wait_all_mem();
-        __syncthreads();   // block rb landed everywhere; every wave is done with the last block
-        if (rbn < p.RB) dma_block(rbn, buf ^ 1);
+    const int first = next_needed(0);
+    if (role != 0 && first < p.RB) dma_block(first, 0);
 
-        if (cls != kMaskDead) {   // uniform over the wave
-            const Swz z = make_swz<D>(lane);
-            f32x16 sa, pa;
+    const int eq = p.scal[0], edo = p.scal[1];
+    const int ksx = load_ds_exponent(p);
+
+    if (role == 0) {
+        // ================= S waves
+        const float sc2 = p.scale * ldexpf(1.0f, -eq) * kLog2e;
+        const float dsf = ldexpf(1.0f, -ksx);
+        const float pf = ldexpf(1.0f, kPScaleLog2);
+        int buf = 0;
+        for (int rb = first; rb < p.RB;) {
+            const int rbn = next_needed(rb + 1);
+            const int cls = kb_class(rb);
+            wait_all_mem();
+            __syncthreads();   // A: block rb landed; the exchange slots are free
+            if (cls != kMaskDead) {
+                const Swz z = make_swz<D>(lane);
+                const _Float16* bq = (const _Float16*)(work + buf * L::kBuf);
+                const _Float16* bdo = bq + BLK;
+                const float* lrow = (const float*)(work + buf * L::kBuf + 2 * BLK * 2);
+                const float* drow = lrow + 32;
+                f32x16 sa, pa;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
+                for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                sa = mfma32(frag_rows<D>(bq, 0, ks, lane, z), bk[ks], sa);
-                pa = mfma32(frag_rows<D>(bdo, 0, ks, lane, z), frag_rows<D>(sV, 32 * wave, ks, lane, z), pa);
-                if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the load lookahead
-            }
-            f32x4 l4[4], d4[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                l4[b] = *(const f32x4*)(lrow + 8 * b + 4 * g);
-                d4[b] = *(const f32x4*)(drow + 8 * b + 4 * g);
-            }
-            f16x8 bp[2], bs[2];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float l2 = l4[v >> 2][v & 3];
-                float pv = 0.0f;
-                if (key_ok && l2 != neg_inf()) {
-                    float sv = sa[v] * sc2;
-                    if (cls == kMaskMixed) {
-                        const int r = 32 * rb + crow(v, g);
-                        const int ii = r / p.G, gh = r - (r / p.G) * p.G;
-                        const char* mrow = p.mask + (int64_t)ii * p.m_nb1 +
-                                           (int64_t)(p.Hm == 1 ? 0 : hk * p.G + gh) * p.m_nb2;
-                        sv += mask_at(mrow, p.m_type, myj) * kLog2e;
-                    }
-                    pv = fast_exp2(sv - l2);
+                for (int ks = 0; ks < KS; ++ks) {
+                    sa = mfma32(frag_rows<D>(bq, 0, ks, lane, z), bk[ks], sa);
+                    pa = mfma32(frag_rows<D>(bdo, 0, ks, lane, z), frag_rows<D>(sV, 32 * kb, ks, lane, z), pa);
                 }
-                const float dsv = pv * (pa[v] - d4[v >> 2][v & 3]);
-                bp[v >> 3][v & 7] = (_Float16)(pv * pf);
-                bs[v >> 3][v & 7] = (_Float16)(dsv * dsf);
-            }
+                f16x8 bp[2], bs[2];
 #pragma unroll
-            for (int md = 0; md < MD; ++md) {
+                for (int b = 0; b < 4; ++b) {
+                    const f32x4 l4 = *(const f32x4*)(lrow + 8 * b + 4 * g);
+                    const f32x4 d4 = *(const f32x4*)(drow + 8 * b + 4 * g);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int v = 4 * b + u;
+                        float pv = 0.0f;
+                        if (key_ok && l4[u] != neg_inf()) {
+                            float sv = sa[v] * sc2;
+                            if (cls == kMaskMixed) {
+                                const int r = 32 * rb + crow(v, g);
+                                const int ii = r / p.G, gh = r - (r / p.G) * p.G;
+                                const char* mrow = p.mask + (int64_t)ii * p.m_nb1 +
+                                                   (int64_t)(p.Hm == 1 ? 0 : hk * p.G + gh) * p.m_nb2;
+                                sv += mask_at(mrow, p.m_type, myj) * kLog2e;
+                            }
+                            pv = fast_exp2(sv - l4[u]);
+                        }
+                        const float dsv = pv * (pa[v] - d4[u]);
+                        bp[v >> 3][v & 7] = (_Float16)(pv * pf);
+                        bs[v >> 3][v & 7] = (_Float16)(dsv * dsf);
+                    }
+                }
 #pragma unroll
                 for (int rh = 0; rh < 2; ++rh) {
-                    dvacc[md] = mfma32(frag_cols<D>(bdo, md, 16 * rh, lane, z), bp[rh], dvacc[md]);
-                    dkacc[md] = mfma32(frag_cols<D>(bq, md, 16 * rh, lane, z), bs[rh], dkacc[md]);
+                    *(f16x8*)(exP + rh * 1024 + lane * 16) = bp[rh];
+                    *(f16x8*)(exS + rh * 1024 + lane * 16) = bs[rh];
                 }
-                if ((md & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();   // B: P and dS of block rb are in the exchange
+            rb = rbn;
+            buf ^= 1;
+        }
+        return;
+    }
+
+    // ================= accumulating waves (role 1: dK with q, role 2: dV with dO)
+    f32x16 acc[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[md][v] = 0.0f;
+    const unsigned char* exIn = role == 1 ? exS : exP;
+    int buf = 0;
+    for (int rb = first; rb < p.RB;) {
+        const int rbn = next_needed(rb + 1);
+        const int cls = kb_class(rb);
+        wait_all_mem();
+        __syncthreads();   // A
+        if (rbn < p.RB) dma_block(rbn, buf ^ 1);
+        __syncthreads();   // B
+        if (cls != kMaskDead) {
+            const Swz z = make_swz<D>(lane);
+            const _Float16* src = (const _Float16*)(work + buf * L::kBuf) + (role == 1 ? 0 : BLK);
+            const f16x8 b0 = *(const f16x8*)(exIn + lane * 16);
+            const f16x8 b1 = *(const f16x8*)(exIn + 1024 + lane * 16);
+#pragma unroll
+            for (int md = 0; md < MD; ++md) {
+                acc[md] = mfma32(frag_cols<D>(src, md, 0, lane, z), b0, acc[md]);
+                acc[md] = mfma32(frag_cols<D>(src, md, 16, lane, z), b1, acc[md]);
             }
         }
         rb = rbn;
         buf ^= 1;
     }
-
     if (!key_ok) return;
-    const float fk = p.scale * ldexpf(1.0f, ksx - eq - edo);
-    const float fv = ldexpf(1.0f, -kPScaleLog2 - edo);
-    float* dkr = p.dk + ((int64_t)hk * p.M + myj) * D;
-    float* dvr = p.dv + ((int64_t)hk * p.M + myj) * D;
+    const float fac = role == 1 ? p.scale * ldexpf(1.0f, ksx - eq - edo) : ldexpf(1.0f, -kPScaleLog2 - edo);
+    float* dst = (role == 1 ? p.dk : p.dv) + ((int64_t)hk * p.M + myj) * D;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            f32x4 ok = {dkacc[md][4 * b] * fk, dkacc[md][4 * b + 1] * fk, dkacc[md][4 * b + 2] * fk,
-                        dkacc[md][4 * b + 3] * fk};
-            f32x4 ov = {dvacc[md][4 * b] * fv, dvacc[md][4 * b + 1] * fv, dvacc[md][4 * b + 2] * fv,
-                        dvacc[md][4 * b + 3] * fv};
-            *(f32x4*)(dkr + 32 * md + 8 * b + 4 * g) = ok;
-            *(f32x4*)(dvr + 32 * md + 8 * b + 4 * g) = ov;
+            f32x4 o = {acc[md][4 * b] * fac, acc[md][4 * b + 1] * fac, acc[md][4 * b + 2] * fac,
+                       acc[md][4 * b + 3] * fac};
+            *(f32x4*)(dst + 32 * md + 8 * b + 4 * g) = o;
         }
 }
 

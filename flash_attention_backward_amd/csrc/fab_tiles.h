@@ -26,14 +26,14 @@ FAB_DEV int swz_chunk(int row, int chunk) {
 template <int D>
 FAB_DEV int tile_off(int row, int chunk) { return row * D + 8 * swz_chunk<D>(row, chunk); }
 
-// Per-lane swizzle terms. Both depend only on the lane (tile row blocks start at multiples of
-// 16 rows); they are passed through an opaque move once per loop iteration so that the
-// compiler computes the per-step LDS addresses in the loop instead of keeping (and
-// spilling) one precomputed address per step.
+// Per-lane swizzle terms of the fragment reads below. They depend only on the lane (row
+// blocks start at multiples of 16 rows) and are passed through an opaque move where a loop
+// starts, so that the compiler computes each step's LDS address in the loop instead of
+// keeping one precomputed address per step alive (and spilling them).
 struct Swz {
-    int rows;    // XOR term of a frag_rows read: swizzle of row lane%32
-    int col0;    // XOR term of frag_cols read j = 0
-    int col1;    // XOR term of frag_cols read j = 1
+    int rows;    // XOR term of frag_rows: swizzle of row lane%32
+    int col0;    // XOR term of frag_cols, first transpose read
+    int col1;    // XOR term of frag_cols, second transpose read
 };
 
 FAB_DEV int opaque(int x) {
@@ -120,17 +120,17 @@ struct RawTile {
 
 // Issue the DMA of the raw bytes of keys [j0, j0+KEYS) of head hk into `raw` (q8_0 only).
 // Chunk idx = key*kChunks + c lands at raw + 16*idx; chunks outside the row are skipped.
-template <int D, int KEYS>
+template <int D, int KEYS, int NT = kThreads>
 FAB_DEV void dma_raw_tile(const char* base, int64_t nb1, int64_t nb2, int hk, int j0, int M,
                           unsigned char* raw) {
     using R = Q8Row<D>;
     constexpr int NCH = KEYS * R::kChunks;
-    constexpr int IT = (NCH + kThreads - 1) / kThreads;
+    constexpr int IT = (NCH + NT - 1) / NT;
     const char* hbase = base + (int64_t)hk * nb2;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const int wbase = it * kThreads + wave * 64;   // first chunk of this wave's instruction
+        const int wbase = it * NT + wave * 64;         // first chunk of this wave's instruction
         if (wbase >= NCH) break;                        // wave-uniform
         const int idx = wbase + lane;
         const int key = idx / R::kChunks;
@@ -191,13 +191,13 @@ FAB_DEV f16x8 decode8(const char* rowp, int type, int grp, const unsigned char* 
 }
 
 // Decode keys [j0, j0+KEYS) into the swizzled fp16 tile dst[key][D]. Keys >= M become 0.
-template <int D, int KEYS>
+template <int D, int KEYS, int NT = kThreads>
 FAB_DEV void decode_tile(const char* base, int type, int64_t nb1, int64_t nb2, int hk, int j0,
                          int M, const unsigned char* raw, _Float16* dst) {
     constexpr int GROUPS = D / 8;
     constexpr int ITEMS = KEYS * GROUPS;
     const char* hbase = base + (int64_t)hk * nb2;
-    for (int item = threadIdx.x; item < ITEMS; item += kThreads) {
+    for (int item = threadIdx.x; item < ITEMS; item += NT) {
         const int key = item / GROUPS;
         const int grp = item - key * GROUPS;
         const int j = j0 + key;
