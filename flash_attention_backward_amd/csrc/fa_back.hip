@@ -180,11 +180,11 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
                                                   (g.KT + kClassTilesPerBlock - 1) / kClassTilesPerBlock),
                            dim3(kThreads), 0, st, P);
     pm.mark(1);
-    hipLaunchKernelGGL((qpass_kernel<D, false>), dim3(g.RT * g.Hkv, g.splits), dim3(kThreads), 0, st, P);
+    hipLaunchKernelGGL((qpass_kernel<D, false>), dim3(g.RT * g.Hkv, g.splits), dim3(kQThreads), 0, st, P);
     pm.mark(2);
     hipLaunchKernelGGL(merge_kernel, dim3(g.nbound), dim3(kThreads), 0, st, P);
     pm.mark(3);
-    hipLaunchKernelGGL((qpass_kernel<D, true>), dim3(g.RT * g.Hkv, g.splits), dim3(kThreads), 0, st, P);
+    hipLaunchKernelGGL((qpass_kernel<D, true>), dim3(g.RT * g.Hkv, g.splits), dim3(kQThreads), 0, st, P);
     pm.mark(4);
     if (g.splits > 1) {
         const int64_t n4 = (int64_t)g.Hkv * g.RB * 32 * (D / 4);

@@ -189,27 +189,49 @@ FAB_DEV float mask_at(const char* mrow, int type, int j) {
 
 // ----------------------------------------------------------------------------- query side
 
-// Workgroup: one KV head, kWaves row blocks of 32 rows (one per wave), one key-range split.
-// Each wave keeps its rows' q and dO fragments in registers and walks the split's 64-key
-// tiles; K and V tiles are decoded once per workgroup into LDS and shared by the four
-// waves. The raw q8_0 bytes of tile t+1 are fetched by DMA while tile t is computed.
-// The 32x32 products are computed transposed, S^T = K Q^T, so a lane holds one query row
-// (column lane%32) and 16 keys; the two lanes l and l^32 together hold the row's 32 keys.
+// Workgroup: one KV head, 4 row blocks of 32 rows, one key-range split, and 8 waves:
+//   S waves (0..3)  one row block each; q and dO fragments in registers. For every 32-key
+//                   sub-tile: S^T = K Q^T and dP^T = V dO^T, then walk 1 updates the online
+//                   softmax statistics, walk 2 forms dS = P (dP - delta) and hands it over
+//                   through LDS.
+//   K waves (4..7)  decode sub-tile s+1 of K and V into LDS (its q8_0 bytes were fetched by
+//                   DMA one sub-tile earlier, and they queue the DMA of s+2) while the S waves
+//                   compute s; in walk 2 each also holds the dQ accumulators of one row block
+//                   and consumes the dS of sub-tile s-1: dQ^T += K^T dS^T.
+// K sub-tiles are triple-buffered (used by the S waves at s and the K waves at s+1), V
+// sub-tiles and the dS exchange double-buffered; one barrier per sub-tile. Every wave stays
+// within 256 registers, so each SIMD runs an S wave and a K wave.
+// S^T = K Q^T puts one query row per lane column and 16 keys per lane; lanes l and l^32
+// together hold a row's 32 keys.
+constexpr int kQWaves = 8;
+constexpr int kQThreads = kQWaves * kWave;
+constexpr int kSubKeys = 32;
+
+template <int D>
+struct QLds {
+    static constexpr int kKT = kSubKeys * D;                       // halfs per K or V sub-tile
+    static constexpr int kRaw = RawTile<D, kSubKeys>::kBytes;      // q8_0 bytes of one sub-tile
+    static constexpr int kOffK = 0;                                // 3 K sub-tiles
+    static constexpr int kOffV = kOffK + 3 * kKT * 2;              // 2 V sub-tiles
+    static constexpr int kOffRaw = kOffV + 2 * kKT * 2;            // [2][K, V] raw bytes
+    static constexpr int kOffEx = kOffRaw + 4 * kRaw;              // [2][4 row blocks] dS, 2 KB
+    static constexpr int kBytes = kOffEx + 2 * 4 * 2048;
+};
+
 template <int D, bool GRAD>
-__global__ __launch_bounds__(kThreads, 1) void qpass_kernel(Params p) {
+__global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
+    using L = QLds<D>;
     constexpr int KS = D / 16;     // 16-deep steps of a contraction over d
     constexpr int MD = D / 32;     // 32-wide d blocks of dQ
-    constexpr int RAW = RawTile<D, kQTileKeys>::kBytes;
-    __shared__ __attribute__((aligned(16))) _Float16 sK[kQTileKeys * D];
-    __shared__ __attribute__((aligned(16))) _Float16 sV[kQTileKeys * D];
-    __shared__ __attribute__((aligned(16))) unsigned char sRaw[2][2][RAW];   // [buffer][K, V]
+    __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l32 = lane & 31, g = lane >> 5;
+    const int role = wave >> 2, w4 = wave & 3;
     const int hk = blockIdx.x % p.Hkv;
     const int rt = blockIdx.x / p.Hkv;
     const int split = blockIdx.y;
-    const int rb = rt * kWaves + wave;
+    const int rb = rt * kWaves + w4;
     const bool active = rb < p.RB;
     const int rowsHK = p.RB * 32;
     const int r = rb * 32 + l32;
@@ -217,162 +239,178 @@ __global__ __launch_bounds__(kThreads, 1) void qpass_kernel(Params p) {
     const int h = hk * p.G + gh;
     const bool row_ok = active && r < p.R;
     const int ridx = hk * rowsHK + r;
-    const bool kq8 = p.k_type == FA_BACK_Q8_0, vq8 = p.v_type == FA_BACK_Q8_0;
-
+    const int ktid = threadIdx.x - 4 * kWave;        // K-wave thread index 0..255
+    const int NS = (p.M + kSubKeys - 1) / kSubKeys;
+    const int s_begin = 2 * split * p.tiles_per_split;
+    const int s_end = min(NS, 2 * min(p.KT, (split + 1) * p.tiles_per_split));
     const int eq = p.scal[0], edo = p.scal[1];
-    const float sc2 = p.scale * ldexpf(1.0f, -eq) * kLog2e;
 
-    f16x8 bq[KS], bd[KS];
-    if (active) {
-        const _Float16* rq = p.qr + ((int64_t)hk * rowsHK + r) * D;
-        const _Float16* rd = p.dr + ((int64_t)hk * rowsHK + r) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            bq[ks] = *(const f16x8*)(rq + 16 * ks + 8 * g);
-            bd[ks] = *(const f16x8*)(rd + 16 * ks + 8 * g);
-        }
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int t = 0; t < 8; ++t) bq[ks][t] = bd[ks][t] = (_Float16)0.0f;
+    auto sK = [&](int s) { return (_Float16*)(lds + L::kOffK) + (s % 3) * L::kKT; };
+    auto sV = [&](int s) { return (_Float16*)(lds + L::kOffV) + (s & 1) * L::kKT; };
+    auto rawK = [&](int s) { return lds + L::kOffRaw + ((s & 1) * 2 + 0) * L::kRaw; };
+    auto rawV = [&](int s) { return lds + L::kOffRaw + ((s & 1) * 2 + 1) * L::kRaw; };
+    auto exch = [&](int s) { return lds + L::kOffEx + ((s & 1) * 4 + w4) * 2048; };
+    auto kdma = [&](int s) {
+        if (p.k_type == FA_BACK_Q8_0)
+            dma_raw_tile<D, kSubKeys, 256>(p.k, p.k_nb1, p.k_nb2, hk, s * kSubKeys, p.M, rawK(s), ktid);
+        if (p.v_type == FA_BACK_Q8_0)
+            dma_raw_tile<D, kSubKeys, 256>(p.v, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), ktid);
+    };
+    auto kdecode = [&](int s) {
+        decode_tile<D, kSubKeys, 256>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, s * kSubKeys, p.M, rawK(s), sK(s), ktid);
+        decode_tile<D, kSubKeys, 256>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), sV(s), ktid);
+    };
+    auto wclass = [&](int s) { return active ? mask_class(p, hk, rb, s >> 1) : kMaskDead; };
+
+    // prologue: sub-tile s_begin decoded, the bytes of s_begin+1 on their way
+    if (role == 1 && s_begin < s_end) kdma(s_begin);
+    wait_all_mem();
+    __syncthreads();
+    if (role == 1 && s_begin < s_end) {
+        kdecode(s_begin);
+        if (s_begin + 1 < s_end) kdma(s_begin + 1);
     }
-    const bool has_mask = p.m_type != FA_BACK_NONE;
-    const char* mrow = (has_mask && row_ok)
-        ? p.mask + (int64_t)i * p.m_nb1 + (int64_t)(p.Hm == 1 ? 0 : h) * p.m_nb2 : nullptr;
 
-    // walk 1 state
-    float m_run = neg_inf();
-    double l64 = 0.0, d64 = 0.0;
-    float bmax = 0.0f;
-    // walk 2 state
-    float lse2 = neg_inf(), dlt = 0.0f, dsf = 1.0f;
-    int ksx = 0;
-    f32x16 dqacc[GRAD ? MD : 1];
-    if (GRAD) {
-        if (row_ok) {
-            lse2 = p.row_lse2[ridx];
-            dlt = p.row_dlt[ridx];
+    if (role == 0) {
+        // ================= S waves
+        f16x8 bq[KS], bd[KS];
+        if (active) {
+            const _Float16* rq = p.qr + ((int64_t)hk * rowsHK + r) * D;
+            const _Float16* rd = p.dr + ((int64_t)hk * rowsHK + r) * D;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                bq[ks] = *(const f16x8*)(rq + 16 * ks + 8 * g);
+                bd[ks] = *(const f16x8*)(rd + 16 * ks + 8 * g);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) bq[ks][t] = bd[ks][t] = (_Float16)0.0f;
         }
-        ksx = load_ds_exponent(p);
-        dsf = ldexpf(1.0f, -ksx);
-#pragma unroll
-        for (int md = 0; md < (GRAD ? MD : 1); ++md)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) dqacc[md][v] = 0.0f;
-    }
-    const bool dead = (lse2 == neg_inf());
+        const bool has_mask = p.m_type != FA_BACK_NONE;
+        const char* mrow = (has_mask && row_ok)
+            ? p.mask + (int64_t)i * p.m_nb1 + (int64_t)(p.Hm == 1 ? 0 : h) * p.m_nb2 : nullptr;
+        const float sc2 = p.scale * ldexpf(1.0f, -eq) * kLog2e;
+        // walk 1 state
+        float m_run = neg_inf();
+        double l64 = 0.0, d64 = 0.0;
+        float bmax = 0.0f;
+        // walk 2 state
+        float lse2 = neg_inf(), dlt = 0.0f, dsf = 1.0f;
+        if (GRAD) {
+            if (row_ok) {
+                lse2 = p.row_lse2[ridx];
+                dlt = p.row_dlt[ridx];
+            }
+            dsf = ldexpf(1.0f, -load_ds_exponent(p));
+        }
+        const bool dead = (lse2 == neg_inf());
 
-    const int t0 = split * p.tiles_per_split;
-    const int t1 = min(p.KT, t0 + p.tiles_per_split);
-    if (t0 < t1) {
-        if (kq8) dma_raw_tile<D, kQTileKeys>(p.k, p.k_nb1, p.k_nb2, hk, t0 * kQTileKeys, p.M, sRaw[0][0]);
-        if (vq8) dma_raw_tile<D, kQTileKeys>(p.v, p.v_nb1, p.v_nb2, hk, t0 * kQTileKeys, p.M, sRaw[0][1]);
-    }
-    for (int t = t0; t < t1; ++t) {
-        const int j0 = t * kQTileKeys;
-        const int buf = (t - t0) & 1;
-        wait_all_mem();
-        __syncthreads();   // raw(t) landed everywhere; every wave is done with tile t-1
-        // mask class of this wave's rows; a tile no row of the workgroup sees is skipped whole
-        const int cls = active ? mask_class(p, hk, rb, t) : kMaskDead;
-        bool wg_dead = true;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const int rbw = rt * kWaves + w;
-            wg_dead = wg_dead && (rbw >= p.RB || mask_class(p, hk, rbw, t) == kMaskDead);
-        }
-        if (t + 1 < t1) {
-            if (kq8) dma_raw_tile<D, kQTileKeys>(p.k, p.k_nb1, p.k_nb2, hk, j0 + kQTileKeys, p.M, sRaw[buf ^ 1][0]);
-            if (vq8) dma_raw_tile<D, kQTileKeys>(p.v, p.v_nb1, p.v_nb2, hk, j0 + kQTileKeys, p.M, sRaw[buf ^ 1][1]);
-        }
-        if (wg_dead) continue;   // uniform over the workgroup
-        decode_tile<D, kQTileKeys>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, sRaw[buf][0], sK);
-        decode_tile<D, kQTileKeys>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, sRaw[buf][1], sV);
-        __syncthreads();
-        if (cls == kMaskDead) continue;   // uniform over the wave (also covers inactive waves)
-        const Swz z = make_swz<D>(lane);
-
-        float s2[GRAD ? 1 : 32], dp[GRAD ? 1 : 32];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int s = s_begin; s <= s_end; ++s) {
+            wait_all_mem();
+            __syncthreads();   // sub-tile s decoded; exchange slot s free
+            if (s == s_end) break;
+            const int cls = wclass(s);
+            if (cls == kMaskDead) continue;
+            const Swz z = make_swz<D>(lane);
+            const _Float16* tk = sK(s);
+            const _Float16* tv = sV(s);
             f32x16 sa, pa;
 #pragma unroll
             for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const f16x8 ak = frag_rows<D>(sK, 32 * kb, ks, lane, z);
-                const f16x8 av = frag_rows<D>(sV, 32 * kb, ks, lane, z);
-                sa = mfma32(ak, bq[ks], sa);
-                pa = mfma32(av, bd[ks], pa);
-                if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the load lookahead
+                sa = mfma32(frag_rows<D>(tk, 0, ks, lane, z), bq[ks], sa);
+                pa = mfma32(frag_rows<D>(tv, 0, ks, lane, z), bd[ks], pa);
             }
-            f16x8 bs[2];
+            const int j0 = s * kSubKeys;
+            float s2[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int key = j0 + 32 * kb + crow(v, g);
+                const int key = j0 + crow(v, g);
                 float sv = sa[v] * sc2;
                 if (!row_ok || key >= p.M) sv = neg_inf();
                 else if (cls == kMaskMixed) sv += mask_at(mrow, p.m_type, key) * kLog2e;
-                if (!GRAD) {
-                    s2[16 * kb + v] = sv;
-                    dp[16 * kb + v] = pa[v];
-                } else {
-                    const float pv = dead ? 0.0f : fast_exp2(sv - lse2);
-                    const float dsv = pv * (pa[v] - dlt);
-                    bs[v >> 3][v & 7] = (_Float16)(dsv * dsf);
-                }
+                s2[v] = sv;
             }
-            if (GRAD) {
+            if (!GRAD) {
+                float tmax = neg_inf();
 #pragma unroll
-                for (int md = 0; md < MD; ++md) {
+                for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s2[v]);
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                const float mnew = fmaxf(m_run, tmax);
+                if (mnew != neg_inf()) {
+                    const float alpha = fast_exp2(m_run - mnew);
+                    float ls = 0.0f, ds = 0.0f, bm = 0.0f;
 #pragma unroll
-                    for (int rh = 0; rh < 2; ++rh) {
-                        const f16x8 a = frag_cols<D>(sK, md, 32 * kb + 16 * rh, lane, z);
-                        dqacc[md] = mfma32(a, bs[rh], dqacc[md]);
+                    for (int v = 0; v < 16; ++v) {
+                        const float e = fast_exp2(s2[v] - mnew);
+                        ls += e;
+                        ds += e * pa[v];
+                        if (s2[v] != neg_inf()) bm = fmaxf(bm, fabsf(pa[v]));
                     }
-                    if ((md & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+                    l64 = l64 * (double)alpha + (double)ls;
+                    d64 = d64 * (double)alpha + (double)ds;
+                    m_run = mnew;
+                    bmax = fmaxf(bmax, bm);
                 }
+            } else {
+                f16x8 bs[2];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float pv = dead ? 0.0f : fast_exp2(s2[v] - lse2);
+                    bs[v >> 3][v & 7] = (_Float16)(pv * (pa[v] - dlt) * dsf);
+                }
+                unsigned char* ex = exch(s);
+                *(f16x8*)(ex + lane * 16) = bs[0];
+                *(f16x8*)(ex + 1024 + lane * 16) = bs[1];
             }
         }
-
-        if (!GRAD) {
-            float tmax = neg_inf();
-#pragma unroll
-            for (int v = 0; v < 32; ++v) tmax = fmaxf(tmax, s2[v]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-            const float mnew = fmaxf(m_run, tmax);
-            if (mnew != neg_inf()) {
-                const float alpha = fast_exp2(m_run - mnew);
-                float ls = 0.0f, ds = 0.0f, bm = 0.0f;
-#pragma unroll
-                for (int v = 0; v < 32; ++v) {
-                    const float e = fast_exp2(s2[v] - mnew);
-                    ls += e;
-                    ds += e * dp[v];
-                    if (s2[v] != neg_inf()) bm = fmaxf(bm, fabsf(dp[v]));
-                }
-                l64 = l64 * (double)alpha + (double)ls;
-                d64 = d64 * (double)alpha + (double)ds;
-                m_run = mnew;
-                bmax = fmaxf(bmax, bm);
+        if (!GRAD && active) {
+            const double lo = l64 + __shfl_xor(l64, 32);
+            const double dd = d64 + __shfl_xor(d64, 32);
+            const float bb = fmaxf(bmax, __shfl_xor(bmax, 32));
+            if (g == 0) {
+                const int64_t idx = (int64_t)split * p.Hkv * rowsHK + ridx;
+                p.part_m[idx] = m_run;
+                p.part_l[idx] = lo;
+                p.part_d[idx] = dd;
+                p.part_b[idx] = bb;
             }
         }
+        return;
     }
 
-    if (!active) return;
-    if (!GRAD) {
-        const double lo = l64 + __shfl_xor(l64, 32);
-        const double dd = d64 + __shfl_xor(d64, 32);
-        const float bb = fmaxf(bmax, __shfl_xor(bmax, 32));
-        if (g == 0) {
-            const int64_t idx = (int64_t)split * p.Hkv * rowsHK + ridx;
-            p.part_m[idx] = m_run;
-            p.part_l[idx] = lo;
-            p.part_d[idx] = dd;
-            p.part_b[idx] = bb;
+    // ================= K waves
+    f32x16 dqacc[GRAD ? MD : 1];
+    if (GRAD) {
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dqacc[md][v] = 0.0f;
+    }
+    for (int s = s_begin; s <= s_end; ++s) {
+        wait_all_mem();
+        __syncthreads();   // sub-tile s decoded and dS of s-1 exchanged
+        if (GRAD && s > s_begin && wclass(s - 1) != kMaskDead) {
+            const Swz z = make_swz<D>(lane);
+            const unsigned char* ex = exch(s - 1);
+            const f16x8 b0 = *(const f16x8*)(ex + lane * 16);
+            const f16x8 b1 = *(const f16x8*)(ex + 1024 + lane * 16);
+            const _Float16* tk = sK(s - 1);
+#pragma unroll
+            for (int md = 0; md < MD; ++md) {
+                dqacc[md] = mfma32(frag_cols<D>(tk, md, 0, lane, z), b0, dqacc[md]);
+                dqacc[md] = mfma32(frag_cols<D>(tk, md, 16, lane, z), b1, dqacc[md]);
+            }
         }
-    } else if (row_ok) {
+        if (s == s_end) break;
+        if (s + 1 < s_end) kdecode(s + 1);
+        if (s + 2 < s_end) kdma(s + 2);
+    }
+    if (GRAD && row_ok) {
+        const int ksx = load_ds_exponent(p);
         const bool direct = p.splits == 1;
         const float fac = direct ? p.scale * ldexpf(1.0f, ksx - edo) : 1.0f;
         float* dst = direct ? p.dq + ((int64_t)h * p.N + i) * D
@@ -530,14 +568,15 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
             const int j0 = key0 + half * kQTileKeys;
             __syncthreads();
             if (p.k_type == FA_BACK_Q8_0)
-                dma_raw_tile<D, kQTileKeys, kKVThreads>(p.k, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK);
+                dma_raw_tile<D, kQTileKeys, kKVThreads>(p.k, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, threadIdx.x);
             if (p.v_type == FA_BACK_Q8_0)
-                dma_raw_tile<D, kQTileKeys, kKVThreads>(p.v, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV);
+                dma_raw_tile<D, kQTileKeys, kKVThreads>(p.v, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV, threadIdx.x);
             wait_all_mem();
             __syncthreads();
-            decode_tile<D, kQTileKeys, kKVThreads>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, sK);
+            decode_tile<D, kQTileKeys, kKVThreads>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, sK,
+                                                   threadIdx.x);
             decode_tile<D, kQTileKeys, kKVThreads>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV,
-                                                   sV + half * kQTileKeys * D);
+                                                   sV + half * kQTileKeys * D, threadIdx.x);
             __syncthreads();
             if (role == 0 && (kb >> 1) == half) {
                 const Swz z = make_swz<D>(lane);

@@ -120,14 +120,15 @@ struct RawTile {
 
 // Issue the DMA of the raw bytes of keys [j0, j0+KEYS) of head hk into `raw` (q8_0 only).
 // Chunk idx = key*kChunks + c lands at raw + 16*idx; chunks outside the row are skipped.
-template <int D, int KEYS, int NT = kThreads>
+// NT threads take part, tid = 0 .. NT-1 being this thread's index among them.
+template <int D, int KEYS, int NT>
 FAB_DEV void dma_raw_tile(const char* base, int64_t nb1, int64_t nb2, int hk, int j0, int M,
-                          unsigned char* raw) {
+                          unsigned char* raw, int tid) {
     using R = Q8Row<D>;
     constexpr int NCH = KEYS * R::kChunks;
     constexpr int IT = (NCH + NT - 1) / NT;
     const char* hbase = base + (int64_t)hk * nb2;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int wbase = it * NT + wave * 64;         // first chunk of this wave's instruction
@@ -191,13 +192,14 @@ FAB_DEV f16x8 decode8(const char* rowp, int type, int grp, const unsigned char* 
 }
 
 // Decode keys [j0, j0+KEYS) into the swizzled fp16 tile dst[key][D]. Keys >= M become 0.
-template <int D, int KEYS, int NT = kThreads>
+// NT threads take part, tid = 0 .. NT-1 being this thread's index among them.
+template <int D, int KEYS, int NT>
 FAB_DEV void decode_tile(const char* base, int type, int64_t nb1, int64_t nb2, int hk, int j0,
-                         int M, const unsigned char* raw, _Float16* dst) {
+                         int M, const unsigned char* raw, _Float16* dst, int tid) {
     constexpr int GROUPS = D / 8;
     constexpr int ITEMS = KEYS * GROUPS;
     const char* hbase = base + (int64_t)hk * nb2;
-    for (int item = threadIdx.x; item < ITEMS; item += NT) {
+    for (int item = tid; item < ITEMS; item += NT) {
         const int key = item / GROUPS;
         const int grp = item - key * GROUPS;
         const int j = j0 + key;
