@@ -257,8 +257,13 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
             dma_raw_tile<D, kSubKeys, 256>(p.v, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), ktid);
     };
     auto kdecode = [&](int s) {
-        decode_tile<D, kSubKeys, 256>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, s * kSubKeys, p.M, rawK(s), sK(s), ktid);
-        decode_tile<D, kSubKeys, 256>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), sV(s), ktid);
+        if (p.k_type == FA_BACK_Q8_0 && p.v_type == FA_BACK_Q8_0) {
+            decode_q8_pair<D, kSubKeys, 256>(p.k, p.k_nb1, p.k_nb2, p.v, p.v_nb1, p.v_nb2, hk, s * kSubKeys,
+                                             p.M, rawK(s), rawV(s), sK(s), sV(s), ktid);
+        } else {
+            decode_tile<D, kSubKeys, 256>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, s * kSubKeys, p.M, rawK(s), sK(s), ktid);
+            decode_tile<D, kSubKeys, 256>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), sV(s), ktid);
+        }
     };
     auto wclass = [&](int s) { return active ? mask_class(p, hk, rb, s >> 1) : kMaskDead; };
 

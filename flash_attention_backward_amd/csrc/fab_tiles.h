@@ -149,28 +149,12 @@ FAB_DEV void dma_raw_tile(const char* base, int64_t nb1, int64_t nb2, int hk, in
     }
 }
 
-// 8 consecutive values of a row, starting at value 8*grp, decoded to fp16.
-//   q8_0: from the staged raw slot (rawslot, row offset `off` within its first chunk)
-//   F32/F16/BF16: straight from global memory (rows are 16-byte aligned)
+// 8 consecutive values of an F32, F16 or BF16 row (16-byte aligned), starting at value 8*grp,
+// rounded to fp16.
 template <int D>
-FAB_DEV f16x8 decode8(const char* rowp, int type, int grp, const unsigned char* rawslot, int off) {
+FAB_DEV f16x8 decode8(const char* rowp, int type, int grp, const unsigned char*, int) {
     f16x8 r;
-    if (type == FA_BACK_Q8_0) {
-        const int blk = grp >> 2;
-        const int so = off + 34 * blk;                  // scale offset within the slot (even)
-        const unsigned short sb = *(const unsigned short*)(rawslot + so);
-        const float sc = (float)__builtin_bit_cast(_Float16, sb);
-        const int qo = so + 2 + 8 * (grp & 3);          // first int8 (even)
-        const unsigned int* wp = (const unsigned int*)(rawslot + (qo & ~3));
-        const unsigned int w0 = wp[0], w1 = wp[1], w2 = wp[2];
-        const unsigned int lo = __builtin_amdgcn_alignbyte(w1, w0, qo & 3);
-        const unsigned int hi = __builtin_amdgcn_alignbyte(w2, w1, qo & 3);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            r[t] = (_Float16)(sc * (float)(signed char)(lo >> (8 * t)));
-            r[4 + t] = (_Float16)(sc * (float)(signed char)(hi >> (8 * t)));
-        }
-    } else if (type == FA_BACK_F32) {
+    if (type == FA_BACK_F32) {
         const f32x4 a = *(const f32x4*)(rowp + 32 * grp);
         const f32x4 b = *(const f32x4*)(rowp + 32 * grp + 16);
 #pragma unroll
@@ -191,28 +175,112 @@ FAB_DEV f16x8 decode8(const char* rowp, int type, int grp, const unsigned char* 
     return r;
 }
 
+// One 32-value q8_0 block of a staged row decoded to fp16: out[c] holds values 8c .. 8c+7.
+// All LDS reads are issued before any arithmetic. Each value is formed as
+// fma(byte ^ 0x80, d, -128 d) = d * q, exact in fp32, then rounded to fp16 (nearest even),
+// the same fp16 an F32 cache holding d * q gives.
+FAB_DEV void decode_q8_block(const unsigned char* slot, int off, int blk, f16x8 out[4]) {
+    const int base = off + 34 * blk;                  // fp16 scale (even offset)
+    const int qb = base + 2;                          // first int8
+    const int sh = qb & 3;
+    const unsigned int* wp = (const unsigned int*)(slot + (qb & ~3));
+    unsigned int w[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) w[k] = wp[k];
+    const unsigned short sb = *(const unsigned short*)(slot + base);
+    const float d = (float)__builtin_bit_cast(_Float16, sb);
+    const float nd = -128.0f * d;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const unsigned int x = __builtin_amdgcn_alignbyte(w[k + 1], w[k], sh) ^ 0x80808080u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            out[k >> 1][4 * (k & 1) + b] = (_Float16)fmaf((float)((x >> (8 * b)) & 0xffu), d, nd);
+    }
+}
+
 // Decode keys [j0, j0+KEYS) into the swizzled fp16 tile dst[key][D]. Keys >= M become 0.
 // NT threads take part, tid = 0 .. NT-1 being this thread's index among them.
+//   q8_0: one item = one 32-value block of a key (from the staged raw bytes)
+//   F32/F16/BF16: one item = 8 values of a key, read from global memory; every load of the
+//   thread is issued before the first conversion
 template <int D, int KEYS, int NT>
 FAB_DEV void decode_tile(const char* base, int type, int64_t nb1, int64_t nb2, int hk, int j0,
                          int M, const unsigned char* raw, _Float16* dst, int tid) {
+    const char* hbase = base + (int64_t)hk * nb2;
+    if (type == FA_BACK_Q8_0) {
+        constexpr int BPR = D / 32;                    // blocks per row
+        constexpr int ITEMS = KEYS * BPR;
+        for (int item = tid; item < ITEMS; item += NT) {
+            const int key = item / BPR, blk = item - (item / BPR) * BPR;
+            const int j = j0 + key;
+            f16x8 out[4];
+            if (j < M) {
+                const int off = (int)((uintptr_t)(hbase + (int64_t)j * nb1) & 15);
+                decode_q8_block(raw + key * Q8Row<D>::kSlot, off, blk, out);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) out[c][t] = (_Float16)0.0f;
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) *(f16x8*)(dst + tile_off<D>(key, 4 * blk + c)) = out[c];
+        }
+        return;
+    }
     constexpr int GROUPS = D / 8;
     constexpr int ITEMS = KEYS * GROUPS;
-    const char* hbase = base + (int64_t)hk * nb2;
-    for (int item = tid; item < ITEMS; item += NT) {
-        const int key = item / GROUPS;
-        const int grp = item - key * GROUPS;
+    constexpr int IT = (ITEMS + NT - 1) / NT;
+    f16x8 vals[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int item = tid + it * NT;
+        const int key = item / GROUPS, grp = item - (item / GROUPS) * GROUPS;
         const int j = j0 + key;
-        f16x8 v;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) vals[it][t] = (_Float16)0.0f;
+        if (item < ITEMS && j < M) vals[it] = decode8<D>(hbase + (int64_t)j * nb1, type, grp, nullptr, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int item = tid + it * NT;
+        const int key = item / GROUPS, grp = item - (item / GROUPS) * GROUPS;
+        if (item < ITEMS) *(f16x8*)(dst + tile_off<D>(key, grp)) = vals[it];
+    }
+}
+
+// K and V q8_0 tiles decoded together (items of both tensors interleaved, so that the LDS
+// reads of one overlap the arithmetic of the other). Same result as two decode_tile calls.
+template <int D, int KEYS, int NT>
+FAB_DEV void decode_q8_pair(const char* kbase, int64_t knb1, int64_t knb2, const char* vbase,
+                            int64_t vnb1, int64_t vnb2, int hk, int j0, int M,
+                            const unsigned char* rawk, const unsigned char* rawv,
+                            _Float16* dstk, _Float16* dstv, int tid) {
+    constexpr int BPR = D / 32;
+    constexpr int ITEMS = KEYS * BPR;                 // per tensor
+    const char* kh = kbase + (int64_t)hk * knb2;
+    const char* vh = vbase + (int64_t)hk * vnb2;
+    for (int item = tid; item < ITEMS; item += NT) {
+        const int key = item / BPR, blk = item - (item / BPR) * BPR;
+        const int j = j0 + key;
+        f16x8 ok[4], ov[4];
         if (j < M) {
-            const char* rowp = hbase + (int64_t)j * nb1;
-            const int off = (int)((uintptr_t)rowp & 15);
-            v = decode8<D>(rowp, type, grp, raw + key * Q8Row<D>::kSlot, off);
+            const int offk = (int)((uintptr_t)(kh + (int64_t)j * knb1) & 15);
+            const int offv = (int)((uintptr_t)(vh + (int64_t)j * vnb1) & 15);
+            decode_q8_block(rawk + key * Q8Row<D>::kSlot, offk, blk, ok);
+            decode_q8_block(rawv + key * Q8Row<D>::kSlot, offv, blk, ov);
         } else {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) v[t] = (_Float16)0.0f;
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) ok[c][t] = ov[c][t] = (_Float16)0.0f;
         }
-        *(f16x8*)(dst + tile_off<D>(key, grp)) = v;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            *(f16x8*)(dstk + tile_off<D>(key, 4 * blk + c)) = ok[c];
+            *(f16x8*)(dstv + tile_off<D>(key, 4 * blk + c)) = ov[c];
+        }
     }
 }
 
