@@ -58,8 +58,9 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(Params p) {
 
 // ----------------------------------------------------------------------------- prep
 
-// One workgroup per (hk, 32-row block): q and dO rows, scaled by the power-of-two prescale,
-// rounded to fp16 and written row-major in the row order r = i*G + g (padding rows are 0).
+// One workgroup per (hk, 32-row block): q and dO rows, scaled by the power-of-two prescale
+// (q also by the sign of the scale), rounded to fp16 and written row-major in the row order
+// r = i*G + g (padding rows are 0).
 template <int D>
 __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
     __shared__ float red[2][kWaves];
@@ -88,7 +89,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
         p.scal[0] = eq;
         p.scal[1] = edo;
     }
-    const float fq = ldexpf(1.0f, eq), fd = ldexpf(1.0f, edo);
+    // q rows also take the sign of the scale, so every score product uses |scale|
+    const float fq = p.scale < 0.0f ? -ldexpf(1.0f, eq) : ldexpf(1.0f, eq), fd = ldexpf(1.0f, edo);
 
     const int hk = blockIdx.x / p.RB, rb = blockIdx.x - (blockIdx.x / p.RB) * p.RB;
     constexpr int GR = D / 8;
@@ -187,6 +189,59 @@ FAB_DEV float mask_at(const char* mrow, int type, int j) {
                                : *(const float*)(mrow + 4 * (int64_t)j);
 }
 
+// ----------------------------------------------------------------------------- product loops
+
+// Two interleaved 32x32 products over d (two independent accumulator chains, so the matrix
+// core never waits for its own previous result), first operands read from LDS PF steps
+// ahead of their use:  sa += A1 * B1,  pa += A2 * B2, where the A operands are frag_rows reads
+// of tiles t1 and t2 (rows m1 .. m1+31, m2a ..) and the B operands come from `b1` / `b2` in
+// registers or, if b2 is null, from frag_rows reads of tile t2b (rows m2b .. m2b+31).
+template <int D, int PF>
+FAB_DEV void mfma_pair_d(const _Float16* t1, int m1, const f16x8* b1, const _Float16* t2, int m2a,
+                         const f16x8* b2, const _Float16* t2b, int m2b, f32x16& sa, f32x16& pa,
+                         int lane, const Swz& z) {
+    constexpr int KS = D / 16;
+    constexpr int NB = PF + 1;
+    f16x8 r1[NB], r2[NB], r3[NB];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+        r1[k] = frag_rows<D>(t1, m1, k, lane, z);
+        r2[k] = frag_rows<D>(t2, m2a, k, lane, z);
+        if (!b2) r3[k] = frag_rows<D>(t2b, m2b, k, lane, z);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        if (ks + PF < KS) {
+            r1[(ks + PF) % NB] = frag_rows<D>(t1, m1, ks + PF, lane, z);
+            r2[(ks + PF) % NB] = frag_rows<D>(t2, m2a, ks + PF, lane, z);
+            if (!b2) r3[(ks + PF) % NB] = frag_rows<D>(t2b, m2b, ks + PF, lane, z);
+        }
+        sa = mfma32(r1[ks % NB], b1[ks], sa);
+        pa = mfma32(r2[ks % NB], b2 ? b2[ks] : r3[ks % NB], pa);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// acc[md] += A(md, rh) * b[rh] over md = 0 .. D/32-1 and rh = 0, 1, with A the frag_cols read
+// (contraction over 32 rows kbase .. kbase+31 of tile t) fetched PF products ahead; the
+// accumulator changes between consecutive products.
+template <int D, int PF>
+FAB_DEV void mfma_cols(const _Float16* t, int kbase, const f16x8 b[2], f32x16* acc, int lane,
+                       const Swz& z) {
+    constexpr int MD = D / 32;
+    constexpr int NP = 2 * MD;                       // products, index n = rh*MD + md
+    constexpr int NB = PF + 1;
+    f16x8 r[NB];
+#pragma unroll
+    for (int n = 0; n < PF; ++n) r[n] = frag_cols<D>(t, n % MD, kbase + 16 * (n / MD), lane, z);
+#pragma unroll
+    for (int n = 0; n < NP; ++n) {
+        if (n + PF < NP) r[(n + PF) % NB] = frag_cols<D>(t, (n + PF) % MD, kbase + 16 * ((n + PF) / MD), lane, z);
+        acc[n % MD] = mfma32(r[n % NB], b[n / MD], acc[n % MD]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // ----------------------------------------------------------------------------- query side
 
 // Workgroup: one KV head, 4 row blocks of 32 rows, one key-range split, and 8 waves:
@@ -194,13 +249,13 @@ FAB_DEV float mask_at(const char* mrow, int type, int j) {
 //                   sub-tile: S^T = K Q^T and dP^T = V dO^T, then walk 1 updates the online
 //                   softmax statistics, walk 2 forms dS = P (dP - delta) and hands it over
 //                   through LDS.
-//   K waves (4..7)  decode sub-tile s+1 of K and V into LDS (its q8_0 bytes were fetched by
-//                   DMA one sub-tile earlier, and they queue the DMA of s+2) while the S waves
-//                   compute s; in walk 2 each also holds the dQ accumulators of one row block
-//                   and consumes the dS of sub-tile s-1: dQ^T += K^T dS^T.
-// K sub-tiles are triple-buffered (used by the S waves at s and the K waves at s+1), V
-// sub-tiles and the dS exchange double-buffered; one barrier per sub-tile. Every wave stays
-// within 256 registers, so each SIMD runs an S wave and a K wave.
+//   K waves (4..7)  queue the DMA of the q8_0 bytes of sub-tile s+2 and decode K and V of
+//                   sub-tile s+1 into LDS while the S waves compute s; in walk 2 each also
+//                   holds the dQ accumulators of one row block and consumes the dS of sub-tile
+//                   s-1: dQ^T += K^T dS^T.
+// A slot holds the K and V tiles of one sub-tile; three slots rotate (S waves at s, decode at
+// s+1, dQ at s-1), the staged bytes and the dS exchange are double-buffered; one barrier per
+// sub-tile. Every wave stays within 256 registers, so each SIMD runs an S wave and a K wave.
 // S^T = K Q^T puts one query row per lane column and 16 keys per lane; lanes l and l^32
 // together hold a row's 32 keys.
 constexpr int kQWaves = 8;
@@ -209,11 +264,11 @@ constexpr int kSubKeys = 32;
 
 template <int D>
 struct QLds {
-    static constexpr int kKT = kSubKeys * D;                       // halfs per K or V sub-tile
+    static constexpr int kTile = kSubKeys * D * 2;                 // bytes of a K or V sub-tile
+    static constexpr int kSlot = 2 * kTile;                        // K tile then V tile
     static constexpr int kRaw = RawTile<D, kSubKeys>::kBytes;      // q8_0 bytes of one sub-tile
-    static constexpr int kOffK = 0;                                // 3 K sub-tiles
-    static constexpr int kOffV = kOffK + 3 * kKT * 2;              // 2 V sub-tiles
-    static constexpr int kOffRaw = kOffV + 2 * kKT * 2;            // [2][K, V] raw bytes
+    static constexpr int kOffSlot = 0;                             // 3 slots
+    static constexpr int kOffRaw = kOffSlot + 3 * kSlot;           // [2][K, V] staged bytes
     static constexpr int kOffEx = kOffRaw + 4 * kRaw;              // [2][4 row blocks] dS, 2 KB
     static constexpr int kBytes = kOffEx + 2 * 4 * 2048;
 };
@@ -225,7 +280,7 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     constexpr int MD = D / 32;     // 32-wide d blocks of dQ
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l32 = lane & 31, g = lane >> 5;
     const int role = wave >> 2, w4 = wave & 3;
     const int hk = blockIdx.x % p.Hkv;
@@ -239,42 +294,16 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     const int h = hk * p.G + gh;
     const bool row_ok = active && r < p.R;
     const int ridx = hk * rowsHK + r;
-    const int ktid = threadIdx.x - 4 * kWave;        // K-wave thread index 0..255
     const int NS = (p.M + kSubKeys - 1) / kSubKeys;
     const int s_begin = 2 * split * p.tiles_per_split;
     const int s_end = min(NS, 2 * min(p.KT, (split + 1) * p.tiles_per_split));
     const int eq = p.scal[0], edo = p.scal[1];
 
-    auto sK = [&](int s) { return (_Float16*)(lds + L::kOffK) + (s % 3) * L::kKT; };
-    auto sV = [&](int s) { return (_Float16*)(lds + L::kOffV) + (s & 1) * L::kKT; };
+    auto slot = [&](int s) { return lds + L::kOffSlot + (s % 3) * L::kSlot; };
     auto rawK = [&](int s) { return lds + L::kOffRaw + ((s & 1) * 2 + 0) * L::kRaw; };
     auto rawV = [&](int s) { return lds + L::kOffRaw + ((s & 1) * 2 + 1) * L::kRaw; };
     auto exch = [&](int s) { return lds + L::kOffEx + ((s & 1) * 4 + w4) * 2048; };
-    auto kdma = [&](int s) {
-        if (p.k_type == FA_BACK_Q8_0)
-            dma_raw_tile<D, kSubKeys, 256>(p.k, p.k_nb1, p.k_nb2, hk, s * kSubKeys, p.M, rawK(s), ktid);
-        if (p.v_type == FA_BACK_Q8_0)
-            dma_raw_tile<D, kSubKeys, 256>(p.v, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), ktid);
-    };
-    auto kdecode = [&](int s) {
-        if (p.k_type == FA_BACK_Q8_0 && p.v_type == FA_BACK_Q8_0) {
-            decode_q8_pair<D, kSubKeys, 256>(p.k, p.k_nb1, p.k_nb2, p.v, p.v_nb1, p.v_nb2, hk, s * kSubKeys,
-                                             p.M, rawK(s), rawV(s), sK(s), sV(s), ktid);
-        } else {
-            decode_tile<D, kSubKeys, 256>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, s * kSubKeys, p.M, rawK(s), sK(s), ktid);
-            decode_tile<D, kSubKeys, 256>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), sV(s), ktid);
-        }
-    };
     auto wclass = [&](int s) { return active ? mask_class(p, hk, rb, s >> 1) : kMaskDead; };
-
-    // prologue: sub-tile s_begin decoded, the bytes of s_begin+1 on their way
-    if (role == 1 && s_begin < s_end) kdma(s_begin);
-    wait_all_mem();
-    __syncthreads();
-    if (role == 1 && s_begin < s_end) {
-        kdecode(s_begin);
-        if (s_begin + 1 < s_end) kdma(s_begin + 1);
-    }
 
     if (role == 0) {
         // ================= S waves
@@ -296,76 +325,116 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         const bool has_mask = p.m_type != FA_BACK_NONE;
         const char* mrow = (has_mask && row_ok)
             ? p.mask + (int64_t)i * p.m_nb1 + (int64_t)(p.Hm == 1 ? 0 : h) * p.m_nb2 : nullptr;
-        const float sc2 = p.scale * ldexpf(1.0f, -eq) * kLog2e;
+        // q rows carry the sign of the scale (prep), so the score scale is positive here
+        const float sc2 = fabsf(p.scale) * ldexpf(1.0f, -eq) * kLog2e;
+        const bool full_rows = active && (rb + 1) * 32 <= p.R;
         // walk 1 state
         float m_run = neg_inf();
         double l64 = 0.0, d64 = 0.0;
         float bmax = 0.0f;
-        // walk 2 state
-        float lse2 = neg_inf(), dlt = 0.0f, dsf = 1.0f;
+        // walk 2 state: p * 2^-ks = exp2(s2 - lse2 - ks)
+        float lse2 = neg_inf(), dlt = 0.0f, lse2k = 0.0f;
         if (GRAD) {
             if (row_ok) {
                 lse2 = p.row_lse2[ridx];
                 dlt = p.row_dlt[ridx];
             }
-            dsf = ldexpf(1.0f, -load_ds_exponent(p));
+            lse2k = lse2 + (float)load_ds_exponent(p);
         }
         const bool dead = (lse2 == neg_inf());
+        const RowWalk<D> rw = make_row_walk<D>(lane);
 
+        // prologue: the K waves stage and decode sub-tile s_begin
+        __syncthreads();
+        int cls_next = s_begin < s_end ? wclass(s_begin) : kMaskDead;
         for (int s = s_begin; s <= s_end; ++s) {
             wait_all_mem();
             __syncthreads();   // sub-tile s decoded; exchange slot s free
             if (s == s_end) break;
-            const int cls = wclass(s);
+            const int cls = cls_next;
+            cls_next = s + 1 < s_end ? wclass(s + 1) : kMaskDead;   // in flight during sub-tile s
             if (cls == kMaskDead) continue;
-            const Swz z = make_swz<D>(lane);
-            const _Float16* tk = sK(s);
-            const _Float16* tv = sV(s);
             f32x16 sa, pa;
 #pragma unroll
             for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                sa = mfma32(frag_rows<D>(tk, 0, ks, lane, z), bq[ks], sa);
-                pa = mfma32(frag_rows<D>(tv, 0, ks, lane, z), bd[ks], pa);
-            }
+            pair_rows<D, 2>(slot(s), bq, bd, sa, pa, rw);
             const int j0 = s * kSubKeys;
-            float s2[16];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = j0 + crow(v, g);
-                float sv = sa[v] * sc2;
-                if (!row_ok || key >= p.M) sv = neg_inf();
-                else if (cls == kMaskMixed) sv += mask_at(mrow, p.m_type, key) * kLog2e;
-                s2[v] = sv;
-            }
+            const bool fast = full_rows && cls == kMaskZero && j0 + kSubKeys <= p.M;
             if (!GRAD) {
-                float tmax = neg_inf();
+                if (fast) {
+                    // every entry visible: the scale is positive, so max(s) = sc2 * max(sa)
+                    float tm = sa[0];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s2[v]);
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-                const float mnew = fmaxf(m_run, tmax);
-                if (mnew != neg_inf()) {
+                    for (int v = 1; v < 16; ++v) tm = fmaxf(tm, sa[v]);
+                    tm = fmaxf(tm, __shfl_xor(tm, 32));
+                    const float mnew = fmaxf(m_run, tm * sc2);
                     const float alpha = fast_exp2(m_run - mnew);
                     float ls = 0.0f, ds = 0.0f, bm = 0.0f;
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const float e = fast_exp2(s2[v] - mnew);
+                        const float e = fast_exp2(fmaf(sa[v], sc2, -mnew));
                         ls += e;
-                        ds += e * pa[v];
-                        if (s2[v] != neg_inf()) bm = fmaxf(bm, fabsf(pa[v]));
+                        ds = fmaf(e, pa[v], ds);
+                        bm = fmaxf(bm, fabsf(pa[v]));
                     }
-                    l64 = l64 * (double)alpha + (double)ls;
-                    d64 = d64 * (double)alpha + (double)ds;
+                    l64 = fma(l64, (double)alpha, (double)ls);
+                    d64 = fma(d64, (double)alpha, (double)ds);
                     m_run = mnew;
                     bmax = fmaxf(bmax, bm);
+                } else {
+                    // masked or ragged sub-tile; an entry with mask 0 gets exactly the
+                    // arithmetic of the path above
+                    float madd[16];
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int key = j0 + crow(v, g);
+                        float mv = 0.0f;
+                        if (!row_ok || key >= p.M) mv = neg_inf();
+                        else if (cls == kMaskMixed) mv = mask_at(mrow, p.m_type, key) * kLog2e;
+                        madd[v] = mv;
+                    }
+                    float tmax = neg_inf();
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (madd[v] != neg_inf()) tmax = fmaxf(tmax, fmaf(sa[v], sc2, madd[v]));
+                    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                    const float mnew = fmaxf(m_run, tmax);
+                    if (mnew != neg_inf()) {
+                        const float alpha = fast_exp2(m_run - mnew);
+                        float ls = 0.0f, ds = 0.0f, bm = 0.0f;
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            if (madd[v] == neg_inf()) continue;
+                            const float e = fast_exp2(fmaf(sa[v], sc2, madd[v] - mnew));
+                            ls += e;
+                            ds = fmaf(e, pa[v], ds);
+                            bm = fmaxf(bm, fabsf(pa[v]));
+                        }
+                        l64 = fma(l64, (double)alpha, (double)ls);
+                        d64 = fma(d64, (double)alpha, (double)ds);
+                        m_run = mnew;
+                        bmax = fmaxf(bmax, bm);
+                    }
                 }
             } else {
                 f16x8 bs[2];
+                if (fast) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const float pv = dead ? 0.0f : fast_exp2(s2[v] - lse2);
-                    bs[v >> 3][v & 7] = (_Float16)(pv * (pa[v] - dlt) * dsf);
+                    for (int v = 0; v < 16; ++v) {
+                        const float pv = fast_exp2(fmaf(sa[v], sc2, -lse2k));
+                        bs[v >> 3][v & 7] = (_Float16)(pv * (pa[v] - dlt));
+                    }
+                } else {
+                    // masked or ragged sub-tile, same arithmetic as above for mask-0 entries
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int key = j0 + crow(v, g);
+                        float mv = 0.0f;
+                        if (!row_ok || key >= p.M) mv = neg_inf();
+                        else if (cls == kMaskMixed) mv = mask_at(mrow, p.m_type, key) * kLog2e;
+                        const float pv = (dead || mv == neg_inf()) ? 0.0f : fast_exp2(fmaf(sa[v], sc2, mv - lse2k));
+                        bs[v >> 3][v & 7] = (_Float16)(pv * (pa[v] - dlt));
+                    }
                 }
                 unsigned char* ex = exch(s);
                 *(f16x8*)(ex + lane * 16) = bs[0];
@@ -388,6 +457,37 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     }
 
     // ================= K waves
+    const int kw = wave - 4;                          // 0..3, uniform
+    const int ktid = kw * 64 + lane;
+    const char* kh = p.k + (int64_t)hk * p.k_nb2;
+    const char* vh = p.v + (int64_t)hk * p.v_nb2;
+    const bool pairq8 = p.k_type == FA_BACK_Q8_0 && p.v_type == FA_BACK_Q8_0;
+    RawDma<D, kSubKeys, 256> dk, dv;
+    dk.init(kh, p.k_nb1, s_begin * kSubKeys, ktid);
+    dv.init(vh, p.v_nb1, s_begin * kSubKeys, ktid);
+    auto kdma = [&](int s) {
+        if (p.k_type == FA_BACK_Q8_0) dk.issue(rawK(s), p.M, kw, lane);
+        if (p.v_type == FA_BACK_Q8_0) dv.issue(rawV(s), p.M, kw, lane);
+    };
+    auto kdecode = [&](int s) {
+        _Float16* tk = (_Float16*)slot(s);
+        _Float16* tv = (_Float16*)(slot(s) + L::kTile);
+        if (pairq8) {
+            decode_q8_pair32<D>(kh, p.k_nb1, vh, p.v_nb1, s * kSubKeys, p.M, rawK(s), rawV(s), tk, tv, kw, lane);
+        } else {
+            decode_tile<D, kSubKeys, 256>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, s * kSubKeys, p.M, rawK(s), tk, ktid);
+            decode_tile<D, kSubKeys, 256>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), tv, ktid);
+        }
+    };
+    // prologue: sub-tile s_begin decoded, the bytes of s_begin+1 on their way
+    if (s_begin < s_end) kdma(s_begin);
+    wait_all_mem();
+    __syncthreads();
+    if (s_begin < s_end) {
+        if (s_begin + 1 < s_end) kdma(s_begin + 1);
+        kdecode(s_begin);
+    }
+
     f32x16 dqacc[GRAD ? MD : 1];
     if (GRAD) {
 #pragma unroll
@@ -395,24 +495,23 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) dqacc[md][v] = 0.0f;
     }
+    const ColWalk<D> cw = make_col_walk<D>(lane);
+    int cls_cur = s_begin < s_end ? wclass(s_begin) : kMaskDead;   // class of sub-tile s
+    int cls_last = kMaskDead;                                        // class of sub-tile s-1
     for (int s = s_begin; s <= s_end; ++s) {
         wait_all_mem();
         __syncthreads();   // sub-tile s decoded and dS of s-1 exchanged
-        if (GRAD && s > s_begin && wclass(s - 1) != kMaskDead) {
-            const Swz z = make_swz<D>(lane);
+        const int cls_prev = cls_last;
+        cls_last = cls_cur;
+        cls_cur = s + 1 < s_end ? wclass(s + 1) : kMaskDead;        // in flight during sub-tile s
+        if (s + 2 < s_end) kdma(s + 2);
+        if (GRAD && s > s_begin && cls_prev != kMaskDead) {
             const unsigned char* ex = exch(s - 1);
-            const f16x8 b0 = *(const f16x8*)(ex + lane * 16);
-            const f16x8 b1 = *(const f16x8*)(ex + 1024 + lane * 16);
-            const _Float16* tk = sK(s - 1);
-#pragma unroll
-            for (int md = 0; md < MD; ++md) {
-                dqacc[md] = mfma32(frag_cols<D>(tk, md, 0, lane, z), b0, dqacc[md]);
-                dqacc[md] = mfma32(frag_cols<D>(tk, md, 16, lane, z), b1, dqacc[md]);
-            }
+            const f16x8 bb[2] = {*(const f16x8*)(ex + lane * 16), *(const f16x8*)(ex + 1024 + lane * 16)};
+            cols_acc<D>(slot(s - 1), bb, dqacc, cw);
         }
         if (s == s_end) break;
         if (s + 1 < s_end) kdecode(s + 1);
-        if (s + 2 < s_end) kdma(s + 2);
     }
     if (GRAD && row_ok) {
         const int ksx = load_ds_exponent(p);
@@ -537,7 +636,8 @@ struct KVLds {
     static constexpr int kExch = 4 * 2 * 2 * 64 * 16;                    // [kb][P,dS][rh][lane] x 16 B
     static constexpr int kSetup = kQTileKeys * D * 2 + 2 * kRaw;         // K half tile + raw
     static constexpr int kWork = 2 * kBuf + kExch;
-    static constexpr int kBytes = kVTile + (kSetup > kWork ? kSetup : kWork);
+    static constexpr int kMaxRB = 4096;                                  // row blocks classed in LDS
+    static constexpr int kBytes = kVTile + (kSetup > kWork ? kSetup : kWork) + 2 * kMaxRB;
 };
 
 template <int D>
@@ -550,6 +650,8 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     _Float16* sV = (_Float16*)lds;                    // [128 keys][D], swizzled
     unsigned char* work = lds + L::kVTile;            // setup scratch, then buffers + exchange
     unsigned char* exch = work + 2 * L::kBuf;
+    unsigned char* clsA = lds + L::kBytes - 2 * L::kMaxRB;   // class of (row block, first 64 keys)
+    unsigned char* clsB = clsA + L::kMaxRB;                  // class of (row block, last 64 keys)
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l32 = lane & 31, g = lane >> 5;
@@ -589,17 +691,23 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                 for (int ks = 0; ks < KS; ++ks) bk[ks] = frag_rows<D>(sK, 32 * (kb & 1), ks, lane, z);
             }
         }
+        // mask classes of the first kMaxRB row blocks for the two 64-key halves, staged once
+        for (int rbx = threadIdx.x; rbx < min(p.RB, L::kMaxRB); rbx += kKVThreads) {
+            clsA[rbx] = (unsigned char)mask_class(p, hk, rbx, 2 * kvt);
+            clsB[rbx] = (unsigned char)(2 * kvt + 1 < p.KT ? mask_class(p, hk, rbx, 2 * kvt + 1) : kMaskDead);
+        }
         __syncthreads();   // the setup region becomes the row-block buffers
     }
 
     // ---- row-block schedule (identical in every role)
-    auto kb_class = [&](int rbx) -> int {
-        return myt < p.KT ? mask_class(p, hk, rbx, myt) : kMaskDead;
+    auto half_class = [&](int rbx, int half) -> int {
+        if (rbx < L::kMaxRB) return half ? clsB[rbx] : clsA[rbx];
+        const int t = 2 * kvt + half;
+        return t < p.KT ? mask_class(p, hk, rbx, t) : kMaskDead;
     };
+    auto kb_class = [&](int rbx) -> int { return half_class(rbx, kb >> 1); };
     auto block_needed = [&](int rbx) -> bool {
-        const int ta = 2 * kvt, tb = 2 * kvt + 1;
-        return mask_class(p, hk, rbx, ta) != kMaskDead ||
-               (tb < p.KT && mask_class(p, hk, rbx, tb) != kMaskDead);
+        return half_class(rbx, 0) != kMaskDead || half_class(rbx, 1) != kMaskDead;
     };
     auto next_needed = [&](int rbx) -> int {
         while (rbx < p.RB && !block_needed(rbx)) ++rbx;
@@ -635,9 +743,10 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
 
     if (role == 0) {
         // ================= S waves
-        const float sc2 = p.scale * ldexpf(1.0f, -eq) * kLog2e;
+        const float sc2 = fabsf(p.scale) * ldexpf(1.0f, -eq) * kLog2e;   // q carries the sign
         const float dsf = ldexpf(1.0f, -ksx);
         const float pf = ldexpf(1.0f, kPScaleLog2);
+        const RowWalk<D> rw = make_row_walk<D>(lane);
         int buf = 0;
         for (int rb = first; rb < p.RB;) {
             const int rbn = next_needed(rb + 1);
@@ -645,19 +754,13 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
             wait_all_mem();
             __syncthreads();   // A: block rb landed; the exchange slots are free
             if (cls != kMaskDead) {
-                const Swz z = make_swz<D>(lane);
-                const _Float16* bq = (const _Float16*)(work + buf * L::kBuf);
-                const _Float16* bdo = bq + BLK;
+                const unsigned char* tq = work + buf * L::kBuf;
                 const float* lrow = (const float*)(work + buf * L::kBuf + 2 * BLK * 2);
                 const float* drow = lrow + 32;
                 f32x16 sa, pa;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    sa = mfma32(frag_rows<D>(bq, 0, ks, lane, z), bk[ks], sa);
-                    pa = mfma32(frag_rows<D>(bdo, 0, ks, lane, z), frag_rows<D>(sV, 32 * kb, ks, lane, z), pa);
-                }
+                pair_rows_kv<D, 1, BLK * 2>(tq, (const unsigned char*)(sV + 32 * kb * D), bk, sa, pa, rw);
                 f16x8 bp[2], bs[2];
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
@@ -726,7 +829,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
         buf ^= 1;
     }
     if (!key_ok) return;
-    const float fac = role == 1 ? p.scale * ldexpf(1.0f, ksx - eq - edo) : ldexpf(1.0f, -kPScaleLog2 - edo);
+    const float fac = role == 1 ? fabsf(p.scale) * ldexpf(1.0f, ksx - eq - edo) : ldexpf(1.0f, -kPScaleLog2 - edo);
     float* dst = (role == 1 ? p.dk : p.dv) + ((int64_t)hk * p.M + myj) * D;
 #pragma unroll
     for (int md = 0; md < MD; ++md)

@@ -106,10 +106,12 @@ FAB_DEV void wait_all_mem() {
 
 // q8_0 row geometry: D/32 blocks of 34 bytes; a row's bytes are staged in LDS as the
 // 16-byte-aligned chunks that cover it (the row may start at any even address).
+// The slot of a row in LDS has an odd number of 16-byte chunks, so that dword reads of the
+// same block of 16 consecutive keys spread over the banks.
 template <int D>
 struct Q8Row {
     static constexpr int kBytes = D / 32 * 34;
-    static constexpr int kChunks = (kBytes + 29) / 16;   // covers a 14-byte misalignment
+    static constexpr int kChunks = ((kBytes + 29) / 16) | 1;   // covers a 14-byte misalignment
     static constexpr int kSlot = kChunks * 16;
 };
 
@@ -180,6 +182,7 @@ FAB_DEV f16x8 decode8(const char* rowp, int type, int grp, const unsigned char*,
 // fma(byte ^ 0x80, d, -128 d) = d * q, exact in fp32, then rounded to fp16 (nearest even),
 // the same fp16 an F32 cache holding d * q gives.
 FAB_DEV void decode_q8_block(const unsigned char* slot, int off, int blk, f16x8 out[4]) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     const int base = off + 34 * blk;                  // fp16 scale (even offset)
     const int qb = base + 2;                          // first int8
     const int sh = qb & 3;
@@ -189,13 +192,20 @@ FAB_DEV void decode_q8_block(const unsigned char* slot, int off, int blk, f16x8 
     for (int k = 0; k < 9; ++k) w[k] = wp[k];
     const unsigned short sb = *(const unsigned short*)(slot + base);
     const float d = (float)__builtin_bit_cast(_Float16, sb);
-    const float nd = -128.0f * d;
+    const float c = -1152.0f * d;                     // exact: 9 * 2^7 * d needs 15 bits
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
+        // bytes u = q + 128; fp16 with bit pattern 0x64uu is exactly 1024 + u, so
+        // (1024 + u) * d - 1152 * d = q * d is formed exactly in fp32 and rounded once to fp16
         const unsigned int x = __builtin_amdgcn_alignbyte(w[k + 1], w[k], sh) ^ 0x80808080u;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-            out[k >> 1][4 * (k & 1) + b] = (_Float16)fmaf((float)((x >> (8 * b)) & 0xffu), d, nd);
+        const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u));
+        const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u));
+        f16x8& o = out[k >> 1];
+        const int b = 4 * (k & 1);
+        o[b + 0] = (_Float16)fmaf((float)lo.x, d, c);
+        o[b + 1] = (_Float16)fmaf((float)lo.y, d, c);
+        o[b + 2] = (_Float16)fmaf((float)hi.x, d, c);
+        o[b + 3] = (_Float16)fmaf((float)hi.y, d, c);
     }
 }
 
@@ -250,37 +260,257 @@ FAB_DEV void decode_tile(const char* base, int type, int64_t nb1, int64_t nb2, i
     }
 }
 
-// K and V q8_0 tiles decoded together (items of both tensors interleaved, so that the LDS
-// reads of one overlap the arithmetic of the other). Same result as two decode_tile calls.
-template <int D, int KEYS, int NT>
-FAB_DEV void decode_q8_pair(const char* kbase, int64_t knb1, int64_t knb2, const char* vbase,
-                            int64_t vnb1, int64_t vnb2, int hk, int j0, int M,
-                            const unsigned char* rawk, const unsigned char* rawv,
-                            _Float16* dstk, _Float16* dstv, int tid) {
-    constexpr int BPR = D / 32;
-    constexpr int ITEMS = KEYS * BPR;                 // per tensor
-    const char* kh = kbase + (int64_t)hk * knb2;
-    const char* vh = vbase + (int64_t)hk * vnb2;
-    for (int item = tid; item < ITEMS; item += NT) {
-        const int key = item / BPR, blk = item - (item / BPR) * BPR;
+// K and V q8_0 sub-tiles of 32 keys decoded together by 256 threads (4 waves). One item is
+// one 32-value block of one key. A wave-instruction covers 16 keys in the order
+// 0,1,4,5,8,9,12,13,2,3,6,7,10,11,14,15 (plus 16 for the second half) times min(4, D/32)
+// blocks, so that the 16-byte stores of 16 lanes land on 16 distinct bank groups of the
+// swizzled tile and the dword reads of the staged bytes hit each bank at most twice.
+FAB_DEV int perm16(int t) { return (t & 1) | ((t & 6) << 1) | ((t & 8) >> 2); }
+
+template <int D>
+FAB_DEV void decode_q8_pair32(const char* kh, int64_t knb1, const char* vh, int64_t vnb1, int j0, int M,
+                              const unsigned char* rawk, const unsigned char* rawv, _Float16* dstk,
+                              _Float16* dstv, int wave, int lane) {
+    constexpr int BPR = D / 32;                       // blocks per row
+    constexpr int BL = BPR >= 4 ? 4 : BPR;            // blocks per wave-instruction
+    constexpr int KL = 64 / BL;                       // keys per wave-instruction
+    constexpr int KG = KL / 16;
+    constexpr int UPT = BPR / 2;                      // wave-instructions per tensor
+    const int klo = perm16(lane & 15) + 16 * ((lane >> 4) % KG);
+    const int blo = (lane >> 4) / KG;
+#pragma unroll
+    for (int u0 = 0; u0 < 2 * UPT; u0 += 4) {
+        const int u = u0 + wave;                      // wave-uniform
+        if (u >= 2 * UPT) break;
+        const bool isv = u >= UPT;
+        const int uu = isv ? u - UPT : u;
+        const int key = klo + KL * (uu % (32 / KL));
+        const int blk = blo + BL * (uu / (32 / KL));
         const int j = j0 + key;
-        f16x8 ok[4], ov[4];
+        f16x8 o[4];
         if (j < M) {
-            const int offk = (int)((uintptr_t)(kh + (int64_t)j * knb1) & 15);
-            const int offv = (int)((uintptr_t)(vh + (int64_t)j * vnb1) & 15);
-            decode_q8_block(rawk + key * Q8Row<D>::kSlot, offk, blk, ok);
-            decode_q8_block(rawv + key * Q8Row<D>::kSlot, offv, blk, ov);
+            const char* h = isv ? vh : kh;
+            const int64_t nb1 = isv ? vnb1 : knb1;
+            const int off = (int)(((uint32_t)(uintptr_t)h + (uint32_t)j * (uint32_t)nb1) & 15u);
+            decode_q8_block((isv ? rawv : rawk) + key * Q8Row<D>::kSlot, off, blk, o);
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
-                for (int t = 0; t < 8; ++t) ok[c][t] = ov[c][t] = (_Float16)0.0f;
+                for (int t = 0; t < 8; ++t) o[c][t] = (_Float16)0.0f;
         }
+        _Float16* dst = isv ? dstv : dstk;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            *(f16x8*)(dstk + tile_off<D>(key, 4 * blk + c)) = ok[c];
-            *(f16x8*)(dstv + tile_off<D>(key, 4 * blk + c)) = ov[c];
+        for (int c = 0; c < 4; ++c) *(f16x8*)(dst + tile_off<D>(key, 4 * blk + c)) = o[c];
+    }
+}
+
+// DMA of consecutive q8_0 sub-tiles (KEYS keys each, sub-tile after sub-tile) into a staging
+// buffer by NT threads. The per-lane row pointers are kept and advanced by KEYS rows per call,
+// so each call costs a few adds and compares per 16-byte chunk.
+template <int D, int KEYS, int NT>
+struct RawDma {
+    using R = Q8Row<D>;
+    static constexpr int NCH = KEYS * R::kChunks;
+    static constexpr int IT = (NCH + NT - 1) / NT;
+    const char* row[IT];   // start of the row this lane's chunk `it` belongs to
+    int j[IT];             // its key index
+    int c16[IT];           // byte offset of the chunk inside the aligned row
+    bool live[IT];         // the chunk index lies inside the sub-tile
+    int64_t step;          // KEYS rows
+
+    FAB_DEV void init(const char* hbase, int64_t nb1, int j0, int tid) {
+        step = (int64_t)KEYS * nb1;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = it * NT + tid;
+            const int key = idx / R::kChunks;
+            live[it] = idx < NCH;
+            j[it] = j0 + key;
+            c16[it] = 16 * (idx - key * R::kChunks);
+            row[it] = hbase + (int64_t)(j0 + key) * nb1;
         }
+    }
+    // wave: this thread's wave among the NT threads (uniform); raw: staging buffer
+    FAB_DEV void issue(unsigned char* raw, int M, int wave, int lane) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int wbase = it * NT + wave * 64;    // first chunk of this wave's instruction
+            if (wbase >= NCH) break;                   // wave-uniform
+            const uintptr_t a = (uintptr_t)row[it];
+            const uintptr_t src = (a & ~(uintptr_t)15) + (uintptr_t)c16[it];
+            if (live[it] && j[it] < M && src < a + R::kBytes) dma16((const void*)src, raw + 16 * wbase);
+            row[it] += step;
+            j[it] += KEYS;
+        }
+        (void)lane;
+    }
+};
+
+// ----------------------------------------------------------------------------- Gray walks
+
+// Fragment reads stepped in Gray-code order: step t uses index gray(t) = t ^ (t >> 1), so
+// consecutive steps differ in one bit b = ctz(t + 1) and, under the XOR swizzle, the lane's
+// LDS address changes by a per-lane +-delta: one add per step.
+FAB_DEV constexpr int gray(int t) { return t ^ (t >> 1); }
+FAB_DEV constexpr int gray_bit(int t) { return __builtin_ctz(t + 1); }
+
+FAB_DEV int swz_term(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+// frag_rows reads (rows m0 + lane%32, d = 16*ks + 8*(lane/32) ..) of a swizzled [row][D] tile:
+// byte offset of step ks = 0 for m0 = 0 and the per-bit steps of ks.
+template <int D>
+struct RowWalk {
+    static constexpr int KS = D / 16;
+    static constexpr int NB = KS == 16 ? 4 : (KS == 8 ? 3 : 2);
+    int a0;
+    int e[NB];   // step when bit b of ks goes 0 -> 1; minus it for 1 -> 0
+};
+
+template <int D>
+FAB_DEV RowWalk<D> make_row_walk(int lane) {
+    constexpr int CM = (D / 8) - 1;
+    const int zr = swz_term(lane & 31) & CM, c = zr >> 1, g = lane >> 5;
+    RowWalk<D> w;
+    w.a0 = opaque((lane & 31) * D * 2 + 16 * (g ^ (zr & 1)) + 32 * c);
+#pragma unroll
+    for (int b = 0; b < RowWalk<D>::NB; ++b) w.e[b] = opaque(((c >> b) & 1) ? -(32 << b) : (32 << b));
+    return w;
+}
+
+// byte offset change from step t to t+1 of a Gray walk with per-bit steps e
+template <int NB>
+FAB_DEV int gray_step(int t, const int (&e)[NB]) {
+    const int b = gray_bit(t);
+    return ((gray(t) >> b) & 1) ? -e[b] : e[b];
+}
+
+// frag_cols reads of a swizzled [row][D] tile, md stepped in Gray order: byte offsets of the
+// two transpose reads for md = 0, kbase = 0 and their per-bit steps of md.
+template <int D>
+struct ColWalk {
+    static constexpr int MD = D / 32;
+    static constexpr int NB = MD == 8 ? 3 : (MD == 4 ? 2 : 1);
+    int a0[2];
+    int e[2][NB];
+};
+
+template <int D>
+FAB_DEV ColWalk<D> make_col_walk(int lane) {
+    constexpr int CM = (D / 8) - 1;
+    const int g = lane >> 5, h16 = (lane >> 4) & 1, s = lane & 15;
+    ColWalk<D> w;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = 8 * j + 4 * g + (s >> 2);
+        const int zc = swz_term(row) & CM;
+        const int cc = (2 * h16 + ((s & 3) >> 1)) ^ (zc & 3);
+        const int ee = zc >> 2;
+        w.a0[j] = opaque(row * D * 2 + 16 * (4 * ee + cc) + 8 * (s & 1));
+#pragma unroll
+        for (int b = 0; b < ColWalk<D>::NB; ++b) w.e[j][b] = opaque(((ee >> b) & 1) ? -(64 << b) : (64 << b));
+    }
+    return w;
+}
+
+FAB_DEV f16x4 tr_read(const unsigned char* p) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+    return __builtin_bit_cast(f16x4, v);
+}
+
+FAB_DEV f16x8 join(f16x4 a, f16x4 b) {
+    f16x8 r;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        r[t] = a[t];
+        r[4 + t] = b[t];
+    }
+    return r;
+}
+
+// sa += K Q^T and pa += V dO^T over d for one 32-key sub-tile: A operands from the K tile at
+// `tile` and the V tile right after it (same rows), B operands bq/bd in registers; reads
+// issued PF steps ahead, the two accumulator chains interleaved.
+template <int D, int PF>
+FAB_DEV void pair_rows(const unsigned char* tile, const f16x8* bq, const f16x8* bd, f32x16& sa,
+                       f32x16& pa, const RowWalk<D>& w) {
+    constexpr int KS = D / 16, NB = PF + 1;
+    constexpr int VOFF = 32 * D * 2;                  // V tile follows the 32-row K tile
+    int a = w.a0;                                     // offset of the next step to read
+    f16x8 rk[NB], rv[NB];
+#pragma unroll
+    for (int t = 0; t < PF; ++t) {
+        rk[t] = *(const f16x8*)(tile + a);
+        rv[t] = *(const f16x8*)(tile + a + VOFF);
+        if (t + 1 < KS) a += gray_step(t, w.e);
+    }
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+        if (t + PF < KS) {
+            rk[(t + PF) % NB] = *(const f16x8*)(tile + a);
+            rv[(t + PF) % NB] = *(const f16x8*)(tile + a + VOFF);
+            if (t + PF + 1 < KS) a += gray_step(t + PF, w.e);
+        }
+        const int ks = gray(t);
+        sa = mfma32(rk[t % NB], bq[ks], sa);
+        pa = mfma32(rv[t % NB], bd[ks], pa);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Key-side pair: sa += Q K^T (A: q rows of the tile at tq, B: bk in registers) and
+// pa += dO V^T (A: dO rows of the tile at tq + DOFF, B: V rows of the tile at tv), over d in
+// the same Gray order as pair_rows, so both sides sum every score in the same order.
+template <int D, int PF, int DOFF>
+FAB_DEV void pair_rows_kv(const unsigned char* tq, const unsigned char* tv, const f16x8* bk, f32x16& sa,
+                          f32x16& pa, const RowWalk<D>& w) {
+    constexpr int KS = D / 16, NB = PF + 1;
+    int a = w.a0;
+    f16x8 rq[NB], rd[NB], rv[NB];
+#pragma unroll
+    for (int t = 0; t < PF; ++t) {
+        rq[t] = *(const f16x8*)(tq + a);
+        rd[t] = *(const f16x8*)(tq + a + DOFF);
+        rv[t] = *(const f16x8*)(tv + a);
+        if (t + 1 < KS) a += gray_step(t, w.e);
+    }
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+        if (t + PF < KS) {
+            rq[(t + PF) % NB] = *(const f16x8*)(tq + a);
+            rd[(t + PF) % NB] = *(const f16x8*)(tq + a + DOFF);
+            rv[(t + PF) % NB] = *(const f16x8*)(tv + a);
+            if (t + PF + 1 < KS) a += gray_step(t + PF, w.e);
+        }
+        sa = mfma32(rq[t % NB], bk[gray(t)], sa);
+        pa = mfma32(rd[t % NB], rv[t % NB], pa);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// acc[md] += A(md, 0) b[0] + A(md, 1) b[1] for md = 0 .. D/32-1, A(md, rh) the frag_cols read
+// of rows 16*rh .. 16*rh+15 of the tile at `tile` (a contraction over its 32 rows); md in Gray
+// order with the reads of the next md issued before the products of this one.
+template <int D>
+FAB_DEV void cols_acc(const unsigned char* tile, const f16x8 b[2], f32x16* acc, const ColWalk<D>& w) {
+    constexpr int MD = D / 32;
+    constexpr int RH = 16 * D * 2;                    // bytes of 16 rows
+    int a0 = w.a0[0], a1 = w.a0[1];
+    f16x8 r0[2], r1[2];
+    r0[0] = join(tr_read(tile + a0), tr_read(tile + a1));
+    r1[0] = join(tr_read(tile + a0 + RH), tr_read(tile + a1 + RH));
+#pragma unroll
+    for (int t = 0; t < MD; ++t) {
+        if (t + 1 < MD) {
+            a0 += gray_step(t, w.e[0]);
+            a1 += gray_step(t, w.e[1]);
+            r0[(t + 1) & 1] = join(tr_read(tile + a0), tr_read(tile + a1));
+            r1[(t + 1) & 1] = join(tr_read(tile + a0 + RH), tr_read(tile + a1 + RH));
+        }
+        const int md = gray(t);
+        acc[md] = mfma32(r0[t & 1], b[0], acc[md]);
+        acc[md] = mfma32(r1[t & 1], b[1], acc[md]);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
