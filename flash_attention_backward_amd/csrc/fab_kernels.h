@@ -611,33 +611,34 @@ __global__ __launch_bounds__(kThreads) void dqreduce_kernel(Params p) {
 
 // ----------------------------------------------------------------------------- key side
 
-// Workgroup: one KV head, 128 keys in 4 blocks of 32, and 12 waves with one of three roles
-// per key block (wave w: role w/4, key block w%4, so each SIMD runs one wave of each role):
-//   S wave  K fragments in registers, V tile in LDS: S = Q K^T and dP = dO V^T for every
-//           32-row block, then P and dS, handed over through LDS
-//   dK wave dK^T += Q^T dS   (128 accumulator registers)
-//   dV wave dV^T += dO^T P   (128 accumulator registers)
-// Each role runs its own loop over the row blocks with the same two barriers per block, so
-// the compiler keeps only that role's state live and every wave stays within the 170
-// registers that three waves per SIMD allow. The q and dO row blocks (fp16, row-major, with
-// their lse/delta) are copied HBM -> LDS once per workgroup by DMA, double-buffered.
-// S = Q K^T puts one key per lane column and 16 rows per lane, which is the layout the
-// second operand of the dK/dV products needs; their first operands are transpose reads of
-// the same LDS blocks.
-constexpr int kKVWaves = 12;
+// Workgroup: one KV head, 128 keys in 4 blocks of 32, and 8 waves: one pair per key block kb.
+//   A wave (w = kb)      K fragments of its 32 keys in registers. Per 32-row block:
+//                        S = Q K^T, P = exp(S - lse) in fp32 (its fp16 image p*2^15 goes to
+//                        LDS for the B wave); then, with dP from the B wave, dS = P (dP - delta)
+//                        in fp32 and dK^T += Q^T dS, the dS image taken straight from registers.
+//   B wave (w = 4 + kb)  V fragments in registers. Per row block: dP = dO V^T, handed to the A
+//                        wave in fp32 through LDS; then dV^T += dO^T P from the P image.
+// Two barriers per row block: phase 1 runs S (A) and dP (B) side by side, phase 2 runs dK (A)
+// and dV (B). The q and dO row blocks (fp16, row-major, with their lse/delta) are copied
+// HBM -> LDS by DMA once per workgroup and double-buffered; the copy of the next block is
+// queued at the start of each block. Every wave stays within 256 registers.
+// S = Q K^T puts one key per lane column and 16 rows per lane: the layout of the second
+// operand of the dK/dV products, whose first operands are transpose reads of the row blocks.
+constexpr int kKVWaves = 8;
 constexpr int kKVThreads = kKVWaves * kWave;
 
 template <int D>
 struct KVLds {
-    static constexpr int kBlk = 32 * D;                                  // halfs per row block
+    static constexpr int kBlk = 32 * D * 2;                              // bytes of a 32-row block
+    static constexpr int kBuf = 2 * kBlk + 256;                          // q, dO, 32 lse, 32 delta
+    static constexpr int kExP = 4 * 2048;                                // [kb][rh][lane] P images
+    static constexpr int kExD = 4 * 4096;                                // [kb][4][lane] dP, fp32
+    static constexpr int kExF = 4 * 4096;                                // [kb][4][lane] P, fp32 (A only)
+    static constexpr int kWork = 2 * kBuf + kExP + kExD + kExF;
     static constexpr int kRaw = RawTile<D, kQTileKeys>::kBytes;
-    static constexpr int kVTile = kKVKeys * D * 2;                       // resident V tile
-    static constexpr int kBuf = 2 * kBlk * 2 + 256;                      // q, dO, 32 lse, 32 delta
-    static constexpr int kExch = 4 * 2 * 2 * 64 * 16;                    // [kb][P,dS][rh][lane] x 16 B
-    static constexpr int kSetup = kQTileKeys * D * 2 + 2 * kRaw;         // K half tile + raw
-    static constexpr int kWork = 2 * kBuf + kExch;
+    static constexpr int kSetup = 2 * kQTileKeys * D * 2 + 2 * kRaw;     // K, V half tiles + bytes
     static constexpr int kMaxRB = 4096;                                  // row blocks classed in LDS
-    static constexpr int kBytes = kVTile + (kSetup > kWork ? kSetup : kWork) + 2 * kMaxRB;
+    static constexpr int kBytes = (kSetup > kWork ? kSetup : kWork) + 2 * kMaxRB;
 };
 
 template <int D>
@@ -645,30 +646,32 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     using L = KVLds<D>;
     constexpr int KS = D / 16;
     constexpr int MD = D / 32;
-    constexpr int BLK = L::kBlk;
+    constexpr int NI = L::kBlk / 1024;                // 64-lane x 16-byte DMA instructions per tensor
+    constexpr int NIW = (2 * NI + kKVWaves - 1) / kKVWaves;
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
-    _Float16* sV = (_Float16*)lds;                    // [128 keys][D], swizzled
-    unsigned char* work = lds + L::kVTile;            // setup scratch, then buffers + exchange
-    unsigned char* exch = work + 2 * L::kBuf;
+    unsigned char* work = lds;                        // setup scratch, then buffers + exchange
+    unsigned char* exP = work + 2 * L::kBuf;
+    unsigned char* exD = exP + L::kExP;
+    unsigned char* exF = exD + L::kExD;
     unsigned char* clsA = lds + L::kBytes - 2 * L::kMaxRB;   // class of (row block, first 64 keys)
     unsigned char* clsB = clsA + L::kMaxRB;                  // class of (row block, last 64 keys)
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l32 = lane & 31, g = lane >> 5;
-    const int role = wave >> 2, kb = wave & 3;
+    const int role = wave >> 2, kb = wave & 3;        // role 0: A (S, dK), role 1: B (dP, dV)
     const int hk = blockIdx.x % p.Hkv;
     const int kvt = blockIdx.x / p.Hkv;
     const int key0 = kvt * kKVKeys;
     const int myj = key0 + 32 * kb + l32;
     const bool key_ok = myj < p.M;
     const int rowsHK = p.RB * 32;
-    const int myt = 2 * kvt + (kb >> 1);              // 64-key tile of this key block
 
-    // ---- setup: V tile resident in LDS; K fragments into the S waves' registers
-    f16x8 bk[KS];
+    // ---- setup: K (A waves) or V (B waves) fragments of the wave's 32 keys into registers
+    f16x8 bkv[KS];
     {
         _Float16* sK = (_Float16*)work;
-        unsigned char* rawK = work + kQTileKeys * D * 2;
+        _Float16* sV = sK + kQTileKeys * D;
+        unsigned char* rawK = work + 2 * kQTileKeys * D * 2;
         unsigned char* rawV = rawK + L::kRaw;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -682,13 +685,14 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
             __syncthreads();
             decode_tile<D, kQTileKeys, kKVThreads>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, sK,
                                                    threadIdx.x);
-            decode_tile<D, kQTileKeys, kKVThreads>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV,
-                                                   sV + half * kQTileKeys * D, threadIdx.x);
+            decode_tile<D, kQTileKeys, kKVThreads>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV, sV,
+                                                   threadIdx.x);
             __syncthreads();
-            if (role == 0 && (kb >> 1) == half) {
+            if ((kb >> 1) == half) {
                 const Swz z = make_swz<D>(lane);
+                const _Float16* src = role == 0 ? sK : sV;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) bk[ks] = frag_rows<D>(sK, 32 * (kb & 1), ks, lane, z);
+                for (int ks = 0; ks < KS; ++ks) bkv[ks] = frag_rows<D>(src, 32 * (kb & 1), ks, lane, z);
             }
         }
         // mask classes of the first kMaxRB row blocks for the two 64-key halves, staged once
@@ -699,13 +703,12 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
         __syncthreads();   // the setup region becomes the row-block buffers
     }
 
-    // ---- row-block schedule (identical in every role)
+    // ---- row-block schedule (identical in every wave)
     auto half_class = [&](int rbx, int half) -> int {
         if (rbx < L::kMaxRB) return half ? clsB[rbx] : clsA[rbx];
         const int t = 2 * kvt + half;
         return t < p.KT ? mask_class(p, hk, rbx, t) : kMaskDead;
     };
-    auto kb_class = [&](int rbx) -> int { return half_class(rbx, kb >> 1); };
     auto block_needed = [&](int rbx) -> bool {
         return half_class(rbx, 0) != kMaskDead || half_class(rbx, 1) != kMaskDead;
     };
@@ -713,124 +716,157 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
         while (rbx < p.RB && !block_needed(rbx)) ++rbx;
         return rbx;
     };
-    // DMA of row block rbx (q, dO and their 32 lse / 32 delta values) into buffer b, issued by
-    // the 8 accumulating waves; the LDS copy is swizzled by choosing each lane's source chunk
+    // DMA of row block rbx (q, dO and their 32 lse / 32 delta values) into buffer b by all 8
+    // waves. The LDS copy is swizzled by choosing each lane's source chunk; those choices are
+    // the same for every block, so they are computed once.
+    const char* qbase = (const char*)(p.qr + (int64_t)hk * rowsHK * D);
+    const char* dbase = (const char*)(p.dr + (int64_t)hk * rowsHK * D);
     auto dma_block = [&](int rbx, int b) {
-        constexpr int NI = BLK / 512;                 // 64-lane x 16-byte instructions per tensor
-        const int aw = wave - 4;                      // 0..7
         unsigned char* base = work + b * L::kBuf;
-        for (int ins = aw; ins < 2 * NI; ins += 8) {
+        const int64_t blk = (int64_t)rbx * L::kBlk;
+#pragma unroll
+        for (int k = 0; k < NIW; ++k) {
+            const int ins = wave + kKVWaves * k;     // uniform
+            if (ins >= 2 * NI) break;
             const int ten = ins / NI, ii = ins - (ins / NI) * NI;
             const int P = ii * 64 + lane;
             const int row = P / (D / 8), pc = P - (P / (D / 8)) * (D / 8);
-            const int c = swz_chunk<D>(row, pc);
-            const _Float16* src = (ten ? p.dr : p.qr) + (((int64_t)hk * rowsHK + rbx * 32 + row) * D + 8 * c);
-            dma16(src, base + ten * BLK * 2 + ii * 1024);
+            const int off = (row * D + 8 * swz_chunk<D>(row, pc)) * 2;
+            dma16((ten ? dbase : qbase) + blk + off, base + ten * L::kBlk + ii * 1024);
         }
-        if (aw == 7 && lane < 16) {
+        if (wave == kKVWaves - 1 && lane < 16) {
             const float* src = (lane < 8 ? p.row_lse2 : p.row_dlt) + (int64_t)hk * rowsHK + rbx * 32 + 4 * (lane & 7);
-            dma16(src, base + 2 * BLK * 2);
+            dma16(src, base + 2 * L::kBlk);
         }
     };
-    unsigned char* exP = exch + (kb * 2 + 0) * 2048;   // P  B-operand images [rh][lane] x 16 B
-    unsigned char* exS = exch + (kb * 2 + 1) * 2048;   // dS B-operand images
-
-    const int first = next_needed(0);
-    if (role != 0 && first < p.RB) dma_block(first, 0);
 
     const int eq = p.scal[0], edo = p.scal[1];
     const int ksx = load_ds_exponent(p);
+    const int first = next_needed(0);
+    if (first < p.RB) dma_block(first, 0);
 
-    if (role == 0) {
-        // ================= S waves
-        const float sc2 = fabsf(p.scale) * ldexpf(1.0f, -eq) * kLog2e;   // q carries the sign
-        const float dsf = ldexpf(1.0f, -ksx);
-        const float pf = ldexpf(1.0f, kPScaleLog2);
-        const RowWalk<D> rw = make_row_walk<D>(lane);
-        int buf = 0;
-        for (int rb = first; rb < p.RB;) {
-            const int rbn = next_needed(rb + 1);
-            const int cls = kb_class(rb);
-            wait_all_mem();
-            __syncthreads();   // A: block rb landed; the exchange slots are free
-            if (cls != kMaskDead) {
-                const unsigned char* tq = work + buf * L::kBuf;
-                const float* lrow = (const float*)(work + buf * L::kBuf + 2 * BLK * 2);
-                const float* drow = lrow + 32;
-                f32x16 sa, pa;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
-                pair_rows_kv<D, 1, BLK * 2>(tq, (const unsigned char*)(sV + 32 * kb * D), bk, sa, pa, rw);
-                f16x8 bp[2], bs[2];
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const f32x4 l4 = *(const f32x4*)(lrow + 8 * b + 4 * g);
-                    const f32x4 d4 = *(const f32x4*)(drow + 8 * b + 4 * g);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int v = 4 * b + u;
-                        float pv = 0.0f;
-                        if (key_ok && l4[u] != neg_inf()) {
-                            float sv = sa[v] * sc2;
-                            if (cls == kMaskMixed) {
-                                const int r = 32 * rb + crow(v, g);
-                                const int ii = r / p.G, gh = r - (r / p.G) * p.G;
-                                const char* mrow = p.mask + (int64_t)ii * p.m_nb1 +
-                                                   (int64_t)(p.Hm == 1 ? 0 : hk * p.G + gh) * p.m_nb2;
-                                sv += mask_at(mrow, p.m_type, myj) * kLog2e;
-                            }
-                            pv = fast_exp2(sv - l4[u]);
-                        }
-                        const float dsv = pv * (pa[v] - d4[u]);
-                        bp[v >> 3][v & 7] = (_Float16)(pv * pf);
-                        bs[v >> 3][v & 7] = (_Float16)(dsv * dsf);
-                    }
-                }
-#pragma unroll
-                for (int rh = 0; rh < 2; ++rh) {
-                    *(f16x8*)(exP + rh * 1024 + lane * 16) = bp[rh];
-                    *(f16x8*)(exS + rh * 1024 + lane * 16) = bs[rh];
-                }
-            }
-            __syncthreads();   // B: P and dS of block rb are in the exchange
-            rb = rbn;
-            buf ^= 1;
-        }
-        return;
-    }
-
-    // ================= accumulating waves (role 1: dK with q, role 2: dV with dO)
     f32x16 acc[MD];
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[md][v] = 0.0f;
-    const unsigned char* exIn = role == 1 ? exS : exP;
-    int buf = 0;
-    for (int rb = first; rb < p.RB;) {
-        const int rbn = next_needed(rb + 1);
-        const int cls = kb_class(rb);
-        wait_all_mem();
-        __syncthreads();   // A
-        if (rbn < p.RB) dma_block(rbn, buf ^ 1);
-        __syncthreads();   // B
-        if (cls != kMaskDead) {
-            const Swz z = make_swz<D>(lane);
-            const _Float16* src = (const _Float16*)(work + buf * L::kBuf) + (role == 1 ? 0 : BLK);
-            const f16x8 b0 = *(const f16x8*)(exIn + lane * 16);
-            const f16x8 b1 = *(const f16x8*)(exIn + 1024 + lane * 16);
+    const RowWalkX rw = make_row_walk_x<D>(lane);
+    const ColWalkX cw = make_col_walk_x<D>(lane);
+    unsigned char* myP = exP + kb * 2048;             // P image [rh][lane] x 16 B
+    unsigned char* myD = exD + kb * 4096;             // dP [4][lane] x 16 B
+    unsigned char* myF = exF + kb * 4096;             // P in fp32, kept by the A wave across phase 1
+
+    if (role == 0) {
+        // ================= A waves: S, P, then dS and dK
+        const float sc2 = fabsf(p.scale) * ldexpf(1.0f, -eq) * kLog2e;   // q carries the sign
+        const float dsf = ldexpf(1.0f, -ksx);
+        const float pf = ldexpf(1.0f, kPScaleLog2);
+        int buf = 0;
+        for (int rb = first; rb < p.RB;) {
+            const int rbn = next_needed(rb + 1);
+            const int cls = half_class(rb, kb >> 1);
+            wait_all_mem();
+            __syncthreads();   // X: block rb landed in buffer `buf`; the exchange is free
+            if (rbn < p.RB) dma_block(rbn, buf ^ 1);
+            const unsigned char* tq = work + buf * L::kBuf;
+            const float* lrow = (const float*)(tq + 2 * L::kBlk);
+            const float* drow = lrow + 32;
+            if (cls != kMaskDead) {
+                f32x16 sa;
 #pragma unroll
-            for (int md = 0; md < MD; ++md) {
-                acc[md] = mfma32(frag_cols<D>(src, md, 0, lane, z), b0, acc[md]);
-                acc[md] = mfma32(frag_cols<D>(src, md, 16, lane, z), b1, acc[md]);
+                for (int v = 0; v < 16; ++v) sa[v] = 0.0f;
+                rows_chain_x<D, 1>(tq, bkv, sa, rw);
+                if (cls == kMaskMixed) {
+                    // mask terms staged through the wave's fp32 P slot by a rolled loop, so the
+                    // masked case costs the loop below no registers; a fully masked row (and
+                    // every padding row past R, lse = -inf) reads no mask
+#pragma unroll 1
+                    for (int v = 0; v < 16; ++v) {
+                        const int b = v >> 2, u = v & 3;
+                        float mv = neg_inf();
+                        if (key_ok && lrow[8 * b + 4 * g + u] != neg_inf()) {
+                            const int r = 32 * rb + crow(v, g);
+                            const int ii = r / p.G, gh = r - (r / p.G) * p.G;
+                            const char* mrow = p.mask + (int64_t)ii * p.m_nb1 +
+                                               (int64_t)(p.Hm == 1 ? 0 : hk * p.G + gh) * p.m_nb2;
+                            mv = mask_at(mrow, p.m_type, myj) * kLog2e;
+                        }
+                        ((float*)(myF + (b * 64 + lane) * 16))[u] = mv;
+                    }
+                }
+                const float mdef = key_ok ? 0.0f : neg_inf();
+                f16x8 bp[2];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const f32x4 l4 = *(const f32x4*)(lrow + 8 * b + 4 * g);
+                    f32x4 m4 = {mdef, mdef, mdef, mdef};
+                    if (cls == kMaskMixed) m4 = *(const f32x4*)(myF + (b * 64 + lane) * 16);
+                    f32x4 p4;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int v = 4 * b + u;
+                        // a fully masked row has lse = -inf: use +inf so that p = 0
+                        const float lr = l4[u] != neg_inf() ? l4[u] : -neg_inf();
+                        p4[u] = fast_exp2(fmaf(sa[v], sc2, m4[u] - lr));
+                        bp[v >> 3][v & 7] = (_Float16)(p4[u] * pf);
+                    }
+                    *(f32x4*)(myF + (b * 64 + lane) * 16) = p4;
+                }
+#pragma unroll
+                for (int rh = 0; rh < 2; ++rh) *(f16x8*)(myP + rh * 1024 + lane * 16) = bp[rh];
             }
+            __syncthreads();   // Y: P and dP exchanged
+            if (cls != kMaskDead) {
+                f16x8 bs[2];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const f32x4 dp4 = *(const f32x4*)(myD + (b * 64 + lane) * 16);
+                    const f32x4 p4 = *(const f32x4*)(myF + (b * 64 + lane) * 16);
+                    const f32x4 d4 = *(const f32x4*)(drow + 8 * b + 4 * g);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int v = 4 * b + u;
+                        bs[v >> 3][v & 7] = (_Float16)(p4[u] * (dp4[u] - d4[u]) * dsf);
+                    }
+                }
+                cols_acc_x<D>(tq, bs, acc, cw);
+            }
+            rb = rbn;
+            buf ^= 1;
         }
-        rb = rbn;
-        buf ^= 1;
+    } else {
+        // ================= B waves: dP, then dV
+        int buf = 0;
+        for (int rb = first; rb < p.RB;) {
+            const int rbn = next_needed(rb + 1);
+            const int cls = half_class(rb, kb >> 1);
+            wait_all_mem();
+            __syncthreads();   // X
+            if (rbn < p.RB) dma_block(rbn, buf ^ 1);
+            const unsigned char* tq = work + buf * L::kBuf;
+            if (cls != kMaskDead) {
+                f32x16 pa;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) pa[v] = 0.0f;
+                rows_chain_x<D, 1>(tq + L::kBlk, bkv, pa, rw);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const f32x4 o = {pa[4 * b], pa[4 * b + 1], pa[4 * b + 2], pa[4 * b + 3]};
+                    *(f32x4*)(myD + (b * 64 + lane) * 16) = o;
+                }
+            }
+            __syncthreads();   // Y
+            if (cls != kMaskDead) {
+                const f16x8 bp[2] = {*(const f16x8*)(myP + lane * 16), *(const f16x8*)(myP + 1024 + lane * 16)};
+                cols_acc_x<D>(tq + L::kBlk, bp, acc, cw);
+            }
+            rb = rbn;
+            buf ^= 1;
+        }
     }
     if (!key_ok) return;
-    const float fac = role == 1 ? fabsf(p.scale) * ldexpf(1.0f, ksx - eq - edo) : ldexpf(1.0f, -kPScaleLog2 - edo);
-    float* dst = (role == 1 ? p.dk : p.dv) + ((int64_t)hk * p.M + myj) * D;
+    const float fac = role == 0 ? fabsf(p.scale) * ldexpf(1.0f, ksx - eq - edo) : ldexpf(1.0f, -kPScaleLog2 - edo);
+    float* dst = (role == 0 ? p.dk : p.dv) + ((int64_t)hk * p.M + myj) * D;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll

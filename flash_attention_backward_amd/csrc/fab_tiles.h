@@ -458,6 +458,94 @@ FAB_DEV void pair_rows(const unsigned char* tile, const f16x8* bq, const f16x8* 
     }
 }
 
+// acc += A B over d for a 32x32 block: A operands frag_rows of the tile at `t` (its rows
+// 0..31), B operands b[ks] in registers; steps in Gray order, reads PF steps ahead.
+template <int D, int PF>
+FAB_DEV void rows_chain(const unsigned char* t, const f16x8* b, f32x16& acc, const RowWalk<D>& w) {
+    constexpr int KS = D / 16, NB = PF + 1;
+    int a = w.a0;
+    f16x8 r[NB];
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+        r[s] = *(const f16x8*)(t + a);
+        if (s + 1 < KS) a += gray_step(s, w.e);
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        if (s + PF < KS) {
+            r[(s + PF) % NB] = *(const f16x8*)(t + a);
+            if (s + PF + 1 < KS) a += gray_step(s + PF, w.e);
+        }
+        acc = mfma32(r[s % NB], b[gray(s)], acc);
+    }
+}
+
+// Compact forms of the two walks for waves short of registers: the address of step s is
+// rebuilt from the lane's base and XOR term (an XOR and a shift-add) instead of stepping.
+struct RowWalkX {
+    int base;   // byte offset of the lane's row and half (g ^ zr0) part
+    int c;      // ks is XORed with c
+};
+template <int D>
+FAB_DEV RowWalkX make_row_walk_x(int lane) {
+    constexpr int CM = (D / 8) - 1;
+    const int zr = swz_term(lane & 31) & CM, g = lane >> 5;
+    return {opaque((lane & 31) * D * 2 + 16 * (g ^ (zr & 1))), opaque(zr >> 1)};
+}
+FAB_DEV int row_addr(const RowWalkX& w, int ks) { return w.base + 32 * (ks ^ w.c); }
+
+struct ColWalkX {
+    int base[2];   // byte offsets of the two transpose reads without the md part
+    int ee[2];     // md is XORed with ee
+};
+template <int D>
+FAB_DEV ColWalkX make_col_walk_x(int lane) {
+    constexpr int CM = (D / 8) - 1;
+    const int g = lane >> 5, h16 = (lane >> 4) & 1, s = lane & 15;
+    ColWalkX w;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = 8 * j + 4 * g + (s >> 2);
+        const int zc = swz_term(row) & CM;
+        const int cc = (2 * h16 + ((s & 3) >> 1)) ^ (zc & 3);
+        w.base[j] = opaque(row * D * 2 + 16 * cc + 8 * (s & 1));
+        w.ee[j] = opaque(zc >> 2);
+    }
+    return w;
+}
+
+// rows_chain with the compact walk
+template <int D, int PF>
+FAB_DEV void rows_chain_x(const unsigned char* t, const f16x8* b, f32x16& acc, const RowWalkX& w) {
+    constexpr int KS = D / 16, NB = PF + 1;
+    f16x8 r[NB];
+#pragma unroll
+    for (int s = 0; s < PF; ++s) r[s] = *(const f16x8*)(t + row_addr(w, gray(s)));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        if (s + PF < KS) r[(s + PF) % NB] = *(const f16x8*)(t + row_addr(w, gray(s + PF)));
+        acc = mfma32(r[s % NB], b[gray(s)], acc);
+    }
+}
+
+// cols_acc with the compact walk, reads right before use
+template <int D>
+FAB_DEV void cols_acc_x(const unsigned char* t, const f16x8 b[2], f32x16* acc, const ColWalkX& w) {
+    constexpr int MD = D / 32;
+    constexpr int RH = 16 * D * 2;
+#pragma unroll
+    for (int s = 0; s < MD; ++s) {
+        const int md = gray(s);
+        const int a0 = w.base[0] + 64 * (md ^ w.ee[0]);
+        const int a1 = w.base[1] + 64 * (md ^ w.ee[1]);
+        const f16x8 r0 = join(tr_read(t + a0), tr_read(t + a1));
+        const f16x8 r1 = join(tr_read(t + a0 + RH), tr_read(t + a1 + RH));
+        acc[md] = mfma32(r0, b[0], acc[md]);
+        acc[md] = mfma32(r1, b[1], acc[md]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Key-side pair: sa += Q K^T (A: q rows of the tile at tq, B: bk in registers) and
 // pa += dO V^T (A: dO rows of the tile at tq + DOFF, B: V rows of the tile at tv), over d in
 // the same Gray order as pair_rows, so both sides sum every score in the same order.
@@ -489,27 +577,40 @@ FAB_DEV void pair_rows_kv(const unsigned char* tq, const unsigned char* tv, cons
 }
 
 // acc[md] += A(md, 0) b[0] + A(md, 1) b[1] for md = 0 .. D/32-1, A(md, rh) the frag_cols read
-// of rows 16*rh .. 16*rh+15 of the tile at `tile` (a contraction over its 32 rows); md in Gray
-// order with the reads of the next md issued before the products of this one.
-template <int D>
-FAB_DEV void cols_acc(const unsigned char* tile, const f16x8 b[2], f32x16* acc, const ColWalk<D>& w) {
+// of rows 16*rh .. 16*rh+15 of the tile at `t` (a contraction over its 32 rows); md in Gray
+// order. PF = 1 issues the reads of the next md before the products of this one (8 more
+// registers), PF = 0 reads right before use.
+template <int D, int PF = 1>
+FAB_DEV void cols_acc(const unsigned char* t, const f16x8 b[2], f32x16* acc, const ColWalk<D>& w) {
     constexpr int MD = D / 32;
     constexpr int RH = 16 * D * 2;                    // bytes of 16 rows
     int a0 = w.a0[0], a1 = w.a0[1];
-    f16x8 r0[2], r1[2];
-    r0[0] = join(tr_read(tile + a0), tr_read(tile + a1));
-    r1[0] = join(tr_read(tile + a0 + RH), tr_read(tile + a1 + RH));
+    f16x8 r0[PF + 1], r1[PF + 1];
+    if (PF) {
+        r0[0] = join(tr_read(t + a0), tr_read(t + a1));
+        r1[0] = join(tr_read(t + a0 + RH), tr_read(t + a1 + RH));
+    }
 #pragma unroll
-    for (int t = 0; t < MD; ++t) {
-        if (t + 1 < MD) {
-            a0 += gray_step(t, w.e[0]);
-            a1 += gray_step(t, w.e[1]);
-            r0[(t + 1) & 1] = join(tr_read(tile + a0), tr_read(tile + a1));
-            r1[(t + 1) & 1] = join(tr_read(tile + a0 + RH), tr_read(tile + a1 + RH));
+    for (int s = 0; s < MD; ++s) {
+        const int cur = PF ? (s & 1) : 0;
+        if (PF) {
+            if (s + 1 < MD) {
+                a0 += gray_step(s, w.e[0]);
+                a1 += gray_step(s, w.e[1]);
+                r0[(s + 1) & 1] = join(tr_read(t + a0), tr_read(t + a1));
+                r1[(s + 1) & 1] = join(tr_read(t + a0 + RH), tr_read(t + a1 + RH));
+            }
+        } else {
+            r0[0] = join(tr_read(t + a0), tr_read(t + a1));
+            r1[0] = join(tr_read(t + a0 + RH), tr_read(t + a1 + RH));
+            if (s + 1 < MD) {
+                a0 += gray_step(s, w.e[0]);
+                a1 += gray_step(s, w.e[1]);
+            }
         }
-        const int md = gray(t);
-        acc[md] = mfma32(r0[t & 1], b[0], acc[md]);
-        acc[md] = mfma32(r1[t & 1], b[1], acc[md]);
+        const int md = gray(s);
+        acc[md] = mfma32(r0[cur], b[0], acc[md]);
+        acc[md] = mfma32(r1[cur], b[1], acc[md]);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
