@@ -136,8 +136,9 @@ FAB_DEV int load_ds_exponent(const Params& p) {
 constexpr int kClassTilesPerBlock = 16;
 
 __global__ __launch_bounds__(kThreads) void maskclass_kernel(Params p) {
-    __shared__ int red[2][kWaves];
+    __shared__ unsigned int red[kClassTilesPerBlock][kWaves];
     const int hc = blockIdx.x / p.RB, rb = blockIdx.x - (blockIdx.x / p.RB) * p.RB;
+    const int wave = threadIdx.x >> 6;
     const int rr = threadIdx.x >> 3, kg = threadIdx.x & 7;
     const int r = rb * 32 + rr;
     const bool row_ok = r < p.R;
@@ -145,36 +146,63 @@ __global__ __launch_bounds__(kThreads) void maskclass_kernel(Params p) {
     const char* mrow = p.mask + (int64_t)i * p.m_nb1 + (int64_t)(p.Hm == 1 ? 0 : hc * p.G + gh) * p.m_nb2;
     const int tb = blockIdx.y * kClassTilesPerBlock;
     const int te = min(p.KT, tb + kClassTilesPerBlock);
-    for (int t = tb; t < te; ++t) {
-        bool all0 = true, allinf = true;
-        if (row_ok) {
+    const int esz = p.m_type == FA_BACK_F16 ? 2 : 4;
+    // 16-byte loads of 8 consecutive entries when the rows allow them
+    const bool vec = (((uintptr_t)p.mask | (uintptr_t)p.m_nb1 | (uintptr_t)p.m_nb2) & 15) == 0;
+    // entries of this thread in every tile: keys t*64 + 8*kg .. +7; all loads issued first
+    u32x4 raw[kClassTilesPerBlock][2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int j = t * kQTileKeys + 8 * kg + e;
-                if (j < p.M) {
-                    const float x = p.m_type == FA_BACK_F16 ? (float)*(const _Float16*)(mrow + 2 * (int64_t)j)
-                                                             : *(const float*)(mrow + 4 * (int64_t)j);
+    for (int k = 0; k < kClassTilesPerBlock; ++k) {
+        const int t = tb + k;
+        const int j = t * kQTileKeys + 8 * kg;
+        raw[k][0] = raw[k][1] = u32x4{0u, 0u, 0u, 0u};
+        if (row_ok && t < te && vec && j + 8 <= p.M) {
+            raw[k][0] = *(const u32x4*)(mrow + (int64_t)j * esz);
+            if (esz == 4) raw[k][1] = *(const u32x4*)(mrow + (int64_t)j * esz + 16);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kClassTilesPerBlock; ++k) {
+        const int t = tb + k;
+        const int j = t * kQTileKeys + 8 * kg;
+        bool all0 = true, allinf = true;
+        if (row_ok && t < te) {
+            if (vec && j + 8 <= p.M) {
+                if (esz == 2) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const unsigned int x = raw[k][0][w];
+                        // fp16 zero: bits 0x0000 or 0x8000; fp16 -inf: 0xfc00
+                        all0 = all0 && ((x & 0x7fff7fffu) == 0u);
+                        allinf = allinf && (x == 0xfc00fc00u);
+                    }
+                } else {
+#pragma unroll
+                    for (int w = 0; w < 8; ++w) {
+                        const unsigned int x = raw[k][w >> 2][w & 3];
+                        all0 = all0 && ((x & 0x7fffffffu) == 0u);
+                        allinf = allinf && (x == (unsigned int)kNegInfBits);
+                    }
+                }
+            } else {
+                for (int e = 0; e < 8; ++e) {
+                    if (j + e >= p.M) break;
+                    const float x = p.m_type == FA_BACK_F16 ? (float)*(const _Float16*)(mrow + 2 * (int64_t)(j + e))
+                                                             : *(const float*)(mrow + 4 * (int64_t)(j + e));
                     all0 = all0 && (x == 0.0f);
                     allinf = allinf && (x == neg_inf());
                 }
             }
         }
         const bool w0 = __all(all0), winf = __all(allinf);
-        if ((threadIdx.x & 63) == 0) {
-            red[0][threadIdx.x >> 6] = w0;
-            red[1][threadIdx.x >> 6] = winf;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            bool b0 = true, binf = true;
-            for (int w = 0; w < kWaves; ++w) {
-                b0 = b0 && red[0][w];
-                binf = binf && red[1][w];
-            }
-            p.mcls[((int64_t)hc * p.RB + rb) * p.KT + t] =
-                (unsigned char)(binf ? kMaskDead : (b0 ? kMaskZero : kMaskMixed));
-        }
-        __syncthreads();
+        if ((threadIdx.x & 63) == 0) red[k][wave] = (w0 ? 1u : 0u) | (winf ? 2u : 0u);
+    }
+    __syncthreads();
+    if (threadIdx.x < kClassTilesPerBlock && tb + (int)threadIdx.x < te) {
+        unsigned int f = 3u;
+        for (int w = 0; w < kWaves; ++w) f &= red[threadIdx.x][w];
+        p.mcls[((int64_t)hc * p.RB + rb) * p.KT + tb + threadIdx.x] =
+            (unsigned char)((f & 2u) ? kMaskDead : ((f & 1u) ? kMaskZero : kMaskMixed));
     }
 }
 
