@@ -33,6 +33,9 @@ int64_t elem_size(int type) {
 struct Geometry {
     int D, Dv, H, Hkv, G, N, M, Hm;
     int R, RB, RT, KT, splits, tiles_per_split, KVT;
+    bool w1keys;           // walk 1 by key tiles (else by row tiles)
+    int KT1, RS1, w1_rbs;  // its 256-key tiles, row splits and row blocks per workgroup
+    int nparts;            // walk-1 records per row
     int npart, nbound;
     fa_back_layout layout;
     // workspace offsets (bytes)
@@ -113,9 +116,39 @@ int validate(const fa_back_desc* d, Geometry* g) {
         g->tiles_per_split = tps;
         g->splits = g->KT > 0 ? (g->KT + tps - 1) / tps : 1;
     }
+    // walk 1 by key tiles when the cache is long next to the rows (each K/V tile is then
+    // decoded once per 256 keys instead of once per 128 rows); FA_BACK_WALK1=keys|rows
+    // overrides the choice
+    {
+        g->KT1 = (g->M + kW1Keys - 1) / kW1Keys;
+        bool keys = g->M >= 2 * (int64_t)g->R;
+        if (const char* e = std::getenv("FA_BACK_WALK1")) {
+            if (!std::strcmp(e, "keys")) keys = true;
+            if (!std::strcmp(e, "rows")) keys = false;
+        }
+        g->w1keys = keys && g->M > 0 && g->R > 0;
+        g->RS1 = 1;
+        g->w1_rbs = g->RB;
+        if (g->w1keys) {
+            // row splits: fill whole rounds of 256 workgroups, keep >= 16 row blocks each
+            const int rs_min = (g->RB + W1Lds<64>::kMaxRB - 1) / W1Lds<64>::kMaxRB;
+            int best = rs_min;
+            double best_eff = -1.0;
+            for (int rs = rs_min; rs <= 16; ++rs) {
+                const int rbs = (g->RB + rs - 1) / rs;
+                if (rs > rs_min && rbs < 16) break;
+                const double n = (double)g->KT1 * g->Hkv * rs / 256.0;
+                const double eff = n / std::ceil(n);
+                if (eff > best_eff + 1e-9) { best_eff = eff; best = rs; }
+            }
+            g->w1_rbs = (g->RB + best - 1) / best;
+            g->RS1 = (g->RB + g->w1_rbs - 1) / g->w1_rbs;
+        }
+        g->nparts = g->w1keys ? g->KT1 : g->splits;
+    }
     g->npart = (int)std::min<int64_t>(512, std::max<int64_t>(1, N * H / 8));
     const int64_t total_rows = (int64_t)g->Hkv * g->RB * 32;
-    g->nbound = (int)std::min<int64_t>(256, std::max<int64_t>(1, (total_rows + kThreads - 1) / kThreads));
+    g->nbound = (int)std::min<int64_t>(kMergeMaxBlocks, std::max<int64_t>(1, (total_rows + kMergeRows - 1) / kMergeRows));
 
     // packed output
     fa_back_layout& L = g->layout;
@@ -129,7 +162,7 @@ int validate(const fa_back_desc* d, Geometry* g) {
     uint64_t o = 0;
     auto take = [&](uint64_t bytes) { const uint64_t at = o; o = align_up(o + bytes, kAlign); return at; };
     const uint64_t frag = 2ull * total_rows * D;
-    const uint64_t prow = (uint64_t)g->splits * total_rows;
+    const uint64_t prow = (uint64_t)std::max(g->splits, g->nparts) * total_rows;
     g->ws_absmax = take(8ull * g->npart);
     g->ws_scal = take(64);
     g->ws_qr = take(frag);
@@ -180,7 +213,10 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
                                                   (g.KT + kClassTilesPerBlock - 1) / kClassTilesPerBlock),
                            dim3(kThreads), 0, st, P);
     pm.mark(1);
-    hipLaunchKernelGGL((qpass_kernel<D, false>), dim3(g.RT * g.Hkv, g.splits), dim3(kQThreads), 0, st, P);
+    if (g.w1keys)
+        hipLaunchKernelGGL(walk1_keys_kernel<D>, dim3(g.KT1 * g.Hkv, g.RS1), dim3(kW1Threads), 0, st, P);
+    else
+        hipLaunchKernelGGL((qpass_kernel<D, false>), dim3(g.RT * g.Hkv, g.splits), dim3(kQThreads), 0, st, P);
     pm.mark(2);
     hipLaunchKernelGGL(merge_kernel, dim3(g.nbound), dim3(kThreads), 0, st, P);
     pm.mark(3);
@@ -290,6 +326,7 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     P.D = g.D; P.H = g.H; P.Hkv = g.Hkv; P.G = g.G; P.N = g.N; P.M = g.M; P.Hm = g.Hm;
     P.R = g.R; P.RB = g.RB; P.RT = g.RT; P.KT = g.KT; P.splits = g.splits;
     P.tiles_per_split = g.tiles_per_split; P.KVT = g.KVT;
+    P.w1_rbs = g.w1_rbs; P.nparts = g.nparts;
     P.scale = ds.scale;
     char* o = (char*)out;
     P.dq = (float*)(o + g.layout.off_dq);

@@ -47,6 +47,8 @@ struct Params {
     int splits;       // key-range splits of the query-side passes
     int tiles_per_split;
     int KVT;          // 128-key tiles of the key-side pass
+    int w1_rbs;       // walk 1 by key tiles: row blocks per workgroup
+    int nparts;       // walk-1 records per row that the merge combines (splits or key tiles)
     float scale;
     // outputs (packed)
     float* dq;
@@ -60,7 +62,7 @@ struct Params {
     int* scal;            // [0] = e_q, [1] = e_do (power-of-two exponents)
     _Float16* qr;         // [Hkv][RB*32][D]  q rows scaled by 2^e_q, fp16, row-major
     _Float16* dr;         // [Hkv][RB*32][D]  dO rows scaled by 2^e_do, fp16, row-major
-    float* part_m;        // [splits][Hkv*RB*32]  running max (log2 units)
+    float* part_m;        // [nparts][Hkv*RB*32]  running max (log2 units)
     double* part_l;       // softmax sum at part_m
     double* part_d;       // sum of e * dp at part_m (dp in 2^e_do units)
     float* part_b;        // max |dp| over visible keys

@@ -121,7 +121,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
 
 // ----------------------------------------------------------------------------- helpers
 
-// dS exponent: every workgroup of a wave reduces the merge kernel's bound partials.
+// dS exponent: every wave reduces the merge kernel's bound partials. It ends in a wave-wide
+// reduction, so every lane of the wave must call it (never from a lane-divergent branch).
 FAB_DEV int load_ds_exponent(const Params& p) {
     float b = 0.0f;
     for (int t = threadIdx.x & 63; t < p.nbound; t += 64) b = fmaxf(b, p.bound_part[t]);
@@ -541,8 +542,9 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         if (s == s_end) break;
         if (s + 1 < s_end) kdecode(s + 1);
     }
+    // (a wave-wide reduction: taken by every lane, before the per-row branch)
+    const int ksx = GRAD ? load_ds_exponent(p) : 0;
     if (GRAD && row_ok) {
-        const int ksx = load_ds_exponent(p);
         const bool direct = p.splits == 1;
         const float fac = direct ? p.scale * ldexpf(1.0f, ksx - edo) : 1.0f;
         float* dst = direct ? p.dq + ((int64_t)h * p.N + i) * D
@@ -558,58 +560,317 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     }
 }
 
+// ----------------------------------------------------------------------------- walk 1 by keys
+
+// Walk 1 with the keys owned (used when the cache is long next to the rows): a workgroup takes
+// one KV head, 256 keys (8 waves x 32 keys) and a range of 32-row blocks. The K and V fragments
+// of a wave's keys are decoded once into its registers; per row block (q/dO rows DMA'd into
+// LDS, double-buffered) each wave computes S^T = K Q^T and dP^T = V dO^T and, per query row over
+// its 32 keys, the max m, l = sum exp2(s - m) and d' = sum exp2(s - m) dp (fp32) and max |dp|.
+// The 8 waves' values of a row are merged in fp64 in wave order by the last wave, one block
+// later, and written as the row's record for this 256-key tile; the merge kernel combines a
+// row's records in tile order. Rows no key of the tile sees get an empty record.
+constexpr int kW1Waves = 8;
+constexpr int kW1Threads = kW1Waves * kWave;
+constexpr int kW1Keys = kW1Waves * 32;
+
+template <int D>
+struct W1Lds {
+    static constexpr int kBlk = 32 * D * 2;                              // bytes of a 32-row block
+    static constexpr int kBuf = 2 * kBlk;                                // q, dO
+    static constexpr int kRec = kW1Waves * 32 * 16;                      // [wave][row] {m, l, d, b}
+    static constexpr int kWork = 2 * kBuf + 2 * kRec;
+    static constexpr int kRaw = RawTile<D, kQTileKeys>::kBytes;
+    static constexpr int kSetup = 2 * kQTileKeys * D * 2 + 2 * kRaw;     // K, V 64-key tiles + bytes
+    static constexpr int kMaxRB = 4096;                                  // row blocks per workgroup
+    static constexpr int kTiles = kW1Keys / kQTileKeys;                  // 64-key class tiles
+    static constexpr int kBytes = (kSetup > kWork ? kSetup : kWork) + kTiles * kMaxRB;
+};
+
+template <int D>
+__global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
+    using L = W1Lds<D>;
+    constexpr int KS = D / 16;
+    constexpr int NI = L::kBlk / 1024;                // 64-lane x 16-byte DMA instructions per tensor
+    constexpr int NIW = (2 * NI + kW1Waves - 1) / kW1Waves;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
+    unsigned char* work = lds;
+    unsigned char* recs = work + 2 * L::kBuf;                         // [2][wave][row] x 16 B
+    unsigned char* cls = lds + L::kBytes - L::kTiles * L::kMaxRB;     // [tile][row block - rb0]
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int l32 = lane & 31, g = lane >> 5;
+    const int hk = blockIdx.x % p.Hkv;
+    const int kt = blockIdx.x / p.Hkv;
+    const int key0 = kt * kW1Keys;
+    const int wkey0 = key0 + 32 * wave;
+    const int mytile = wave / 2;                      // 64-key class tile of this wave
+    const int rb0 = blockIdx.y * p.w1_rbs;
+    const int rb1 = min(p.RB, rb0 + p.w1_rbs);
+    const int nloc = rb1 > rb0 ? rb1 - rb0 : 0;
+    const int rowsHK = p.RB * 32;
+    const int64_t total = (int64_t)p.Hkv * rowsHK;
+    const int64_t rec0 = (int64_t)kt * total + (int64_t)hk * rowsHK;   // record index of row 0
+
+    // ---- setup: K and V fragments of the wave's 32 keys into registers (keys >= M are 0)
+    f16x8 bk[KS], bv[KS];
+    {
+        _Float16* sK = (_Float16*)work;
+        _Float16* sV = sK + kQTileKeys * D;
+        unsigned char* rawK = work + 2 * kQTileKeys * D * 2;
+        unsigned char* rawV = rawK + L::kRaw;
+#pragma unroll 1
+        for (int qt = 0; qt < L::kTiles; ++qt) {
+            const int j0 = key0 + qt * kQTileKeys;
+            __syncthreads();
+            if (p.k_type == FA_BACK_Q8_0)
+                dma_raw_tile<D, kQTileKeys, kW1Threads>(p.k, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, threadIdx.x);
+            if (p.v_type == FA_BACK_Q8_0)
+                dma_raw_tile<D, kQTileKeys, kW1Threads>(p.v, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV, threadIdx.x);
+            wait_all_mem();
+            __syncthreads();
+            decode_tile<D, kQTileKeys, kW1Threads>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, sK,
+                                                   threadIdx.x);
+            decode_tile<D, kQTileKeys, kW1Threads>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV, sV,
+                                                   threadIdx.x);
+            __syncthreads();
+            if (mytile == qt) {
+                const Swz z = make_swz<D>(lane);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    bk[ks] = frag_rows<D>(sK, 32 * (wave & 1), ks, lane, z);
+                    bv[ks] = frag_rows<D>(sV, 32 * (wave & 1), ks, lane, z);
+                }
+            }
+        }
+        // mask classes of (row block, 64-key tile) for the workgroup's row blocks and tiles
+        for (int idx = threadIdx.x; idx < L::kTiles * nloc; idx += kW1Threads) {
+            const int t = idx / nloc, lr = idx - (idx / nloc) * nloc;
+            const int tile = key0 / kQTileKeys + t;
+            cls[t * L::kMaxRB + lr] = (unsigned char)(tile < p.KT ? mask_class(p, hk, rb0 + lr, tile) : kMaskDead);
+        }
+        __syncthreads();   // the setup region becomes the row-block buffers
+    }
+    auto tcls = [&](int rbx, int t) -> int { return cls[t * L::kMaxRB + (rbx - rb0)]; };
+    auto needed = [&](int rbx) -> bool {
+#pragma unroll
+        for (int t = 0; t < L::kTiles; ++t)
+            if (tcls(rbx, t) != kMaskDead) return true;
+        return false;
+    };
+    auto next_needed = [&](int rbx) -> int {
+        while (rbx < rb1 && !needed(rbx)) ++rbx;
+        return rbx;
+    };
+    // empty records for the rows of blocks no key of this tile sees
+    for (int idx = threadIdx.x; idx < 32 * nloc; idx += kW1Threads) {
+        const int rbx = rb0 + idx / 32;
+        if (needed(rbx)) continue;
+        const int64_t ri = rec0 + (int64_t)rb0 * 32 + idx;
+        p.part_m[ri] = neg_inf();
+        p.part_l[ri] = 0.0;
+        p.part_d[ri] = 0.0;
+        p.part_b[ri] = 0.0f;
+    }
+
+    const char* qbase = (const char*)(p.qr + (int64_t)hk * rowsHK * D);
+    const char* dbase = (const char*)(p.dr + (int64_t)hk * rowsHK * D);
+    auto dma_block = [&](int rbx, int b) {
+        unsigned char* base = work + b * L::kBuf;
+        const int64_t blk = (int64_t)rbx * L::kBlk;
+#pragma unroll
+        for (int k = 0; k < NIW; ++k) {
+            const int ins = wave + kW1Waves * k;     // uniform
+            if (ins >= 2 * NI) break;
+            const int ten = ins / NI, ii = ins - (ins / NI) * NI;
+            const int P = ii * 64 + lane;
+            const int row = P / (D / 8), pc = P - (P / (D / 8)) * (D / 8);
+            const int off = (row * D + 8 * swz_chunk<D>(row, pc)) * 2;
+            dma16((ten ? dbase : qbase) + blk + off, base + ten * L::kBlk + ii * 1024);
+        }
+    };
+    // the last wave merges the 8 records of each row of a finished block (fixed wave order)
+    auto merge_block = [&](int rbx, const unsigned char* rec) {
+        const f32x4* rr = (const f32x4*)rec;
+        float mx = neg_inf(), bb = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kW1Waves; ++w) {
+            const f32x4 x = rr[w * 32 + l32];
+            mx = fmaxf(mx, x[0]);
+            bb = fmaxf(bb, x[3]);
+        }
+        double ls = 0.0, ds = 0.0;
+        if (mx != neg_inf()) {
+#pragma unroll
+            for (int w = 0; w < kW1Waves; ++w) {
+                const f32x4 x = rr[w * 32 + l32];
+                if (x[0] != neg_inf()) {
+                    const double f = (double)fast_exp2(x[0] - mx);
+                    ls = fma((double)x[1], f, ls);
+                    ds = fma((double)x[2], f, ds);
+                }
+            }
+        }
+        const int64_t ri = rec0 + (int64_t)rbx * 32 + l32;
+        p.part_m[ri] = mx;
+        p.part_l[ri] = ls;
+        p.part_d[ri] = ds;
+        p.part_b[ri] = bb;
+    };
+
+    const float sc2 = fabsf(p.scale) * ldexpf(1.0f, -p.scal[0]) * kLog2e;   // q carries the sign
+    const bool has_mask = p.m_type != FA_BACK_NONE;
+    const RowWalk<D> rw = make_row_walk<D>(lane);
+    const int first = next_needed(rb0);
+    if (first < rb1) dma_block(first, 0);
+    int buf = 0, prev = -1;
+    for (int rb = first;;) {
+        const int rbn = rb < rb1 ? next_needed(rb + 1) : rb1;
+        wait_all_mem();
+        __syncthreads();   // block rb landed in `buf`; the records of `prev` are complete
+        if (rbn < rb1) dma_block(rbn, buf ^ 1);
+        if (prev >= 0 && wave == kW1Waves - 1 && lane < 32) merge_block(prev, recs + (buf ^ 1) * L::kRec);
+        if (rb >= rb1) break;
+        const int c = tcls(rb, mytile);
+        float m = neg_inf(), l = 0.0f, d = 0.0f, b = 0.0f;
+        if (c != kMaskDead) {
+            const unsigned char* tq = work + buf * L::kBuf;
+            f32x16 sa, pa;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
+            pair_rows_t<D, 2, L::kBlk>(tq, bk, bv, sa, pa, rw);
+            const int r = 32 * rb + l32;
+            if (c == kMaskZero && wkey0 + 32 <= p.M && (rb + 1) * 32 <= p.R) {
+                // every entry visible; the scale is positive, so max(s) = sc2 * max(sa)
+                float tm = sa[0];
+#pragma unroll
+                for (int v = 1; v < 16; ++v) tm = fmaxf(tm, sa[v]);
+                m = fmaxf(tm, __shfl_xor(tm, 32)) * sc2;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float e = fast_exp2(fmaf(sa[v], sc2, -m));
+                    l += e;
+                    d = fmaf(e, pa[v], d);
+                    b = fmaxf(b, fabsf(pa[v]));
+                }
+            } else {
+                // masked or ragged: same arithmetic as above for visible mask-0 entries
+                const bool row_ok = r < p.R;
+                const char* mrow = nullptr;
+                if (has_mask && row_ok && c == kMaskMixed) {
+                    const int i = r / p.G, gh = r - (r / p.G) * p.G;
+                    mrow = p.mask + (int64_t)i * p.m_nb1 + (int64_t)(p.Hm == 1 ? 0 : hk * p.G + gh) * p.m_nb2;
+                }
+                float madd[16];
+                float tm = neg_inf();
+                const int kbase = opaque(wkey0);   // keeps per-key offsets out of the loop preheader
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = kbase + crow(v, g);
+                    float mv = 0.0f;
+                    if (!row_ok || key >= p.M) mv = neg_inf();
+                    else if (mrow) mv = mask_at(mrow, p.m_type, key) * kLog2e;
+                    madd[v] = mv;
+                    if (mv != neg_inf()) tm = fmaxf(tm, fmaf(sa[v], sc2, mv));
+                }
+                m = fmaxf(tm, __shfl_xor(tm, 32));
+                if (m != neg_inf()) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        if (madd[v] == neg_inf()) continue;
+                        const float e = fast_exp2(fmaf(sa[v], sc2, madd[v] - m));
+                        l += e;
+                        d = fmaf(e, pa[v], d);
+                        b = fmaxf(b, fabsf(pa[v]));
+                    }
+                }
+            }
+            l += __shfl_xor(l, 32);
+            d += __shfl_xor(d, 32);
+            b = fmaxf(b, __shfl_xor(b, 32));
+        }
+        if (g == 0) {
+            const f32x4 rec = {m, l, d, b};
+            *(f32x4*)(recs + buf * L::kRec + (wave * 32 + l32) * 16) = rec;
+        }
+        prev = rb;
+        rb = rbn;
+        buf ^= 1;
+    }
+}
+
 // ----------------------------------------------------------------------------- merge
 
-// One thread per row of every KV head: merge the splits in order, write LSE and delta.
+// Merge of the walk-1 records of every row (one record per key-range split or key tile), then
+// LSE and delta. A block takes 64 consecutive rows; wave w takes records w, w+4, ... of each
+// row (loads coalesced across the rows), and the four partial results meet in LDS in wave
+// order. Each block also leaves max(max|dp| + |delta|) over its rows in bound_part.
+constexpr int kMergeRows = 64;
+constexpr int kMergeMaxBlocks = 4096;
+
 __global__ __launch_bounds__(kThreads) void merge_kernel(Params p) {
-    __shared__ float red[kWaves];
+    __shared__ float smax[kWaves][kMergeRows];
+    __shared__ double sl[kWaves][kMergeRows], sd[kWaves][kMergeRows];
+    __shared__ float sb[kWaves][kMergeRows];
     const int rowsHK = p.RB * 32;
     const int total = p.Hkv * rowsHK;
-    float bmax = 0.0f;
-    for (int ridx = blockIdx.x * kThreads + threadIdx.x; ridx < total; ridx += gridDim.x * kThreads) {
+    const int lr = threadIdx.x & 63, grp = threadIdx.x >> 6;
+    float bound = 0.0f;
+    for (int base = blockIdx.x * kMergeRows; base < total; base += gridDim.x * kMergeRows) {
+        const int ridx = base + lr;
+        const bool ok = ridx < total;
         float mx = neg_inf();
-        for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.part_m[(int64_t)s * total + ridx]);
-        float lse2 = neg_inf();
-        double dl = 0.0, lnat = 0.0;
+        if (ok)
+            for (int s = grp; s < p.nparts; s += kWaves) mx = fmaxf(mx, p.part_m[(int64_t)s * total + ridx]);
+        smax[grp][lr] = mx;
+        __syncthreads();
+        mx = fmaxf(fmaxf(smax[0][lr], smax[1][lr]), fmaxf(smax[2][lr], smax[3][lr]));
+        double Ls = 0.0, Ds = 0.0;
         float b = 0.0f;
-        if (mx != neg_inf()) {
-            double Ls = 0.0, Ds = 0.0;
-            for (int s = 0; s < p.splits; ++s) {
+        if (ok && mx != neg_inf()) {
+            for (int s = grp; s < p.nparts; s += kWaves) {
                 const int64_t idx = (int64_t)s * total + ridx;
                 const float m = p.part_m[idx];
-                if (m != neg_inf()) {
-                    const double f = exp2((double)m - (double)mx);
-                    Ls += p.part_l[idx] * f;
-                    Ds += p.part_d[idx] * f;
-                }
                 b = fmaxf(b, p.part_b[idx]);
+                if (m != neg_inf()) {
+                    const double f = (double)fast_exp2(m - mx);   // 1 for the record holding the max
+                    Ls = fma(p.part_l[idx], f, Ls);
+                    Ds = fma(p.part_d[idx], f, Ds);
+                }
             }
-            const double l2 = (double)mx + log2(Ls);
-            lse2 = (float)l2;
-            lnat = l2 * kLn2;
-            dl = Ds / Ls;
-            b += fabsf((float)dl);
         }
-        p.row_lse2[ridx] = lse2;
-        p.row_dlt[ridx] = (float)dl;
-        bmax = fmaxf(bmax, b);
-        const int hk = ridx / rowsHK, r = ridx - (ridx / rowsHK) * rowsHK;
-        if (r < p.R) {
-            const int i = r / p.G, g = r - (r / p.G) * p.G;
-            const int h = hk * p.G + g;
-            const int edo = p.scal[1];
-            p.lse[(int64_t)h * p.N + i] = (mx == neg_inf()) ? neg_inf() : (float)lnat;
-            p.delta[(int64_t)h * p.N + i] = (float)ldexp(dl, -edo);
+        sl[grp][lr] = Ls;
+        sd[grp][lr] = Ds;
+        sb[grp][lr] = b;
+        __syncthreads();
+        if (grp == 0 && ok) {
+            float lse2 = neg_inf();
+            double dl = 0.0, lnat = 0.0;
+            if (mx != neg_inf()) {
+                const double L = ((sl[0][lr] + sl[1][lr]) + sl[2][lr]) + sl[3][lr];
+                const double Dd = ((sd[0][lr] + sd[1][lr]) + sd[2][lr]) + sd[3][lr];
+                const double l2 = (double)mx + log2(L);
+                lse2 = (float)l2;
+                lnat = l2 * kLn2;
+                dl = Dd / L;
+                bound = fmaxf(bound, fmaxf(fmaxf(sb[0][lr], sb[1][lr]), fmaxf(sb[2][lr], sb[3][lr])) +
+                                         fabsf((float)dl));
+            }
+            p.row_lse2[ridx] = lse2;
+            p.row_dlt[ridx] = (float)dl;
+            const int hk = ridx / rowsHK, r = ridx - (ridx / rowsHK) * rowsHK;
+            if (r < p.R) {
+                const int i = r / p.G, g = r - (r / p.G) * p.G;
+                const int h = hk * p.G + g;
+                p.lse[(int64_t)h * p.N + i] = (mx == neg_inf()) ? neg_inf() : (float)lnat;
+                p.delta[(int64_t)h * p.N + i] = (float)ldexp(dl, -p.scal[1]);
+            }
         }
+        __syncthreads();   // the LDS rows are reused by the next chunk
     }
-    bmax = wave_max(bmax);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = bmax;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float b = red[0];
-        for (int w = 1; w < kWaves; ++w) b = fmaxf(b, red[w]);
-        p.bound_part[blockIdx.x] = b;
-    }
+    if (grp != 0) return;
+    bound = wave_max(bound);
+    if (lr == 0) p.bound_part[blockIdx.x] = bound;
 }
 
 // ----------------------------------------------------------------------------- dQ reduce

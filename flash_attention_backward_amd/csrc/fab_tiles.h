@@ -546,6 +546,35 @@ FAB_DEV void cols_acc_x(const unsigned char* t, const f16x8 b[2], f32x16* acc, c
     }
 }
 
+// Transposed pair for key-owned waves: sa += K Q^T (A: bk in registers, B: q rows of the tile
+// at t) and pa += V dO^T (A: bv, B: dO rows of the tile at t + DOFF), over d in the Gray order
+// of pair_rows, reads PF steps ahead. One query row per lane column, 16 keys per lane.
+template <int D, int PF, int DOFF>
+FAB_DEV void pair_rows_t(const unsigned char* t, const f16x8* bk, const f16x8* bv, f32x16& sa, f32x16& pa,
+                         const RowWalk<D>& w) {
+    constexpr int KS = D / 16, NB = PF + 1;
+    int a = w.a0;
+    f16x8 rq[NB], rd[NB];
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+        rq[s] = *(const f16x8*)(t + a);
+        rd[s] = *(const f16x8*)(t + a + DOFF);
+        if (s + 1 < KS) a += gray_step(s, w.e);
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        if (s + PF < KS) {
+            rq[(s + PF) % NB] = *(const f16x8*)(t + a);
+            rd[(s + PF) % NB] = *(const f16x8*)(t + a + DOFF);
+            if (s + PF + 1 < KS) a += gray_step(s + PF, w.e);
+        }
+        const int ks = gray(s);
+        sa = mfma32(bk[ks], rq[s % NB], sa);
+        pa = mfma32(bv[ks], rd[s % NB], pa);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Key-side pair: sa += Q K^T (A: q rows of the tile at tq, B: bk in registers) and
 // pa += dO V^T (A: dO rows of the tile at tq + DOFF, B: V rows of the tile at tv), over d in
 // the same Gray order as pair_rows, so both sides sum every score in the same order.

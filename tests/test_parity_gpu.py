@@ -105,7 +105,10 @@ def test_strided_cache_equals_contiguous_bitwise():
         assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
 
 
-def test_gqa_equals_replicated_heads():
+@pytest.mark.parametrize("mode", ["rows", "keys"])
+def test_gqa_equals_replicated_heads(mode, monkeypatch):
+    # the same walk-1 variant for both runs: the shape-based choice could differ between them
+    monkeypatch.setenv("FA_BACK_WALK1", mode)
     p = fa_inputs.make_custom("gqa", D=128, H=6, Hkv=2, N=33, M=150, mask="tail", k_type="q8_0",
                               v_type="q8_0")
     rep = fa_inputs.Problem(**{**p.__dict__})
@@ -120,3 +123,23 @@ def test_gqa_equals_replicated_heads():
     for k in ("dk", "dv"):
         summed = b[k].astype(np.float64).reshape(p.Hkv, p.G, p.M, p.D).sum(axis=1)
         assert O.nmse(a[k], summed) <= 1e-10, k
+
+
+# Walk 1 runs by row tiles or by key tiles (chosen from the shape; FA_BACK_WALK1 overrides the
+# choice when the plan is created). Both must meet the bar on the same inputs.
+WALK1_CASES = ["c0", "c1_causal", "ragged_d128_headmask", "ragged_d64_q8", "ragged_d256_f32mask",
+               "all_masked", "single_key"]
+
+
+def _walk1_problem(name):
+    if name.startswith("c"):
+        return fa_inputs.make(name)
+    return fa_inputs.make_custom(**next(c for c in RAGGED if c["name"] == name))
+
+
+@pytest.mark.parametrize("mode", ["rows", "keys"])
+@pytest.mark.parametrize("name", WALK1_CASES)
+def test_walk1_variants(name, mode, monkeypatch):
+    monkeypatch.setenv("FA_BACK_WALK1", mode)
+    say(f"[walk1 {mode}]")
+    _parity(_walk1_problem(name))
