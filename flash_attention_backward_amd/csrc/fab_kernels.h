@@ -567,9 +567,9 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
 // of a wave's keys are decoded once into its registers; per row block (q/dO rows DMA'd into
 // LDS, double-buffered) each wave computes S^T = K Q^T and dP^T = V dO^T and, per query row over
 // its 32 keys, the max m, l = sum exp2(s - m) and d' = sum exp2(s - m) dp (fp32) and max |dp|.
-// The 8 waves' values of a row are merged in fp64 in wave order by the last wave, one block
-// later, and written as the row's record for this 256-key tile; the merge kernel combines a
-// row's records in tile order. Rows no key of the tile sees get an empty record.
+// One block later the 8 waves' values of a row are merged (a fixed butterfly over the waves)
+// and written as the row's record for this 256-key tile; the merge kernel combines a row's
+// records in tile order. Rows no key of the tile sees get an empty record.
 constexpr int kW1Waves = 8;
 constexpr int kW1Threads = kW1Waves * kWave;
 constexpr int kW1Keys = kW1Waves * 32;
@@ -581,8 +581,8 @@ struct W1Lds {
     static constexpr int kRec = kW1Waves * 32 * 16;                      // [wave][row] {m, l, d, b}
     static constexpr int kWork = 2 * kBuf + 2 * kRec;
     static constexpr int kRaw = RawTile<D, kQTileKeys>::kBytes;
-    static constexpr int kSetup = 2 * kQTileKeys * D * 2 + 2 * kRaw;     // K, V 64-key tiles + bytes
-    static constexpr int kMaxRB = 4096;                                  // row blocks per workgroup
+    static constexpr int kSetup = 2 * kQTileKeys * D * 2 + 4 * kRaw;     // K, V 64-key tiles + [2][K, V] bytes
+    static constexpr int kMaxRB = 2048;                                  // row blocks per workgroup
     static constexpr int kTiles = kW1Keys / kQTileKeys;                  // 64-key class tiles
     static constexpr int kBytes = (kSetup > kWork ? kSetup : kWork) + kTiles * kMaxRB;
 };
@@ -617,21 +617,27 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
     {
         _Float16* sK = (_Float16*)work;
         _Float16* sV = sK + kQTileKeys * D;
-        unsigned char* rawK = work + 2 * kQTileKeys * D * 2;
-        unsigned char* rawV = rawK + L::kRaw;
+        unsigned char* raw0 = work + 2 * kQTileKeys * D * 2;          // [2][K, V] staged bytes
+        auto rawK = [&](int qt) { return raw0 + ((qt & 1) * 2 + 0) * L::kRaw; };
+        auto rawV = [&](int qt) { return raw0 + ((qt & 1) * 2 + 1) * L::kRaw; };
+        auto stage = [&](int qt) {
+            const int j0 = key0 + qt * kQTileKeys;
+            if (p.k_type == FA_BACK_Q8_0)
+                dma_raw_tile<D, kQTileKeys, kW1Threads>(p.k, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK(qt), threadIdx.x);
+            if (p.v_type == FA_BACK_Q8_0)
+                dma_raw_tile<D, kQTileKeys, kW1Threads>(p.v, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV(qt), threadIdx.x);
+        };
+        // the bytes of quarter qt+1 are on their way while quarter qt is decoded
+        stage(0);
 #pragma unroll 1
         for (int qt = 0; qt < L::kTiles; ++qt) {
             const int j0 = key0 + qt * kQTileKeys;
-            __syncthreads();
-            if (p.k_type == FA_BACK_Q8_0)
-                dma_raw_tile<D, kQTileKeys, kW1Threads>(p.k, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, threadIdx.x);
-            if (p.v_type == FA_BACK_Q8_0)
-                dma_raw_tile<D, kQTileKeys, kW1Threads>(p.v, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV, threadIdx.x);
             wait_all_mem();
-            __syncthreads();
-            decode_tile<D, kQTileKeys, kW1Threads>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, sK,
+            __syncthreads();   // bytes of qt landed; the decoded tiles of qt-1 are read
+            if (qt + 1 < L::kTiles) stage(qt + 1);
+            decode_tile<D, kQTileKeys, kW1Threads>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK(qt), sK,
                                                    threadIdx.x);
-            decode_tile<D, kQTileKeys, kW1Threads>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV, sV,
+            decode_tile<D, kQTileKeys, kW1Threads>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV(qt), sV,
                                                    threadIdx.x);
             __syncthreads();
             if (mytile == qt) {
@@ -643,6 +649,8 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
                 }
             }
         }
+        wait_all_mem();
+        __syncthreads();
         // mask classes of (row block, 64-key tile) for the workgroup's row blocks and tiles
         for (int idx = threadIdx.x; idx < L::kTiles * nloc; idx += kW1Threads) {
             const int t = idx / nloc, lr = idx - (idx / nloc) * nloc;
