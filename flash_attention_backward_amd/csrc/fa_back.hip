@@ -130,16 +130,16 @@ int validate(const fa_back_desc* d, Geometry* g) {
         g->RS1 = 1;
         g->w1_rbs = g->RB;
         if (g->w1keys) {
-            // row splits: fill whole rounds of 256 workgroups, keep >= 16 row blocks each
+            // row splits: minimise rounds of 256 workgroups x (setup + row blocks per workgroup),
+            // the setup (decoding 256 keys) counted as 8 row blocks
             const int rs_min = (g->RB + W1Lds<64>::kMaxRB - 1) / W1Lds<64>::kMaxRB;
             int best = rs_min;
-            double best_eff = -1.0;
+            double best_cost = 1e300;
             for (int rs = rs_min; rs <= 16; ++rs) {
                 const int rbs = (g->RB + rs - 1) / rs;
-                if (rs > rs_min && rbs < 16) break;
-                const double n = (double)g->KT1 * g->Hkv * rs / 256.0;
-                const double eff = n / std::ceil(n);
-                if (eff > best_eff + 1e-9) { best_eff = eff; best = rs; }
+                const double rounds = std::ceil((double)g->KT1 * g->Hkv * rs / 256.0);
+                const double cost = rounds * (8.0 + rbs);
+                if (cost < best_cost - 1e-9) { best_cost = cost; best = rs; }
             }
             g->w1_rbs = (g->RB + best - 1) / best;
             g->RS1 = (g->RB + g->w1_rbs - 1) / g->w1_rbs;

@@ -567,9 +567,9 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
 // of a wave's keys are decoded once into its registers; per row block (q/dO rows DMA'd into
 // LDS, double-buffered) each wave computes S^T = K Q^T and dP^T = V dO^T and, per query row over
 // its 32 keys, the max m, l = sum exp2(s - m) and d' = sum exp2(s - m) dp (fp32) and max |dp|.
-// One block later the 8 waves' values of a row are merged (a fixed butterfly over the waves)
-// and written as the row's record for this 256-key tile; the merge kernel combines a row's
-// records in tile order. Rows no key of the tile sees get an empty record.
+// One block later the 8 waves' values of a row are merged in wave order and written as the
+// row's record for this 256-key tile; the merge kernel combines a row's records in tile
+// order. Rows no key of the tile sees get an empty record.
 constexpr int kW1Waves = 8;
 constexpr int kW1Threads = kW1Waves * kWave;
 constexpr int kW1Keys = kW1Waves * 32;
@@ -579,7 +579,7 @@ struct W1Lds {
     static constexpr int kBlk = 32 * D * 2;                              // bytes of a 32-row block
     static constexpr int kBuf = 2 * kBlk;                                // q, dO
     static constexpr int kRec = kW1Waves * 32 * 16;                      // [wave][row] {m, l, d, b}
-    static constexpr int kWork = 2 * kBuf + 2 * kRec;
+    static constexpr int kWork = 2 * kBuf + 3 * kRec;
     static constexpr int kRaw = RawTile<D, kQTileKeys>::kBytes;
     static constexpr int kSetup = 2 * kQTileKeys * D * 2 + 4 * kRaw;     // K, V 64-key tiles + [2][K, V] bytes
     static constexpr int kMaxRB = 2048;                                  // row blocks per workgroup
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
     constexpr int NIW = (2 * NI + kW1Waves - 1) / kW1Waves;
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
     unsigned char* work = lds;
-    unsigned char* recs = work + 2 * L::kBuf;                         // [2][wave][row] x 16 B
+    unsigned char* recs = work + 2 * L::kBuf;                         // [3][wave][row] x 16 B
     unsigned char* cls = lds + L::kBytes - L::kTiles * L::kMaxRB;     // [tile][row block - rb0]
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -697,8 +697,9 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
             dma16((ten ? dbase : qbase) + blk + off, base + ten * L::kBlk + ii * 1024);
         }
     };
-    // the last wave merges the 8 records of each row of a finished block (fixed wave order)
-    auto merge_block = [&](int rbx, const unsigned char* rec) {
+    // the 8 records of a row of a finished block are merged in wave order; waves 0..3 (which
+    // finish their products first) take 8 rows each, one per lane
+    auto merge_block = [&](int rbx, const unsigned char* rec, int l32) {
         const f32x4* rr = (const f32x4*)rec;
         float mx = neg_inf(), bb = 0.0f;
 #pragma unroll
@@ -707,103 +708,140 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
             mx = fmaxf(mx, x[0]);
             bb = fmaxf(bb, x[3]);
         }
-        double ls = 0.0, ds = 0.0;
+        // eight partial sums of 32 keys each: combined in fp32 (the row's records of all key
+        // tiles are combined in fp64 by the merge kernel)
+        float ls = 0.0f, ds = 0.0f;
         if (mx != neg_inf()) {
 #pragma unroll
             for (int w = 0; w < kW1Waves; ++w) {
                 const f32x4 x = rr[w * 32 + l32];
-                if (x[0] != neg_inf()) {
-                    const double f = (double)fast_exp2(x[0] - mx);
-                    ls = fma((double)x[1], f, ls);
-                    ds = fma((double)x[2], f, ds);
-                }
+                const float f = x[0] == neg_inf() ? 0.0f : fast_exp2(x[0] - mx);   // 1 at the max
+                ls = fmaf(x[1], f, ls);
+                ds = fmaf(x[2], f, ds);
             }
         }
         const int64_t ri = rec0 + (int64_t)rbx * 32 + l32;
         p.part_m[ri] = mx;
-        p.part_l[ri] = ls;
-        p.part_d[ri] = ds;
+        p.part_l[ri] = (double)ls;
+        p.part_d[ri] = (double)ds;
         p.part_b[ri] = bb;
     };
 
     const float sc2 = fabsf(p.scale) * ldexpf(1.0f, -p.scal[0]) * kLog2e;   // q carries the sign
     const bool has_mask = p.m_type != FA_BACK_NONE;
     const RowWalk<D> rw = make_row_walk<D>(lane);
-    const int first = next_needed(rb0);
-    if (first < rb1) dma_block(first, 0);
-    int buf = 0, prev = -1;
-    for (int rb = first;;) {
-        const int rbn = rb < rb1 ? next_needed(rb + 1) : rb1;
-        wait_all_mem();
-        __syncthreads();   // block rb landed in `buf`; the records of `prev` are complete
-        if (rbn < rb1) dma_block(rbn, buf ^ 1);
-        if (prev >= 0 && wave == kW1Waves - 1 && lane < 32) merge_block(prev, recs + (buf ^ 1) * L::kRec);
-        if (rb >= rb1) break;
-        const int c = tcls(rb, mytile);
+
+    // statistics of one row block from its S^T (sa) and dP^T (pa) over this wave's 32 keys when a
+    // mask or a ragged edge is involved
+    auto stats_slow = [&](int rbx, int c, const f32x16& sa, const f32x16& pa) -> f32x4 {
         float m = neg_inf(), l = 0.0f, d = 0.0f, b = 0.0f;
-        if (c != kMaskDead) {
-            const unsigned char* tq = work + buf * L::kBuf;
+        const int r = 32 * rbx + l32;
+        const bool row_ok = r < p.R;
+        const char* mrow = nullptr;
+        if (has_mask && row_ok && c == kMaskMixed) {
+            const int i = r / p.G, gh = r - (r / p.G) * p.G;
+            mrow = p.mask + (int64_t)i * p.m_nb1 + (int64_t)(p.Hm == 1 ? 0 : hk * p.G + gh) * p.m_nb2;
+        }
+        float madd[16];
+        float tm = neg_inf();
+        const int kbase = opaque(wkey0);   // keeps per-key offsets out of the loop preheader
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int key = kbase + crow(v, g);
+            float mv = 0.0f;
+            if (!row_ok || key >= p.M) mv = neg_inf();
+            else if (mrow) mv = mask_at(mrow, p.m_type, key) * kLog2e;
+            madd[v] = mv;
+            if (mv != neg_inf()) tm = fmaxf(tm, fmaf(sa[v], sc2, mv));
+        }
+        m = fmaxf(tm, __shfl_xor(tm, 32));
+        if (m != neg_inf()) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                if (madd[v] == neg_inf()) continue;
+                const float e = fast_exp2(fmaf(sa[v], sc2, madd[v] - m));
+                l += e;
+                d = fmaf(e, pa[v], d);
+                b = fmaxf(b, fabsf(pa[v]));
+            }
+        }
+        l += __shfl_xor(l, 32);
+        d += __shfl_xor(d, 32);
+        b = fmaxf(b, __shfl_xor(b, 32));
+        return f32x4{m, l, d, b};
+    };
+    auto fast_ok = [&](int rbx, int c) { return c == kMaskZero && wkey0 + 32 <= p.M && (rbx + 1) * 32 <= p.R; };
+
+    // the same statistics without products to overlap (last block, or the next one is dead)
+    auto stats_fast = [&](const f32x16& sa, const f32x16& pa) -> f32x4 {
+        float tm = neg_inf(), l = 0.0f, d = 0.0f, b = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tm = fmaxf(tm, sa[v]);
+        const float m = fmaxf(tm, __shfl_xor(tm, 32)) * sc2;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float e = fast_exp2(fmaf(sa[v], sc2, -m));
+            l += e;
+            d = fmaf(e, pa[v], d);
+            b = fmaxf(b, fabsf(pa[v]));
+        }
+        l += __shfl_xor(l, 32);
+        d += __shfl_xor(d, 32);
+        b = fmaxf(b, __shfl_xor(b, 32));
+        return f32x4{m, l, d, b};
+    };
+    auto put_rec = [&](int bufx, const f32x4& rec) {
+        if (g == 0) *(f32x4*)(recs + bufx * L::kRec + (wave * 32 + l32) * 16) = rec;
+    };
+    auto nextv = [&](int rbx) -> int {
+        const int x = next_needed(rbx + 1);
+        return x < rb1 ? x : -1;
+    };
+    auto stats = [&](int rbx, int c, const f32x16& sa, const f32x16& pa) -> f32x4 {
+        if (c == kMaskDead) return f32x4{neg_inf(), 0.0f, 0.0f, 0.0f};
+        return fast_ok(rbx, c) ? stats_fast(sa, pa) : stats_slow(rbx, c, sa, pa);
+    };
+
+    // Iteration i takes the needed blocks c0 = b_i and cp = b_(i-1). On each SIMD the two waves
+    // run half an iteration apart: a late wave (4..7) forms the products of c0 and then their
+    // statistics; an early wave (0..3) first forms the statistics of cp from the products it
+    // kept in registers (and merges the records of b_(i-2)), then the products of c0. So one
+    // wave's exponentials overlap the other's matrix products. The DMA of b_(i+1) goes into the
+    // buffer of cp, which no wave reads any more; the records of block b sit in buffer b%3.
+    const bool early = wave < kW1Waves / 2;
+    int c0 = next_needed(rb0);
+    c0 = c0 < rb1 ? c0 : -1;
+    if (c0 >= 0) dma_block(c0, 0);
+    int cp = -1, cpp = -1;
+    f32x16 ha, hp;   // early waves: products of cp
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ha[v] = hp[v] = 0.0f;
+    for (int i = 0;; ++i) {
+        const int c1 = c0 >= 0 ? nextv(c0) : -1;
+        wait_all_mem();
+        __syncthreads();   // c0 landed; the records of cpp are complete
+        if (c1 >= 0) dma_block(c1, (i + 1) & 1);
+        if (early) {
+            if (cp >= 0) put_rec((i + 2) % 3, stats(cp, tcls(cp, mytile), ha, hp));
+            if (cpp >= 0 && lane < 8) merge_block(cpp, recs + ((i + 1) % 3) * L::kRec, 8 * wave + lane);
+        }
+        if (c0 < 0 && cp < 0) break;
+        if (c0 >= 0) {
+            const int c = tcls(c0, mytile);
             f32x16 sa, pa;
 #pragma unroll
             for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
-            pair_rows_t<D, 2, L::kBlk>(tq, bk, bv, sa, pa, rw);
-            const int r = 32 * rb + l32;
-            if (c == kMaskZero && wkey0 + 32 <= p.M && (rb + 1) * 32 <= p.R) {
-                // every entry visible; the scale is positive, so max(s) = sc2 * max(sa)
-                float tm = sa[0];
-#pragma unroll
-                for (int v = 1; v < 16; ++v) tm = fmaxf(tm, sa[v]);
-                m = fmaxf(tm, __shfl_xor(tm, 32)) * sc2;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const float e = fast_exp2(fmaf(sa[v], sc2, -m));
-                    l += e;
-                    d = fmaf(e, pa[v], d);
-                    b = fmaxf(b, fabsf(pa[v]));
-                }
+            if (c != kMaskDead) pair_rows_t<D, 2, L::kBlk>(work + (i & 1) * L::kBuf, bk, bv, sa, pa, rw);
+            if (early) {
+                ha = sa;
+                hp = pa;
             } else {
-                // masked or ragged: same arithmetic as above for visible mask-0 entries
-                const bool row_ok = r < p.R;
-                const char* mrow = nullptr;
-                if (has_mask && row_ok && c == kMaskMixed) {
-                    const int i = r / p.G, gh = r - (r / p.G) * p.G;
-                    mrow = p.mask + (int64_t)i * p.m_nb1 + (int64_t)(p.Hm == 1 ? 0 : hk * p.G + gh) * p.m_nb2;
-                }
-                float madd[16];
-                float tm = neg_inf();
-                const int kbase = opaque(wkey0);   // keeps per-key offsets out of the loop preheader
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int key = kbase + crow(v, g);
-                    float mv = 0.0f;
-                    if (!row_ok || key >= p.M) mv = neg_inf();
-                    else if (mrow) mv = mask_at(mrow, p.m_type, key) * kLog2e;
-                    madd[v] = mv;
-                    if (mv != neg_inf()) tm = fmaxf(tm, fmaf(sa[v], sc2, mv));
-                }
-                m = fmaxf(tm, __shfl_xor(tm, 32));
-                if (m != neg_inf()) {
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        if (madd[v] == neg_inf()) continue;
-                        const float e = fast_exp2(fmaf(sa[v], sc2, madd[v] - m));
-                        l += e;
-                        d = fmaf(e, pa[v], d);
-                        b = fmaxf(b, fabsf(pa[v]));
-                    }
-                }
+                put_rec(i % 3, stats(c0, c, sa, pa));
             }
-            l += __shfl_xor(l, 32);
-            d += __shfl_xor(d, 32);
-            b = fmaxf(b, __shfl_xor(b, 32));
         }
-        if (g == 0) {
-            const f32x4 rec = {m, l, d, b};
-            *(f32x4*)(recs + buf * L::kRec + (wave * 32 + l32) * 16) = rec;
-        }
-        prev = rb;
-        rb = rbn;
-        buf ^= 1;
+        cpp = cp;
+        cp = c0;
+        c0 = c1;
     }
 }
 
