@@ -305,6 +305,9 @@ struct QLds {
 template <int D, bool GRAD>
 __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     using L = QLds<D>;
+    // with 8 q8_0 wave-instructions per sub-tile (D = 256) the S waves decode the V half, one
+    // wave-instruction each, after their products; the K waves decode the K half
+    constexpr bool kSplitDecode = Q8Pair<D>::U == 8;
     constexpr int KS = D / 16;     // 16-deep steps of a contraction over d
     constexpr int MD = D / 32;     // 32-wide d blocks of dQ
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
@@ -373,8 +376,18 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         const bool dead = (lse2 == neg_inf());
         const RowWalk<D> rw = make_row_walk<D>(lane);
 
-        // prologue: the K waves stage and decode sub-tile s_begin
+        const bool sdec = kSplitDecode && p.k_type == FA_BACK_Q8_0 && p.v_type == FA_BACK_Q8_0;
+        const char* kh = p.k + (int64_t)hk * p.k_nb2;
+        const char* vh = p.v + (int64_t)hk * p.v_nb2;
+        // the V half of sub-tile t, staged by the K waves
+        auto sdecode = [&](int t) {
+            decode_q8_pair32<D>(kh, p.k_nb1, vh, p.v_nb1, t * kSubKeys, p.M, rawK(t), rawV(t),
+                                (_Float16*)slot(t), (_Float16*)(slot(t) + L::kTile),
+                                Q8Pair<D>::UPT + w4, Q8Pair<D>::U, lane);
+        };
+        // prologue: the K waves stage sub-tile s_begin and decode its K half
         __syncthreads();
+        if (sdec && s_begin < s_end) sdecode(s_begin);
         int cls_next = s_begin < s_end ? wclass(s_begin) : kMaskDead;
         for (int s = s_begin; s <= s_end; ++s) {
             wait_all_mem();
@@ -382,7 +395,10 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
             if (s == s_end) break;
             const int cls = cls_next;
             cls_next = s + 1 < s_end ? wclass(s + 1) : kMaskDead;   // in flight during sub-tile s
-            if (cls == kMaskDead) continue;
+            if (cls == kMaskDead) {
+                if (sdec && s + 1 < s_end) sdecode(s + 1);
+                continue;
+            }
             f32x16 sa, pa;
 #pragma unroll
             for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
@@ -469,6 +485,7 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
                 *(f16x8*)(ex + lane * 16) = bs[0];
                 *(f16x8*)(ex + 1024 + lane * 16) = bs[1];
             }
+            if (sdec && s + 1 < s_end) sdecode(s + 1);
         }
         if (!GRAD && active) {
             const double lo = l64 + __shfl_xor(l64, 32);
@@ -502,7 +519,8 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         _Float16* tk = (_Float16*)slot(s);
         _Float16* tv = (_Float16*)(slot(s) + L::kTile);
         if (pairq8) {
-            decode_q8_pair32<D>(kh, p.k_nb1, vh, p.v_nb1, s * kSubKeys, p.M, rawK(s), rawV(s), tk, tv, kw, lane);
+            decode_q8_pair32<D>(kh, p.k_nb1, vh, p.v_nb1, s * kSubKeys, p.M, rawK(s), rawV(s), tk, tv, kw,
+                                kSplitDecode ? Q8Pair<D>::UPT : Q8Pair<D>::U, lane);
         } else {
             decode_tile<D, kSubKeys, 256>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, s * kSubKeys, p.M, rawK(s), tk, ktid);
             decode_tile<D, kSubKeys, 256>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), tv, ktid);

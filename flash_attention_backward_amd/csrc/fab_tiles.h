@@ -178,9 +178,10 @@ FAB_DEV f16x8 decode8(const char* rowp, int type, int grp, const unsigned char*,
 }
 
 // One 32-value q8_0 block of a staged row decoded to fp16: out[c] holds values 8c .. 8c+7.
-// All LDS reads are issued before any arithmetic. Each value is formed as
-// fma(byte ^ 0x80, d, -128 d) = d * q, exact in fp32, then rounded to fp16 (nearest even),
-// the same fp16 an F32 cache holding d * q gives.
+// All LDS reads are issued before any arithmetic. A byte u = q + 128 placed under the fp16
+// exponent pattern 0x64 reads as 1024 + u; subtracting 1152 gives q exactly, and one fp16
+// product with the scale rounds q * d once (nearest even), which is the fp16 an F32 cache
+// holding d * q gives. Both steps run on packed fp16 pairs.
 FAB_DEV void decode_q8_block(const unsigned char* slot, int off, int blk, f16x8 out[4]) {
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     const int base = off + 34 * blk;                  // fp16 scale (even offset)
@@ -191,21 +192,22 @@ FAB_DEV void decode_q8_block(const unsigned char* slot, int off, int blk, f16x8 
 #pragma unroll
     for (int k = 0; k < 9; ++k) w[k] = wp[k];
     const unsigned short sb = *(const unsigned short*)(slot + base);
-    const float d = (float)__builtin_bit_cast(_Float16, sb);
-    const float c = -1152.0f * d;                     // exact: 9 * 2^7 * d needs 15 bits
+    const _Float16 dh = __builtin_bit_cast(_Float16, sb);
+    const h2 d2 = {dh, dh};
+    const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        // bytes u = q + 128; fp16 with bit pattern 0x64uu is exactly 1024 + u, so
-        // (1024 + u) * d - 1152 * d = q * d is formed exactly in fp32 and rounded once to fp16
         const unsigned int x = __builtin_amdgcn_alignbyte(w[k + 1], w[k], sh) ^ 0x80808080u;
         const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u));
         const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u));
+        const h2 a = (lo + bias) * d2;
+        const h2 c = (hi + bias) * d2;
         f16x8& o = out[k >> 1];
         const int b = 4 * (k & 1);
-        o[b + 0] = (_Float16)fmaf((float)lo.x, d, c);
-        o[b + 1] = (_Float16)fmaf((float)lo.y, d, c);
-        o[b + 2] = (_Float16)fmaf((float)hi.x, d, c);
-        o[b + 3] = (_Float16)fmaf((float)hi.y, d, c);
+        o[b + 0] = a.x;
+        o[b + 1] = a.y;
+        o[b + 2] = c.x;
+        o[b + 3] = c.y;
     }
 }
 
@@ -268,40 +270,52 @@ FAB_DEV void decode_tile(const char* base, int type, int64_t nb1, int64_t nb2, i
 FAB_DEV int perm16(int t) { return (t & 1) | ((t & 6) << 1) | ((t & 8) >> 2); }
 
 template <int D>
+struct Q8Pair {
+    static constexpr int BPR = D / 32;                // blocks per row
+    static constexpr int BL = BPR >= 4 ? 4 : BPR;     // blocks per wave-instruction
+    static constexpr int KL = 64 / BL;                // keys per wave-instruction
+    static constexpr int KG = KL / 16;
+    static constexpr int UPT = BPR / 2;               // wave-instructions per tensor
+    static constexpr int U = 2 * UPT;                 // wave-instructions per sub-tile pair
+};
+
+// Wave-instruction u (0 .. U-1; K first, then V) of the pair decode.
+template <int D>
+FAB_DEV void decode_q8_item(const char* kh, int64_t knb1, const char* vh, int64_t vnb1, int j0, int M,
+                            const unsigned char* rawk, const unsigned char* rawv, _Float16* dstk,
+                            _Float16* dstv, int u, int lane) {
+    using Q = Q8Pair<D>;
+    const bool isv = u >= Q::UPT;
+    const int uu = isv ? u - Q::UPT : u;
+    const int key = perm16(lane & 15) + 16 * ((lane >> 4) % Q::KG) + Q::KL * (uu % (32 / Q::KL));
+    const int blk = (lane >> 4) / Q::KG + Q::BL * (uu / (32 / Q::KL));
+    const int j = j0 + key;
+    f16x8 o[4];
+    if (j < M) {
+        const char* h = isv ? vh : kh;
+        const int64_t nb1 = isv ? vnb1 : knb1;
+        const int off = (int)(((uint32_t)(uintptr_t)h + (uint32_t)j * (uint32_t)nb1) & 15u);
+        decode_q8_block((isv ? rawv : rawk) + key * Q8Row<D>::kSlot, off, blk, o);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) o[c][t] = (_Float16)0.0f;
+    }
+    _Float16* dst = isv ? dstv : dstk;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) *(f16x8*)(dst + tile_off<D>(key, 4 * blk + c)) = o[c];
+}
+
+// The wave-instructions u = first, first + 4, ... below `last` for one of 4 waves.
+template <int D>
 FAB_DEV void decode_q8_pair32(const char* kh, int64_t knb1, const char* vh, int64_t vnb1, int j0, int M,
                               const unsigned char* rawk, const unsigned char* rawv, _Float16* dstk,
-                              _Float16* dstv, int wave, int lane) {
-    constexpr int BPR = D / 32;                       // blocks per row
-    constexpr int BL = BPR >= 4 ? 4 : BPR;            // blocks per wave-instruction
-    constexpr int KL = 64 / BL;                       // keys per wave-instruction
-    constexpr int KG = KL / 16;
-    constexpr int UPT = BPR / 2;                      // wave-instructions per tensor
-    const int klo = perm16(lane & 15) + 16 * ((lane >> 4) % KG);
-    const int blo = (lane >> 4) / KG;
+                              _Float16* dstv, int first, int last, int lane) {
 #pragma unroll
-    for (int u0 = 0; u0 < 2 * UPT; u0 += 4) {
-        const int u = u0 + wave;                      // wave-uniform
-        if (u >= 2 * UPT) break;
-        const bool isv = u >= UPT;
-        const int uu = isv ? u - UPT : u;
-        const int key = klo + KL * (uu % (32 / KL));
-        const int blk = blo + BL * (uu / (32 / KL));
-        const int j = j0 + key;
-        f16x8 o[4];
-        if (j < M) {
-            const char* h = isv ? vh : kh;
-            const int64_t nb1 = isv ? vnb1 : knb1;
-            const int off = (int)(((uint32_t)(uintptr_t)h + (uint32_t)j * (uint32_t)nb1) & 15u);
-            decode_q8_block((isv ? rawv : rawk) + key * Q8Row<D>::kSlot, off, blk, o);
-        } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-                for (int t = 0; t < 8; ++t) o[c][t] = (_Float16)0.0f;
-        }
-        _Float16* dst = isv ? dstv : dstk;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) *(f16x8*)(dst + tile_off<D>(key, 4 * blk + c)) = o[c];
+    for (int u = first; u < Q8Pair<D>::U; u += 4) {
+        if (u >= last) break;                          // wave-uniform
+        decode_q8_item<D>(kh, knb1, vh, vnb1, j0, M, rawk, rawv, dstk, dstv, u, lane);
     }
 }
 
