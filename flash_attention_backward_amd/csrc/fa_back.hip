@@ -91,6 +91,7 @@ int validate(const fa_back_desc* d, Geometry* g) {
     if ((rc = check_strides(k, k.type != FA_BACK_Q8_0)) || (rc = check_strides(v, v.type != FA_BACK_Q8_0)))
         return rc;
     if (has_mask && (rc = check_strides(m, false))) return rc;
+    if (k.nb[1] >= ((int64_t)1 << 32) || v.nb[1] >= ((int64_t)1 << 32)) return FA_BACK_EUNSUPPORTED;
     // supported sizes
     if (D != Dv || (D != 64 && D != 128 && D != 256)) return FA_BACK_EUNSUPPORTED;
     const int64_t G = H / Hkv;

@@ -299,7 +299,8 @@ struct QLds {
     static constexpr int kOffSlot = 0;                             // 3 slots
     static constexpr int kOffRaw = kOffSlot + 3 * kSlot;           // [2][K, V] staged bytes
     static constexpr int kOffEx = kOffRaw + 4 * kRaw;              // [2][4 row blocks] dS, 2 KB
-    static constexpr int kBytes = kOffEx + 2 * 4 * 2048;
+    static constexpr int kOffCls = kOffEx + 2 * 4 * 2048;          // [2][4 row blocks] mask class
+    static constexpr int kBytes = kOffCls + 16;
 };
 
 template <int D, bool GRAD>
@@ -336,6 +337,9 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     auto rawV = [&](int s) { return lds + L::kOffRaw + ((s & 1) * 2 + 1) * L::kRaw; };
     auto exch = [&](int s) { return lds + L::kOffEx + ((s & 1) * 4 + w4) * 2048; };
     auto wclass = [&](int s) { return active ? mask_class(p, hk, rb, s >> 1) : kMaskDead; };
+    // the class of sub-tile s for row block w4, passed from the K waves (which load it from
+    // HBM one sub-tile ahead) to the S waves
+    unsigned char* clsx = lds + L::kOffCls;
 
     if (role == 0) {
         // ================= S waves
@@ -385,16 +389,29 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
                                 (_Float16*)slot(t), (_Float16*)(slot(t) + L::kTile),
                                 Q8Pair<D>::UPT + w4, Q8Pair<D>::U, lane);
         };
-        // prologue: the K waves stage sub-tile s_begin and decode its K half
+        // q8_0 bytes are staged by these waves: the LDS reads that follow the DMA here are
+        // plain loads, which the compiler does not hold back for the DMA in flight (it makes
+        // transpose reads wait for it)
+        RawDma<D, kSubKeys, 256> dk, dv;
+        dk.init(kh, p.k_nb1, s_begin * kSubKeys, w4 * 64 + lane);
+        dv.init(vh, p.v_nb1, s_begin * kSubKeys, w4 * 64 + lane);
+        auto sdma = [&](int t) {
+            if (p.k_type == FA_BACK_Q8_0) dk.issue(rawK(t), p.M, w4);
+            if (p.v_type == FA_BACK_Q8_0) dv.issue(rawV(t), p.M, w4);
+        };
+        // prologue: sub-tile s_begin staged and decoded (V half here, K half by the K waves),
+        // the bytes of s_begin+1 on their way
+        if (s_begin < s_end) sdma(s_begin);
+        wait_all_mem();
         __syncthreads();
+        if (s_begin + 1 < s_end) sdma(s_begin + 1);
         if (sdec && s_begin < s_end) sdecode(s_begin);
-        int cls_next = s_begin < s_end ? wclass(s_begin) : kMaskDead;
         for (int s = s_begin; s <= s_end; ++s) {
             wait_all_mem();
-            __syncthreads();   // sub-tile s decoded; exchange slot s free
+            __syncthreads();   // sub-tile s decoded and its class posted; exchange slot s free
             if (s == s_end) break;
-            const int cls = cls_next;
-            cls_next = s + 1 < s_end ? wclass(s + 1) : kMaskDead;   // in flight during sub-tile s
+            if (s + 2 < s_end) sdma(s + 2);
+            const int cls = __builtin_amdgcn_readfirstlane(clsx[(s & 1) * 4 + w4]);
             if (cls == kMaskDead) {
                 if (sdec && s + 1 < s_end) sdecode(s + 1);
                 continue;
@@ -508,13 +525,6 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     const char* kh = p.k + (int64_t)hk * p.k_nb2;
     const char* vh = p.v + (int64_t)hk * p.v_nb2;
     const bool pairq8 = p.k_type == FA_BACK_Q8_0 && p.v_type == FA_BACK_Q8_0;
-    RawDma<D, kSubKeys, 256> dk, dv;
-    dk.init(kh, p.k_nb1, s_begin * kSubKeys, ktid);
-    dv.init(vh, p.v_nb1, s_begin * kSubKeys, ktid);
-    auto kdma = [&](int s) {
-        if (p.k_type == FA_BACK_Q8_0) dk.issue(rawK(s), p.M, kw, lane);
-        if (p.v_type == FA_BACK_Q8_0) dv.issue(rawV(s), p.M, kw, lane);
-    };
     auto kdecode = [&](int s) {
         _Float16* tk = (_Float16*)slot(s);
         _Float16* tv = (_Float16*)(slot(s) + L::kTile);
@@ -524,16 +534,16 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         } else {
             decode_tile<D, kSubKeys, 256>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, s * kSubKeys, p.M, rawK(s), tk, ktid);
             decode_tile<D, kSubKeys, 256>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), tv, ktid);
+            // nothing of this path stays in flight: where the two paths join, the compiler
+            // would otherwise make the q8_0 path wait for its loads, and with them the DMA
+            wait_all_mem();
         }
     };
-    // prologue: sub-tile s_begin decoded, the bytes of s_begin+1 on their way
-    if (s_begin < s_end) kdma(s_begin);
-    wait_all_mem();
+    // prologue: the S waves stage sub-tile s_begin; its class is posted
+    int cls_cur = s_begin < s_end ? wclass(s_begin) : kMaskDead;    // class of sub-tile s
+    if (lane == 0) clsx[(s_begin & 1) * 4 + kw] = (unsigned char)cls_cur;
     __syncthreads();
-    if (s_begin < s_end) {
-        if (s_begin + 1 < s_end) kdma(s_begin + 1);
-        kdecode(s_begin);
-    }
+    if (s_begin < s_end) kdecode(s_begin);
 
     f32x16 dqacc[GRAD ? MD : 1];
     if (GRAD) {
@@ -543,15 +553,16 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
             for (int v = 0; v < 16; ++v) dqacc[md][v] = 0.0f;
     }
     const ColWalk<D> cw = make_col_walk<D>(lane);
-    int cls_cur = s_begin < s_end ? wclass(s_begin) : kMaskDead;   // class of sub-tile s
     int cls_last = kMaskDead;                                        // class of sub-tile s-1
+    int cls_nx = s_begin + 1 < s_end ? wclass(s_begin + 1) : kMaskDead;   // s+1, in flight
     for (int s = s_begin; s <= s_end; ++s) {
         wait_all_mem();
         __syncthreads();   // sub-tile s decoded and dS of s-1 exchanged
         const int cls_prev = cls_last;
         cls_last = cls_cur;
-        cls_cur = s + 1 < s_end ? wclass(s + 1) : kMaskDead;        // in flight during sub-tile s
-        if (s + 2 < s_end) kdma(s + 2);
+        cls_cur = cls_nx;                                            // class of sub-tile s+1
+        if (lane == 0 && s + 1 < s_end) clsx[((s + 1) & 1) * 4 + kw] = (unsigned char)cls_cur;
+        cls_nx = s + 2 < s_end ? wclass(s + 2) : kMaskDead;          // in flight during sub-tile s
         if (GRAD && s > s_begin && cls_prev != kMaskDead) {
             const unsigned char* ex = exch(s - 1);
             const f16x8 bb[2] = {*(const f16x8*)(ex + lane * 16), *(const f16x8*)(ex + 1024 + lane * 16)};

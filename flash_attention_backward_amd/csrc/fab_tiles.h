@@ -320,44 +320,68 @@ FAB_DEV void decode_q8_pair32(const char* kh, int64_t knb1, const char* vh, int6
 }
 
 // DMA of consecutive q8_0 sub-tiles (KEYS keys each, sub-tile after sub-tile) into a staging
-// buffer by NT threads. The per-lane row pointers are kept and advanced by KEYS rows per call,
-// so each call costs a few adds and compares per 16-byte chunk.
+// buffer by NT threads; the row stride must be below 2^32. When the stride is a multiple of 16
+// every row has the same alignment, so a chunk's source address only advances by KEYS rows from
+// one sub-tile to the next and whether it holds bytes of its row never changes: a lane keeps the
+// address of each chunk it moves and a sub-tile that lies inside [0, M) costs one 64-bit add per
+// chunk. Otherwise (and for the last sub-tile) the address is formed from the key and the
+// chunk's offset inside the aligned-down row.
 template <int D, int KEYS, int NT>
 struct RawDma {
     using R = Q8Row<D>;
     static constexpr int NCH = KEYS * R::kChunks;
     static constexpr int IT = (NCH + NT - 1) / NT;
-    const char* row[IT];   // start of the row this lane's chunk `it` belongs to
-    int j[IT];             // its key index
-    int c16[IT];           // byte offset of the chunk inside the aligned row
-    bool live[IT];         // the chunk index lies inside the sub-tile
-    int64_t step;          // KEYS rows
+    const char* base;      // the head's key 0 (wave-uniform)
+    uint32_t nb1;          // row stride in bytes
+    int j0;                // first key of the next sub-tile (wave-uniform)
+    bool fixed;            // nb1 % 16 == 0 (wave-uniform)
+    int kc[IT];            // key | (chunk byte offset << 8); -1 past the last chunk
+    uint64_t src[IT];      // source of chunk `it` of the next sub-tile (fixed strides)
+    bool on[IT];           // chunk `it` holds bytes of its row (fixed strides)
 
-    FAB_DEV void init(const char* hbase, int64_t nb1, int j0, int tid) {
-        step = (int64_t)KEYS * nb1;
+    FAB_DEV void init(const char* hbase, int64_t row_stride, int first_key, int tid) {
+        base = hbase;
+        nb1 = (uint32_t)row_stride;
+        j0 = first_key;
+        fixed = (nb1 & 15u) == 0;
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             const int idx = it * NT + tid;
             const int key = idx / R::kChunks;
-            live[it] = idx < NCH;
-            j[it] = j0 + key;
-            c16[it] = 16 * (idx - key * R::kChunks);
-            row[it] = hbase + (int64_t)(j0 + key) * nb1;
+            kc[it] = idx < NCH ? key | ((16 * (idx - key * R::kChunks)) << 8) : -1;
+            const int c16 = kc[it] >> 8;
+            const uint64_t a = (uint64_t)(uintptr_t)base + (uint64_t)(uint32_t)(j0 + key) * nb1;
+            src[it] = (a & ~(uint64_t)15) + (uint32_t)c16;
+            on[it] = kc[it] >= 0 && (uint32_t)c16 < (uint32_t)(a & 15) + (uint32_t)R::kBytes;
         }
     }
     // wave: this thread's wave among the NT threads (uniform); raw: staging buffer
-    FAB_DEV void issue(unsigned char* raw, int M, int wave, int lane) {
+    FAB_DEV void issue(unsigned char* raw, int M, int wave) {
+        const uint64_t step = (uint64_t)KEYS * nb1;
+        if (fixed && j0 + KEYS <= M) {
 #pragma unroll
-        for (int it = 0; it < IT; ++it) {
-            const int wbase = it * NT + wave * 64;    // first chunk of this wave's instruction
-            if (wbase >= NCH) break;                   // wave-uniform
-            const uintptr_t a = (uintptr_t)row[it];
-            const uintptr_t src = (a & ~(uintptr_t)15) + (uintptr_t)c16[it];
-            if (live[it] && j[it] < M && src < a + R::kBytes) dma16((const void*)src, raw + 16 * wbase);
-            row[it] += step;
-            j[it] += KEYS;
+            for (int it = 0; it < IT; ++it) {
+                const int wbase = it * NT + wave * 64;
+                if (wbase >= NCH) break;               // wave-uniform
+                if (on[it]) dma16((const void*)(uintptr_t)src[it], raw + 16 * wbase);
+                src[it] += step;
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const int wbase = it * NT + wave * 64;
+                if (wbase >= NCH) break;               // wave-uniform
+                const int key = kc[it] & 255, c16 = kc[it] >> 8;
+                const int j = j0 + key;
+                const uint64_t a = (uint64_t)(uintptr_t)base + (uint64_t)(uint32_t)j * nb1;
+                const uint64_t sa = (a & ~(uint64_t)15) + (uint32_t)c16;
+                // only chunks holding bytes of this row
+                if (kc[it] >= 0 && j < M && (uint32_t)c16 < (uint32_t)(a & 15) + (uint32_t)R::kBytes)
+                    dma16((const void*)(uintptr_t)sa, raw + 16 * wbase);
+                src[it] += step;
+            }
         }
-        (void)lane;
+        j0 += KEYS;
     }
 };
 

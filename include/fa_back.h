@@ -49,7 +49,7 @@
  *
  * Supported: D == Dv in {64, 128, 256}; H % Hkv == 0; N, M >= 0 (N == 0: dK = dV = 0;
  * M == 0: every row is fully masked); F32/F16/BF16 K or V rows 16-byte aligned (base and
- * strides); Q8_0 rows 2-byte aligned.
+ * strides); Q8_0 rows 2-byte aligned; K and V row strides (nb[1]) below 2^32 bytes.
  */
 #ifndef FA_BACK_H
 #define FA_BACK_H
