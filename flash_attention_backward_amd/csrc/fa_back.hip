@@ -33,6 +33,7 @@ int64_t elem_size(int type) {
 struct Geometry {
     int D, Dv, H, Hkv, G, N, M, Hm;
     int R, RB, RT, KT, splits, tiles_per_split, KVT;
+    int kv_full, kv_tail, kv_split;   // key side: unsplit tiles, split tiles, parts per split tile
     bool w1keys;           // walk 1 by key tiles (else by row tiles)
     int KT1, RS1, w1_rbs;  // its 256-key tiles, row splits and row blocks per workgroup
     int nparts;            // walk-1 records per row
@@ -40,7 +41,7 @@ struct Geometry {
     fa_back_layout layout;
     // workspace offsets (bytes)
     uint64_t ws_absmax, ws_scal, ws_qr, ws_dr;
-    uint64_t ws_pm, ws_pl, ws_pd, ws_pb, ws_lse2, ws_dlt, ws_bound, ws_dqp, ws_mcls;
+    uint64_t ws_pm, ws_pl, ws_pd, ws_pb, ws_lse2, ws_dlt, ws_bound, ws_dqp, ws_mcls, ws_kvp;
 };
 
 bool tensor_nonneg(const fa_back_tensor& t) {
@@ -105,6 +106,15 @@ int validate(const fa_back_desc* d, Geometry* g) {
     g->RT = (g->RB + kWaves - 1) / kWaves;
     g->KT = (g->M + kQTileKeys - 1) / kQTileKeys;
     g->KVT = (g->M + kKVKeys - 1) / kKVKeys;
+    // key side: one workgroup per CU at a time (LDS), so the tiles past the last full round of
+    // kCUs workgroups would run nearly alone; each of them is split into up to 4 row ranges
+    {
+        const int T = g->KVT * (int)Hkv;
+        const int tail = T > kCUs ? T % kCUs : 0;
+        g->kv_tail = (tail > 0 && tail <= kCUs / 2) ? tail : 0;
+        g->kv_split = g->kv_tail ? std::min(4, kCUs / g->kv_tail) : 1;
+        g->kv_full = T - g->kv_tail;
+    }
     // key-range splits of the query-side passes: aim for >= 512 workgroups (two per CU on
     // 256 CUs) but keep >= 4 key tiles per split so the dQ partials stay small
     {
@@ -131,14 +141,14 @@ int validate(const fa_back_desc* d, Geometry* g) {
         g->RS1 = 1;
         g->w1_rbs = g->RB;
         if (g->w1keys) {
-            // row splits: minimise rounds of 256 workgroups x (setup + row blocks per workgroup),
+            // row splits: minimise rounds of kCUs workgroups x (setup + row blocks per workgroup),
             // the setup (decoding 256 keys) counted as 8 row blocks
             const int rs_min = (g->RB + W1Lds<64>::kMaxRB - 1) / W1Lds<64>::kMaxRB;
             int best = rs_min;
             double best_cost = 1e300;
             for (int rs = rs_min; rs <= 16; ++rs) {
                 const int rbs = (g->RB + rs - 1) / rs;
-                const double rounds = std::ceil((double)g->KT1 * g->Hkv * rs / 256.0);
+                const double rounds = std::ceil((double)g->KT1 * g->Hkv * rs / (double)kCUs);
                 const double cost = rounds * (8.0 + rbs);
                 if (cost < best_cost - 1e-9) { best_cost = cost; best = rs; }
             }
@@ -177,6 +187,7 @@ int validate(const fa_back_desc* d, Geometry* g) {
     g->ws_bound = take(4ull * g->nbound);
     g->ws_dqp = take(g->splits > 1 ? 4ull * g->splits * total_rows * D : 0);
     g->ws_mcls = take(has_mask ? (uint64_t)(Hm == 1 ? 1 : g->Hkv) * g->RB * g->KT : 0);
+    g->ws_kvp = take(4ull * g->kv_tail * g->kv_split * 2 * kKVKeys * D);
     L.workspace_bytes = std::max<uint64_t>(o, kAlign);
     return FA_BACK_OK;
 }
@@ -229,7 +240,12 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
         hipLaunchKernelGGL(dqreduce_kernel<D>, dim3(blocks), dim3(kThreads), 0, st, P);
     }
     pm.mark(5);
-    hipLaunchKernelGGL(kvpass_kernel<D>, dim3(g.KVT * g.Hkv), dim3(kKVThreads), 0, st, P);
+    hipLaunchKernelGGL(kvpass_kernel<D>, dim3(g.kv_full + g.kv_tail * g.kv_split), dim3(kKVThreads), 0, st, P);
+    if (g.kv_tail) {
+        const int64_t n4 = (int64_t)g.kv_tail * 2 * kKVKeys * (D / 4);
+        const int blocks = (int)std::min<int64_t>(2048, (n4 + kThreads - 1) / kThreads);
+        hipLaunchKernelGGL(kvreduce_kernel<D>, dim3(blocks), dim3(kThreads), 0, st, P, g.kv_tail);
+    }
     pm.mark(6);
     return hipGetLastError() == hipSuccess ? FA_BACK_OK : FA_BACK_EHIP;
 }
@@ -351,6 +367,9 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     P.nbound = g.nbound;
     P.dq_part = (float*)(w + g.ws_dqp);
     P.mcls = (unsigned char*)(w + g.ws_mcls);
+    P.kv_full = g.kv_full;
+    P.kv_split = g.kv_split;
+    P.kv_part = (float*)(w + g.ws_kvp);
 
     hipStream_t st = (hipStream_t)stream;
     hipEvent_t ev[FA_BACK_NUM_PHASES + 1];

@@ -22,6 +22,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kRowBlock = 32;     // rows per MFMA block (the 32 of a 32x32x16 product)
 constexpr int kQTileKeys = 64;    // keys per tile in the query-side passes
+constexpr int kCUs = 256;         // compute units of an MI355X (workgroup rounds)
 constexpr int kKVKeys = 128;      // keys owned by one key-side workgroup (32 per wave)
 constexpr int kPScaleLog2 = 15;   // P is rounded to fp16 as p * 2^15 (p <= 1)
 constexpr int kNegInfBits = 0xff800000;
@@ -72,6 +73,10 @@ struct Params {
     int nbound;
     float* dq_part;       // [splits][Hkv*RB*32][D] when splits > 1
     unsigned char* mcls;  // [Hc][RB][KT] mask class of (row block, 64-key tile); Hc = Hm==1 ? 1 : Hkv
+    // key side: workgroups 0 .. kv_full-1 own one 128-key tile (tile = workgroup); each of the
+    // remaining tiles is split into kv_split row ranges whose dK/dV go to kv_part
+    int kv_full, kv_split;
+    float* kv_part;       // [tail tile][part][dK, dV][128 keys][D]
 };
 
 // Mask classes of a (32-row block, 64-key tile): no masking needed, every entry -inf, other.

@@ -1023,8 +1023,16 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l32 = lane & 31, g = lane >> 5;
     const int role = wave >> 2, kb = wave & 3;        // role 0: A (S, dK), role 1: B (dP, dV)
-    const int hk = blockIdx.x % p.Hkv;
-    const int kvt = blockIdx.x / p.Hkv;
+    // tile and row range: the tiles of the last, partial round of workgroups are split by rows
+    const int wg = blockIdx.x;
+    const bool split = wg >= p.kv_full;
+    const int tile = split ? p.kv_full + (wg - p.kv_full) / p.kv_split : wg;
+    const int part = split ? (wg - p.kv_full) % p.kv_split : 0;
+    const int nsplit = split ? p.kv_split : 1;
+    const int rb_lo = (int)((int64_t)p.RB * part / nsplit);
+    const int rb_hi = (int)((int64_t)p.RB * (part + 1) / nsplit);
+    const int hk = tile % p.Hkv;
+    const int kvt = tile / p.Hkv;
     const int key0 = kvt * kKVKeys;
     const int myj = key0 + 32 * kb + l32;
     const bool key_ok = myj < p.M;
@@ -1077,7 +1085,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
         return half_class(rbx, 0) != kMaskDead || half_class(rbx, 1) != kMaskDead;
     };
     auto next_needed = [&](int rbx) -> int {
-        while (rbx < p.RB && !block_needed(rbx)) ++rbx;
+        while (rbx < rb_hi && !block_needed(rbx)) ++rbx;
         return rbx;
     };
     // DMA of row block rbx (q, dO and their 32 lse / 32 delta values) into buffer b by all 8
@@ -1106,8 +1114,8 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
 
     const int eq = p.scal[0], edo = p.scal[1];
     const int ksx = load_ds_exponent(p);
-    const int first = next_needed(0);
-    if (first < p.RB) dma_block(first, 0);
+    const int first = next_needed(rb_lo);
+    if (first < rb_hi) dma_block(first, 0);
 
     f32x16 acc[MD];
 #pragma unroll
@@ -1126,12 +1134,12 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
         const float dsf = ldexpf(1.0f, -ksx);
         const float pf = ldexpf(1.0f, kPScaleLog2);
         int buf = 0;
-        for (int rb = first; rb < p.RB;) {
+        for (int rb = first; rb < rb_hi;) {
             const int rbn = next_needed(rb + 1);
             const int cls = half_class(rb, kb >> 1);
             wait_all_mem();
             __syncthreads();   // X: block rb landed in buffer `buf`; the exchange is free
-            if (rbn < p.RB) dma_block(rbn, buf ^ 1);
+            if (rbn < rb_hi) dma_block(rbn, buf ^ 1);
             const unsigned char* tq = work + buf * L::kBuf;
             const float* lrow = (const float*)(tq + 2 * L::kBlk);
             const float* drow = lrow + 32;
@@ -1201,12 +1209,12 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     } else {
         // ================= B waves: dP, then dV
         int buf = 0;
-        for (int rb = first; rb < p.RB;) {
+        for (int rb = first; rb < rb_hi;) {
             const int rbn = next_needed(rb + 1);
             const int cls = half_class(rb, kb >> 1);
             wait_all_mem();
             __syncthreads();   // X
-            if (rbn < p.RB) dma_block(rbn, buf ^ 1);
+            if (rbn < rb_hi) dma_block(rbn, buf ^ 1);
             const unsigned char* tq = work + buf * L::kBuf;
             if (cls != kMaskDead) {
                 f32x16 pa;
@@ -1230,7 +1238,9 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     }
     if (!key_ok) return;
     const float fac = role == 0 ? fabsf(p.scale) * ldexpf(1.0f, ksx - eq - edo) : ldexpf(1.0f, -kPScaleLog2 - edo);
-    float* dst = (role == 0 ? p.dk : p.dv) + ((int64_t)hk * p.M + myj) * D;
+    float* dst = split ? p.kv_part + ((((int64_t)(tile - p.kv_full) * p.kv_split + part) * 2 + role) * kKVKeys +
+                                      32 * kb + l32) * D
+                       : (role == 0 ? p.dk : p.dv) + ((int64_t)hk * p.M + myj) * D;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -1244,6 +1254,32 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
 // ----------------------------------------------------------------------------- fills
 
 // Degenerate shapes: N == 0 (dK = dV = 0) or M == 0 (every row fully masked).
+// dK and dV of the split key tiles: the kv_split row-range parts summed in part order.
+template <int D>
+__global__ __launch_bounds__(kThreads) void kvreduce_kernel(Params p, int tail) {
+    const int64_t n4 = (int64_t)tail * 2 * kKVKeys * (D / 4);
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4; e += (int64_t)gridDim.x * blockDim.x) {
+        const int c4 = (int)(e % (D / 4));
+        const int64_t kr = e / (D / 4);
+        const int key = (int)(kr % kKVKeys);
+        const int role = (int)((kr / kKVKeys) % 2);
+        const int tt = (int)(kr / (2 * kKVKeys));
+        const int tile = p.kv_full + tt;
+        const int hk = tile % p.Hkv, kvt = tile / p.Hkv;
+        const int j = kvt * kKVKeys + key;
+        if (j >= p.M) continue;
+        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int part = 0; part < p.kv_split; ++part) {
+            const f32x4 v = *(const f32x4*)(p.kv_part + ((((int64_t)tt * p.kv_split + part) * 2 + role) * kKVKeys + key) * D + 4 * c4);
+            s[0] += v[0];
+            s[1] += v[1];
+            s[2] += v[2];
+            s[3] += v[3];
+        }
+        *(f32x4*)((role == 0 ? p.dk : p.dv) + ((int64_t)hk * p.M + j) * D + 4 * c4) = s;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void fill_kernel(float* a, int64_t n, float val) {
     for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += (int64_t)gridDim.x * kThreads)
         a[e] = val;
