@@ -112,6 +112,13 @@ def test_validation_mask_and_kv_alignment():
         d.q.nb[1] = 4 * 96; d.q.nb[2] = 4 * 96 * 64
     _expect(B.EUNSUPPORTED, unsupported_d, "c1_f32kv")
 
+    # K/V row strides must stay below 2^32 bytes (the DMA forms row addresses in 32 bits)
+    def huge_k_row_stride(d): d.k.nb[1] = 1 << 32
+    _expect(B.EUNSUPPORTED, huge_k_row_stride)
+
+    def huge_v_row_stride(d): d.v.nb[1] = (1 << 32) + 32
+    _expect(B.EUNSUPPORTED, huge_v_row_stride, "c1_f32kv")
+
 
 def test_null_arguments():
     lib = fab.load_library()
