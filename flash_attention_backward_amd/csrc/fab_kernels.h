@@ -306,9 +306,9 @@ struct QLds {
 template <int D, bool GRAD>
 __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     using L = QLds<D>;
-    // with 8 q8_0 wave-instructions per sub-tile (D = 256) the S waves decode the V half, one
-    // wave-instruction each, after their products; the K waves decode the K half
-    constexpr bool kSplitDecode = Q8Pair<D>::U == 8;
+    // The K waves decode whole sub-tiles. (Handing the V half to the S waves was measured: with
+    // the DMA queued from the S waves, they are the busier role.)
+    constexpr bool kSplitDecode = false;
     constexpr int KS = D / 16;     // 16-deep steps of a contraction over d
     constexpr int MD = D / 32;     // 32-wide d blocks of dQ
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
