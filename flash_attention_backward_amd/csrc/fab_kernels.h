@@ -1011,7 +1011,6 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     constexpr int KS = D / 16;
     constexpr int MD = D / 32;
     constexpr int NI = L::kBlk / 1024;                // 64-lane x 16-byte DMA instructions per tensor
-    constexpr int NIW = (2 * NI + kKVWaves - 1) / kKVWaves;
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
     unsigned char* work = lds;                        // setup scratch, then buffers + exchange
     unsigned char* exP = work + 2 * L::kBuf;
@@ -1093,12 +1092,13 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     // the same for every block, so they are computed once.
     const char* qbase = (const char*)(p.qr + (int64_t)hk * rowsHK * D);
     const char* dbase = (const char*)(p.dr + (int64_t)hk * rowsHK * D);
-    auto dma_block = [&](int rbx, int b) {
+    // nw waves issue it; wi is this wave's index among them (both uniform)
+    auto dma_block = [&](int rbx, int b, int nw, int wi) {
         unsigned char* base = work + b * L::kBuf;
         const int64_t blk = (int64_t)rbx * L::kBlk;
 #pragma unroll
-        for (int k = 0; k < NIW; ++k) {
-            const int ins = wave + kKVWaves * k;     // uniform
+        for (int k = 0; k < 2 * NI; ++k) {
+            const int ins = wi + nw * k;             // uniform
             if (ins >= 2 * NI) break;
             const int ten = ins / NI, ii = ins - (ins / NI) * NI;
             const int P = ii * 64 + lane;
@@ -1106,7 +1106,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
             const int off = (row * D + 8 * swz_chunk<D>(row, pc)) * 2;
             dma16((ten ? dbase : qbase) + blk + off, base + ten * L::kBlk + ii * 1024);
         }
-        if (wave == kKVWaves - 1 && lane < 16) {
+        if (wi == nw - 1 && lane < 16) {
             const float* src = (lane < 8 ? p.row_lse2 : p.row_dlt) + (int64_t)hk * rowsHK + rbx * 32 + 4 * (lane & 7);
             dma16(src, base + 2 * L::kBlk);
         }
@@ -1115,7 +1115,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     const int eq = p.scal[0], edo = p.scal[1];
     const int ksx = load_ds_exponent(p);
     const int first = next_needed(rb_lo);
-    if (first < rb_hi) dma_block(first, 0);
+    if (first < rb_hi) dma_block(first, 0, kKVWaves, wave);
 
     f32x16 acc[MD];
 #pragma unroll
@@ -1139,7 +1139,6 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
             const int cls = half_class(rb, kb >> 1);
             wait_all_mem();
             __syncthreads();   // X: block rb landed in buffer `buf`; the exchange is free
-            if (rbn < rb_hi) dma_block(rbn, buf ^ 1);
             const unsigned char* tq = work + buf * L::kBuf;
             const float* lrow = (const float*)(tq + 2 * L::kBlk);
             const float* drow = lrow + 32;
@@ -1187,7 +1186,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
 #pragma unroll
                 for (int rh = 0; rh < 2; ++rh) *(f16x8*)(myP + rh * 1024 + lane * 16) = bp[rh];
             }
-            __syncthreads();   // Y: P and dP exchanged
+            lds_barrier();     // Y: P and dP exchanged (the next block's DMA stays in flight)
             if (cls != kMaskDead) {
                 f16x8 bs[2];
 #pragma unroll
@@ -1214,7 +1213,6 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
             const int cls = half_class(rb, kb >> 1);
             wait_all_mem();
             __syncthreads();   // X
-            if (rbn < rb_hi) dma_block(rbn, buf ^ 1);
             const unsigned char* tq = work + buf * L::kBuf;
             if (cls != kMaskDead) {
                 f32x16 pa;
@@ -1227,10 +1225,12 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                     *(f32x4*)(myD + (b * 64 + lane) * 16) = o;
                 }
             }
-            __syncthreads();   // Y
+            // the next block's DMA, queued while the A wave forms P
+            if (rbn < rb_hi) dma_block(rbn, buf ^ 1, 4, kb);
+            lds_barrier();     // Y
             if (cls != kMaskDead) {
                 const f16x8 bp[2] = {*(const f16x8*)(myP + lane * 16), *(const f16x8*)(myP + 1024 + lane * 16)};
-                cols_acc_x<D>(tq + L::kBlk, bp, acc, cw);
+                cols_acc_x<D, true>(tq + L::kBlk, bp, acc, cw);
             }
             rb = rbn;
             buf ^= 1;
