@@ -621,7 +621,6 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
     using L = W1Lds<D>;
     constexpr int KS = D / 16;
     constexpr int NI = L::kBlk / 1024;                // 64-lane x 16-byte DMA instructions per tensor
-    constexpr int NIW = (2 * NI + kW1Waves - 1) / kW1Waves;
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
     unsigned char* work = lds;
     unsigned char* recs = work + 2 * L::kBuf;                         // [3][wave][row] x 16 B
@@ -712,12 +711,13 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
 
     const char* qbase = (const char*)(p.qr + (int64_t)hk * rowsHK * D);
     const char* dbase = (const char*)(p.dr + (int64_t)hk * rowsHK * D);
-    auto dma_block = [&](int rbx, int b) {
+    // nw waves issue it; wi is this wave's index among them (both uniform)
+    auto dma_block = [&](int rbx, int b, int nw, int wi) {
         unsigned char* base = work + b * L::kBuf;
         const int64_t blk = (int64_t)rbx * L::kBlk;
 #pragma unroll
-        for (int k = 0; k < NIW; ++k) {
-            const int ins = wave + kW1Waves * k;     // uniform
+        for (int k = 0; k < 2 * NI; ++k) {
+            const int ins = wi + nw * k;     // uniform
             if (ins >= 2 * NI) break;
             const int ten = ins / NI, ii = ins - (ins / NI) * NI;
             const int P = ii * 64 + lane;
@@ -840,7 +840,7 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
     const bool early = wave < kW1Waves / 2;
     int c0 = next_needed(rb0);
     c0 = c0 < rb1 ? c0 : -1;
-    if (c0 >= 0) dma_block(c0, 0);
+    if (c0 >= 0) dma_block(c0, 0, kW1Waves, wave);
     int cp = -1, cpp = -1;
     f32x16 ha, hp;   // early waves: products of cp
 #pragma unroll
@@ -849,7 +849,6 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
         const int c1 = c0 >= 0 ? nextv(c0) : -1;
         wait_all_mem();
         __syncthreads();   // c0 landed; the records of cpp are complete
-        if (c1 >= 0) dma_block(c1, (i + 1) & 1);
         if (early) {
             if (cp >= 0) put_rec((i + 2) % 3, stats(cp, tcls(cp, mytile), ha, hp));
             if (cpp >= 0 && lane < 8) merge_block(cpp, recs + ((i + 1) % 3) * L::kRec, 8 * wave + lane);
@@ -861,6 +860,9 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
             if (c != kMaskDead) pair_rows_t<D, 2, L::kBlk>(work + (i & 1) * L::kBuf, bk, bv, sa, pa, rw);
+            // the next block's DMA is queued by the late waves after their products (queued by
+            // all waves at the barrier, the later ones stall behind the earlier ones' copies)
+            if (c1 >= 0 && !early) dma_block(c1, (i + 1) & 1, kW1Waves / 2, wave - kW1Waves / 2);
             if (early) {
                 ha = sa;
                 hp = pa;
