@@ -67,7 +67,8 @@ struct Params {
     double* part_l;       // softmax sum at part_m
     double* part_d;       // sum of e * dp at part_m (dp in 2^e_do units)
     float* part_b;        // max |dp| over visible keys
-    float* row_lse2;      // [Hkv*RB*32]  lse in log2 units, -inf for dead or padding rows
+    float* row_lse2;      // [Hkv*RB*32]  lse in log2 units, +inf for dead or padding rows (so that
+                          //   exp2(s - lse2) is 0 for them with no test)
     float* row_dlt;       // [Hkv*RB*32]  delta in 2^e_do units
     float* bound_part;    // [nbound] per-block max of max|dp| + |delta|
     int nbound;
@@ -93,6 +94,7 @@ FAB_DEV f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
 }
 
 FAB_DEV float neg_inf() { return __int_as_float(kNegInfBits); }
+FAB_DEV float pos_inf() { return -neg_inf(); }
 
 FAB_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

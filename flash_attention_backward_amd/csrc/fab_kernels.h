@@ -369,7 +369,7 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         double l64 = 0.0, d64 = 0.0;
         float bmax = 0.0f;
         // walk 2 state: p * 2^-ks = exp2(s2 - lse2 - ks)
-        float lse2 = neg_inf(), dlt = 0.0f, lse2k = 0.0f;
+        float lse2 = pos_inf(), dlt = 0.0f, lse2k = 0.0f;
         if (GRAD) {
             if (row_ok) {
                 lse2 = p.row_lse2[ridx];
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
             }
             lse2k = lse2 + (float)load_ds_exponent(p);
         }
-        const bool dead = (lse2 == neg_inf());
+        const bool dead = (lse2 == pos_inf());
         const RowWalk<D> rw = make_row_walk<D>(lane);
 
         const bool sdec = kSplitDecode && p.k_type == FA_BACK_Q8_0 && p.v_type == FA_BACK_Q8_0;
@@ -921,7 +921,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p) {
         sb[grp][lr] = b;
         __syncthreads();
         if (grp == 0 && ok) {
-            float lse2 = neg_inf();
+            float lse2 = pos_inf();   // dead or padding row
             double dl = 0.0, lnat = 0.0;
             if (mx != neg_inf()) {
                 const double L = ((sl[0][lr] + sl[1][lr]) + sl[2][lr]) + sl[3][lr];
@@ -1133,6 +1133,8 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     if (role == 0) {
         // ================= A waves: S, P, then dS and dK
         const float sc2 = fabsf(p.scale) * ldexpf(1.0f, -eq) * kLog2e;   // q carries the sign
+        // P is formed as p * 2^15 (the 2^15 of the fp16 image added to the exponent); its fp32
+        // copy carries the dS factor 2^(-ks-15), so that dS = copy * (dP - delta)
         const float dsf = ldexpf(1.0f, -ksx);
         const float pf = ldexpf(1.0f, kPScaleLog2);
         int buf = 0;
@@ -1150,14 +1152,15 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                 for (int v = 0; v < 16; ++v) sa[v] = 0.0f;
                 rows_chain_x<D, 1>(tq, bkv, sa, rw);
                 if (cls == kMaskMixed) {
-                    // mask terms staged through the wave's fp32 P slot by a rolled loop, so the
-                    // masked case costs the loop below no registers; a fully masked row (and
-                    // every padding row past R, lse = -inf) reads no mask
+                    // mask terms (plus the image exponent 15) staged through the wave's fp32 P
+                    // slot by a rolled loop, so the masked case costs the loop below no
+                    // registers; a fully masked row (and every padding row past R, lse2 = +inf)
+                    // reads no mask
 #pragma unroll 1
                     for (int v = 0; v < 16; ++v) {
                         const int b = v >> 2, u = v & 3;
                         float mv = neg_inf();
-                        if (key_ok && lrow[8 * b + 4 * g + u] != neg_inf()) {
+                        if (key_ok && lrow[8 * b + 4 * g + u] != pos_inf()) {
                             const int r = 32 * rb + crow(v, g);
                             const int ii = r / p.G, gh = r - (r / p.G) * p.G;
                             const char* mrow = p.mask + (int64_t)ii * p.m_nb1 +
@@ -1178,9 +1181,8 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int v = 4 * b + u;
-                        // a fully masked row has lse = -inf: use +inf so that p = 0
-                        const float lr = l4[u] != neg_inf() ? l4[u] : -neg_inf();
-                        p4[u] = fast_exp2(fmaf(sa[v], sc2, m4[u] - lr));
+                        // p * 2^15; 0 for a dead row (lse2 = +inf) or a masked key
+                        p4[u] = fast_exp2(fmaf(sa[v], sc2, m4[u] - l4[u]));
                         bp[v >> 3][v & 7] = (_Float16)(p4[u] * pf);
                     }
                     *(f32x4*)(myF + (b * 64 + lane) * 16) = p4;
