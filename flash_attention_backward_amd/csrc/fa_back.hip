@@ -220,10 +220,13 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
     hipLaunchKernelGGL(absmax_kernel, dim3(g.npart), dim3(kThreads), 0, st, P);
     pm.mark(0);
     hipLaunchKernelGGL(prep_kernel<D>, dim3(g.Hkv * g.RB), dim3(kThreads), 0, st, P);
-    if (g.Hm > 0)
-        hipLaunchKernelGGL(maskclass_kernel, dim3((g.Hm == 1 ? 1 : g.Hkv) * g.RB,
-                                                  (g.KT + kClassTilesPerBlock - 1) / kClassTilesPerBlock),
-                           dim3(kThreads), 0, st, P);
+    if (g.Hm > 0) {
+        const dim3 grid((g.Hm == 1 ? 1 : g.Hkv) * g.RB, (g.KT + kClassTilesPerBlock - 1) / kClassTilesPerBlock);
+        if (P.m_type == FA_BACK_F16)
+            hipLaunchKernelGGL(maskclass_kernel<2>, grid, dim3(kThreads), 0, st, P);
+        else
+            hipLaunchKernelGGL(maskclass_kernel<4>, grid, dim3(kThreads), 0, st, P);
+    }
     pm.mark(1);
     if (g.w1keys)
         hipLaunchKernelGGL(walk1_keys_kernel<D>, dim3(g.KT1 * g.Hkv, g.RS1), dim3(kW1Threads), 0, st, P);

@@ -136,30 +136,36 @@ FAB_DEV int load_ds_exponent(const Params& p) {
 // Grid: x = Hc * RB (Hc = 1 when the mask is shared by all heads), y = tile groups of 16.
 constexpr int kClassTilesPerBlock = 16;
 
+// ESZ: bytes per mask entry (2: F16, 4: F32). With one mask head the mask row depends on the
+// query row i only, and the G rows r = i*G + g share it: a thread whose row repeats the previous
+// row's i reads nothing (its entries count as both 0 and -inf, neutral for the all-lanes tests).
+template <int ESZ>
 __global__ __launch_bounds__(kThreads) void maskclass_kernel(Params p) {
     __shared__ unsigned int red[kClassTilesPerBlock][kWaves];
     const int hc = blockIdx.x / p.RB, rb = blockIdx.x - (blockIdx.x / p.RB) * p.RB;
     const int wave = threadIdx.x >> 6;
     const int rr = threadIdx.x >> 3, kg = threadIdx.x & 7;
     const int r = rb * 32 + rr;
-    const bool row_ok = r < p.R;
     const int i = r / p.G, gh = r - (r / p.G) * p.G;
+    const bool repeat = p.Hm == 1 && rr > 0 && (r - 1) / p.G == i;
+    const bool row_ok = r < p.R && !repeat;
     const char* mrow = p.mask + (int64_t)i * p.m_nb1 + (int64_t)(p.Hm == 1 ? 0 : hc * p.G + gh) * p.m_nb2;
     const int tb = blockIdx.y * kClassTilesPerBlock;
     const int te = min(p.KT, tb + kClassTilesPerBlock);
-    const int esz = p.m_type == FA_BACK_F16 ? 2 : 4;
+    constexpr int esz = ESZ;
     // 16-byte loads of 8 consecutive entries when the rows allow them
     const bool vec = (((uintptr_t)p.mask | (uintptr_t)p.m_nb1 | (uintptr_t)p.m_nb2) & 15) == 0;
     // entries of this thread in every tile: keys t*64 + 8*kg .. +7; all loads issued first
-    u32x4 raw[kClassTilesPerBlock][2];
+    u32x4 raw[kClassTilesPerBlock][ESZ / 2];
 #pragma unroll
     for (int k = 0; k < kClassTilesPerBlock; ++k) {
         const int t = tb + k;
         const int j = t * kQTileKeys + 8 * kg;
-        raw[k][0] = raw[k][1] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int h = 0; h < ESZ / 2; ++h) raw[k][h] = u32x4{0u, 0u, 0u, 0u};
         if (row_ok && t < te && vec && j + 8 <= p.M) {
-            raw[k][0] = *(const u32x4*)(mrow + (int64_t)j * esz);
-            if (esz == 4) raw[k][1] = *(const u32x4*)(mrow + (int64_t)j * esz + 16);
+#pragma unroll
+            for (int h = 0; h < ESZ / 2; ++h) raw[k][h] = *(const u32x4*)(mrow + (int64_t)j * esz + 16 * h);
         }
     }
 #pragma unroll
@@ -169,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void maskclass_kernel(Params p) {
         bool all0 = true, allinf = true;
         if (row_ok && t < te) {
             if (vec && j + 8 <= p.M) {
-                if (esz == 2) {
+                if constexpr (ESZ == 2) {
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
                         const unsigned int x = raw[k][0][w];
