@@ -1139,8 +1139,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     if (role == 0) {
         // ================= A waves: S, P, then dS and dK
         const float sc2 = fabsf(p.scale) * ldexpf(1.0f, -eq) * kLog2e;   // q carries the sign
-        // P is formed as p * 2^15 (the 2^15 of the fp16 image added to the exponent); its fp32
-        // copy carries the dS factor 2^(-ks-15), so that dS = copy * (dP - delta)
+        // dS = P (dP - delta) 2^-ks; the fp16 image of P for the B wave is p * 2^15
         const float dsf = ldexpf(1.0f, -ksx);
         const float pf = ldexpf(1.0f, kPScaleLog2);
         int buf = 0;
