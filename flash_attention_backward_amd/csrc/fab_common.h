@@ -67,8 +67,9 @@ struct Params {
     double* part_l;       // softmax sum at part_m
     double* part_d;       // sum of e * dp at part_m (dp in 2^e_do units)
     float* part_b;        // max |dp| over visible keys
-    float* row_lse2;      // [Hkv*RB*32]  lse in log2 units, +inf for dead or padding rows (so that
-                          //   exp2(s - lse2) is 0 for them with no test)
+    float* row_lse2;      // [Hkv*RB*32]  lse in log2 units minus kPScaleLog2, so that exp2(s - row_lse2)
+                          //   is the P image p * 2^15; +inf for dead or padding rows (the image is 0
+                          //   for them with no test)
     float* row_dlt;       // [Hkv*RB*32]  delta in 2^e_do units
     float* bound_part;    // [nbound] per-block max of max|dp| + |delta|
     int nbound;

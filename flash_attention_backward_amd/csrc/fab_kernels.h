@@ -374,14 +374,14 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         float m_run = neg_inf();
         double l64 = 0.0, d64 = 0.0;
         float bmax = 0.0f;
-        // walk 2 state: p * 2^-ks = exp2(s2 - lse2 - ks)
+        // walk 2 state: p * 2^-ks = exp2(s2 - lse2 - ks), lse2 stored less the image exponent
         float lse2 = pos_inf(), dlt = 0.0f, lse2k = 0.0f;
         if (GRAD) {
             if (row_ok) {
                 lse2 = p.row_lse2[ridx];
                 dlt = p.row_dlt[ridx];
             }
-            lse2k = lse2 + (float)load_ds_exponent(p);
+            lse2k = lse2 + (float)(load_ds_exponent(p) + kPScaleLog2);
         }
         const bool dead = (lse2 == pos_inf());
         const RowWalk<D> rw = make_row_walk<D>(lane);
@@ -862,10 +862,10 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
         if (c0 < 0 && cp < 0) break;
         if (c0 >= 0) {
             const int c = tcls(c0, mytile);
+            // the products of a block that is dead for this wave's keys are formed too (stats
+            // gives it the empty record): no zero fill, and no copy of the early waves' products
             f32x16 sa, pa;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
-            if (c != kMaskDead) pair_rows_t<D, 2, L::kBlk>(work + (i & 1) * L::kBuf, bk, bv, sa, pa, rw);
+            pair_rows_t<D, 2, L::kBlk, true>(work + (i & 1) * L::kBuf, bk, bv, sa, pa, rw);
             // the next block's DMA is queued by the late waves after their products (queued by
             // all waves at the barrier, the later ones stall behind the earlier ones' copies)
             if (c1 >= 0 && !early) dma_block(c1, (i + 1) & 1, kW1Waves / 2, wave - kW1Waves / 2);
@@ -933,7 +933,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p) {
                 const double L = ((sl[0][lr] + sl[1][lr]) + sl[2][lr]) + sl[3][lr];
                 const double Dd = ((sd[0][lr] + sd[1][lr]) + sd[2][lr]) + sd[3][lr];
                 const double l2 = (double)mx + log2(L);
-                lse2 = (float)l2;
+                lse2 = (float)(l2 - kPScaleLog2);   // stored less the P image exponent
                 lnat = l2 * kLn2;
                 dl = Dd / L;
                 bound = fmaxf(bound, fmaxf(fmaxf(sb[0][lr], sb[1][lr]), fmaxf(sb[2][lr], sb[3][lr])) +
@@ -1139,9 +1139,9 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     if (role == 0) {
         // ================= A waves: S, P, then dS and dK
         const float sc2 = fabsf(p.scale) * ldexpf(1.0f, -eq) * kLog2e;   // q carries the sign
-        // dS = P (dP - delta) 2^-ks; the fp16 image of P for the B wave is p * 2^15
-        const float dsf = ldexpf(1.0f, -ksx);
-        const float pf = ldexpf(1.0f, kPScaleLog2);
+        // the exponential gives the P image p * 2^15 (the stored lse carries the 15), rounded to
+        // fp16 for the B wave; dS = P (dP - delta) 2^-ks = image (dP - delta) 2^(-ks-15)
+        const float dsf = ldexpf(1.0f, -ksx - kPScaleLog2);
         int buf = 0;
         for (int rb = first; rb < rb_hi;) {
             const int rbn = next_needed(rb + 1);
@@ -1157,10 +1157,9 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                 for (int v = 0; v < 16; ++v) sa[v] = 0.0f;
                 rows_chain_x<D, 1>(tq, bkv, sa, rw);
                 if (cls == kMaskMixed) {
-                    // mask terms (plus the image exponent 15) staged through the wave's fp32 P
-                    // slot by a rolled loop, so the masked case costs the loop below no
-                    // registers; a fully masked row (and every padding row past R, lse2 = +inf)
-                    // reads no mask
+                    // mask terms staged through the wave's fp32 P slot by a rolled loop, so the
+                    // masked case costs the loop below no registers; a fully masked row (and every
+                    // padding row past R, lse2 = +inf) reads no mask
 #pragma unroll 1
                     for (int v = 0; v < 16; ++v) {
                         const int b = v >> 2, u = v & 3;
@@ -1175,23 +1174,28 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                         ((float*)(myF + (b * 64 + lane) * 16))[u] = mv;
                     }
                 }
-                const float mdef = key_ok ? 0.0f : neg_inf();
+                // the image p * 2^15; 0 for a dead row (lse2 = +inf) or a masked key. Without a
+                // mask, a key past M (zero K row) gets an image too: it only reaches that key's
+                // own dK and dV columns, which are never written.
                 f16x8 bp[2];
+                auto image = [&](bool mixed) {
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const f32x4 l4 = *(const f32x4*)(lrow + 8 * b + 4 * g);
-                    f32x4 m4 = {mdef, mdef, mdef, mdef};
-                    if (cls == kMaskMixed) m4 = *(const f32x4*)(myF + (b * 64 + lane) * 16);
-                    f32x4 p4;
+                    for (int b = 0; b < 4; ++b) {
+                        const f32x4 l4 = *(const f32x4*)(lrow + 8 * b + 4 * g);
+                        f32x4 m4 = {0.0f, 0.0f, 0.0f, 0.0f};
+                        if (mixed) m4 = *(const f32x4*)(myF + (b * 64 + lane) * 16);
+                        f32x4 p4;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int v = 4 * b + u;
-                        // p * 2^15; 0 for a dead row (lse2 = +inf) or a masked key
-                        p4[u] = fast_exp2(fmaf(sa[v], sc2, m4[u] - l4[u]));
-                        bp[v >> 3][v & 7] = (_Float16)(p4[u] * pf);
+                        for (int u = 0; u < 4; ++u) {
+                            const int v = 4 * b + u;
+                            p4[u] = fast_exp2(mixed ? fmaf(sa[v], sc2, m4[u] - l4[u]) : fmaf(sa[v], sc2, -l4[u]));
+                            bp[v >> 3][v & 7] = (_Float16)p4[u];
+                        }
+                        *(f32x4*)(myF + (b * 64 + lane) * 16) = p4;
                     }
-                    *(f32x4*)(myF + (b * 64 + lane) * 16) = p4;
-                }
+                };
+                if (cls == kMaskMixed) image(true);
+                else image(false);
 #pragma unroll
                 for (int rh = 0; rh < 2; ++rh) *(f16x8*)(myP + rh * 1024 + lane * 16) = bp[rh];
             }

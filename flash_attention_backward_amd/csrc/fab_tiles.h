@@ -626,8 +626,9 @@ FAB_DEV void cols_acc_x(const unsigned char* t, const f16x8 b[2], f32x16* acc, c
 
 // Transposed pair for key-owned waves: sa += K Q^T (A: bk in registers, B: q rows of the tile
 // at t) and pa += V dO^T (A: bv, B: dO rows of the tile at t + DOFF), over d in the Gray order
-// of pair_rows, reads PF steps ahead. One query row per lane column, 16 keys per lane.
-template <int D, int PF, int DOFF>
+// of pair_rows, reads PF steps ahead. One query row per lane column, 16 keys per lane. ZERO:
+// the sums start from zero instead of from sa and pa.
+template <int D, int PF, int DOFF, bool ZERO = false>
 FAB_DEV void pair_rows_t(const unsigned char* t, const f16x8* bk, const f16x8* bv, f32x16& sa, f32x16& pa,
                          const RowWalk<D>& w) {
     constexpr int KS = D / 16, NB = PF + 1;
@@ -647,8 +648,8 @@ FAB_DEV void pair_rows_t(const unsigned char* t, const f16x8* bk, const f16x8* b
             if (s + PF + 1 < KS) a += gray_step(s + PF, w.e);
         }
         const int ks = gray(s);
-        sa = mfma32(bk[ks], rq[s % NB], sa);
-        pa = mfma32(bv[ks], rd[s % NB], pa);
+        sa = mfma32(bk[ks], rq[s % NB], (ZERO && s == 0) ? f32x16{} : sa);
+        pa = mfma32(bv[ks], rd[s % NB], (ZERO && s == 0) ? f32x16{} : pa);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
