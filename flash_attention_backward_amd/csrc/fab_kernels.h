@@ -865,7 +865,9 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
             // the products of a block that is dead for this wave's keys are formed too (stats
             // gives it the empty record): no zero fill, and no copy of the early waves' products
             f32x16 sa, pa;
+            mfma_prio_hi();
             pair_rows_t<D, 2, L::kBlk, true>(work + (i & 1) * L::kBuf, bk, bv, sa, pa, rw);
+            mfma_prio_lo();
             // the next block's DMA is queued by the late waves after their products (queued by
             // all waves at the barrier, the later ones stall behind the earlier ones' copies)
             if (c1 >= 0 && !early) dma_block(c1, (i + 1) & 1, kW1Waves / 2, wave - kW1Waves / 2);
@@ -1155,7 +1157,9 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                 f32x16 sa;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) sa[v] = 0.0f;
+                mfma_prio_hi();
                 rows_chain_x<D, 1>(tq, bkv, sa, rw);
+                mfma_prio_lo();
                 if (cls == kMaskMixed) {
                     // mask terms staged through the wave's fp32 P slot by a rolled loop, so the
                     // masked case costs the loop below no registers; a fully masked row (and every
@@ -1213,7 +1217,9 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                         bs[v >> 3][v & 7] = (_Float16)(p4[u] * (dp4[u] - d4[u]) * dsf);
                     }
                 }
+                mfma_prio_hi();
                 cols_acc_x<D>(tq, bs, acc, cw);
+                mfma_prio_lo();
             }
             rb = rbn;
             buf ^= 1;
@@ -1231,7 +1237,9 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                 f32x16 pa;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) pa[v] = 0.0f;
+                mfma_prio_hi();
                 rows_chain_x<D, 1>(tq + L::kBlk, bkv, pa, rw);
+                mfma_prio_lo();
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const f32x4 o = {pa[4 * b], pa[4 * b + 1], pa[4 * b + 2], pa[4 * b + 3]};
@@ -1243,7 +1251,9 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
             lds_barrier();     // Y
             if (cls != kMaskDead) {
                 const f16x8 bp[2] = {*(const f16x8*)(myP + lane * 16), *(const f16x8*)(myP + 1024 + lane * 16)};
+                mfma_prio_hi();
                 cols_acc_x<D, true>(tq + L::kBlk, bp, acc, cw);
+                mfma_prio_lo();
             }
             rb = rbn;
             buf ^= 1;

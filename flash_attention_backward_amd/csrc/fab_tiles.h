@@ -36,6 +36,13 @@ struct Swz {
     int col1;    // XOR term of frag_cols, second transpose read
 };
 
+// Issue priority of the calling wave around a chain of matrix products. The other wave on the
+// SIMD is then mostly doing vector work; with the chain at the higher priority, each product
+// issues as soon as the matrix unit is free instead of waiting behind that work (issue goes to
+// the older wave when priorities are equal).
+FAB_DEV void mfma_prio_hi() { __builtin_amdgcn_s_setprio(3); }
+FAB_DEV void mfma_prio_lo() { __builtin_amdgcn_s_setprio(0); }
+
 FAB_DEV int opaque(int x) {
     asm volatile("" : "+v"(x));
     return x;
