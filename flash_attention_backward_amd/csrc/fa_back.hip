@@ -107,12 +107,20 @@ int validate(const fa_back_desc* d, Geometry* g) {
     g->KT = (g->M + kQTileKeys - 1) / kQTileKeys;
     g->KVT = (g->M + kKVKeys - 1) / kKVKeys;
     // key side: one workgroup per CU at a time (LDS), so the tiles past the last full round of
-    // kCUs workgroups would run nearly alone; each of them is split into up to 4 row ranges
+    // kCUs workgroups would run nearly alone; each of them is split into up to 4 row ranges.
+    // A workgroup lists at most KVLds::kMaxRB row blocks, so with more rows every tile is split
+    // into ranges of at most that many.
     {
         const int T = g->KVT * (int)Hkv;
-        const int tail = T > kCUs ? T % kCUs : 0;
-        g->kv_tail = (tail > 0 && tail <= kCUs / 2) ? tail : 0;
-        g->kv_split = g->kv_tail ? std::min(4, kCUs / g->kv_tail) : 1;
+        const int pmin = (g->RB + KVLds<64>::kMaxRB - 1) / KVLds<64>::kMaxRB;
+        if (pmin > 1) {
+            g->kv_tail = T;
+            g->kv_split = pmin;
+        } else {
+            const int tail = T > kCUs ? T % kCUs : 0;
+            g->kv_tail = (tail > 0 && tail <= kCUs / 2) ? tail : 0;
+            g->kv_split = g->kv_tail ? std::min(4, kCUs / g->kv_tail) : 1;
+        }
         g->kv_full = T - g->kv_tail;
     }
     // key-range splits of the query-side passes: aim for >= 512 workgroups (two per CU on

@@ -1011,8 +1011,9 @@ struct KVLds {
     static constexpr int kWork = 2 * kBuf + kExP + kExD + kExF;
     static constexpr int kRaw = RawTile<D, kQTileKeys>::kBytes;
     static constexpr int kSetup = 2 * kQTileKeys * D * 2 + 2 * kRaw;     // K, V half tiles + bytes
-    static constexpr int kMaxRB = 4096;                                  // row blocks classed in LDS
-    static constexpr int kBytes = (kSetup > kWork ? kSetup : kWork) + 2 * kMaxRB;
+    static constexpr int kMaxRB = 4096;                                  // row blocks listed per workgroup
+    static constexpr int kTail = 6 * kMaxRB + 16;                        // list, two class rows, count
+    static constexpr int kBytes = (kSetup > kWork ? kSetup : kWork) + kTail;
 };
 
 template <int D>
@@ -1026,8 +1027,10 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     unsigned char* exP = work + 2 * L::kBuf;
     unsigned char* exD = exP + L::kExP;
     unsigned char* exF = exD + L::kExD;
-    unsigned char* clsA = lds + L::kBytes - 2 * L::kMaxRB;   // class of (row block, first 64 keys)
-    unsigned char* clsB = clsA + L::kMaxRB;                  // class of (row block, last 64 keys)
+    uint32_t* sched = (uint32_t*)(lds + L::kBytes - L::kTail);          // needed row blocks of a chunk
+    unsigned char* clsA = (unsigned char*)(sched + L::kMaxRB);         // class of (row block, first 64 keys)
+    unsigned char* clsB = clsA + L::kMaxRB;                             // class of (row block, last 64 keys)
+    int* nsched = (int*)(clsB + L::kMaxRB);
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l32 = lane & 31, g = lane >> 5;
@@ -1076,56 +1079,47 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                 for (int ks = 0; ks < KS; ++ks) bkv[ks] = frag_rows<D>(src, 32 * (kb & 1), ks, lane, z);
             }
         }
-        // mask classes of the first kMaxRB row blocks for the two 64-key halves, staged once
-        for (int rbx = threadIdx.x; rbx < min(p.RB, L::kMaxRB); rbx += kKVThreads) {
-            clsA[rbx] = (unsigned char)mask_class(p, hk, rbx, 2 * kvt);
-            clsB[rbx] = (unsigned char)(2 * kvt + 1 < p.KT ? mask_class(p, hk, rbx, 2 * kvt + 1) : kMaskDead);
-        }
         __syncthreads();   // the setup region becomes the row-block buffers
     }
 
-    // ---- row-block schedule (identical in every wave)
-    auto half_class = [&](int rbx, int half) -> int {
-        if (rbx < L::kMaxRB) return half ? clsB[rbx] : clsA[rbx];
-        const int t = 2 * kvt + half;
-        return t < p.KT ? mask_class(p, hk, rbx, t) : kMaskDead;
-    };
-    auto block_needed = [&](int rbx) -> bool {
-        return half_class(rbx, 0) != kMaskDead || half_class(rbx, 1) != kMaskDead;
-    };
-    auto next_needed = [&](int rbx) -> int {
-        while (rbx < rb_hi && !block_needed(rbx)) ++rbx;
-        return rbx;
-    };
     // DMA of row block rbx (q, dO and their 32 lse / 32 delta values) into buffer b by all 8
     // waves. The LDS copy is swizzled by choosing each lane's source chunk; those choices are
     // the same for every block, so they are computed once.
     const char* qbase = (const char*)(p.qr + (int64_t)hk * rowsHK * D);
     const char* dbase = (const char*)(p.dr + (int64_t)hk * rowsHK * D);
-    // nw waves issue it; wi is this wave's index among them (both uniform)
+    // nw waves issue it; wi is this wave's index among them (both uniform). The copies are
+    // hidden from the compiler (dma16_hidden), so the transpose reads of the products do not
+    // wait for them; every wave waits for its own copies before the block barrier.
+    // Instruction ii covers rows 64*ii/(D/8) ..; the swizzle repeats every 16 rows, i.e. every
+    // IP = D/32 instructions, so a lane's source offset is that of ii % IP plus a uniform
+    // 16-row step added to the base.
+    constexpr int IP = D / 32;
     auto dma_block = [&](int rbx, int b, int nw, int wi) {
-        unsigned char* base = work + b * L::kBuf;
+        const uint32_t base = lds_addr(work + b * L::kBuf);
         const int64_t blk = (int64_t)rbx * L::kBlk;
 #pragma unroll
         for (int k = 0; k < 2 * NI; ++k) {
             const int ins = wi + nw * k;             // uniform
             if (ins >= 2 * NI) break;
             const int ten = ins / NI, ii = ins - (ins / NI) * NI;
-            const int P = ii * 64 + lane;
+            const int i0 = ii % IP;
+            const int P = i0 * 64 + lane;
             const int row = P / (D / 8), pc = P - (P / (D / 8)) * (D / 8);
-            const int off = (row * D + 8 * swz_chunk<D>(row, pc)) * 2;
-            dma16((ten ? dbase : qbase) + blk + off, base + ten * L::kBlk + ii * 1024);
+            const uint32_t off = (uint32_t)((row * D + 8 * swz_chunk<D>(row, pc)) * 2);
+            const char* sb = (ten ? dbase : qbase) + blk + (int64_t)(ii / IP) * (16 * D * 2);
+            dma16_hidden(sb, off, base + ten * L::kBlk + ii * 1024);
         }
         if (wi == nw - 1 && lane < 16) {
-            const float* src = (lane < 8 ? p.row_lse2 : p.row_dlt) + (int64_t)hk * rowsHK + rbx * 32 + 4 * (lane & 7);
-            dma16(src, base + 2 * L::kBlk);
+            const float* lb = p.row_lse2 + (int64_t)hk * rowsHK + rbx * 32;
+            const float* db = p.row_dlt + (int64_t)hk * rowsHK + rbx * 32;
+            // lanes 0-7 copy the 32 lse values, lanes 8-15 the 32 delta values
+            if (lane < 8) dma16_hidden(lb, 16 * lane, base + 2 * L::kBlk);
+            else dma16_hidden(db, 16 * (lane - 8), base + 2 * L::kBlk);
         }
     };
 
     const int eq = p.scal[0], edo = p.scal[1];
     const int ksx = load_ds_exponent(p);
-    const int first = next_needed(rb_lo);
-    if (first < rb_hi) dma_block(first, 0, kKVWaves, wave);
 
     f32x16 acc[MD];
 #pragma unroll
@@ -1138,6 +1132,38 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     unsigned char* myD = exD + kb * 4096;             // dP [4][lane] x 16 B
     unsigned char* myF = exF + kb * 4096;             // P in fp32, kept by the A wave across phase 1
 
+    // ---- the needed row blocks (those with a 64-key half not fully masked) are listed in order
+    // in LDS with both classes, entry = (rb - rb_lo) | class(first 64 keys) << 24 |
+    // class(last 64 keys) << 28, so that a wave finds its next block with one early LDS read
+    // instead of searching the class rows before each barrier. The host splits the rows of a
+    // tile so that no workgroup has more than kMaxRB row blocks (a longer range would be cut).
+    {
+    const int c0 = rb_lo;
+    const int c1 = min(rb_hi, c0 + L::kMaxRB);
+    for (int rbx = c0 + (int)threadIdx.x; rbx < c1; rbx += kKVThreads) {
+        clsA[rbx - c0] = (unsigned char)mask_class(p, hk, rbx, 2 * kvt);
+        clsB[rbx - c0] = (unsigned char)(2 * kvt + 1 < p.KT ? mask_class(p, hk, rbx, 2 * kvt + 1) : kMaskDead);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int cnt = 0;
+        for (int b0 = c0; b0 < c1; b0 += 64) {
+            const int rbx = b0 + lane;
+            const uint32_t ca = rbx < c1 ? clsA[rbx - c0] : (uint32_t)kMaskDead;
+            const uint32_t cb = rbx < c1 ? clsB[rbx - c0] : (uint32_t)kMaskDead;
+            const bool need = ca != (uint32_t)kMaskDead || cb != (uint32_t)kMaskDead;
+            const unsigned long long m = __ballot(need);
+            if (need) sched[cnt + __popcll(m & ((1ull << lane) - 1ull))] = (uint32_t)(rbx - c0) | (ca << 24) | (cb << 28);
+            cnt += __popcll(m);
+        }
+        if (lane == 0) *nsched = cnt;
+    }
+    __syncthreads();
+    const int n = __builtin_amdgcn_readfirstlane(*nsched);
+    if (n > 0) {
+    uint32_t ent = __builtin_amdgcn_readfirstlane(sched[0]);
+    dma_block(c0 + (int)(ent & 0xffffffu), 0, kKVWaves, wave);
+
     if (role == 0) {
         // ================= A waves: S, P, then dS and dK
         const float sc2 = fabsf(p.scale) * ldexpf(1.0f, -eq) * kLog2e;   // q carries the sign
@@ -1145,11 +1171,12 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
         // fp16 for the B wave; dS = P (dP - delta) 2^-ks = image (dP - delta) 2^(-ks-15)
         const float dsf = ldexpf(1.0f, -ksx - kPScaleLog2);
         int buf = 0;
-        for (int rb = first; rb < rb_hi;) {
-            const int rbn = next_needed(rb + 1);
-            const int cls = half_class(rb, kb >> 1);
+        for (int k = 0; k < n; ++k) {
+            const int rb = c0 + (int)(ent & 0xffffffu);
+            const int cls = (int)(ent >> (24 + 4 * (kb >> 1))) & 0xf;
             wait_all_mem();
             __syncthreads();   // X: block rb landed in buffer `buf`; the exchange is free
+            const uint32_t nxt = sched[k + 1 < n ? k + 1 : k];   // next entry, used after the products
             const unsigned char* tq = work + buf * L::kBuf;
             const float* lrow = (const float*)(tq + 2 * L::kBlk);
             const float* drow = lrow + 32;
@@ -1158,7 +1185,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) sa[v] = 0.0f;
                 mfma_prio_hi();
-                rows_chain_x<D, 1>(tq, bkv, sa, rw);
+                rows_chain_pf<D, 2>(tq, bkv, sa, rw);
                 mfma_prio_lo();
                 if (cls == kMaskMixed) {
                     // mask terms staged through the wave's fp32 P slot by a rolled loop, so the
@@ -1218,27 +1245,28 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                     }
                 }
                 mfma_prio_hi();
-                cols_acc_x<D>(tq, bs, acc, cw);
+                cols_acc_pf<D>(tq, bs, acc, cw);
                 mfma_prio_lo();
             }
-            rb = rbn;
+            ent = __builtin_amdgcn_readfirstlane(nxt);
             buf ^= 1;
         }
     } else {
         // ================= B waves: dP, then dV
         int buf = 0;
-        for (int rb = first; rb < rb_hi;) {
-            const int rbn = next_needed(rb + 1);
-            const int cls = half_class(rb, kb >> 1);
+        for (int k = 0; k < n; ++k) {
+            const int rb = c0 + (int)(ent & 0xffffffu);
+            const int cls = (int)(ent >> (24 + 4 * (kb >> 1))) & 0xf;
             wait_all_mem();
             __syncthreads();   // X
+            const uint32_t nxt = sched[k + 1 < n ? k + 1 : k];   // next entry, used after the products
             const unsigned char* tq = work + buf * L::kBuf;
             if (cls != kMaskDead) {
                 f32x16 pa;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) pa[v] = 0.0f;
                 mfma_prio_hi();
-                rows_chain_x<D, 1>(tq + L::kBlk, bkv, pa, rw);
+                rows_chain_pf<D, 2>(tq + L::kBlk, bkv, pa, rw);
                 mfma_prio_lo();
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
@@ -1247,18 +1275,19 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                 }
             }
             // the next block's DMA, queued while the A wave forms P
-            if (rbn < rb_hi) dma_block(rbn, buf ^ 1, 4, kb);
+            if (k + 1 < n) dma_block(c0 + (int)(__builtin_amdgcn_readfirstlane(nxt) & 0xffffffu), buf ^ 1, 4, kb);
             lds_barrier();     // Y
             if (cls != kMaskDead) {
                 const f16x8 bp[2] = {*(const f16x8*)(myP + lane * 16), *(const f16x8*)(myP + 1024 + lane * 16)};
                 mfma_prio_hi();
-                cols_acc_x<D, true>(tq + L::kBlk, bp, acc, cw);
+                cols_acc_pf<D>(tq + L::kBlk, bp, acc, cw);
                 mfma_prio_lo();
             }
-            rb = rbn;
+            ent = __builtin_amdgcn_readfirstlane(nxt);
             buf ^= 1;
         }
     }
+    } }   // rows listed
     if (!key_ok) return;
     const float fac = role == 0 ? fabsf(p.scale) * ldexpf(1.0f, ksx - eq - edo) : ldexpf(1.0f, -kPScaleLog2 - edo);
     float* dst = split ? p.kv_part + ((((int64_t)(tile - p.kv_full) * p.kv_split + part) * 2 + role) * kKVKeys +

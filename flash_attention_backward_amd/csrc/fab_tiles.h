@@ -102,6 +102,24 @@ FAB_DEV void dma16(const void* gsrc, void* lds_wave_base) {
     __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
 }
 
+// The same copy from a uniform base plus a per-lane 32-bit byte offset, written out so that the
+// compiler does not see it. The compiler makes every transpose read wait for all LDS DMA it
+// knows to be in flight; a copy issued here stays in flight across them. The caller waits for
+// it explicitly (wait_all_mem) before any read of its destination, and never reads or writes
+// that destination while it is in flight. M0 is saved and restored around the copy.
+FAB_DEV void dma16_hidden(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
+    int keep;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(keep)
+        : "v"(voff), "s"(sbase), "s"(lds_wave_base)
+        : "memory");
+}
+
 // Wait for this wave's outstanding memory operations (DMA included) and make the compiler
 // assume LDS may have changed.
 FAB_DEV void wait_all_mem() {
@@ -583,6 +601,22 @@ FAB_DEV void rows_chain_x(const unsigned char* t, const f16x8* b, f32x16& acc, c
     }
 }
 
+// rows_chain_x with the reads held PF steps ahead of their products (a scheduling barrier
+// after each product keeps the scheduler from sinking them next to their use)
+template <int D, int PF>
+FAB_DEV void rows_chain_pf(const unsigned char* t, const f16x8* b, f32x16& acc, const RowWalkX& w) {
+    constexpr int KS = D / 16, NB = PF + 1;
+    f16x8 r[NB];
+#pragma unroll
+    for (int s = 0; s < PF; ++s) r[s] = *(const f16x8*)(t + row_addr(w, gray(s)));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        if (s + PF < KS) r[(s + PF) % NB] = *(const f16x8*)(t + row_addr(w, gray(s + PF)));
+        acc = mfma32(r[s % NB], b[gray(s)], acc);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // The four transpose reads of one cols step (rows 0..15 and 16..31 of the tile at LDS byte
 // address `t`, offsets a0 and a1) in one statement that also waits for them. Written out
 // because the compiler holds a transpose-read builtin back until every LDS DMA the wave has in
@@ -627,6 +661,31 @@ FAB_DEV void cols_acc_x(const unsigned char* t, const f16x8 b[2], f32x16* acc, c
         }
         acc[md] = mfma32(r0, b[0], acc[md]);
         acc[md] = mfma32(r1, b[1], acc[md]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// cols_acc with the compact walk, each step's transpose reads issued one step ahead (two
+// fragment sets in flight). The wave must have no LDS DMA in flight that the compiler knows of.
+template <int D>
+FAB_DEV void cols_acc_pf(const unsigned char* t, const f16x8 b[2], f32x16* acc, const ColWalkX& w) {
+    constexpr int MD = D / 32;
+    constexpr int RH = 16 * D * 2;
+    f16x8 r0[2], r1[2];
+    auto rd = [&](int s) {
+        const int md = gray(s);
+        const int a0 = w.base[0] + 64 * (md ^ w.ee[0]);
+        const int a1 = w.base[1] + 64 * (md ^ w.ee[1]);
+        r0[s & 1] = join(tr_read(t + a0), tr_read(t + a1));
+        r1[s & 1] = join(tr_read(t + a0 + RH), tr_read(t + a1 + RH));
+    };
+    rd(0);
+#pragma unroll
+    for (int s = 0; s < MD; ++s) {
+        if (s + 1 < MD) rd(s + 1);
+        const int md = gray(s);
+        acc[md] = mfma32(r0[s & 1], b[0], acc[md]);
+        acc[md] = mfma32(r1[s & 1], b[1], acc[md]);
         __builtin_amdgcn_sched_barrier(0);
     }
 }

@@ -48,6 +48,13 @@ RAGGED = [
          masked_rows=[(0, i) for i in range(9)]),
     dict(name="near_const_v_bf16", D=128, H=4, Hkv=1, N=64, M=256, mask="tail", v_offset=1.0,
          v_spread=1e-3, q_type="bf16", d_type="bf16", k_type="bf16", v_type="bf16"),
+    # fully masked 32-row blocks (3 and 10) between live ones: the key side skips them
+    dict(name="dead_row_blocks", D=128, H=2, Hkv=1, N=200, M=300, mask="random",
+         masked_rows=[(0, i) for i in list(range(48, 64)) + list(range(160, 176))],
+         k_type="q8_0", v_type="q8_0"),
+    # 132000 rows over one KV head (4125 row blocks): every key tile is split into row ranges
+    dict(name="long_rows_split", D=64, H=8, Hkv=1, N=16500, M=40, mask="none",
+         k_type="q8_0", v_type="q8_0"),
 ]
 
 
