@@ -1008,10 +1008,10 @@ struct KVLds {
     static constexpr int kExP = 4 * 2048;                                // [kb][rh][lane] P images
     static constexpr int kExD = 4 * 4096;                                // [kb][4][lane] dP, fp32
     static constexpr int kExF = 4 * 4096;                                // [kb][4][lane] P, fp32 (A only)
-    static constexpr int kWork = 2 * kBuf + kExP + kExD + kExF;
+    static constexpr int kWork = 3 * kBuf + kExP + kExD + kExF;
     static constexpr int kRaw = RawTile<D, kQTileKeys>::kBytes;
     static constexpr int kSetup = 2 * kQTileKeys * D * 2 + 2 * kRaw;     // K, V half tiles + bytes
-    static constexpr int kMaxRB = 4096;                                  // row blocks listed per workgroup
+    static constexpr int kMaxRB = 2048;                                  // row blocks listed per workgroup
     static constexpr int kTail = 6 * kMaxRB + 16;                        // list, two class rows, count
     static constexpr int kBytes = (kSetup > kWork ? kSetup : kWork) + kTail;
 };
@@ -1024,7 +1024,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     constexpr int NI = L::kBlk / 1024;                // 64-lane x 16-byte DMA instructions per tensor
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
     unsigned char* work = lds;                        // setup scratch, then buffers + exchange
-    unsigned char* exP = work + 2 * L::kBuf;
+    unsigned char* exP = work + 3 * L::kBuf;
     unsigned char* exD = exP + L::kExP;
     unsigned char* exF = exD + L::kExD;
     uint32_t* sched = (uint32_t*)(lds + L::kBytes - L::kTail);          // needed row blocks of a chunk
@@ -1097,6 +1097,13 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     auto dma_block = [&](int rbx, int b, int nw, int wi) {
         const uint32_t base = lds_addr(work + b * L::kBuf);
         const int64_t blk = (int64_t)rbx * L::kBlk;
+        if (wi == nw - 1 && lane < 16) {
+            // first in the batch: lanes 0-7 copy the 32 lse values, lanes 8-15 the 32 delta values
+            const float* lb = p.row_lse2 + (int64_t)hk * rowsHK + rbx * 32;
+            const float* db = p.row_dlt + (int64_t)hk * rowsHK + rbx * 32;
+            if (lane < 8) dma16_hidden(lb, 16 * lane, base + 2 * L::kBlk);
+            else dma16_hidden(db, 16 * (lane - 8), base + 2 * L::kBlk);
+        }
 #pragma unroll
         for (int k = 0; k < 2 * NI; ++k) {
             const int ins = wi + nw * k;             // uniform
@@ -1108,13 +1115,6 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
             const uint32_t off = (uint32_t)((row * D + 8 * swz_chunk<D>(row, pc)) * 2);
             const char* sb = (ten ? dbase : qbase) + blk + (int64_t)(ii / IP) * (16 * D * 2);
             dma16_hidden(sb, off, base + ten * L::kBlk + ii * 1024);
-        }
-        if (wi == nw - 1 && lane < 16) {
-            const float* lb = p.row_lse2 + (int64_t)hk * rowsHK + rbx * 32;
-            const float* db = p.row_dlt + (int64_t)hk * rowsHK + rbx * 32;
-            // lanes 0-7 copy the 32 lse values, lanes 8-15 the 32 delta values
-            if (lane < 8) dma16_hidden(lb, 16 * lane, base + 2 * L::kBlk);
-            else dma16_hidden(db, 16 * (lane - 8), base + 2 * L::kBlk);
         }
     };
 
@@ -1162,7 +1162,14 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     const int n = __builtin_amdgcn_readfirstlane(*nsched);
     if (n > 0) {
     uint32_t ent = __builtin_amdgcn_readfirstlane(sched[0]);
-    dma_block(c0 + (int)(ent & 0xffffffu), 0, kKVWaves, wave);
+    // Row blocks go through three buffers, each copied two blocks ahead of its use. The A waves
+    // copy block 0 and then wait for all of their copies at every block barrier. The B waves
+    // copy block 1 and, in each iteration k, block k+2 (past the end of the list: block k
+    // again, into the free buffer), so that at every block barrier exactly their newest batch,
+    // D/32 instructions, stays in flight (the wave that also copies lse/delta issues 2 more,
+    // first in its batch, so they are the ones waited for early).
+    if (role == 0) dma_block(c0 + (int)(ent & 0xffffffu), 0, 4, kb);
+    else if (n > 1) dma_block(c0 + (int)(__builtin_amdgcn_readfirstlane(sched[1]) & 0xffffffu), 1, 4, kb);
 
     if (role == 0) {
         // ================= A waves: S, P, then dS and dK
@@ -1170,14 +1177,13 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
         // the exponential gives the P image p * 2^15 (the stored lse carries the 15), rounded to
         // fp16 for the B wave; dS = P (dP - delta) 2^-ks = image (dP - delta) 2^(-ks-15)
         const float dsf = ldexpf(1.0f, -ksx - kPScaleLog2);
-        int buf = 0;
+        int bi = 0;
         for (int k = 0; k < n; ++k) {
             const int rb = c0 + (int)(ent & 0xffffffu);
             const int cls = (int)(ent >> (24 + 4 * (kb >> 1))) & 0xf;
-            wait_all_mem();
-            __syncthreads();   // X: block rb landed in buffer `buf`; the exchange is free
+            dma_barrier<0>();   // X: block rb landed in buffer bi; the exchange is free
             const uint32_t nxt = sched[k + 1 < n ? k + 1 : k];   // next entry, used after the products
-            const unsigned char* tq = work + buf * L::kBuf;
+            const unsigned char* tq = work + bi * L::kBuf;
             const float* lrow = (const float*)(tq + 2 * L::kBlk);
             const float* drow = lrow + 32;
             if (cls != kMaskDead) {
@@ -1185,7 +1191,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) sa[v] = 0.0f;
                 mfma_prio_hi();
-                rows_chain_pf<D, 2>(tq, bkv, sa, rw);
+                rows_chain_x<D, 1>(tq, bkv, sa, rw);
                 mfma_prio_lo();
                 if (cls == kMaskMixed) {
                     // mask terms staged through the wave's fp32 P slot by a rolled loop, so the
@@ -1249,24 +1255,23 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                 mfma_prio_lo();
             }
             ent = __builtin_amdgcn_readfirstlane(nxt);
-            buf ^= 1;
+            bi = bi == 2 ? 0 : bi + 1;
         }
     } else {
         // ================= B waves: dP, then dV
-        int buf = 0;
+        int bi = 0;
         for (int k = 0; k < n; ++k) {
             const int rb = c0 + (int)(ent & 0xffffffu);
             const int cls = (int)(ent >> (24 + 4 * (kb >> 1))) & 0xf;
-            wait_all_mem();
-            __syncthreads();   // X
+            dma_barrier<D / 32>();   // X: block rb landed; the copy of block k+1 stays in flight
             const uint32_t nxt = sched[k + 1 < n ? k + 1 : k];   // next entry, used after the products
-            const unsigned char* tq = work + buf * L::kBuf;
+            const unsigned char* tq = work + bi * L::kBuf;
             if (cls != kMaskDead) {
                 f32x16 pa;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) pa[v] = 0.0f;
                 mfma_prio_hi();
-                rows_chain_pf<D, 2>(tq + L::kBlk, bkv, pa, rw);
+                rows_chain_x<D, 1>(tq + L::kBlk, bkv, pa, rw);
                 mfma_prio_lo();
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
@@ -1274,8 +1279,9 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                     *(f32x4*)(myD + (b * 64 + lane) * 16) = o;
                 }
             }
-            // the next block's DMA, queued while the A wave forms P
-            if (k + 1 < n) dma_block(c0 + (int)(__builtin_amdgcn_readfirstlane(nxt) & 0xffffffu), buf ^ 1, 4, kb);
+            // the copy of the block two ahead (into the buffer of block k-1), queued while the A wave forms P
+            dma_block(k + 2 < n ? c0 + (int)(__builtin_amdgcn_readfirstlane(sched[k + 2]) & 0xffffffu) : rb,
+                      bi == 0 ? 2 : bi - 1, 4, kb);
             lds_barrier();     // Y
             if (cls != kMaskDead) {
                 const f16x8 bp[2] = {*(const f16x8*)(myP + lane * 16), *(const f16x8*)(myP + 1024 + lane * 16)};
@@ -1284,10 +1290,11 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                 mfma_prio_lo();
             }
             ent = __builtin_amdgcn_readfirstlane(nxt);
-            buf ^= 1;
+            bi = bi == 2 ? 0 : bi + 1;
         }
     }
     } }   // rows listed
+    wait_all_mem();   // no copy is left in flight when the wave ends
     if (!key_ok) return;
     const float fac = role == 0 ? fabsf(p.scale) * ldexpf(1.0f, ksx - eq - edo) : ldexpf(1.0f, -kPScaleLog2 - edo);
     float* dst = split ? p.kv_part + ((((int64_t)(tile - p.kv_full) * p.kv_split + part) * 2 + role) * kKVKeys +

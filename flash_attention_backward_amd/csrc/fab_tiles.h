@@ -137,6 +137,17 @@ FAB_DEV void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier once this wave's LDS operations, and all but its V most recent vector memory
+// operations, have completed: the V most recent are LDS DMA of a later buffer, left in flight.
+template <int V>
+FAB_DEV void dma_barrier() {
+    static_assert(V >= 0 && V < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4));   // vmcnt(V) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ----------------------------------------------------------------------------- q8_0 rows
 
 // q8_0 row geometry: D/32 blocks of 34 bytes; a row's bytes are staged in LDS as the
