@@ -619,7 +619,8 @@ struct W1Lds {
     static constexpr int kSetup = 2 * kQTileKeys * D * 2 + 4 * kRaw;     // K, V 64-key tiles + [2][K, V] bytes
     static constexpr int kMaxRB = 2048;                                  // row blocks per workgroup
     static constexpr int kTiles = kW1Keys / kQTileKeys;                  // 64-key class tiles
-    static constexpr int kBytes = (kSetup > kWork ? kSetup : kWork) + kTiles * kMaxRB;
+    static constexpr int kList = 4 * kMaxRB + 16;                        // needed blocks, count
+    static constexpr int kBytes = (kSetup > kWork + kList ? kSetup : kWork + kList) + kTiles * kMaxRB;
 };
 
 template <int D>
@@ -631,6 +632,10 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
     unsigned char* work = lds;
     unsigned char* recs = work + 2 * L::kBuf;                         // [3][wave][row] x 16 B
     unsigned char* cls = lds + L::kBytes - L::kTiles * L::kMaxRB;     // [tile][row block - rb0]
+    // the needed row blocks in order, entry = (rb - rb0) | class of 64-key tile t << (16 + 2t);
+    // built after the setup, in its region past the row-block buffers and records
+    uint32_t* list = (uint32_t*)(work + L::kWork);
+    int* nlist = (int*)(list + L::kMaxRB);
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l32 = lane & 31, g = lane >> 5;
@@ -700,10 +705,6 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
             if (tcls(rbx, t) != kMaskDead) return true;
         return false;
     };
-    auto next_needed = [&](int rbx) -> int {
-        while (rbx < rb1 && !needed(rbx)) ++rbx;
-        return rbx;
-    };
     // empty records for the rows of blocks no key of this tile sees
     for (int idx = threadIdx.x; idx < 32 * nloc; idx += kW1Threads) {
         const int rbx = rb0 + idx / 32;
@@ -714,6 +715,29 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
         p.part_d[ri] = 0.0;
         p.part_b[ri] = 0.0f;
     }
+
+    if (wave == 0) {
+        int cnt = 0;
+        for (int b0 = 0; b0 < nloc; b0 += 64) {
+            const int lr = b0 + lane;
+            uint32_t code = (uint32_t)lr;
+            bool need = false;
+            if (lr < nloc) {
+#pragma unroll
+                for (int t = 0; t < L::kTiles; ++t) {
+                    const uint32_t c = cls[t * L::kMaxRB + lr];
+                    code |= c << (16 + 2 * t);
+                    need = need || c != (uint32_t)kMaskDead;
+                }
+            }
+            const unsigned long long m = __ballot(need);
+            if (need) list[cnt + __popcll(m & ((1ull << lane) - 1ull))] = code;
+            cnt += __popcll(m);
+        }
+        if (lane == 0) *nlist = cnt;
+    }
+    __syncthreads();
+    const int n = __builtin_amdgcn_readfirstlane(*nlist);
 
     const char* qbase = (const char*)(p.qr + (int64_t)hk * rowsHK * D);
     const char* dbase = (const char*)(p.dr + (int64_t)hk * rowsHK * D);
@@ -828,10 +852,6 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
     auto put_rec = [&](int bufx, const f32x4& rec) {
         if (g == 0) *(f32x4*)(recs + bufx * L::kRec + (wave * 32 + l32) * 16) = rec;
     };
-    auto nextv = [&](int rbx) -> int {
-        const int x = next_needed(rbx + 1);
-        return x < rb1 ? x : -1;
-    };
     auto stats = [&](int rbx, int c, const f32x16& sa, const f32x16& pa) -> f32x4 {
         if (c == kMaskDead) return f32x4{neg_inf(), 0.0f, 0.0f, 0.0f};
         return fast_ok(rbx, c) ? stats_fast(sa, pa) : stats_slow(rbx, c, sa, pa);
@@ -844,30 +864,44 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
     // wave's exponentials overlap the other's matrix products. The DMA of b_(i+1) goes into the
     // buffer of cp, which no wave reads any more; the records of block b sit in buffer b%3.
     const bool early = wave < kW1Waves / 2;
-    int c0 = next_needed(rb0);
-    c0 = c0 < rb1 ? c0 : -1;
+    auto eblock = [&](uint32_t e) { return rb0 + (int)(e & 0xffffu); };
+    auto eclass = [&](uint32_t e) { return (int)(e >> (16 + 2 * mytile)) & 3; };
+    const uint32_t e0 = n > 0 ? __builtin_amdgcn_readfirstlane(list[0]) : 0u;
+    int c0 = n > 0 ? eblock(e0) : -1;
+    int k0 = n > 0 ? eclass(e0) : kMaskDead;   // this wave's class of c0
     if (c0 >= 0) dma_block(c0, 0, kW1Waves, wave);
-    int cp = -1, cpp = -1;
+    int cp = -1, cpp = -1, kp = kMaskDead;
     f32x16 ha, hp;   // early waves: products of cp
 #pragma unroll
     for (int v = 0; v < 16; ++v) ha[v] = hp[v] = 0.0f;
     for (int i = 0;; ++i) {
-        const int c1 = c0 >= 0 ? nextv(c0) : -1;
         wait_all_mem();
         __syncthreads();   // c0 landed; the records of cpp are complete
+        // the list entry of the next block: read by the early waves under their statistics, by
+        // the late waves after their products (not held across the products)
+        const int inext = i + 1 < n ? i + 1 : 0;
+        uint32_t e1 = 0;
         if (early) {
-            if (cp >= 0) put_rec((i + 2) % 3, stats(cp, tcls(cp, mytile), ha, hp));
+            const uint32_t e1v = list[inext];
+            if (cp >= 0) put_rec((i + 2) % 3, stats(cp, kp, ha, hp));
             if (cpp >= 0 && lane < 8) merge_block(cpp, recs + ((i + 1) % 3) * L::kRec, 8 * wave + lane);
+            e1 = __builtin_amdgcn_readfirstlane(e1v);
         }
         if (c0 < 0 && cp < 0) break;
+        int c1 = -1, k1 = kMaskDead;
         if (c0 >= 0) {
-            const int c = tcls(c0, mytile);
+            const int c = k0;
             // the products of a block that is dead for this wave's keys are formed too (stats
             // gives it the empty record): no zero fill, and no copy of the early waves' products
             f32x16 sa, pa;
             mfma_prio_hi();
             pair_rows_t<D, 2, L::kBlk, true>(work + (i & 1) * L::kBuf, bk, bv, sa, pa, rw);
             mfma_prio_lo();
+            if (!early) e1 = __builtin_amdgcn_readfirstlane(list[inext]);
+            if (i + 1 < n) {
+                c1 = eblock(e1);
+                k1 = eclass(e1);
+            }
             // the next block's DMA is queued by the late waves after their products (queued by
             // all waves at the barrier, the later ones stall behind the earlier ones' copies)
             if (c1 >= 0 && !early) dma_block(c1, (i + 1) & 1, kW1Waves / 2, wave - kW1Waves / 2);
@@ -880,7 +914,9 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
         }
         cpp = cp;
         cp = c0;
+        kp = k0;
         c0 = c1;
+        k0 = k1;
     }
 }
 
