@@ -1021,17 +1021,19 @@ __global__ __launch_bounds__(kThreads) void dqreduce_kernel(Params p) {
 
 // ----------------------------------------------------------------------------- key side
 
-// Workgroup: one KV head, 128 keys in 4 blocks of 32, and 8 waves: one pair per key block kb.
-//   A wave (w = kb)      K fragments of its 32 keys in registers. Per 32-row block:
-//                        S = Q K^T, P = exp(S - lse) in fp32 (its fp16 image p*2^15 goes to
-//                        LDS for the B wave); then, with dP from the B wave, dS = P (dP - delta)
-//                        in fp32 and dK^T += Q^T dS, the dS image taken straight from registers.
-//   B wave (w = 4 + kb)  V fragments in registers. Per row block: dP = dO V^T, handed to the A
-//                        wave in fp32 through LDS; then dV^T += dO^T P from the P image.
-// Two barriers per row block: phase 1 runs S (A) and dP (B) side by side, phase 2 runs dK (A)
-// and dV (B). The q and dO row blocks (fp16, row-major, with their lse/delta) are copied
-// HBM -> LDS by DMA once per workgroup and double-buffered; the copy of the next block is
-// queued at the start of each block. Every wave stays within 256 registers.
+// Workgroup: one KV head, 128 keys in 4 blocks of 32, and 8 waves: one pair per key block kb,
+// both waves of a pair on the same SIMD.
+//   X wave (w = kb)      K fragments of its 32 keys in registers. Per 32-row block: S = Q K^T,
+//                        P = exp(S - lse) in fp32 (its image p*2^15 goes to LDS in fp32 for the
+//                        Y wave), then dV^T += dO^T P from its own fp16 image.
+//   Y wave (w = 4 + kb)  V fragments in registers. Per row block: dK^T += Q^T dS of the previous
+//                        block (its dS kept in registers, its q rows still in their buffer),
+//                        dP = dO V^T; then, with P from the X wave, dS = P (dP - delta) in fp32.
+// Two barriers per row block. Neither wave waits for the other's products: the X wave's
+// exponentials run beside the Y wave's dK and dP products, the Y wave's dS arithmetic beside
+// the X wave's dV products. The q and dO row blocks (fp16, row-major, with their lse/delta) are
+// copied HBM -> LDS by DMA once per workgroup through three buffers, each two blocks ahead.
+// Every wave stays within 256 registers.
 // S = Q K^T puts one key per lane column and 16 rows per lane: the layout of the second
 // operand of the dK/dV products, whose first operands are transpose reads of the row blocks.
 constexpr int kKVWaves = 8;
@@ -1041,10 +1043,9 @@ template <int D>
 struct KVLds {
     static constexpr int kBlk = 32 * D * 2;                              // bytes of a 32-row block
     static constexpr int kBuf = 2 * kBlk + 256;                          // q, dO, 32 lse, 32 delta
-    static constexpr int kExP = 4 * 2048;                                // [kb][rh][lane] P images
-    static constexpr int kExD = 4 * 4096;                                // [kb][4][lane] dP, fp32
-    static constexpr int kExF = 4 * 4096;                                // [kb][4][lane] P, fp32 (A only)
-    static constexpr int kWork = 3 * kBuf + kExP + kExD + kExF;
+    static constexpr int kExF = 4 * 4096;                                // [kb][4][lane] P image, fp32
+    static constexpr int kExD = 4 * 4096;                                // [kb][4][lane] dP, fp32 (Y only)
+    static constexpr int kWork = 3 * kBuf + kExF + kExD;
     static constexpr int kRaw = RawTile<D, kQTileKeys>::kBytes;
     static constexpr int kSetup = 2 * kQTileKeys * D * 2 + 2 * kRaw;     // K, V half tiles + bytes
     static constexpr int kMaxRB = 2048;                                  // row blocks listed per workgroup
@@ -1060,9 +1061,8 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     constexpr int NI = L::kBlk / 1024;                // 64-lane x 16-byte DMA instructions per tensor
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
     unsigned char* work = lds;                        // setup scratch, then buffers + exchange
-    unsigned char* exP = work + 3 * L::kBuf;
-    unsigned char* exD = exP + L::kExP;
-    unsigned char* exF = exD + L::kExD;
+    unsigned char* exF = work + 3 * L::kBuf;             // P images from the X to the Y waves
+    unsigned char* exD = exF + L::kExF;                  // dP parked by the Y waves across the barrier
     uint32_t* sched = (uint32_t*)(lds + L::kBytes - L::kTail);          // needed row blocks of a chunk
     unsigned char* clsA = (unsigned char*)(sched + L::kMaxRB);         // class of (row block, first 64 keys)
     unsigned char* clsB = clsA + L::kMaxRB;                             // class of (row block, last 64 keys)
@@ -1162,11 +1162,10 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     for (int md = 0; md < MD; ++md)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[md][v] = 0.0f;
-    const RowWalkX rw = make_row_walk_x<D>(lane);
-    const ColWalkX cw = make_col_walk_x<D>(lane);
-    unsigned char* myP = exP + kb * 2048;             // P image [rh][lane] x 16 B
-    unsigned char* myD = exD + kb * 4096;             // dP [4][lane] x 16 B
-    unsigned char* myF = exF + kb * 4096;             // P in fp32, kept by the A wave across phase 1
+    const RowWalkX rw0 = make_row_walk_x<D>(lane);
+    const ColWalkX cw0 = make_col_walk_x<D>(lane);
+    unsigned char* myF = exF + kb * 4096;             // the pair's P image in fp32 [4][lane] x 16 B
+    unsigned char* myD = exD + kb * 4096;             // the Y wave's dP [4][lane] x 16 B
 
     // ---- the needed row blocks (those with a 64-key half not fully masked) are listed in order
     // in LDS with both classes, entry = (rb - rb_lo) | class(first 64 keys) << 24 |
@@ -1208,20 +1207,27 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     else if (n > 1) dma_block(c0 + (int)(__builtin_amdgcn_readfirstlane(sched[1]) & 0xffffffu), 1, 4, kb);
 
     if (role == 0) {
-        // ================= A waves: S, P, then dS and dK
+        // ================= X waves (K fragments): S, P, then dV += P^T dO with their own P
         const float sc2 = fabsf(p.scale) * ldexpf(1.0f, -eq) * kLog2e;   // q carries the sign
-        // the exponential gives the P image p * 2^15 (the stored lse carries the 15), rounded to
-        // fp16 for the B wave; dS = P (dP - delta) 2^-ks = image (dP - delta) 2^(-ks-15)
-        const float dsf = ldexpf(1.0f, -ksx - kPScaleLog2);
         int bi = 0;
         for (int k = 0; k < n; ++k) {
             const int rb = c0 + (int)(ent & 0xffffffu);
             const int cls = (int)(ent >> (24 + 4 * (kb >> 1))) & 0xf;
-            dma_barrier<0>();   // X: block rb landed in buffer bi; the exchange is free
+            dma_barrier<0>();   // X: block rb landed in buffer bi; the Y wave has read the last P
             const uint32_t nxt = sched[k + 1 < n ? k + 1 : k];   // next entry, used after the products
             const unsigned char* tq = work + bi * L::kBuf;
+            // the walks pass through an opaque move here, so that the per-step offsets are formed
+            // in the loop rather than hoisted out of it and held (the registers are short)
+            ColWalkX cw;
+            cw.base[0] = opaque(cw0.base[0]);
+            cw.base[1] = opaque(cw0.base[1]);
+            cw.ee[0] = opaque(cw0.ee[0]);
+            cw.ee[1] = opaque(cw0.ee[1]);
+            RowWalkX rw;
+            rw.base = opaque(rw0.base);
+            rw.c = opaque(rw0.c);
             const float* lrow = (const float*)(tq + 2 * L::kBlk);
-            const float* drow = lrow + 32;
+            f16x8 bp[2];
             if (cls != kMaskDead) {
                 f32x16 sa;
 #pragma unroll
@@ -1247,10 +1253,10 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                         ((float*)(myF + (b * 64 + lane) * 16))[u] = mv;
                     }
                 }
-                // the image p * 2^15; 0 for a dead row (lse2 = +inf) or a masked key. Without a
-                // mask, a key past M (zero K row) gets an image too: it only reaches that key's
-                // own dK and dV columns, which are never written.
-                f16x8 bp[2];
+                // the image p * 2^15 (the stored lse carries the 15): rounded to fp16 for the dV
+                // products here, in fp32 to the Y wave for dS. 0 for a dead row (lse2 = +inf) or
+                // a masked key. Without a mask, a key past M (zero K row) gets an image too: it
+                // only reaches that key's own dK and dV columns, which are never written.
                 auto image = [&](bool mixed) {
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
@@ -1269,12 +1275,69 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                 };
                 if (cls == kMaskMixed) image(true);
                 else image(false);
-#pragma unroll
-                for (int rh = 0; rh < 2; ++rh) *(f16x8*)(myP + rh * 1024 + lane * 16) = bp[rh];
             }
-            lds_barrier();     // Y: P and dP exchanged (the next block's DMA stays in flight)
+            lds_barrier();     // Y: P published for the Y wave (the copies in flight stay so)
             if (cls != kMaskDead) {
-                f16x8 bs[2];
+                mfma_prio_hi();
+                cols_acc_pf<D>(tq + L::kBlk, bp, acc, cw);
+                mfma_prio_lo();
+            }
+            ent = __builtin_amdgcn_readfirstlane(nxt);
+            bi = bi == 2 ? 0 : bi + 1;
+        }
+    } else {
+        // ================= Y waves (V fragments): dK of the previous block, dP, then dS
+        // dS = P (dP - delta) 2^-ks = image (dP - delta) 2^(-ks-15); it is kept in registers for
+        // the dK products of the next iteration, whose q rows stay in their buffer until then
+        const float dsf = ldexpf(1.0f, -ksx - kPScaleLog2);
+        int bi = 0, bprev = 0;
+        bool live = false;    // the block in bprev needs its dK products (bs holds its dS)
+        f16x8 bs[2];
+        for (int k = 0; k < n; ++k) {
+            const int rb = c0 + (int)(ent & 0xffffffu);
+            const int cls = (int)(ent >> (24 + 4 * (kb >> 1))) & 0xf;
+            dma_barrier<D / 32>();   // X: block rb landed; the copy of block k+1 stays in flight
+            const uint32_t nxt = sched[k + 1 < n ? k + 1 : k];   // next entry, used after the products
+            const unsigned char* tq = work + bi * L::kBuf;
+            // the walks pass through an opaque move here, so that the per-step offsets are formed
+            // in the loop rather than hoisted out of it and held (the registers are short)
+            ColWalkX cw;
+            cw.base[0] = opaque(cw0.base[0]);
+            cw.base[1] = opaque(cw0.base[1]);
+            cw.ee[0] = opaque(cw0.ee[0]);
+            cw.ee[1] = opaque(cw0.ee[1]);
+            RowWalkX rw;
+            rw.base = opaque(rw0.base);
+            rw.c = opaque(rw0.c);
+            if (live) {
+                mfma_prio_hi();
+                cols_acc_x<D>(work + bprev * L::kBuf, bs, acc, cw);
+                mfma_prio_lo();
+            }
+            if (cls != kMaskDead) {
+                f32x16 pa;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) pa[v] = 0.0f;
+                mfma_prio_hi();
+                rows_chain_x<D, 1>(tq + L::kBlk, bkv, pa, rw);
+                mfma_prio_lo();
+                // parked in LDS across the barrier and the copy (registers are short there)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const f32x4 o = {pa[4 * b], pa[4 * b + 1], pa[4 * b + 2], pa[4 * b + 3]};
+                    *(f32x4*)(myD + (b * 64 + lane) * 16) = o;
+                }
+            }
+            lds_barrier();     // Y: P of block rb published; the buffer of block k-1 is read
+            // the copy of the block two ahead, into the buffer of block k-1 (past the end of the
+            // list: block k again)
+            dma_block(k + 2 < n ? c0 + (int)(__builtin_amdgcn_readfirstlane(sched[k + 2]) & 0xffffffu) : rb,
+                      bi == 0 ? 2 : bi - 1, 4, kb);
+            // dS is formed for a dead block too (and then not used): assigned on every path, the
+            // previous block's dS is dead once its products are issued
+            live = cls != kMaskDead;
+            {
+                const float* drow = (const float*)(tq + 2 * L::kBlk) + 32;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const f32x4 dp4 = *(const f32x4*)(myD + (b * 64 + lane) * 16);
@@ -1286,56 +1349,25 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                         bs[v >> 3][v & 7] = (_Float16)(p4[u] * (dp4[u] - d4[u]) * dsf);
                     }
                 }
-                mfma_prio_hi();
-                cols_acc_pf<D>(tq, bs, acc, cw);
-                mfma_prio_lo();
             }
+            bprev = bi;
             ent = __builtin_amdgcn_readfirstlane(nxt);
             bi = bi == 2 ? 0 : bi + 1;
         }
-    } else {
-        // ================= B waves: dP, then dV
-        int bi = 0;
-        for (int k = 0; k < n; ++k) {
-            const int rb = c0 + (int)(ent & 0xffffffu);
-            const int cls = (int)(ent >> (24 + 4 * (kb >> 1))) & 0xf;
-            dma_barrier<D / 32>();   // X: block rb landed; the copy of block k+1 stays in flight
-            const uint32_t nxt = sched[k + 1 < n ? k + 1 : k];   // next entry, used after the products
-            const unsigned char* tq = work + bi * L::kBuf;
-            if (cls != kMaskDead) {
-                f32x16 pa;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) pa[v] = 0.0f;
-                mfma_prio_hi();
-                rows_chain_x<D, 1>(tq + L::kBlk, bkv, pa, rw);
-                mfma_prio_lo();
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const f32x4 o = {pa[4 * b], pa[4 * b + 1], pa[4 * b + 2], pa[4 * b + 3]};
-                    *(f32x4*)(myD + (b * 64 + lane) * 16) = o;
-                }
-            }
-            // the copy of the block two ahead (into the buffer of block k-1), queued while the A wave forms P
-            dma_block(k + 2 < n ? c0 + (int)(__builtin_amdgcn_readfirstlane(sched[k + 2]) & 0xffffffu) : rb,
-                      bi == 0 ? 2 : bi - 1, 4, kb);
-            lds_barrier();     // Y
-            if (cls != kMaskDead) {
-                const f16x8 bp[2] = {*(const f16x8*)(myP + lane * 16), *(const f16x8*)(myP + 1024 + lane * 16)};
-                mfma_prio_hi();
-                cols_acc_pf<D>(tq + L::kBlk, bp, acc, cw);
-                mfma_prio_lo();
-            }
-            ent = __builtin_amdgcn_readfirstlane(nxt);
-            bi = bi == 2 ? 0 : bi + 1;
+        if (live) {
+            mfma_prio_hi();
+            cols_acc_pf<D>(work + bprev * L::kBuf, bs, acc, cw0);
+            mfma_prio_lo();
         }
     }
     } }   // rows listed
     wait_all_mem();   // no copy is left in flight when the wave ends
     if (!key_ok) return;
-    const float fac = role == 0 ? fabsf(p.scale) * ldexpf(1.0f, ksx - eq - edo) : ldexpf(1.0f, -kPScaleLog2 - edo);
-    float* dst = split ? p.kv_part + ((((int64_t)(tile - p.kv_full) * p.kv_split + part) * 2 + role) * kKVKeys +
+    const int outk = role == 0 ? 1 : 0;               // X waves hold dV, Y waves dK
+    const float fac = outk == 0 ? fabsf(p.scale) * ldexpf(1.0f, ksx - eq - edo) : ldexpf(1.0f, -kPScaleLog2 - edo);
+    float* dst = split ? p.kv_part + ((((int64_t)(tile - p.kv_full) * p.kv_split + part) * 2 + outk) * kKVKeys +
                                       32 * kb + l32) * D
-                       : (role == 0 ? p.dk : p.dv) + ((int64_t)hk * p.M + myj) * D;
+                       : (outk == 0 ? p.dk : p.dv) + ((int64_t)hk * p.M + myj) * D;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
