@@ -612,49 +612,12 @@ FAB_DEV void rows_chain_x(const unsigned char* t, const f16x8* b, f32x16& acc, c
     }
 }
 
-// rows_chain_x with the reads held PF steps ahead of their products (a scheduling barrier
-// after each product keeps the scheduler from sinking them next to their use)
-template <int D, int PF>
-FAB_DEV void rows_chain_pf(const unsigned char* t, const f16x8* b, f32x16& acc, const RowWalkX& w) {
-    constexpr int KS = D / 16, NB = PF + 1;
-    f16x8 r[NB];
-#pragma unroll
-    for (int s = 0; s < PF; ++s) r[s] = *(const f16x8*)(t + row_addr(w, gray(s)));
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        if (s + PF < KS) r[(s + PF) % NB] = *(const f16x8*)(t + row_addr(w, gray(s + PF)));
-        acc = mfma32(r[s % NB], b[gray(s)], acc);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// The four transpose reads of one cols step (rows 0..15 and 16..31 of the tile at LDS byte
-// address `t`, offsets a0 and a1) in one statement that also waits for them. Written out
-// because the compiler holds a transpose-read builtin back until every LDS DMA the wave has in
-// flight has landed; the statement's results are complete when it ends, so nothing reads them
-// early.
-template <int RH>
-FAB_DEV void tr_read_quad(uint32_t t, int a0, int a1, f16x8& r0, f16x8& r1) {
-    s16x4 x0, x1, x2, x3;
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %4\n\t"
-        "ds_read_b64_tr_b16 %1, %5\n\t"
-        "ds_read_b64_tr_b16 %2, %4 offset:%6\n\t"
-        "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
-        : "v"(t + (uint32_t)a0), "v"(t + (uint32_t)a1), "n"(RH));
-    r0 = join(__builtin_bit_cast(f16x4, x0), __builtin_bit_cast(f16x4, x1));
-    r1 = join(__builtin_bit_cast(f16x4, x2), __builtin_bit_cast(f16x4, x3));
-}
-
 FAB_DEV uint32_t lds_addr(const unsigned char* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
 }
 
-// cols_acc with the compact walk, reads right before use; ASYNC: the wave has LDS DMA in
-// flight, so the reads go through tr_read_quad
-template <int D, bool ASYNC = false>
+// cols_acc with the compact walk, reads right before use (8 registers of fragments)
+template <int D>
 FAB_DEV void cols_acc_x(const unsigned char* t, const f16x8 b[2], f32x16* acc, const ColWalkX& w) {
     constexpr int MD = D / 32;
     constexpr int RH = 16 * D * 2;
@@ -663,13 +626,8 @@ FAB_DEV void cols_acc_x(const unsigned char* t, const f16x8 b[2], f32x16* acc, c
         const int md = gray(s);
         const int a0 = w.base[0] + 64 * (md ^ w.ee[0]);
         const int a1 = w.base[1] + 64 * (md ^ w.ee[1]);
-        f16x8 r0, r1;
-        if (ASYNC) {
-            tr_read_quad<RH>(lds_addr(t), a0, a1, r0, r1);
-        } else {
-            r0 = join(tr_read(t + a0), tr_read(t + a1));
-            r1 = join(tr_read(t + a0 + RH), tr_read(t + a1 + RH));
-        }
+        const f16x8 r0 = join(tr_read(t + a0), tr_read(t + a1));
+        const f16x8 r1 = join(tr_read(t + a0 + RH), tr_read(t + a1 + RH));
         acc[md] = mfma32(r0, b[0], acc[md]);
         acc[md] = mfma32(r1, b[1], acc[md]);
         __builtin_amdgcn_sched_barrier(0);
