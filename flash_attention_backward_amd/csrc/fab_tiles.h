@@ -721,39 +721,32 @@ FAB_DEV void pair_rows_kv(const unsigned char* tq, const unsigned char* tv, cons
 
 // acc[md] += A(md, 0) b[0] + A(md, 1) b[1] for md = 0 .. D/32-1, A(md, rh) the frag_cols read
 // of rows 16*rh .. 16*rh+15 of the tile at `t` (a contraction over its 32 rows); md in Gray
-// order. PF = 1 issues the reads of the next md before the products of this one (8 more
-// registers), PF = 0 reads right before use.
+// order. The reads run PF steps ahead of their products (8 registers per step); PF = 0 reads
+// right before use.
 template <int D, int PF = 1>
 FAB_DEV void cols_acc(const unsigned char* t, const f16x8 b[2], f32x16* acc, const ColWalk<D>& w) {
     constexpr int MD = D / 32;
     constexpr int RH = 16 * D * 2;                    // bytes of 16 rows
+    constexpr int NB = PF + 1;
     int a0 = w.a0[0], a1 = w.a0[1];
-    f16x8 r0[PF + 1], r1[PF + 1];
-    if (PF) {
-        r0[0] = join(tr_read(t + a0), tr_read(t + a1));
-        r1[0] = join(tr_read(t + a0 + RH), tr_read(t + a1 + RH));
-    }
+    f16x8 r0[NB], r1[NB];
+    // the reads of step s + PF (md = gray(s + PF)); the walk is stepped as they are issued
+    auto rd = [&](int q) {
+        r0[q % NB] = join(tr_read(t + a0), tr_read(t + a1));
+        r1[q % NB] = join(tr_read(t + a0 + RH), tr_read(t + a1 + RH));
+        if (q + 1 < MD) {
+            a0 += gray_step(q, w.e[0]);
+            a1 += gray_step(q, w.e[1]);
+        }
+    };
+#pragma unroll
+    for (int q = 0; q < PF; ++q) rd(q);
 #pragma unroll
     for (int s = 0; s < MD; ++s) {
-        const int cur = PF ? (s & 1) : 0;
-        if (PF) {
-            if (s + 1 < MD) {
-                a0 += gray_step(s, w.e[0]);
-                a1 += gray_step(s, w.e[1]);
-                r0[(s + 1) & 1] = join(tr_read(t + a0), tr_read(t + a1));
-                r1[(s + 1) & 1] = join(tr_read(t + a0 + RH), tr_read(t + a1 + RH));
-            }
-        } else {
-            r0[0] = join(tr_read(t + a0), tr_read(t + a1));
-            r1[0] = join(tr_read(t + a0 + RH), tr_read(t + a1 + RH));
-            if (s + 1 < MD) {
-                a0 += gray_step(s, w.e[0]);
-                a1 += gray_step(s, w.e[1]);
-            }
-        }
+        if (s + PF < MD) rd(s + PF);
         const int md = gray(s);
-        acc[md] = mfma32(r0[cur], b[0], acc[md]);
-        acc[md] = mfma32(r1[cur], b[1], acc[md]);
+        acc[md] = mfma32(r0[s % NB], b[0], acc[md]);
+        acc[md] = mfma32(r1[s % NB], b[1], acc[md]);
         __builtin_amdgcn_sched_barrier(0);
     }
 }

@@ -52,6 +52,12 @@ RAGGED = [
     dict(name="dead_row_blocks", D=128, H=2, Hkv=1, N=200, M=300, mask="random",
          masked_rows=[(0, i) for i in list(range(48, 64)) + list(range(160, 176))],
          k_type="q8_0", v_type="q8_0"),
+    # two row blocks per KV head at D=256: the key side's list holds exactly two entries
+    dict(name="kv_two_blocks", D=256, H=2, Hkv=1, N=32, M=200, mask="tail", k_type="q8_0", v_type="f16"),
+    # four row blocks, the first and the last fully masked: only the middle two are listed
+    dict(name="kv_live_middle_blocks", D=128, H=4, Hkv=1, N=32, M=96, mask="random",
+         masked_rows=[(0, i) for i in list(range(0, 8)) + list(range(24, 32))],
+         k_type="q8_0", v_type="q8_0"),
     # 132000 rows over one KV head (4125 row blocks): every key tile is split into row ranges
     dict(name="long_rows_split", D=64, H=8, Hkv=1, N=16500, M=40, mask="none",
          k_type="q8_0", v_type="q8_0"),
