@@ -28,14 +28,27 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(Params p) {
     __shared__ float red[2][kWaves];
     float mq = 0.0f, md = 0.0f;
     const int rows = p.N * p.H;
-    for (int row = blockIdx.x; row < rows; row += gridDim.x) {
-        // q row (i, h) and dO row (h, i) for the same linear index
-        const int i = row / p.H, h = row - (row / p.H) * p.H;
-        for (int c = threadIdx.x; c < p.D; c += kThreads) {
-            const float xq = load_scalar(p.q + c * p.q_nb0 + i * p.q_nb1 + h * p.q_nb2, p.q_type);
-            const float xd = load_scalar(p.d + c * p.d_nb0 + h * p.d_nb1 + i * p.d_nb2, p.d_type);
-            mq = fmaxf(mq, fabsf(xq));
-            md = fmaxf(md, fabsf(xd));
+    // kThreads / D rows per step (D <= kThreads), each thread one element of one of them; four
+    // steps' loads are issued before any is used
+    const int rpi = kThreads / p.D, c = threadIdx.x % p.D, sub = threadIdx.x / p.D;
+    const int stride = gridDim.x * rpi;
+    for (int row0 = blockIdx.x * rpi + sub; row0 < rows; row0 += 4 * stride) {
+        float xq[4], xd[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            // q row (i, h) and dO row (h, i) for the same linear index
+            const int row = row0 + u * stride;
+            xq[u] = xd[u] = 0.0f;
+            if (row < rows) {
+                const int i = row / p.H, h = row - (row / p.H) * p.H;
+                xq[u] = load_scalar(p.q + c * p.q_nb0 + i * p.q_nb1 + h * p.q_nb2, p.q_type);
+                xd[u] = load_scalar(p.d + c * p.d_nb0 + h * p.d_nb1 + i * p.d_nb2, p.d_type);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            mq = fmaxf(mq, fabsf(xq[u]));
+            md = fmaxf(md, fabsf(xd[u]));
         }
     }
     mq = wave_max(mq);
@@ -941,14 +954,17 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p) {
         const int ridx = base + lr;
         const bool ok = ridx < total;
         float mx = neg_inf();
-        if (ok)
+        if (ok) {
+#pragma unroll 8
             for (int s = grp; s < p.nparts; s += kWaves) mx = fmaxf(mx, p.part_m[(int64_t)s * total + ridx]);
+        }
         smax[grp][lr] = mx;
         __syncthreads();
         mx = fmaxf(fmaxf(smax[0][lr], smax[1][lr]), fmaxf(smax[2][lr], smax[3][lr]));
         double Ls = 0.0, Ds = 0.0;
         float b = 0.0f;
         if (ok && mx != neg_inf()) {
+#pragma unroll 4
             for (int s = grp; s < p.nparts; s += kWaves) {
                 const int64_t idx = (int64_t)s * total + ridx;
                 const float m = p.part_m[idx];
