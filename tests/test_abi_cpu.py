@@ -150,3 +150,16 @@ def test_status_strings():
     assert fab.status_string(0) == "ok"
     assert "shape" in fab.status_string(-2)
     assert fab.status_string(12345) == "unknown status"
+
+
+def test_key_side_row_split_workspace():
+    """With more than 2048 row blocks of 32 rows per KV head, the key side splits every key tile
+    into row ranges whose partial dK/dV (2 x 128 keys x D floats per range) live in the
+    workspace; at 2048 row blocks exactly, nothing is split."""
+    def ws(n):
+        p = fa_inputs.make_custom(name="split", D=64, H=4, Hkv=1, N=n, M=256, mask="none")
+        return fab.fa_back_layout_query(B.describe(p)).workspace_bytes
+    at, past = ws(16384), ws(16392)          # G*N/32 = 2048 and 2049 row blocks
+    parts = 4 * 2 * 2 * 2 * 128 * 64         # floats: 2 key tiles x 2 ranges x (dK, dV) x 128 keys x D
+    assert past - at >= parts
+    assert past - at < parts + (1 << 16)     # the other terms grow by 8 query rows only

@@ -141,7 +141,7 @@ def test_gqa_equals_replicated_heads(mode, monkeypatch):
 # Walk 1 runs by row tiles or by key tiles (chosen from the shape; FA_BACK_WALK1 overrides the
 # choice when the plan is created). Both must meet the bar on the same inputs.
 WALK1_CASES = ["c0", "c1_causal", "ragged_d128_headmask", "ragged_d64_q8", "ragged_d256_f32mask",
-               "all_masked", "single_key"]
+               "all_masked", "single_key", "dead_row_blocks", "kv_live_middle_blocks"]
 
 
 def _walk1_problem(name):
