@@ -123,6 +123,16 @@ def causal_tail_mask(N: int, M: int, Hm: int = 1, typ: str = "f16") -> np.ndarra
     return np.broadcast_to(row, (Hm, N, M)).copy()
 
 
+def implicit_causal(p: Problem) -> Problem:
+    """The same problem with its one-head causal-tail mask passed as the storage-free mask type
+    (the library forms it from i and j). The explicit array stays on the problem for the CPU
+    oracle."""
+    if p.mask is None or p.mask.shape[0] != 1 or not np.array_equal(
+            np.asarray(p.mask, np.float32), causal_tail_mask(p.N, p.M, 1, "f32")):
+        raise ValueError(f"{p.name}: the mask is not a one-head causal-tail mask")
+    return dataclasses.replace(p, name=p.name + "_implicit", mask_type="causal_tail")
+
+
 # ----------------------------------------------------------------------------- configs
 
 def _draws(rng, H, Hkv, N, M, D, Dv):

@@ -65,7 +65,8 @@ int validate(const fa_back_desc* d, Geometry* g) {
     auto is_kv = [&](int t) { return is_act(t) || t == FA_BACK_Q8_0; };
     if (!is_act(q.type) || !is_act(dd.type) || !is_kv(k.type) || !is_kv(v.type)) return FA_BACK_EUNSUPPORTED;
     const bool has_mask = m.type != FA_BACK_NONE;
-    if (has_mask && m.type != FA_BACK_F32 && m.type != FA_BACK_F16) return FA_BACK_EUNSUPPORTED;
+    const bool causal = m.type == FA_BACK_CAUSAL_TAIL;   // implicit: no storage, no strides
+    if (has_mask && !causal && m.type != FA_BACK_F32 && m.type != FA_BACK_F16) return FA_BACK_EUNSUPPORTED;
     if (!std::isfinite(d->scale)) return FA_BACK_EINVAL;
     if (!tensor_nonneg(q) || !tensor_nonneg(k) || !tensor_nonneg(v) || !tensor_nonneg(dd) ||
         (has_mask && !tensor_nonneg(m)))
@@ -85,13 +86,14 @@ int validate(const fa_back_desc* d, Geometry* g) {
         if (m.ne[0] != M || m.ne[1] != N) return FA_BACK_ESHAPE;
         Hm = m.ne[2];
         if (Hm != 1 && Hm != H) return FA_BACK_ESHAPE;
+        if (causal && Hm != 1) return FA_BACK_ESHAPE;
     }
     // strides: rows contiguous; F32/F16/BF16 cache rows are read with 16-byte loads
     int rc;
     if ((rc = check_strides(q, false)) || (rc = check_strides(dd, false))) return rc;
     if ((rc = check_strides(k, k.type != FA_BACK_Q8_0)) || (rc = check_strides(v, v.type != FA_BACK_Q8_0)))
         return rc;
-    if (has_mask && (rc = check_strides(m, false))) return rc;
+    if (has_mask && !causal && (rc = check_strides(m, false))) return rc;
     if (k.nb[1] >= ((int64_t)1 << 32) || v.nb[1] >= ((int64_t)1 << 32)) return FA_BACK_EUNSUPPORTED;
     // supported sizes
     if (D != Dv || (D != 64 && D != 128 && D != 256)) return FA_BACK_EUNSUPPORTED;
@@ -194,7 +196,9 @@ int validate(const fa_back_desc* d, Geometry* g) {
     g->ws_dlt = take(4ull * total_rows);
     g->ws_bound = take(4ull * g->nbound);
     g->ws_dqp = take(g->splits > 1 ? 4ull * g->splits * total_rows * D : 0);
-    g->ws_mcls = take(has_mask ? (uint64_t)(Hm == 1 ? 1 : g->Hkv) * g->RB * g->KT : 0);
+    // mask classes: stored masks only (the causal-tail classes are computed where needed)
+    const bool stored_mask = has_mask && d->mask.type != FA_BACK_CAUSAL_TAIL;
+    g->ws_mcls = take(stored_mask ? (uint64_t)(Hm == 1 ? 1 : g->Hkv) * g->RB * g->KT : 0);
     g->ws_kvp = take(4ull * g->kv_tail * g->kv_split * 2 * kKVKeys * D);
     L.workspace_bytes = std::max<uint64_t>(o, kAlign);
     return FA_BACK_OK;
@@ -228,7 +232,7 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
     hipLaunchKernelGGL(absmax_kernel, dim3(g.npart), dim3(kThreads), 0, st, P);
     pm.mark(0);
     hipLaunchKernelGGL(prep_kernel<D>, dim3(g.Hkv * g.RB), dim3(kThreads), 0, st, P);
-    if (g.Hm > 0) {
+    if (g.Hm > 0 && P.m_type != FA_BACK_CAUSAL_TAIL) {
         const dim3 grid((g.Hm == 1 ? 1 : g.Hkv) * g.RB, (g.KT + kClassTilesPerBlock - 1) / kClassTilesPerBlock);
         if (P.m_type == FA_BACK_F16)
             hipLaunchKernelGGL(maskclass_kernel<2>, grid, dim3(kThreads), 0, st, P);
@@ -324,7 +328,8 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     // a tensor without elements may be passed as NULL
     const bool q_empty = (int64_t)g.N * g.H == 0, kv_empty = (int64_t)g.M == 0;
     if ((!q && !q_empty) || (!d && !q_empty) || (!k && !kv_empty) || (!v && !kv_empty)) return FA_BACK_EINVAL;
-    const bool has_mask = ds.mask.type != FA_BACK_NONE;
+    const bool causal = ds.mask.type == FA_BACK_CAUSAL_TAIL;
+    const bool has_mask = ds.mask.type != FA_BACK_NONE && !causal;   // a stored mask
     if (!has_mask && mask) return FA_BACK_EINVAL;
     if (has_mask && !mask && (int64_t)g.M * g.N != 0) return FA_BACK_EINVAL;
     auto misaligned = [](const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) != 0; };
@@ -348,7 +353,7 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     P.d_nb0 = ds.d.nb[0]; P.d_nb1 = ds.d.nb[1]; P.d_nb2 = ds.d.nb[2];
     P.k_nb1 = ds.k.nb[1]; P.k_nb2 = ds.k.nb[2];
     P.v_nb1 = ds.v.nb[1]; P.v_nb2 = ds.v.nb[2];
-    P.m_nb0 = ds.mask.nb[0]; P.m_nb1 = ds.mask.nb[1]; P.m_nb2 = ds.mask.nb[2];
+    if (!causal) { P.m_nb0 = ds.mask.nb[0]; P.m_nb1 = ds.mask.nb[1]; P.m_nb2 = ds.mask.nb[2]; }
     P.q_type = ds.q.type; P.d_type = ds.d.type; P.k_type = ds.k.type; P.v_type = ds.v.type;
     P.m_type = ds.mask.type;
     P.D = g.D; P.H = g.H; P.Hkv = g.Hkv; P.G = g.G; P.N = g.N; P.M = g.M; P.Hm = g.Hm;

@@ -228,6 +228,16 @@ __global__ __launch_bounds__(kThreads) void maskclass_kernel(Params p) {
 
 FAB_DEV int mask_class(const Params& p, int hk, int rb, int t) {
     if (p.m_type == FA_BACK_NONE) return kMaskZero;
+    if (p.m_type == FA_BACK_CAUSAL_TAIL) {
+        // query row i sees keys j <= M - N + i; the block's rows r < R hold query rows ilo..ihi
+        // and the tile keys j0..j1 < M: the class the stored mask would get
+        const int ilo = (32 * rb) / p.G, ihi = min(32 * rb + 31, p.R - 1) / p.G;
+        const int j0 = t * kQTileKeys, j1 = min(j0 + kQTileKeys - 1, p.M - 1);
+        const int off = p.M - p.N;
+        if (j0 > off + ihi) return kMaskDead;
+        if (j1 <= off + ilo) return kMaskZero;
+        return kMaskMixed;
+    }
     const int hc = p.Hm == 1 ? 0 : hk;
     return p.mcls[((int64_t)hc * p.RB + rb) * p.KT + t];
 }
@@ -235,6 +245,12 @@ FAB_DEV int mask_class(const Params& p, int hk, int rb, int t) {
 FAB_DEV float mask_at(const char* mrow, int type, int j) {
     return type == FA_BACK_F16 ? (float)*(const _Float16*)(mrow + 2 * (int64_t)j)
                                : *(const float*)(mrow + 4 * (int64_t)j);
+}
+
+// Mask entry of key j for query row i (whose stored mask row is mrow, if any).
+FAB_DEV float mask_value(const Params& p, const char* mrow, int i, int j) {
+    if (p.m_type == FA_BACK_CAUSAL_TAIL) return j <= p.M - p.N + i ? 0.0f : neg_inf();
+    return mask_at(mrow, p.m_type, j);
 }
 
 // ----------------------------------------------------------------------------- product loops
@@ -471,7 +487,7 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
                         const int key = j0 + crow(v, g);
                         float mv = 0.0f;
                         if (!row_ok || key >= p.M) mv = neg_inf();
-                        else if (cls == kMaskMixed) mv = mask_at(mrow, p.m_type, key) * kLog2e;
+                        else if (cls == kMaskMixed) mv = mask_value(p, mrow, i, key) * kLog2e;
                         madd[v] = mv;
                     }
                     float tmax = neg_inf();
@@ -512,7 +528,7 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
                         const int key = j0 + crow(v, g);
                         float mv = 0.0f;
                         if (!row_ok || key >= p.M) mv = neg_inf();
-                        else if (cls == kMaskMixed) mv = mask_at(mrow, p.m_type, key) * kLog2e;
+                        else if (cls == kMaskMixed) mv = mask_value(p, mrow, i, key) * kLog2e;
                         const float pv = (dead || mv == neg_inf()) ? 0.0f : fast_exp2(fmaf(sa[v], sc2, mv - lse2k));
                         bs[v >> 3][v & 7] = (_Float16)(pv * (pa[v] - dlt));
                     }
@@ -810,8 +826,10 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
         const int r = 32 * rbx + l32;
         const bool row_ok = r < p.R;
         const char* mrow = nullptr;
-        if (has_mask && row_ok && c == kMaskMixed) {
-            const int i = r / p.G, gh = r - (r / p.G) * p.G;
+        const int i = r / p.G;
+        const bool use_mask = has_mask && row_ok && c == kMaskMixed;
+        if (use_mask) {
+            const int gh = r - (r / p.G) * p.G;
             mrow = p.mask + (int64_t)i * p.m_nb1 + (int64_t)(p.Hm == 1 ? 0 : hk * p.G + gh) * p.m_nb2;
         }
         float madd[16];
@@ -822,7 +840,7 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
             const int key = kbase + crow(v, g);
             float mv = 0.0f;
             if (!row_ok || key >= p.M) mv = neg_inf();
-            else if (mrow) mv = mask_at(mrow, p.m_type, key) * kLog2e;
+            else if (use_mask) mv = mask_value(p, mrow, i, key) * kLog2e;
             madd[v] = mv;
             if (mv != neg_inf()) tm = fmaxf(tm, fmaf(sa[v], sc2, mv));
         }
@@ -1264,7 +1282,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                             const int ii = r / p.G, gh = r - (r / p.G) * p.G;
                             const char* mrow = p.mask + (int64_t)ii * p.m_nb1 +
                                                (int64_t)(p.Hm == 1 ? 0 : hk * p.G + gh) * p.m_nb2;
-                            mv = mask_at(mrow, p.m_type, myj) * kLog2e;
+                            mv = mask_value(p, mrow, ii, myj) * kLog2e;
                         }
                         ((float*)(myF + (b * 64 + lane) * 16))[u] = mv;
                     }

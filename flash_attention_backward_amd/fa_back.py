@@ -15,7 +15,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa_back.so")
 
 NONE, F32, F16, BF16, Q8_0 = -1, 0, 1, 2, 8
-TYPE_IDS = {"none": NONE, "f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0}
+CAUSAL_TAIL = 16   # mask type only: query i sees keys j <= M - N + i, nothing stored
+TYPE_IDS = {"none": NONE, "f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "causal_tail": CAUSAL_TAIL}
 ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, Q8_0: 34}
 
 OK, EINVAL, ESHAPE, ESTRIDE, EUNSUPPORTED, EHIP, EALIGN = 0, -1, -2, -3, -4, -5, -6
@@ -176,6 +177,9 @@ def describe(p) -> Desc:
     ds.d = make_tensor(p.d_type, ne, nb)
     if p.mask is None:
         ds.mask = make_tensor(NONE, (0, 0, 0), (0, 0, 0))
+    elif p.mask_type == "causal_tail":
+        # the array (kept for the CPU oracle) is not passed: the library forms the mask itself
+        ds.mask = make_tensor(CAUSAL_TAIL, (p.M, p.N, 1), (0, 0, 0))
     else:
         ne, nb = _ggml(p.mask, p.mask_type, p.M)
         ds.mask = make_tensor(p.mask_type, ne, nb)
@@ -203,7 +207,8 @@ class DeviceProblem:
         self.desc = describe(p)
         self.plan, self.layout = fa_back_create(self.desc, self.device.index or 0)
         self.bufs = {n: _to_device(getattr(p, n), self.device) for n in ("q", "k", "v", "d")}
-        self.bufs["mask"] = None if p.mask is None else _to_device(p.mask, self.device)
+        self.bufs["mask"] = (None if p.mask is None or p.mask_type == "causal_tail"
+                             else _to_device(p.mask, self.device))
         self.out = torch.empty(int(self.layout.out_bytes), dtype=torch.uint8, device=self.device)
         self.ws = torch.empty(int(self.layout.workspace_bytes), dtype=torch.uint8, device=self.device)
         if poison:

@@ -22,7 +22,12 @@
  *     v    ne = {Dv, M, Hkv}   F32 | F16 | BF16 | Q8_0
  *     d    ne = {Dv, H, N  }   F32 | F16 | BF16          (dO; note the H, N order, as the
  *                                                         operator's "Layout and shape" states)
- *     mask ne = {M,  N, Hm }   F32 | F16, Hm in {1, H}; type FA_BACK_NONE for no mask
+ *     mask ne = {M,  N, Hm }   F32 | F16, Hm in {1, H}; type FA_BACK_NONE for no mask;
+ *                              type FA_BACK_CAUSAL_TAIL for the causal-tail mask without
+ *                              storage: ne = {M, N, 1}, nb ignored, and fa_back_run takes
+ *                              mask = NULL. Query row i then sees keys j <= M - N + i (mask
+ *                              entry 0) and no others (-inf), for every head: the results are
+ *                              bitwise those of the same mask stored as F16 or F32.
  * nb[0] must equal the element size (34 bytes per 32-value block for Q8_0), i.e. each row
  * is contiguous; rows and heads may have any positive stride (e.g. a cache view whose heads
  * are interleaved per cell). A Q8_0 block is a little-endian fp16 scale followed by 32 int8;
@@ -67,6 +72,7 @@ extern "C" {
 #define FA_BACK_F16 1
 #define FA_BACK_BF16 2
 #define FA_BACK_Q8_0 8
+#define FA_BACK_CAUSAL_TAIL 16 /* mask only: query i sees keys j <= M - N + i; no storage */
 
 /* status codes (no entry point aborts or exits) */
 #define FA_BACK_OK 0

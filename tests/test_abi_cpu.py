@@ -163,3 +163,21 @@ def test_key_side_row_split_workspace():
     parts = 4 * 2 * 2 * 2 * 128 * 64         # floats: 2 key tiles x 2 ranges x (dK, dV) x 128 keys x D
     assert past - at >= parts
     assert past - at < parts + (1 << 16)     # the other terms grow by 8 query rows only
+
+
+def test_implicit_causal_tail_descriptor():
+    """The storage-free causal-tail mask: extents {M, N, 1}, strides ignored; one mask head
+    only; no mask-class table in the workspace."""
+    p = fa_inputs.make("c1_causal")
+    lib = fab.load_library()
+    d = B.describe(fa_inputs.implicit_causal(p))
+    lay = B.Layout()
+    assert lib.fa_back_layout_query(ctypes.byref(d), ctypes.byref(lay)) == B.OK
+    ref = fab.fa_back_layout_query(B.describe(p))
+    assert lay.out_bytes == ref.out_bytes and lay.off_delta == ref.off_delta
+    assert lay.workspace_bytes < ref.workspace_bytes
+    d.mask.ne[2] = 2                                   # more than one mask head
+    assert lib.fa_back_layout_query(ctypes.byref(d), ctypes.byref(lay)) == B.ESHAPE
+    d.mask.ne[2] = 1
+    d.mask.ne[0] = p.M + 1                             # extents must be {M, N, 1}
+    assert lib.fa_back_layout_query(ctypes.byref(d), ctypes.byref(lay)) == B.ESHAPE

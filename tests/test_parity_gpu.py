@@ -156,3 +156,35 @@ def test_walk1_variants(name, mode, monkeypatch):
     monkeypatch.setenv("FA_BACK_WALK1", mode)
     say(f"[walk1 {mode}]")
     _parity(_walk1_problem(name))
+
+
+# The causal-tail mask without storage (FA_BACK_CAUSAL_TAIL): the library forms the mask from
+# i and j, and must give bitwise the results of the same mask stored as F16, under both walk-1
+# variants (N < M, N > M with fully masked rows, N = M, D = 256, the long-cache pilot).
+IMPLICIT_CASES = [
+    ("c1_causal", None),
+    ("c4n16", None),
+    ("impl_n_gt_m", dict(D=128, H=4, Hkv=2, N=100, M=60, mask="tail", k_type="q8_0", v_type="q8_0")),
+    ("impl_d256", dict(D=256, H=6, Hkv=1, N=45, M=300, mask="tail", k_type="q8_0", v_type="q8_0")),
+    ("impl_square", dict(D=64, H=2, Hkv=1, N=150, M=150, mask="tail", q_type="bf16", d_type="bf16",
+                         k_type="bf16", v_type="bf16")),
+]
+
+
+def _implicit_problem(name, cfg):
+    return fa_inputs.make(name) if cfg is None else fa_inputs.make_custom(name=name, **cfg)
+
+
+@pytest.mark.parametrize("mode", ["rows", "keys"])
+@pytest.mark.parametrize("name,cfg", IMPLICIT_CASES, ids=[c[0] for c in IMPLICIT_CASES])
+def test_implicit_causal_tail_bitwise(name, cfg, mode, monkeypatch):
+    monkeypatch.setenv("FA_BACK_WALK1", mode)
+    p = _implicit_problem(name, cfg)
+    a, _, _ = run_gpu(p)
+    b, _, _ = run_gpu(fa_inputs.implicit_causal(p))
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+
+
+def test_implicit_causal_tail_parity():
+    _parity(fa_inputs.implicit_causal(fa_inputs.make_custom(name="impl_parity", **IMPLICIT_CASES[2][1])))
