@@ -12,11 +12,14 @@ library's kernels, so the dominant kernel's average duration is measured live ov
 timed region. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c4n16|c3|...]
-                  [--mask stored|implicit]
+                  [--mask stored|implicit] [--saved]
 
 --mask implicit passes the workload's causal-tail mask as the storage-free mask type (the
 library forms it from the row and key indices) instead of the stored F16 mask; the metric's
-workload is the stored mask.
+workload is the stored mask. --saved times fa_back_run_saved (forward-saved LSE and O; walk 1
+and the merge are not run) with the LSE that fa_back_run itself produces on the same inputs
+and a synthetic F32 O drawn N(0,1) (its values only set delta and the dS bound); its work is
+counted as 2*V*(3D + 4Dv) (walk 2 and the key side).
 """
 import argparse
 import json
@@ -133,6 +136,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--mask", choices=("stored", "implicit"), default="stored")
+    ap.add_argument("--saved", action="store_true", help="time the saved-statistics entry")
     ap.add_argument("--cpu-rows", type=int, default=768, help="query rows in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -144,6 +148,7 @@ def main():
               f"(got --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     import fa_inputs
     import flash_attention_backward_amd as fab
@@ -157,16 +162,29 @@ def main():
     dev = torch.device("cuda:0")
     dp = fab.DeviceProblem(p, dev, poison=False)
     stream = torch.cuda.current_stream(dev)
+    if args.saved:
+        # the LSE of the full operator on the same inputs, and a synthetic O
+        dp.run()
+        torch.cuda.synchronize()
+        lse_t = torch.from_numpy(np.ascontiguousarray(dp.outputs()["lse"], dtype=np.float32)).to(dev)
+        gen = torch.Generator(device="cpu").manual_seed(p.seed + 1)
+        o_t = torch.randn((p.H, p.N, p.Dv), generator=gen, dtype=torch.float32).to(dev)
+        run = lambda: dp.run_saved(lse_t, o_t, stream)
+        run_timed = lambda: dp.run_saved(lse_t, o_t, stream, timed=True)
+        flops["full"] = 2 * flops["visible"] * (3 * p.D + 4 * p.Dv)
+    else:
+        run = dp.run
+        run_timed = lambda: dp.run_timed(stream)
     log(f"warmup x{args.warmup}")
     for _ in range(args.warmup):
-        dp.run()
+        run()
     torch.cuda.synchronize()
     log(f"timing x{args.steps}")
     phases = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        phases.append(dp.run_timed(stream))
+        phases.append(run_timed())
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
@@ -184,13 +202,15 @@ def main():
     kname = KERNEL_NAMES[dom].replace("D", str(p.D), 1)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_F16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
-                "traffic": measured_traffic(kname, args.workload) if args.mask == "stored" else None,
+                "traffic": (measured_traffic(kname, args.workload)
+                            if args.mask == "stored" and not args.saved else None),
                 "kernel": kname, "phase": dom,
                 "flops_per_launch": dom_flops, "avg_launch_ms": round(mean_phase[dom], 4)}
     value = flops["full"] / (ms * 1e-3) / 1e12
     rec = {
-        "metric": (METRIC if args.workload == "c4" and args.mask == "stored"
-                   else f"attn-backward TFLOP/s + ms/call, {args.workload} mask {args.mask}"),
+        "metric": (METRIC if args.workload == "c4" and args.mask == "stored" and not args.saved
+                   else f"attn-backward TFLOP/s + ms/call, {args.workload} mask {args.mask}"
+                        + (" saved LSE/O" if args.saved else "")),
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "ms_per_call": call_stats,
         "higher_is_better": True,
@@ -198,7 +218,8 @@ def main():
         "config": {"workload": describe_workload(p), "N": p.N, "M": p.M, "H": p.H, "Hkv": p.Hkv,
                    "D": p.D, "Dv": p.Dv, "q_type": p.q_type, "k_type": p.k_type, "v_type": p.v_type,
                    "mask": p.mask_type, "seed": p.seed},
-        "flops": {"count": "2*V*(5D+4Dv), V = visible (row, key, head) triples",
+        "flops": {"count": ("2*V*(3D+4Dv)" if args.saved else "2*V*(5D+4Dv)") +
+                           ", V = visible (row, key, head) triples",
                   "visible": flops["visible"], "full": flops["full"], "five_gemm": flops["five"],
                   "tflops_five_gemm": round(flops["five"] / (ms * 1e-3) / 1e12, 3)},
         "phase_ms": {k: round(v, 4) for k, v in mean_phase.items()},
@@ -209,7 +230,7 @@ def main():
     torch.cuda.empty_cache()
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
-    if not args.no_cpu_baseline and args.workload == "c4" and args.mask == "stored":
+    if not args.no_cpu_baseline and args.workload == "c4" and args.mask == "stored" and not args.saved:
         rec["cpu_baseline"] = cpu_baseline(args.cpu_rows)
     else:
         rec["cpu_baseline"] = None

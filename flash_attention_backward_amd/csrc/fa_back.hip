@@ -15,6 +15,8 @@ using namespace fab;
 
 namespace {
 
+constexpr int kVmaxBlocks = 256;   // partial max |v| blocks of fa_back_run_saved
+
 constexpr uint64_t kAlign = 256;
 
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
@@ -41,7 +43,7 @@ struct Geometry {
     fa_back_layout layout;
     // workspace offsets (bytes)
     uint64_t ws_absmax, ws_scal, ws_qr, ws_dr;
-    uint64_t ws_pm, ws_pl, ws_pd, ws_pb, ws_lse2, ws_dlt, ws_bound, ws_dqp, ws_mcls, ws_kvp;
+    uint64_t ws_pm, ws_pl, ws_pd, ws_pb, ws_lse2, ws_dlt, ws_bound, ws_dqp, ws_mcls, ws_kvp, ws_vmax;
 };
 
 bool tensor_nonneg(const fa_back_tensor& t) {
@@ -200,6 +202,7 @@ int validate(const fa_back_desc* d, Geometry* g) {
     const bool stored_mask = has_mask && d->mask.type != FA_BACK_CAUSAL_TAIL;
     g->ws_mcls = take(stored_mask ? (uint64_t)(Hm == 1 ? 1 : g->Hkv) * g->RB * g->KT : 0);
     g->ws_kvp = take(4ull * g->kv_tail * g->kv_split * 2 * kKVKeys * D);
+    g->ws_vmax = take(4ull * kVmaxBlocks);   // fa_back_run_saved only
     L.workspace_bytes = std::max<uint64_t>(o, kAlign);
     return FA_BACK_OK;
 }
@@ -240,13 +243,21 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
             hipLaunchKernelGGL(maskclass_kernel<4>, grid, dim3(kThreads), 0, st, P);
     }
     pm.mark(1);
-    if (g.w1keys)
-        hipLaunchKernelGGL(walk1_keys_kernel<D>, dim3(g.KT1 * g.Hkv, g.RS1), dim3(kW1Threads), 0, st, P);
-    else
-        hipLaunchKernelGGL((qpass_kernel<D, false>), dim3(g.RT * g.Hkv, g.splits), dim3(kQThreads), 0, st, P);
-    pm.mark(2);
-    hipLaunchKernelGGL(merge_kernel, dim3(g.nbound), dim3(kThreads), 0, st, P);
-    pm.mark(3);
+    if (P.lse_in) {
+        // forward-saved LSE and O: the row statistics without walk 1 and the merge
+        hipLaunchKernelGGL(vmax_kernel, dim3(kVmaxBlocks), dim3(kThreads), 0, st, P);
+        pm.mark(2);
+        hipLaunchKernelGGL(saved_rows_kernel, dim3(g.nbound), dim3(kThreads), 0, st, P);
+        pm.mark(3);
+    } else {
+        if (g.w1keys)
+            hipLaunchKernelGGL(walk1_keys_kernel<D>, dim3(g.KT1 * g.Hkv, g.RS1), dim3(kW1Threads), 0, st, P);
+        else
+            hipLaunchKernelGGL((qpass_kernel<D, false>), dim3(g.RT * g.Hkv, g.splits), dim3(kQThreads), 0, st, P);
+        pm.mark(2);
+        hipLaunchKernelGGL(merge_kernel, dim3(g.nbound), dim3(kThreads), 0, st, P);
+        pm.mark(3);
+    }
     hipLaunchKernelGGL((qpass_kernel<D, true>), dim3(g.RT * g.Hkv, g.splits), dim3(kQThreads), 0, st, P);
     pm.mark(4);
     if (g.splits > 1) {
@@ -320,14 +331,15 @@ int fa_back_create(const fa_back_desc* desc, int device, fa_back_plan** plan, fa
 void fa_back_destroy(fa_back_plan* plan) { delete plan; }
 
 static int run_impl(const fa_back_plan* plan, const void* q, const void* k, const void* v,
-                    const void* d, const void* mask, void* out, void* workspace, void* stream,
-                    float* phase_ms) {
+                    const void* d, const void* mask, const float* lse_in, const float* o_in, bool saved,
+                    void* out, void* workspace, void* stream, float* phase_ms) {
     if (!plan || !out || !workspace) return FA_BACK_EINVAL;
     const fa_back_desc& ds = plan->desc;
     const Geometry& g = plan->geo;
     // a tensor without elements may be passed as NULL
     const bool q_empty = (int64_t)g.N * g.H == 0, kv_empty = (int64_t)g.M == 0;
     if ((!q && !q_empty) || (!d && !q_empty) || (!k && !kv_empty) || (!v && !kv_empty)) return FA_BACK_EINVAL;
+    if (saved && (!lse_in || !o_in) && !q_empty) return FA_BACK_EINVAL;
     const bool causal = ds.mask.type == FA_BACK_CAUSAL_TAIL;
     const bool has_mask = ds.mask.type != FA_BACK_NONE && !causal;   // a stored mask
     if (!has_mask && mask) return FA_BACK_EINVAL;
@@ -337,6 +349,7 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     if (misaligned(q, elem_size(ds.q.type)) || misaligned(d, elem_size(ds.d.type)) ||
         misaligned(k, kv_align(ds.k.type)) || misaligned(v, kv_align(ds.v.type)) ||
         (has_mask && misaligned(mask, elem_size(ds.mask.type))) || misaligned(out, kAlign) ||
+        (saved && (misaligned(lse_in, 4) || misaligned(o_in, 4))) ||
         misaligned(workspace, kAlign))
         return FA_BACK_EALIGN;
 
@@ -386,6 +399,12 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     P.kv_full = g.kv_full;
     P.kv_split = g.kv_split;
     P.kv_part = (float*)(w + g.ws_kvp);
+    if (saved && !q_empty) {
+        P.lse_in = lse_in;
+        P.o_in = o_in;
+        P.vmax_part = (float*)(w + g.ws_vmax);
+        P.nvpart = kVmaxBlocks;
+    }
 
     hipStream_t st = (hipStream_t)stream;
     hipEvent_t ev[FA_BACK_NUM_PHASES + 1];
@@ -418,14 +437,27 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
 
 int fa_back_run(const fa_back_plan* plan, const void* q, const void* k, const void* v, const void* d,
                 const void* mask, void* out, void* workspace, void* stream) {
-    return run_impl(plan, q, k, v, d, mask, out, workspace, stream, nullptr);
+    return run_impl(plan, q, k, v, d, mask, nullptr, nullptr, false, out, workspace, stream, nullptr);
 }
 
 int fa_back_run_timed(const fa_back_plan* plan, const void* q, const void* k, const void* v,
                       const void* d, const void* mask, void* out, void* workspace, void* stream,
                       float* phase_ms) {
     if (!phase_ms) return FA_BACK_EINVAL;
-    return run_impl(plan, q, k, v, d, mask, out, workspace, stream, phase_ms);
+    return run_impl(plan, q, k, v, d, mask, nullptr, nullptr, false, out, workspace, stream, phase_ms);
+}
+
+int fa_back_run_saved(const fa_back_plan* plan, const void* q, const void* k, const void* v, const void* d,
+                      const void* mask, const float* lse, const float* o, void* out, void* workspace,
+                      void* stream) {
+    return run_impl(plan, q, k, v, d, mask, lse, o, true, out, workspace, stream, nullptr);
+}
+
+int fa_back_run_saved_timed(const fa_back_plan* plan, const void* q, const void* k, const void* v,
+                            const void* d, const void* mask, const float* lse, const float* o, void* out,
+                            void* workspace, void* stream, float* phase_ms) {
+    if (!phase_ms) return FA_BACK_EINVAL;
+    return run_impl(plan, q, k, v, d, mask, lse, o, true, out, workspace, stream, phase_ms);
 }
 
 }  // extern "C"

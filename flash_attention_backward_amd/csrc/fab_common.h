@@ -79,6 +79,11 @@ struct Params {
     // remaining tiles is split into kv_split row ranges whose dK/dV go to kv_part
     int kv_full, kv_split;
     float* kv_part;       // [tail tile][part][dK, dV][128 keys][D]
+    // forward-saved statistics (fa_back_run_saved); null for the full operator
+    const float* lse_in;  // [H*N] natural-log LSE, row h*N + i
+    const float* o_in;    // [H][N][Dv] forward output O, F32
+    float* vmax_part;     // [nvpart] partial max |v| over the cache
+    int nvpart;
 };
 
 // Mask classes of a (32-row block, 64-key tile): no masking needed, every entry -inf, other.

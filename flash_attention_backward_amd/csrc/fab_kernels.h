@@ -1028,6 +1028,112 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p) {
     if (lr == 0) p.bound_part[blockIdx.x] = bound;
 }
 
+// ----------------------------------------------------------------------------- saved statistics
+
+// With the forward's LSE and O supplied (fa_back_run_saved), the row statistics come from them
+// instead of from walk 1 and the merge. delta = rowsum(dO o O) is the definition of delta the
+// pages give ("The math in fattn_back_q": delta is rowsum(dO o O), computed there without O);
+// the dS prescale needs a bound of |dp - delta| that walk 1 would have measured, taken here
+// as sum_c |dO_c| * max |v| + |delta| (Hoelder), which holds for every key.
+
+// Partial max |v| over the cache: for q8_0 the block scale times 128 (|q| <= 128), otherwise
+// every element. Grid-stride over V rows; partial per block.
+static __global__ __launch_bounds__(kThreads) void vmax_kernel(Params p) {
+    float vm = 0.0f;
+    const int64_t rows = (int64_t)p.M * p.Hkv;
+    if (p.v_type == FA_BACK_Q8_0) {
+        const int bpr = p.D / 32;
+        const int64_t n = rows * bpr;
+        for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += (int64_t)gridDim.x * kThreads) {
+            const int64_t row = e / bpr;
+            const int b = (int)(e - row * bpr);
+            const int hk = (int)(row / p.M), j = (int)(row - (int64_t)hk * p.M);
+            const char* blk = p.v + (int64_t)hk * p.v_nb2 + (int64_t)j * p.v_nb1 + 34 * b;
+            vm = fmaxf(vm, fabsf((float)*(const _Float16*)blk) * 128.0f);
+        }
+    } else {
+        const int64_t n = rows * p.D;
+        const int es = p.v_type == FA_BACK_F32 ? 4 : 2;
+        for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += (int64_t)gridDim.x * kThreads) {
+            const int64_t row = e / p.D;
+            const int c = (int)(e - row * p.D);
+            const int hk = (int)(row / p.M), j = (int)(row - (int64_t)hk * p.M);
+            vm = fmaxf(vm, fabsf(load_scalar(p.v + (int64_t)hk * p.v_nb2 + (int64_t)j * p.v_nb1 + (int64_t)c * es,
+                                             p.v_type)));
+        }
+    }
+    __shared__ float red[kWaves];
+    vm = wave_max(vm);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = vm;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float a = red[0];
+        for (int w = 1; w < kWaves; ++w) a = fmaxf(a, red[w]);
+        p.vmax_part[blockIdx.x] = a;
+    }
+}
+
+// Row statistics from the saved LSE and O, one wave per row (rows r = i*G + g of each KV head,
+// padding rows past R included): the log2-LSE less the P image exponent (+inf for a fully
+// masked or padding row), delta in the dO-scaled units of the products, the LSE and delta
+// outputs, and per block the max of the dS bound over its rows.
+static __global__ __launch_bounds__(kThreads) void saved_rows_kernel(Params p) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rowsHK = p.RB * 32;
+    const int total = p.Hkv * rowsHK;
+    const int edo = p.scal[1];
+    float vmax = 0.0f;
+    for (int t = lane; t < p.nvpart; t += 64) vmax = fmaxf(vmax, p.vmax_part[t]);
+    vmax = wave_max(vmax) * 1.001f;   // the fp16 rounding of the products' V values
+    float bound = 0.0f;
+    for (int ridx = blockIdx.x * kWaves + wave; ridx < total; ridx += gridDim.x * kWaves) {
+        const int hk = ridx / rowsHK, r = ridx - hk * rowsHK;
+        float lse2 = pos_inf(), dlt = 0.0f;
+        if (r < p.R) {
+            const int i = r / p.G, g = r - (r / p.G) * p.G;
+            const int h = hk * p.G + g;
+            const float lse = p.lse_in[(int64_t)h * p.N + i];
+            double dl = 0.0;
+            float l1 = 0.0f;
+            if (lse != neg_inf()) {
+                const float* orow = p.o_in + ((int64_t)h * p.N + i) * p.D;
+                for (int c = lane; c < p.D; c += 64) {
+                    const float x = load_scalar(p.d + (int64_t)c * p.d_nb0 + (int64_t)h * p.d_nb1 + (int64_t)i * p.d_nb2,
+                                                p.d_type);
+                    dl = fma((double)x, (double)orow[c], dl);
+                    l1 += fabsf(x);
+                }
+                // fixed-order wave sums
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) {
+                    dl += __shfl_xor(dl, o);
+                    l1 += __shfl_xor(l1, o);
+                }
+                lse2 = (float)((double)lse * (1.0 / kLn2) - kPScaleLog2);
+                dlt = (float)ldexp(dl, edo);
+                bound = fmaxf(bound, ldexpf(l1, edo) * vmax + fabsf(dlt));
+            }
+            if (lane == 0) {
+                p.lse[(int64_t)h * p.N + i] = lse;
+                p.delta[(int64_t)h * p.N + i] = (float)dl;
+            }
+        }
+        if (lane == 0) {
+            p.row_lse2[ridx] = lse2;
+            p.row_dlt[ridx] = dlt;
+        }
+    }
+    __shared__ float red[kWaves];
+    bound = wave_max(bound);
+    if (lane == 0) red[wave] = bound;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float a = red[0];
+        for (int w = 1; w < kWaves; ++w) a = fmaxf(a, red[w]);
+        p.bound_part[blockIdx.x] = a;
+    }
+}
+
 // ----------------------------------------------------------------------------- dQ reduce
 
 template <int D>

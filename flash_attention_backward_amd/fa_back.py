@@ -65,6 +65,11 @@ def load_library():
     lib.fa_back_run.restype = ctypes.c_int
     lib.fa_back_run_timed.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 8 + [ctypes.POINTER(ctypes.c_float)]
     lib.fa_back_run_timed.restype = ctypes.c_int
+    lib.fa_back_run_saved.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 10
+    lib.fa_back_run_saved.restype = ctypes.c_int
+    lib.fa_back_run_saved_timed.argtypes = ([ctypes.c_void_p] + [ctypes.c_void_p] * 10 +
+                                            [ctypes.POINTER(ctypes.c_float)])
+    lib.fa_back_run_saved_timed.restype = ctypes.c_int
     lib.fa_back_destroy.argtypes = [ctypes.c_void_p]
     lib.fa_back_destroy.restype = None
     lib.fa_back_status_string.argtypes = [ctypes.c_int]
@@ -120,6 +125,23 @@ def fa_back_run_timed(plan, q: int, k: int, v: int, d: int, mask: Optional[int],
     if rc != OK:
         raise FaBackError(rc, "fa_back_run_timed")
     return list(ms)
+
+
+def fa_back_run_saved(plan, q: int, k: int, v: int, d: int, mask: Optional[int], lse: int, o: int,
+                      out: int, workspace: int, stream: int = 0, timed: bool = False):
+    """fa_back_run with the forward's LSE (F32, row h*N + i) and O (F32 [Dv, N, H]); with
+    timed=True it blocks and returns the phase times like fa_back_run_timed."""
+    lib = load_library()
+    if timed:
+        ms = (ctypes.c_float * NUM_PHASES)()
+        rc = lib.fa_back_run_saved_timed(plan, q, k, v, d, mask or None, lse or None, o or None, out,
+                                         workspace, stream or None, ms)
+    else:
+        rc = lib.fa_back_run_saved(plan, q, k, v, d, mask or None, lse or None, o or None, out,
+                                   workspace, stream or None)
+    if rc != OK:
+        raise FaBackError(rc, "fa_back_run_saved")
+    return list(ms) if timed else None
 
 
 def fa_back_destroy(plan) -> None:
@@ -232,6 +254,17 @@ class DeviceProblem:
                                  self.bufs["v"].data_ptr(), self.bufs["d"].data_ptr(),
                                  None if m is None else m.data_ptr(), self.out.data_ptr(),
                                  self.ws.data_ptr(), s.cuda_stream)
+
+    def run_saved(self, lse, o, stream=None, timed=False):
+        """Run with saved statistics: lse and o are device tensors (float32, lse (H, N) and
+        o (H, N, Dv), contiguous)."""
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        m = self.bufs["mask"]
+        return fa_back_run_saved(self.plan, self.bufs["q"].data_ptr(), self.bufs["k"].data_ptr(),
+                                 self.bufs["v"].data_ptr(), self.bufs["d"].data_ptr(),
+                                 None if m is None else m.data_ptr(), lse.data_ptr(), o.data_ptr(),
+                                 self.out.data_ptr(), self.ws.data_ptr(), s.cuda_stream, timed)
 
     def outputs(self) -> dict:
         return unpack(self.out.cpu().numpy(), self.layout, self.p)

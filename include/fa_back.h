@@ -138,6 +138,28 @@ int fa_back_run_timed(const fa_back_plan* plan, const void* q, const void* k, co
                       const void* d, const void* mask, void* out, void* workspace, void* stream,
                       float* phase_ms);
 
+/* fa_back_run with the forward's saved statistics: the natural-log LSE of every row (F32,
+ * N*H floats at row h*N + i, -inf for a fully masked row) and the forward output
+ * O = softmax(S) V (F32, contiguous [Dv, N, H], element (c, i, h) at (h*N + i)*Dv + c), both
+ * device buffers owned by the caller. delta is then rowsum(dO o O), the definition the
+ * operator's pages give for it (first review, "The math in fattn_back_q"), formed per row,
+ * and the walk over the keys that forms LSE and delta (phases 2 and 3) is not run: phase 2
+ * is a bound of |v| over the cache and phase 3 forms the row statistics from lse and o.
+ * The packed LSE output is the given LSE, the delta output the computed delta. The results
+ * equal fa_back_run's when lse and o are the forward's (same inputs, same mask) up to their
+ * own rounding; nothing checks that they are. Same conventions, buffers and errors as
+ * fa_back_run; lse and o may be NULL only when N*H == 0. This entry is not one the pages'
+ * operator has: it is the form an SDPA backward takes when the forward saved LSE and O (as
+ * the "AMD-AGI/TraceLens PR #757" page models it). */
+int fa_back_run_saved(const fa_back_plan* plan, const void* q, const void* k, const void* v,
+                      const void* d, const void* mask, const float* lse, const float* o, void* out,
+                      void* workspace, void* stream);
+
+/* fa_back_run_saved plus the timing of fa_back_run_timed. */
+int fa_back_run_saved_timed(const fa_back_plan* plan, const void* q, const void* k, const void* v,
+                            const void* d, const void* mask, const float* lse, const float* o,
+                            void* out, void* workspace, void* stream, float* phase_ms);
+
 /* Free a plan (NULL is allowed). */
 void fa_back_destroy(fa_back_plan* plan);
 

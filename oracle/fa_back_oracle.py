@@ -128,6 +128,39 @@ def run_problem(p):
     return flash_attn_back(q, k, v, do, mask, p.scale)
 
 
+def forward_outputs(q, k, v, mask, scale):
+    """What a forward pass saves: per head, S = scale q k^T + mask, lse = log sum_j exp(s_ij)
+    and O = softmax(S) V (the attention output whose rowsum(dO o O) is delta, first review,
+    "The math in fattn_back_q"). A fully masked row has lse = -inf and O = 0. float64,
+    plain definition. Returns (lse (H,N), o (H,N,Dv))."""
+    H, N, _ = q.shape
+    Hkv, M, _ = k.shape
+    G = H // Hkv
+    Hm = 0 if mask is None else mask.shape[0]
+    sc = _scale64(scale)
+    lse = np.zeros((H, N))
+    o = np.zeros((H, N, v.shape[2]))
+    for h in range(H):
+        S = sc * (q[h] @ k[h // G].T)
+        if mask is not None:
+            S = S + mask[h % Hm]
+        m = S.max(axis=1, initial=NEG_INF)
+        dead = ~np.isfinite(m)
+        m_safe = np.where(dead, 0.0, m)
+        E = np.where(dead[:, None], 0.0, np.exp(S - m_safe[:, None]))
+        ssum = E.sum(axis=1)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            lse[h] = np.where(dead, NEG_INF, m_safe + np.log(np.where(dead, 1.0, ssum)))
+            o[h] = np.where(dead[:, None], 0.0, (E @ v[h // G]) / np.where(dead, 1.0, ssum)[:, None])
+    return lse, o
+
+
+def forward_problem(p):
+    """forward_outputs for a Problem-like object."""
+    q, k, v, _, mask = problem_arrays(p)
+    return forward_outputs(q, k, v, mask, p.scale)
+
+
 # ----------------------------------------------------------------------------- sampled outputs
 
 def _row_block(q, k, v, do, mask, sc, h, rows, G, Hm):

@@ -136,6 +136,22 @@ def test_delta_is_rowsum_dO_times_O():
     np.testing.assert_allclose(res["delta"], np.einsum("nhc,hnc->hn", do, outs), rtol=1e-11, atol=1e-13)
 
 
+def test_forward_outputs_match_independent_forward():
+    # the saved statistics the oracle hands to the saved-statistics entry: O against the
+    # independently written forward above, lse against the backward's own
+    for q, k, v, do, mask, scale in (_micro(), ):
+        lse, o = O.forward_outputs(q, k, v, mask, scale)
+        _, outs = forward_loss(q, k, v, do, mask, float(np.float32(scale)))
+        np.testing.assert_allclose(o, outs, rtol=1e-12, atol=1e-14)
+        np.testing.assert_array_equal(lse, O.flash_attn_back(q, k, v, do, mask, scale)["lse"])
+    p = fa_inputs.make("c0")                     # head 1 row 0 fully masked: lse -inf, O = 0
+    q, k, v, do, mask = O.problem_arrays(p)
+    lse, o = O.forward_problem(p)
+    _, outs = forward_loss(q, k, v, do, mask, float(np.float32(p.scale)))
+    np.testing.assert_allclose(o, outs, rtol=1e-11, atol=1e-13)
+    assert lse[1, 0] == -np.inf and not o[1, 0].any()
+
+
 def test_lse_is_logsumexp_fsum():
     p = fa_inputs.make("c0")
     q, k, v, do, mask = O.problem_arrays(p)
