@@ -11,7 +11,7 @@ through fa_back_run_timed, which records HIP events on the launch stream between
 library's kernels, so the dominant kernel's average duration is measured live over the
 timed region. Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c4n16|c3|...]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c4q4|c4n16|c3|...]
                   [--mask stored|implicit] [--saved]
 
 --mask implicit passes the workload's causal-tail mask as the storage-free mask type (the

@@ -100,6 +100,31 @@ def encode_q8_0(x: np.ndarray) -> np.ndarray:
     return out.reshape(*x.shape[:-1], D // QK8_0 * Q8_0_BLOCK_BYTES)
 
 
+Q4_0_BLOCK_BYTES = 18      # 2-byte fp16 scale + 16 bytes of 4-bit values
+
+
+def encode_q4_0(x: np.ndarray) -> np.ndarray:
+    """Encode float32 rows (last axis = D, D % 32 == 0) as q4_0 blocks.
+
+    Per block of 32: m = the value of largest magnitude (with its sign), step = m / -8
+    (float32), code = floor(x/step + 8.5) clamped to [0, 15] (8 for an all-zero block), stored
+    step = fp16(step). Byte t of the 16 holds code t in its low nibble and code t + 16 in its
+    high nibble. Returns uint8 (..., D/32*18)."""
+    x = np.asarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    blk = x.reshape(*x.shape[:-1], D // 32, 32)
+    idx = np.abs(blk).argmax(axis=-1)[..., None]
+    m = np.take_along_axis(blk, idx, axis=-1)
+    step = (m / np.float32(-8.0)).astype(np.float32)
+    safe = np.where(step != 0, step, np.float32(1.0))
+    t = np.where(step != 0, blk / safe, np.float32(0.0)).astype(np.float32)
+    code = np.clip(np.floor(t + np.float32(8.5)), 0, 15).astype(np.uint8)
+    out = np.empty((*x.shape[:-1], D // 32, Q4_0_BLOCK_BYTES), dtype=np.uint8)
+    out[..., 0:2] = step.astype(np.float16).view(np.uint8).reshape(*step.shape[:-1], 2)
+    out[..., 2:] = code[..., :16] | (code[..., 16:] << 4)
+    return out.reshape(*x.shape[:-1], D // 32 * Q4_0_BLOCK_BYTES)
+
+
 def encode(x: np.ndarray, typ: str) -> np.ndarray:
     if typ == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
@@ -109,6 +134,8 @@ def encode(x: np.ndarray, typ: str) -> np.ndarray:
         return to_bf16_bits(x)
     if typ == "q8_0":
         return encode_q8_0(x)
+    if typ == "q4_0":
+        return encode_q4_0(x)
     raise ValueError(typ)
 
 
@@ -160,6 +187,7 @@ def make(name: str, seed: int = 0, mask_type: str = "f16") -> Problem:
     c3        N=M=1024 H32 Hkv8 D128, all bf16, causal;  c3v: V = 1 + 1e-3 z (bf16)
     c4        N2048 M75520 H24 Hkv4 D256, Q/dO F32, K/V q8_0, causal-tail
     c4n8/16   last 8 / 16 query rows of c4 against the same cache
+    c4q4      c4 with K/V encoded q4_0 (same draws);  c4q4n16: its last 16 query rows
     Extra cases at the c1 shape: c1_tinydo (dO x 1e-6), c1_strided (K/V heads interleaved
     per cell), c1_causal (causal-tail mask), c1_f32kv, c1_f16kv, c1_bf16kv.
     Scaled-down shapes for quick parity: 'small_*'.
@@ -206,15 +234,16 @@ def make(name: str, seed: int = 0, mask_type: str = "f16") -> Problem:
         return Problem(name, D, Dv, H, Hkv, N, M, 1.0 / math.sqrt(D),
                        to_bf16_bits(q), "bf16", to_bf16_bits(k), "bf16",
                        to_bf16_bits(v), "bf16", to_bf16_bits(do), "bf16", mask, mk, seed)
-    if name in ("c4", "c4n8", "c4n16"):
+    if name in ("c4", "c4n8", "c4n16", "c4q4", "c4q4n16"):
         D = Dv = 256; H, Hkv, N, M = 24, 4, 2048, 75520
         k, v, q, do = _draws(rng, H, Hkv, N, M, D, Dv)
-        Np = {"c4": N, "c4n8": 8, "c4n16": 16}[name]
+        Np = {"c4": N, "c4n8": 8, "c4n16": 16, "c4q4": N, "c4q4n16": 16}[name]
+        kt = "q4_0" if name.startswith("c4q4") else "q8_0"
         q = np.ascontiguousarray(q[:, N - Np:, :])
         do = np.ascontiguousarray(do[N - Np:, :, :])
         mask = causal_tail_mask(Np, M, 1, mk)
         return Problem(name, D, Dv, H, Hkv, Np, M, 1.0 / math.sqrt(D),
-                       q, "f32", encode_q8_0(k), "q8_0", encode_q8_0(v), "q8_0",
+                       q, "f32", encode(k, kt), kt, encode(v, kt), kt,
                        do, "f32", mask, mk, seed)
     if name.startswith("small_"):
         return make_custom(name, seed=seed, mask_type=mask_type)

@@ -27,6 +27,7 @@ int64_t elem_size(int type) {
         case FA_BACK_F16: return 2;
         case FA_BACK_BF16: return 2;
         case FA_BACK_Q8_0: return 34;   // one 32-value block
+        case FA_BACK_Q4_0: return 18;   // one 32-value block
         default: return 0;
     }
 }
@@ -54,7 +55,7 @@ int check_strides(const fa_back_tensor& t, bool rows16) {
     const int64_t es = elem_size(t.type);
     if (t.nb[0] != es) return FA_BACK_ESTRIDE;
     if (t.nb[1] <= 0 || t.nb[2] <= 0) return FA_BACK_ESTRIDE;
-    const int64_t a = rows16 ? 16 : (t.type == FA_BACK_Q8_0 ? 2 : es);
+    const int64_t a = rows16 ? 16 : (t.type == FA_BACK_Q8_0 || t.type == FA_BACK_Q4_0 ? 2 : es);
     if (t.nb[1] % a || t.nb[2] % a) return FA_BACK_ESTRIDE;
     return FA_BACK_OK;
 }
@@ -64,7 +65,8 @@ int validate(const fa_back_desc* d, Geometry* g) {
     const fa_back_tensor &q = d->q, &k = d->k, &v = d->v, &dd = d->d, &m = d->mask;
     // types
     auto is_act = [](int t) { return t == FA_BACK_F32 || t == FA_BACK_F16 || t == FA_BACK_BF16; };
-    auto is_kv = [&](int t) { return is_act(t) || t == FA_BACK_Q8_0; };
+    auto is_kv = [&](int t) { return is_act(t) || t == FA_BACK_Q8_0 || t == FA_BACK_Q4_0; };
+    auto is_blk = [](int t) { return t == FA_BACK_Q8_0 || t == FA_BACK_Q4_0; };
     if (!is_act(q.type) || !is_act(dd.type) || !is_kv(k.type) || !is_kv(v.type)) return FA_BACK_EUNSUPPORTED;
     const bool has_mask = m.type != FA_BACK_NONE;
     const bool causal = m.type == FA_BACK_CAUSAL_TAIL;   // implicit: no storage, no strides
@@ -81,8 +83,8 @@ int validate(const fa_back_desc* d, Geometry* g) {
     if (v.ne[1] != M || v.ne[2] != Hkv) return FA_BACK_ESHAPE;
     if (dd.ne[0] != Dv || dd.ne[1] != H || dd.ne[2] != N) return FA_BACK_ESHAPE;
     if (H % Hkv) return FA_BACK_ESHAPE;
-    if (k.type == FA_BACK_Q8_0 && D % 32) return FA_BACK_ESHAPE;
-    if (v.type == FA_BACK_Q8_0 && Dv % 32) return FA_BACK_ESHAPE;
+    if (is_blk(k.type) && D % 32) return FA_BACK_ESHAPE;
+    if (is_blk(v.type) && Dv % 32) return FA_BACK_ESHAPE;
     int64_t Hm = 0;
     if (has_mask) {
         if (m.ne[0] != M || m.ne[1] != N) return FA_BACK_ESHAPE;
@@ -93,7 +95,7 @@ int validate(const fa_back_desc* d, Geometry* g) {
     // strides: rows contiguous; F32/F16/BF16 cache rows are read with 16-byte loads
     int rc;
     if ((rc = check_strides(q, false)) || (rc = check_strides(dd, false))) return rc;
-    if ((rc = check_strides(k, k.type != FA_BACK_Q8_0)) || (rc = check_strides(v, v.type != FA_BACK_Q8_0)))
+    if ((rc = check_strides(k, !is_blk(k.type))) || (rc = check_strides(v, !is_blk(v.type))))
         return rc;
     if (has_mask && !causal && (rc = check_strides(m, false))) return rc;
     if (k.nb[1] >= ((int64_t)1 << 32) || v.nb[1] >= ((int64_t)1 << 32)) return FA_BACK_EUNSUPPORTED;
@@ -345,7 +347,7 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     if (!has_mask && mask) return FA_BACK_EINVAL;
     if (has_mask && !mask && (int64_t)g.M * g.N != 0) return FA_BACK_EINVAL;
     auto misaligned = [](const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) != 0; };
-    auto kv_align = [](int t) -> uintptr_t { return t == FA_BACK_Q8_0 ? 2 : 16; };
+    auto kv_align = [](int t) -> uintptr_t { return t == FA_BACK_Q8_0 || t == FA_BACK_Q4_0 ? 2 : 16; };
     if (misaligned(q, elem_size(ds.q.type)) || misaligned(d, elem_size(ds.d.type)) ||
         misaligned(k, kv_align(ds.k.type)) || misaligned(v, kv_align(ds.v.type)) ||
         (has_mask && misaligned(mask, elem_size(ds.mask.type))) || misaligned(out, kAlign) ||

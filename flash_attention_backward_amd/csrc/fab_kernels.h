@@ -312,11 +312,11 @@ FAB_DEV void mfma_cols(const _Float16* t, int kbase, const f16x8 b[2], f32x16* a
 //   S waves (0..3)  one row block each; q and dO fragments in registers. For every 32-key
 //                   sub-tile: S^T = K Q^T and dP^T = V dO^T, then walk 1 updates the online
 //                   softmax statistics, walk 2 forms dS = P (dP - delta) and hands it over
-//                   through LDS.
-//   K waves (4..7)  queue the DMA of the q8_0 bytes of sub-tile s+2 and decode K and V of
-//                   sub-tile s+1 into LDS while the S waves compute s; in walk 2 each also
-//                   holds the dQ accumulators of one row block and consumes the dS of sub-tile
-//                   s-1: dQ^T += K^T dS^T.
+//                   through LDS. They also queue the DMA of the raw q8_0 / q4_0 bytes of
+//                   sub-tile s+2.
+//   K waves (4..7)  decode K and V of sub-tile s+1 into LDS while the S waves compute s; in
+//                   walk 2 each also holds the dQ accumulators of one row block and consumes
+//                   the dS of sub-tile s-1: dQ^T += K^T dS^T.
 // A slot holds the K and V tiles of one sub-tile; three slots rotate (S waves at s, decode at
 // s+1, dQ at s-1), the staged bytes and the dS exchange are double-buffered; one barrier per
 // sub-tile. Every wave stays within 256 registers, so each SIMD runs an S wave and a K wave.
@@ -330,7 +330,7 @@ template <int D>
 struct QLds {
     static constexpr int kTile = kSubKeys * D * 2;                 // bytes of a K or V sub-tile
     static constexpr int kSlot = 2 * kTile;                        // K tile then V tile
-    static constexpr int kRaw = RawTile<D, kSubKeys>::kBytes;      // q8_0 bytes of one sub-tile
+    static constexpr int kRaw = RawTile<D, kSubKeys>::kBytes;      // block bytes of one sub-tile
     static constexpr int kOffSlot = 0;                             // 3 slots
     static constexpr int kOffRaw = kOffSlot + 3 * kSlot;           // [2][K, V] staged bytes
     static constexpr int kOffEx = kOffRaw + 4 * kRaw;              // [2][4 row blocks] dS, 2 KB
@@ -415,24 +415,24 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         const bool dead = (lse2 == pos_inf());
         const RowWalk<D> rw = make_row_walk<D>(lane);
 
-        const bool sdec = kSplitDecode && p.k_type == FA_BACK_Q8_0 && p.v_type == FA_BACK_Q8_0;
+        const bool sdec = kSplitDecode && is_block_type(p.k_type) && is_block_type(p.v_type);
         const char* kh = p.k + (int64_t)hk * p.k_nb2;
         const char* vh = p.v + (int64_t)hk * p.v_nb2;
         // the V half of sub-tile t, staged by the K waves
         auto sdecode = [&](int t) {
-            decode_q8_pair32<D>(kh, p.k_nb1, vh, p.v_nb1, t * kSubKeys, p.M, rawK(t), rawV(t),
+            decode_blk_pair32<D, false>(kh, p.k_nb1, p.k_type, vh, p.v_nb1, p.v_type, t * kSubKeys, p.M, rawK(t), rawV(t),
                                 (_Float16*)slot(t), (_Float16*)(slot(t) + L::kTile),
                                 Q8Pair<D>::UPT + w4, Q8Pair<D>::U, lane);
         };
-        // q8_0 bytes are staged by these waves: the LDS reads that follow the DMA here are
+        // block bytes are staged by these waves: the LDS reads that follow the DMA here are
         // plain loads, which the compiler does not hold back for the DMA in flight (it makes
         // transpose reads wait for it)
         RawDma<D, kSubKeys, 256> dk, dv;
-        dk.init(kh, p.k_nb1, s_begin * kSubKeys, w4 * 64 + lane);
-        dv.init(vh, p.v_nb1, s_begin * kSubKeys, w4 * 64 + lane);
+        dk.init(kh, p.k_nb1, block_row_bytes(p.k_type, D), s_begin * kSubKeys, w4 * 64 + lane);
+        dv.init(vh, p.v_nb1, block_row_bytes(p.v_type, D), s_begin * kSubKeys, w4 * 64 + lane);
         auto sdma = [&](int t) {
-            if (p.k_type == FA_BACK_Q8_0) dk.issue(rawK(t), p.M, w4);
-            if (p.v_type == FA_BACK_Q8_0) dv.issue(rawV(t), p.M, w4);
+            if (is_block_type(p.k_type)) dk.issue(rawK(t), p.M, w4);
+            if (is_block_type(p.v_type)) dv.issue(rawV(t), p.M, w4);
         };
         // prologue: sub-tile s_begin staged and decoded (V half here, K half by the K waves),
         // the bytes of s_begin+1 on their way
@@ -560,17 +560,23 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     const char* kh = p.k + (int64_t)hk * p.k_nb2;
     const char* vh = p.v + (int64_t)hk * p.v_nb2;
     const bool pairq8 = p.k_type == FA_BACK_Q8_0 && p.v_type == FA_BACK_Q8_0;
+    const bool pairblk = is_block_type(p.k_type) && is_block_type(p.v_type);
     auto kdecode = [&](int s) {
         _Float16* tk = (_Float16*)slot(s);
         _Float16* tv = (_Float16*)(slot(s) + L::kTile);
+        constexpr int last = kSplitDecode ? Q8Pair<D>::UPT : Q8Pair<D>::U;
         if (pairq8) {
-            decode_q8_pair32<D>(kh, p.k_nb1, vh, p.v_nb1, s * kSubKeys, p.M, rawK(s), rawV(s), tk, tv, kw,
-                                kSplitDecode ? Q8Pair<D>::UPT : Q8Pair<D>::U, lane);
+            decode_blk_pair32<D, true>(kh, p.k_nb1, p.k_type, vh, p.v_nb1, p.v_type, s * kSubKeys, p.M,
+                                       rawK(s), rawV(s), tk, tv, kw, last, lane);
+        } else if (__builtin_expect(pairblk, 0)) {
+            // laid out away from the q8_0 path: in its place it costs the q8_0 loop 6%
+            decode_blk_pair32<D, false>(kh, p.k_nb1, p.k_type, vh, p.v_nb1, p.v_type, s * kSubKeys, p.M,
+                                        rawK(s), rawV(s), tk, tv, kw, last, lane);
         } else {
             decode_tile<D, kSubKeys, 256>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, s * kSubKeys, p.M, rawK(s), tk, ktid);
             decode_tile<D, kSubKeys, 256>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), tv, ktid);
             // nothing of this path stays in flight: where the two paths join, the compiler
-            // would otherwise make the q8_0 path wait for its loads, and with them the DMA
+            // would otherwise make the block path wait for its loads, and with them the DMA
             wait_all_mem();
         }
     };
@@ -690,10 +696,12 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
         auto rawV = [&](int qt) { return raw0 + ((qt & 1) * 2 + 1) * L::kRaw; };
         auto stage = [&](int qt) {
             const int j0 = key0 + qt * kQTileKeys;
-            if (p.k_type == FA_BACK_Q8_0)
-                dma_raw_tile<D, kQTileKeys, kW1Threads>(p.k, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK(qt), threadIdx.x);
-            if (p.v_type == FA_BACK_Q8_0)
-                dma_raw_tile<D, kQTileKeys, kW1Threads>(p.v, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV(qt), threadIdx.x);
+            if (is_block_type(p.k_type))
+                dma_raw_tile<D, kQTileKeys, kW1Threads>(p.k, p.k_nb1, p.k_nb2, hk, j0, p.M,
+                                                        block_row_bytes(p.k_type, D), rawK(qt), threadIdx.x);
+            if (is_block_type(p.v_type))
+                dma_raw_tile<D, kQTileKeys, kW1Threads>(p.v, p.v_nb1, p.v_nb2, hk, j0, p.M,
+                                                        block_row_bytes(p.v_type, D), rawV(qt), threadIdx.x);
         };
         // the bytes of quarter qt+1 are on their way while quarter qt is decoded
         stage(0);
@@ -1036,20 +1044,23 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p) {
 // the dS prescale needs a bound of |dp - delta| that walk 1 would have measured, taken here
 // as sum_c |dO_c| * max |v| + |delta| (Hoelder), which holds for every key.
 
-// Partial max |v| over the cache: for q8_0 the block scale times 128 (|q| <= 128), otherwise
+// Partial max |v| over the cache: for q8_0 / q4_0 the block scale times 128 / 8, otherwise
 // every element. Grid-stride over V rows; partial per block.
 static __global__ __launch_bounds__(kThreads) void vmax_kernel(Params p) {
     float vm = 0.0f;
     const int64_t rows = (int64_t)p.M * p.Hkv;
-    if (p.v_type == FA_BACK_Q8_0) {
+    if (p.v_type == FA_BACK_Q8_0 || p.v_type == FA_BACK_Q4_0) {
+        // block scale times the largest |q|: 128 (q8_0) or 8 (q4_0)
+        const int bsz = p.v_type == FA_BACK_Q8_0 ? 34 : 18;
+        const float qmax = p.v_type == FA_BACK_Q8_0 ? 128.0f : 8.0f;
         const int bpr = p.D / 32;
         const int64_t n = rows * bpr;
         for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += (int64_t)gridDim.x * kThreads) {
             const int64_t row = e / bpr;
             const int b = (int)(e - row * bpr);
             const int hk = (int)(row / p.M), j = (int)(row - (int64_t)hk * p.M);
-            const char* blk = p.v + (int64_t)hk * p.v_nb2 + (int64_t)j * p.v_nb1 + 34 * b;
-            vm = fmaxf(vm, fabsf((float)*(const _Float16*)blk) * 128.0f);
+            const char* blk = p.v + (int64_t)hk * p.v_nb2 + (int64_t)j * p.v_nb1 + bsz * b;
+            vm = fmaxf(vm, fabsf((float)*(const _Float16*)blk) * qmax);
         }
     } else {
         const int64_t n = rows * p.D;
@@ -1237,10 +1248,12 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
         for (int half = 0; half < 2; ++half) {
             const int j0 = key0 + half * kQTileKeys;
             __syncthreads();
-            if (p.k_type == FA_BACK_Q8_0)
-                dma_raw_tile<D, kQTileKeys, kKVThreads>(p.k, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, threadIdx.x);
-            if (p.v_type == FA_BACK_Q8_0)
-                dma_raw_tile<D, kQTileKeys, kKVThreads>(p.v, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV, threadIdx.x);
+            if (is_block_type(p.k_type))
+                dma_raw_tile<D, kQTileKeys, kKVThreads>(p.k, p.k_nb1, p.k_nb2, hk, j0, p.M,
+                                                        block_row_bytes(p.k_type, D), rawK, threadIdx.x);
+            if (is_block_type(p.v_type))
+                dma_raw_tile<D, kQTileKeys, kKVThreads>(p.v, p.v_nb1, p.v_nb2, hk, j0, p.M,
+                                                        block_row_bytes(p.v_type, D), rawV, threadIdx.x);
             wait_all_mem();
             __syncthreads();
             decode_tile<D, kQTileKeys, kKVThreads>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, sK,

@@ -148,10 +148,15 @@ FAB_DEV void dma_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// ----------------------------------------------------------------------------- q8_0 rows
+// ----------------------------------------------------------------------------- block rows
 
-// q8_0 row geometry: D/32 blocks of 34 bytes; a row's bytes are staged in LDS as the
-// 16-byte-aligned chunks that cover it (the row may start at any even address).
+// q8_0 and q4_0 rows are staged raw in LDS and decoded from there.
+FAB_DEV bool is_block_type(int type) { return type == FA_BACK_Q8_0 || type == FA_BACK_Q4_0; }
+// bytes of one row of D values: D/32 blocks of 34 (q8_0) or 18 (q4_0) bytes
+FAB_DEV int block_row_bytes(int type, int D) { return D / 32 * (type == FA_BACK_Q8_0 ? 34 : 18); }
+
+// Staged row geometry, sized for q8_0 (the longer block row): a row's bytes are staged in LDS
+// as the 16-byte-aligned chunks that cover it (the row may start at any even address).
 // The slot of a row in LDS has an odd number of 16-byte chunks, so that dword reads of the
 // same block of 16 consecutive keys spread over the banks.
 template <int D>
@@ -166,12 +171,13 @@ struct RawTile {
     static constexpr int kBytes = KEYS * Q8Row<D>::kSlot + 16;
 };
 
-// Issue the DMA of the raw bytes of keys [j0, j0+KEYS) of head hk into `raw` (q8_0 only).
-// Chunk idx = key*kChunks + c lands at raw + 16*idx; chunks outside the row are skipped.
+// Issue the DMA of the raw bytes of keys [j0, j0+KEYS) of head hk into `raw` (block types
+// only; rbytes = bytes of one row, at most Q8Row<D>::kBytes). Chunk idx = key*kChunks + c lands
+// at raw + 16*idx; chunks outside the row are skipped.
 // NT threads take part, tid = 0 .. NT-1 being this thread's index among them.
 template <int D, int KEYS, int NT>
 FAB_DEV void dma_raw_tile(const char* base, int64_t nb1, int64_t nb2, int hk, int j0, int M,
-                          unsigned char* raw, int tid) {
+                          int rbytes, unsigned char* raw, int tid) {
     using R = Q8Row<D>;
     constexpr int NCH = KEYS * R::kChunks;
     constexpr int IT = (NCH + NT - 1) / NT;
@@ -191,7 +197,7 @@ FAB_DEV void dma_raw_tile(const char* base, int64_t nb1, int64_t nb2, int hk, in
             const uintptr_t a = (uintptr_t)(hbase + (int64_t)j * nb1);
             const uintptr_t a0 = a & ~(uintptr_t)15;
             src = a0 + 16u * (uintptr_t)c;
-            ok = src < a + R::kBytes;      // only chunks holding bytes of this row
+            ok = src < a + (uintptr_t)rbytes;      // only chunks holding bytes of this row
         }
         if (ok) dma16((const void*)src, raw + 16 * wbase);
     }
@@ -212,6 +218,21 @@ FAB_DEV f16x8 decode8(const char* rowp, int type, int grp, const unsigned char*,
         }
     } else if (type == FA_BACK_F16) {
         r = *(const f16x8*)(rowp + 16 * grp);
+    } else if (type == FA_BACK_Q4_0) {
+        // values 8*grp .. +7: block grp/4, elements 8*(grp%4) ..; elements t < 16 are the low
+        // nibbles of bytes t, elements t >= 16 the high nibbles of bytes t - 16. The row is
+        // 2-byte aligned: the scale and the 8 bytes are read as halfwords. (nibble - 8) * scale
+        // is exact in fp32 and rounds once to fp16, as an F32 cache holding it would.
+        const char* blk = rowp + 18 * (grp >> 2);
+        const float dsc = (float)*(const _Float16*)blk;
+        const unsigned short* qs = (const unsigned short*)(blk + 2 + 8 * (grp & 1));
+        const int sh = (grp & 2) ? 4 : 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const unsigned int w = qs[t];
+            r[2 * t] = (_Float16)((float)((int)((w >> sh) & 15u) - 8) * dsc);
+            r[2 * t + 1] = (_Float16)((float)((int)((w >> (8 + sh)) & 15u) - 8) * dsc);
+        }
     } else {   // BF16
         const u32x4 a = *(const u32x4*)(rowp + 16 * grp);
 #pragma unroll
@@ -257,16 +278,66 @@ FAB_DEV void decode_q8_block(const unsigned char* slot, int off, int blk, f16x8 
     }
 }
 
+// One 32-value q4_0 block of a staged row decoded to fp16: out[c] holds values 8c .. 8c+7.
+// Value t < 16 is the low nibble of byte t, value t >= 16 the high nibble of byte t - 16. A
+// nibble n placed under the fp16 exponent pattern 0x64 reads as 1024 + n; subtracting 1032
+// gives n - 8 exactly, and one fp16 product with the scale rounds (n - 8) * d once, which is
+// the fp16 an F32 cache holding that value gives. Both steps run on packed fp16 pairs.
+FAB_DEV void decode_q4_block(const unsigned char* slot, int off, int blk, f16x8 out[4]) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const int base = off + 18 * blk;                  // fp16 scale (even offset)
+    const int qb = base + 2;                          // first byte of nibbles
+    const int sh = qb & 3;
+    const unsigned int* wp = (const unsigned int*)(slot + (qb & ~3));
+    unsigned int w[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) w[k] = wp[k];
+    const unsigned short sb = *(const unsigned short*)(slot + base);
+    const _Float16 dh = __builtin_bit_cast(_Float16, sb);
+    const h2 d2 = {dh, dh};
+    const h2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {                     // bytes 4k .. 4k+3
+        const unsigned int x = __builtin_amdgcn_alignbyte(w[k + 1], w[k], sh);
+        const unsigned int lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+        const h2 l01 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u));
+        const h2 l23 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u));
+        const h2 h01 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u));
+        const h2 h23 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u));
+        const h2 a = (l01 + bias) * d2, b = (l23 + bias) * d2;
+        const h2 c = (h01 + bias) * d2, e = (h23 + bias) * d2;
+        f16x8& ol = out[k >> 1];
+        f16x8& oh = out[2 + (k >> 1)];
+        const int o = 4 * (k & 1);
+        ol[o + 0] = a.x;
+        ol[o + 1] = a.y;
+        ol[o + 2] = b.x;
+        ol[o + 3] = b.y;
+        oh[o + 0] = c.x;
+        oh[o + 1] = c.y;
+        oh[o + 2] = e.x;
+        oh[o + 3] = e.y;
+    }
+}
+
+// Block blk of a staged q8_0 or q4_0 row.
+FAB_DEV void decode_block(int type, const unsigned char* slot, int off, int blk, f16x8 out[4]) {
+    if (type == FA_BACK_Q8_0)
+        decode_q8_block(slot, off, blk, out);
+    else
+        decode_q4_block(slot, off, blk, out);
+}
+
 // Decode keys [j0, j0+KEYS) into the swizzled fp16 tile dst[key][D]. Keys >= M become 0.
 // NT threads take part, tid = 0 .. NT-1 being this thread's index among them.
-//   q8_0: one item = one 32-value block of a key (from the staged raw bytes)
+//   q8_0, q4_0: one item = one 32-value block of a key (from the staged raw bytes)
 //   F32/F16/BF16: one item = 8 values of a key, read from global memory; every load of the
 //   thread is issued before the first conversion
 template <int D, int KEYS, int NT>
 FAB_DEV void decode_tile(const char* base, int type, int64_t nb1, int64_t nb2, int hk, int j0,
                          int M, const unsigned char* raw, _Float16* dst, int tid) {
     const char* hbase = base + (int64_t)hk * nb2;
-    if (type == FA_BACK_Q8_0) {
+    if (is_block_type(type)) {
         constexpr int BPR = D / 32;                    // blocks per row
         constexpr int ITEMS = KEYS * BPR;
         for (int item = tid; item < ITEMS; item += NT) {
@@ -275,7 +346,7 @@ FAB_DEV void decode_tile(const char* base, int type, int64_t nb1, int64_t nb2, i
             f16x8 out[4];
             if (j < M) {
                 const int off = (int)((uintptr_t)(hbase + (int64_t)j * nb1) & 15);
-                decode_q8_block(raw + key * Q8Row<D>::kSlot, off, blk, out);
+                decode_block(type, raw + key * Q8Row<D>::kSlot, off, blk, out);
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
@@ -308,7 +379,8 @@ FAB_DEV void decode_tile(const char* base, int type, int64_t nb1, int64_t nb2, i
     }
 }
 
-// K and V q8_0 sub-tiles of 32 keys decoded together by 256 threads (4 waves). One item is
+// K and V block-type (q8_0, q4_0) sub-tiles of 32 keys decoded together by 256 threads (4
+// waves). One item is
 // one 32-value block of one key. A wave-instruction covers 16 keys in the order
 // 0,1,4,5,8,9,12,13,2,3,6,7,10,11,14,15 (plus 16 for the second half) times min(4, D/32)
 // blocks, so that the 16-byte stores of 16 lanes land on 16 distinct bank groups of the
@@ -325,11 +397,13 @@ struct Q8Pair {
     static constexpr int U = 2 * UPT;                 // wave-instructions per sub-tile pair
 };
 
-// Wave-instruction u (0 .. U-1; K first, then V) of the pair decode.
-template <int D>
-FAB_DEV void decode_q8_item(const char* kh, int64_t knb1, const char* vh, int64_t vnb1, int j0, int M,
-                            const unsigned char* rawk, const unsigned char* rawv, _Float16* dstk,
-                            _Float16* dstv, int u, int lane) {
+// Wave-instruction u (0 .. U-1; K first, then V) of the pair decode. Q8 (compile time): both
+// tensors are q8_0, with no test of the type in the decode.
+template <int D, bool Q8>
+FAB_DEV void decode_blk_item(const char* kh, int64_t knb1, int ktype, const char* vh, int64_t vnb1,
+                             int vtype, int j0, int M, const unsigned char* rawk,
+                             const unsigned char* rawv, _Float16* dstk, _Float16* dstv, int u,
+                             int lane) {
     using Q = Q8Pair<D>;
     const bool isv = u >= Q::UPT;
     const int uu = isv ? u - Q::UPT : u;
@@ -341,7 +415,11 @@ FAB_DEV void decode_q8_item(const char* kh, int64_t knb1, const char* vh, int64_
         const char* h = isv ? vh : kh;
         const int64_t nb1 = isv ? vnb1 : knb1;
         const int off = (int)(((uint32_t)(uintptr_t)h + (uint32_t)j * (uint32_t)nb1) & 15u);
-        decode_q8_block((isv ? rawv : rawk) + key * Q8Row<D>::kSlot, off, blk, o);
+        const unsigned char* slot = (isv ? rawv : rawk) + key * Q8Row<D>::kSlot;
+        if (Q8)
+            decode_q8_block(slot, off, blk, o);
+        else
+            decode_block(isv ? vtype : ktype, slot, off, blk, o);
     } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
@@ -354,18 +432,19 @@ FAB_DEV void decode_q8_item(const char* kh, int64_t knb1, const char* vh, int64_
 }
 
 // The wave-instructions u = first, first + 4, ... below `last` for one of 4 waves.
-template <int D>
-FAB_DEV void decode_q8_pair32(const char* kh, int64_t knb1, const char* vh, int64_t vnb1, int j0, int M,
-                              const unsigned char* rawk, const unsigned char* rawv, _Float16* dstk,
-                              _Float16* dstv, int first, int last, int lane) {
+template <int D, bool Q8>
+FAB_DEV void decode_blk_pair32(const char* kh, int64_t knb1, int ktype, const char* vh, int64_t vnb1,
+                               int vtype, int j0, int M, const unsigned char* rawk,
+                               const unsigned char* rawv, _Float16* dstk, _Float16* dstv, int first,
+                               int last, int lane) {
 #pragma unroll
     for (int u = first; u < Q8Pair<D>::U; u += 4) {
         if (u >= last) break;                          // wave-uniform
-        decode_q8_item<D>(kh, knb1, vh, vnb1, j0, M, rawk, rawv, dstk, dstv, u, lane);
+        decode_blk_item<D, Q8>(kh, knb1, ktype, vh, vnb1, vtype, j0, M, rawk, rawv, dstk, dstv, u, lane);
     }
 }
 
-// DMA of consecutive q8_0 sub-tiles (KEYS keys each, sub-tile after sub-tile) into a staging
+// DMA of consecutive q8_0 or q4_0 sub-tiles (KEYS keys each, sub-tile after sub-tile) into a staging
 // buffer by NT threads; the row stride must be below 2^32. When the stride is a multiple of 16
 // every row has the same alignment, so a chunk's source address only advances by KEYS rows from
 // one sub-tile to the next and whether it holds bytes of its row never changes: a lane keeps the
@@ -379,15 +458,17 @@ struct RawDma {
     static constexpr int IT = (NCH + NT - 1) / NT;
     const char* base;      // the head's key 0 (wave-uniform)
     uint32_t nb1;          // row stride in bytes
+    uint32_t rbytes;       // bytes of one row (at most R::kBytes)
     int j0;                // first key of the next sub-tile (wave-uniform)
     bool fixed;            // nb1 % 16 == 0 (wave-uniform)
     int kc[IT];            // key | (chunk byte offset << 8); -1 past the last chunk
     uint64_t src[IT];      // source of chunk `it` of the next sub-tile (fixed strides)
     bool on[IT];           // chunk `it` holds bytes of its row (fixed strides)
 
-    FAB_DEV void init(const char* hbase, int64_t row_stride, int first_key, int tid) {
+    FAB_DEV void init(const char* hbase, int64_t row_stride, int row_bytes, int first_key, int tid) {
         base = hbase;
         nb1 = (uint32_t)row_stride;
+        rbytes = (uint32_t)row_bytes;
         j0 = first_key;
         fixed = (nb1 & 15u) == 0;
 #pragma unroll
@@ -398,7 +479,7 @@ struct RawDma {
             const int c16 = kc[it] >> 8;
             const uint64_t a = (uint64_t)(uintptr_t)base + (uint64_t)(uint32_t)(j0 + key) * nb1;
             src[it] = (a & ~(uint64_t)15) + (uint32_t)c16;
-            on[it] = kc[it] >= 0 && (uint32_t)c16 < (uint32_t)(a & 15) + (uint32_t)R::kBytes;
+            on[it] = kc[it] >= 0 && (uint32_t)c16 < (uint32_t)(a & 15) + rbytes;
         }
     }
     // wave: this thread's wave among the NT threads (uniform); raw: staging buffer
@@ -422,7 +503,7 @@ struct RawDma {
                 const uint64_t a = (uint64_t)(uintptr_t)base + (uint64_t)(uint32_t)j * nb1;
                 const uint64_t sa = (a & ~(uint64_t)15) + (uint32_t)c16;
                 // only chunks holding bytes of this row
-                if (kc[it] >= 0 && j < M && (uint32_t)c16 < (uint32_t)(a & 15) + (uint32_t)R::kBytes)
+                if (kc[it] >= 0 && j < M && (uint32_t)c16 < (uint32_t)(a & 15) + rbytes)
                     dma16((const void*)(uintptr_t)sa, raw + 16 * wbase);
                 src[it] += step;
             }

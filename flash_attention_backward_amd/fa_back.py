@@ -14,10 +14,11 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa_back.so")
 
-NONE, F32, F16, BF16, Q8_0 = -1, 0, 1, 2, 8
+NONE, F32, F16, BF16, Q8_0, Q4_0 = -1, 0, 1, 2, 8, 9
 CAUSAL_TAIL = 16   # mask type only: query i sees keys j <= M - N + i, nothing stored
-TYPE_IDS = {"none": NONE, "f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "causal_tail": CAUSAL_TAIL}
-ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, Q8_0: 34}
+TYPE_IDS = {"none": NONE, "f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0,
+            "causal_tail": CAUSAL_TAIL}
+ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, Q8_0: 34, Q4_0: 18}
 
 OK, EINVAL, ESHAPE, ESTRIDE, EUNSUPPORTED, EHIP, EALIGN = 0, -1, -2, -3, -4, -5, -6
 
@@ -179,7 +180,7 @@ def _ggml(x: np.ndarray, typ: str, ne0: int):
         s2 = x.itemsize
         s1 = max(c, 1) * s2
         s0 = max(b, 1) * s1
-    if typ == "q8_0":
+    if typ in ("q8_0", "q4_0"):
         assert s2 == 1
     else:
         assert s2 == x.itemsize == nb0

@@ -18,8 +18,8 @@
  *
  * Tensors are described ggml-style: ne[] are extents innermost first, nb[] byte strides.
  *     q    ne = {D,  N, H  }   F32 | F16 | BF16
- *     k    ne = {D,  M, Hkv}   F32 | F16 | BF16 | Q8_0   (K and V types are independent)
- *     v    ne = {Dv, M, Hkv}   F32 | F16 | BF16 | Q8_0
+ *     k    ne = {D,  M, Hkv}   F32 | F16 | BF16 | Q8_0 | Q4_0   (K and V types independent)
+ *     v    ne = {Dv, M, Hkv}   F32 | F16 | BF16 | Q8_0 | Q4_0
  *     d    ne = {Dv, H, N  }   F32 | F16 | BF16          (dO; note the H, N order, as the
  *                                                         operator's "Layout and shape" states)
  *     mask ne = {M,  N, Hm }   F32 | F16, Hm in {1, H}; type FA_BACK_NONE for no mask;
@@ -31,7 +31,10 @@
  * nb[0] must equal the element size (34 bytes per 32-value block for Q8_0), i.e. each row
  * is contiguous; rows and heads may have any positive stride (e.g. a cache view whose heads
  * are interleaved per cell). A Q8_0 block is a little-endian fp16 scale followed by 32 int8;
- * its value is scale * int8.
+ * its value is scale * int8. A Q4_0 block (18 bytes, nb[0] = 18) is a little-endian fp16
+ * scale followed by 16 bytes; byte t holds element t in its low nibble and element t + 16 in
+ * its high nibble, and an element's value is scale * (nibble - 8) (the ggml q4_0 block, the
+ * format of the served cache on the "torad-labs/llama.cpp PR #71" page).
  *
  * Output: one packed F32 buffer, laid out as the operator's packed result (first review,
  * "Layout and shape"; second review, output index):
@@ -54,7 +57,7 @@
  *
  * Supported: D == Dv in {64, 128, 256}; H % Hkv == 0; N, M >= 0 (N == 0: dK = dV = 0;
  * M == 0: every row is fully masked); F32/F16/BF16 K or V rows 16-byte aligned (base and
- * strides); Q8_0 rows 2-byte aligned; K and V row strides (nb[1]) below 2^32 bytes.
+ * strides); Q8_0 and Q4_0 rows 2-byte aligned; K and V row strides (nb[1]) below 2^32 bytes.
  */
 #ifndef FA_BACK_H
 #define FA_BACK_H
@@ -72,6 +75,7 @@ extern "C" {
 #define FA_BACK_F16 1
 #define FA_BACK_BF16 2
 #define FA_BACK_Q8_0 8
+#define FA_BACK_Q4_0 9
 #define FA_BACK_CAUSAL_TAIL 16 /* mask only: query i sees keys j <= M - N + i; no storage */
 
 /* status codes (no entry point aborts or exits) */

@@ -23,6 +23,9 @@ Readings where the pages are silent or ambiguous:
   - scale enters as float64(float32(scale)), as the operator's parameter is a float.
   - a row is fully masked iff every one of its M mask entries is -inf.
   - q8_0 block = fp16 scale (little-endian) then 32 int8; value = float64(scale) * q.
+  - q4_0 (the served cache's type on the "torad-labs/llama.cpp PR #71" page; the pages do not
+    spell out its block): the ggml block, fp16 scale then 16 bytes, byte t holding element t
+    in its low nibble and element t + 16 in its high one; value = float64(scale) * (nibble - 8).
 Every function here is pinned by tests/test_oracle_*.py (finite differences, a hand-worked
 example, closed forms, invariants and an independent pure-Python loop implementation).
 """
@@ -57,6 +60,18 @@ def widen(x: np.ndarray, typ: str, width: int | None = None) -> np.ndarray:
         step = np.ascontiguousarray(blocks[..., 0:2]).view(np.float16)[..., 0].astype(np.float64)
         qv = np.ascontiguousarray(blocks[..., 2:34]).view(np.int8).astype(np.float64)
         return (step[..., None] * qv).reshape(*raw.shape[:-1], nblk * 32)
+    if typ == "q4_0":
+        # 18-byte blocks: fp16 scale, then 16 bytes; byte t holds element t (low nibble) and
+        # element t + 16 (high nibble); value = scale * (nibble - 8)
+        raw = np.asarray(x, dtype=np.uint8)
+        nblk = raw.shape[-1] // 18
+        if width is not None and nblk * 32 != width:
+            raise ValueError("q4_0 row width mismatch")
+        blocks = np.ascontiguousarray(raw).reshape(*raw.shape[:-1], nblk, 18)
+        step = np.ascontiguousarray(blocks[..., 0:2]).view(np.float16)[..., 0].astype(np.float64)
+        qs = blocks[..., 2:18].astype(np.int64)
+        nib = np.concatenate([qs & 15, qs >> 4], axis=-1).astype(np.float64) - 8.0
+        return (step[..., None] * nib).reshape(*raw.shape[:-1], nblk * 32)
     raise ValueError(f"unknown type {typ}")
 
 

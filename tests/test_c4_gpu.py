@@ -3,7 +3,8 @@
 The N=8 and N=16 pilots (last rows of the same draws, same cache) are checked against the
 full oracle. The full N=2048 run, in the launch configuration the benchmark times, is checked
 on sampled query rows (dQ, LSE, delta) and sampled keys (dK, dV), each computed whole by the
-oracle; the pilots' rows must also equal the full run's last rows (same inputs)."""
+oracle. The q4_0 pilot (c4q4n16: the same draws with the cache encoded q4_0) is checked
+against the full oracle too."""
 import numpy as np
 import pytest
 
@@ -14,7 +15,7 @@ from tests.gpu_util import compare, run_gpu, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["c4n8", "c4n16"])
+@pytest.mark.parametrize("name", ["c4n8", "c4n16", "c4q4n16"])
 def test_pilots_full_oracle(name):
     p = fa_inputs.make(name)
     got, _, _ = run_gpu(p)

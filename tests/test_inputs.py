@@ -72,3 +72,20 @@ def test_near_constant_v_is_bf16_rounded():
     p = fa_inputs.make_custom("nc", D=32, N=8, M=16, v_offset=1.0, v_spread=1e-3, v_type="bf16")
     vals = np.unique(O.widen(p.v, "bf16"))
     assert set(vals.tolist()) <= {1.0 - 2.0 ** -8, 1.0, 1.0 + 2.0 ** -7}
+
+
+def test_q4_0_encoding_round_trip_error():
+    # every code in [0, 15]; the decoded values within one step of the drawn ones (the value of
+    # largest magnitude maps to code 0, so the other side clips at code 15 = +7 steps)
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((3, 5, 64)).astype(np.float32)
+    x[0, 0, :32] = 0.0                                  # an all-zero block
+    raw = fa_inputs.encode_q4_0(x)
+    assert raw.shape == (3, 5, 36) and raw.dtype == np.uint8
+    blocks = raw.reshape(3, 5, 2, 18)
+    step = blocks[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64)
+    codes = np.concatenate([blocks[..., 2:] & 15, blocks[..., 2:] >> 4], axis=-1).astype(np.float64)
+    dec = step[..., None] * (codes - 8.0)
+    err = np.abs(dec - x.reshape(3, 5, 2, 32).astype(np.float64))
+    assert np.all(err <= np.abs(step)[..., None] * (1 + 1e-3) + 1e-6)
+    assert np.all(dec[0, 0, 0] == 0.0)

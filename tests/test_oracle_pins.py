@@ -224,6 +224,41 @@ def test_q8_0_decoding_of_hand_built_blocks(golden_dir):
     np.testing.assert_array_equal(got.ravel(), np.array(expect))
 
 
+def test_q4_0_decoding_of_hand_built_blocks(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "q4_0_blocks.json")))
+    raw = bytearray()
+    expect = []
+    for b in g["blocks"]:
+        h = int(b["scale_fp16_hex"], 16)
+        raw += bytes([h & 0xFF, h >> 8]) + bytes(b["bytes"])
+        expect += b["values"]
+    arr = np.frombuffer(bytes(raw), dtype=np.uint8).reshape(1, 1, -1)
+    got = O.widen(arr, "q4_0", 32 * len(g["blocks"]))
+    np.testing.assert_array_equal(got.ravel(), np.array(expect))
+
+
+def test_q4_0_run_equals_dequantised_f32_run():
+    p = fa_inputs.make_custom(name="q4", D=64, H=4, Hkv=2, N=9, M=40, mask="tail",
+                              k_type="q4_0", v_type="q4_0")
+    # hand decode by integer nibble arithmetic (not the oracle's decoder)
+    def dec(raw):
+        raw = np.asarray(raw)
+        out = np.empty(raw.shape[:-1] + (raw.shape[-1] // 18 * 32,))
+        for b in range(raw.shape[-1] // 18):
+            s = raw[..., 18 * b].astype(np.uint16) | (raw[..., 18 * b + 1].astype(np.uint16) << 8)
+            sc = s.view(np.float16).astype(np.float64)[..., None]
+            body = raw[..., 18 * b + 2:18 * b + 18].astype(np.int64)
+            out[..., 32 * b:32 * b + 16] = sc * ((body % 16) - 8)
+            out[..., 32 * b + 16:32 * b + 32] = sc * ((body // 16) - 8)
+        return out
+    kf, vf = dec(p.k), dec(p.v)
+    a = O.run_problem(p)
+    q, _, _, do, mask = O.problem_arrays(p)
+    b = O.flash_attn_back(q, kf, vf, do, mask, p.scale)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+
+
 def test_bf16_widening_of_hand_built_bits():
     bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x4049, 0x0001], dtype=np.uint16)
     expect = [1.0, -2.0, 1.0 + 2.0 ** -7, 0.0, -0.0, 3.140625, 2.0 ** -133]

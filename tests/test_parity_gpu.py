@@ -52,6 +52,11 @@ RAGGED = [
     dict(name="dead_row_blocks", D=128, H=2, Hkv=1, N=200, M=300, mask="random",
          masked_rows=[(0, i) for i in list(range(48, 64)) + list(range(160, 176))],
          k_type="q8_0", v_type="q8_0"),
+    # q4_0 caches (the served cache type), alone and beside the other types
+    dict(name="q4_0_kv", D=128, H=8, Hkv=2, N=64, M=512, mask="none", k_type="q4_0", v_type="q4_0"),
+    dict(name="q4_0_d256_tail", D=256, H=6, Hkv=1, N=40, M=333, mask="tail", k_type="q4_0", v_type="q4_0"),
+    dict(name="q4_0_k_q8_0_v", D=64, H=4, Hkv=2, N=33, M=150, mask="tail", k_type="q4_0", v_type="q8_0"),
+    dict(name="f16_k_q4_0_v", D=128, H=2, Hkv=1, N=20, M=100, mask="random", k_type="f16", v_type="q4_0"),
     # two row blocks per KV head at D=256: the key side's list holds exactly two entries
     dict(name="kv_two_blocks", D=256, H=2, Hkv=1, N=32, M=200, mask="tail", k_type="q8_0", v_type="f16"),
     # four row blocks, the first and the last fully masked: only the middle two are listed
@@ -109,6 +114,23 @@ def test_q8_0_equals_dequantised_f32_bitwise():
     got_f32, _, _ = run_gpu(q)
     for k in got_q8:
         assert np.array_equal(got_q8[k].view(np.uint32), got_f32[k].view(np.uint32)), k
+
+
+@pytest.mark.parametrize("mode", ["rows", "keys"])
+def test_q4_0_equals_dequantised_f32_bitwise(mode, monkeypatch):
+    # every q4_0 value is exact in F32 and rounds once to fp16 on both paths
+    monkeypatch.setenv("FA_BACK_WALK1", mode)
+    p = fa_inputs.make_custom(name="q4_bits", D=128, H=4, Hkv=2, N=37, M=200, mask="tail",
+                              k_type="q4_0", v_type="q4_0")
+    f = fa_inputs.Problem(**{**p.__dict__})
+    f.name = "q4_bits_f32"
+    f.k = O.widen(p.k, "q4_0", p.D).astype(np.float32)
+    f.v = O.widen(p.v, "q4_0", p.Dv).astype(np.float32)
+    f.k_type = f.v_type = "f32"
+    a, _, _ = run_gpu(p)
+    b, _, _ = run_gpu(f)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
 
 
 def test_strided_cache_equals_contiguous_bitwise():
