@@ -60,6 +60,7 @@ class Problem:
     mask_type: str = "none"
     seed: int = 0
     note: str = ""
+    flags: int = 0          # descriptor flags (1: centre V before its fp16 rounding)
 
     @property
     def Hm(self) -> int:
@@ -253,7 +254,7 @@ def make(name: str, seed: int = 0, mask_type: str = "f16") -> Problem:
 def make_custom(name="custom", *, D=64, H=2, Hkv=1, N=16, M=64, seed=0, q_type="f32",
                 k_type="f32", v_type="f32", d_type="f32", mask="tail", mask_type="f16",
                 Hm=1, scale=None, v_offset=0.0, v_spread=1.0, d_mult=1.0,
-                masked_rows=(), **_ignored) -> Problem:
+                masked_rows=(), flags=0, **_ignored) -> Problem:
     """A parameterised case with the same draw order and distributions as the named configs.
 
     mask: 'none' | 'tail' | 'random' (iid -inf with prob 0.3) ; masked_rows: (hm, i) pairs
@@ -277,7 +278,7 @@ def make_custom(name="custom", *, D=64, H=2, Hkv=1, N=16, M=64, seed=0, q_type="
                    encode(q, q_type) if q_type != "f32" else q, q_type,
                    encode(k, k_type), k_type, encode(v, v_type), v_type,
                    encode(do, d_type) if d_type != "f32" else do, d_type,
-                   m, "none" if m is None else mask_type, seed)
+                   m, "none" if m is None else mask_type, seed, flags=flags)
 
 
 # ----------------------------------------------------------------------------- workload size

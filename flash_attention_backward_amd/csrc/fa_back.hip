@@ -45,6 +45,7 @@ struct Geometry {
     // workspace offsets (bytes)
     uint64_t ws_absmax, ws_scal, ws_qr, ws_dr;
     uint64_t ws_pm, ws_pl, ws_pd, ws_pb, ws_lse2, ws_dlt, ws_bound, ws_dqp, ws_mcls, ws_kvp, ws_vmax;
+    uint64_t ws_vcen;      // [Hkv][D] V centre (FA_BACK_FLAG_CENTER_V only)
 };
 
 bool tensor_nonneg(const fa_back_tensor& t) {
@@ -72,6 +73,8 @@ int validate(const fa_back_desc* d, Geometry* g) {
     const bool causal = m.type == FA_BACK_CAUSAL_TAIL;   // implicit: no storage, no strides
     if (has_mask && !causal && m.type != FA_BACK_F32 && m.type != FA_BACK_F16) return FA_BACK_EUNSUPPORTED;
     if (!std::isfinite(d->scale)) return FA_BACK_EINVAL;
+    if (d->flags & ~FA_BACK_FLAG_CENTER_V) return FA_BACK_EINVAL;
+    if ((d->flags & FA_BACK_FLAG_CENTER_V) && is_blk(v.type)) return FA_BACK_EUNSUPPORTED;
     if (!tensor_nonneg(q) || !tensor_nonneg(k) || !tensor_nonneg(v) || !tensor_nonneg(dd) ||
         (has_mask && !tensor_nonneg(m)))
         return FA_BACK_EINVAL;
@@ -205,6 +208,7 @@ int validate(const fa_back_desc* d, Geometry* g) {
     g->ws_mcls = take(stored_mask ? (uint64_t)(Hm == 1 ? 1 : g->Hkv) * g->RB * g->KT : 0);
     g->ws_kvp = take(4ull * g->kv_tail * g->kv_split * 2 * kKVKeys * D);
     g->ws_vmax = take(4ull * kVmaxBlocks);   // fa_back_run_saved only
+    g->ws_vcen = take((d->flags & FA_BACK_FLAG_CENTER_V) ? 4ull * g->Hkv * D : 0);
     L.workspace_bytes = std::max<uint64_t>(o, kAlign);
     return FA_BACK_OK;
 }
@@ -235,6 +239,7 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
         return hipGetLastError() == hipSuccess ? FA_BACK_OK : FA_BACK_EHIP;
     }
     hipLaunchKernelGGL(absmax_kernel, dim3(g.npart), dim3(kThreads), 0, st, P);
+    if (P.vcen) hipLaunchKernelGGL(vcentre_kernel, dim3(g.Hkv), dim3(kThreads), 0, st, P);
     pm.mark(0);
     hipLaunchKernelGGL(prep_kernel<D>, dim3(g.Hkv * g.RB), dim3(kThreads), 0, st, P);
     if (g.Hm > 0 && P.m_type != FA_BACK_CAUSAL_TAIL) {
@@ -258,6 +263,12 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
             hipLaunchKernelGGL((qpass_kernel<D, false>), dim3(g.RT * g.Hkv, g.splits), dim3(kQThreads), 0, st, P);
         pm.mark(2);
         hipLaunchKernelGGL(merge_kernel, dim3(g.nbound), dim3(kThreads), 0, st, P);
+        if (P.vcen) {
+            // the merge wrote delta - dO . c
+            const int64_t rows = (int64_t)g.H * g.N;
+            const int blocks = (int)std::min<int64_t>(4096, (rows + kWaves - 1) / kWaves);
+            hipLaunchKernelGGL(vcentre_delta_kernel, dim3(blocks), dim3(kThreads), 0, st, P);
+        }
         pm.mark(3);
     }
     hipLaunchKernelGGL((qpass_kernel<D, true>), dim3(g.RT * g.Hkv, g.splits), dim3(kQThreads), 0, st, P);
@@ -401,6 +412,7 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     P.kv_full = g.kv_full;
     P.kv_split = g.kv_split;
     P.kv_part = (float*)(w + g.ws_kvp);
+    if (ds.flags & FA_BACK_FLAG_CENTER_V) P.vcen = (float*)(w + g.ws_vcen);
     if (saved && !q_empty) {
         P.lse_in = lse_in;
         P.o_in = o_in;

@@ -84,6 +84,7 @@ struct Params {
     const float* o_in;    // [H][N][Dv] forward output O, F32
     float* vmax_part;     // [nvpart] partial max |v| over the cache
     int nvpart;
+    float* vcen;          // [Hkv][D] constant taken from V before its fp16 rounding; NULL: none
 };
 
 // Mask classes of a (32-row block, 64-key tile): no masking needed, every entry -inf, other.

@@ -565,16 +565,18 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         _Float16* tk = (_Float16*)slot(s);
         _Float16* tv = (_Float16*)(slot(s) + L::kTile);
         constexpr int last = kSplitDecode ? Q8Pair<D>::UPT : Q8Pair<D>::U;
-        if (pairq8) {
+        // the q8_0 pair decode is laid out as the fall-through path and the others away from
+        // it: with the q4_0 or generic decode in its place, the q8_0 loop ran 6% slower
+        if (__builtin_expect(pairq8, 1)) {
             decode_blk_pair32<D, true>(kh, p.k_nb1, p.k_type, vh, p.v_nb1, p.v_type, s * kSubKeys, p.M,
                                        rawK(s), rawV(s), tk, tv, kw, last, lane);
         } else if (__builtin_expect(pairblk, 0)) {
-            // laid out away from the q8_0 path: in its place it costs the q8_0 loop 6%
             decode_blk_pair32<D, false>(kh, p.k_nb1, p.k_type, vh, p.v_nb1, p.v_type, s * kSubKeys, p.M,
                                         rawK(s), rawV(s), tk, tv, kw, last, lane);
         } else {
             decode_tile<D, kSubKeys, 256>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, s * kSubKeys, p.M, rawK(s), tk, ktid);
-            decode_tile<D, kSubKeys, 256>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), tv, ktid);
+            decode_tile<D, kSubKeys, 256>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), tv, ktid,
+                                          p.vcen ? p.vcen + (int64_t)hk * D : nullptr);
             // nothing of this path stays in flight: where the two paths join, the compiler
             // would otherwise make the block path wait for its loads, and with them the DMA
             wait_all_mem();
@@ -714,7 +716,7 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
             decode_tile<D, kQTileKeys, kW1Threads>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK(qt), sK,
                                                    threadIdx.x);
             decode_tile<D, kQTileKeys, kW1Threads>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV(qt), sV,
-                                                   threadIdx.x);
+                                                   threadIdx.x, p.vcen ? p.vcen + (int64_t)hk * D : nullptr);
             __syncthreads();
             if (mytile == qt) {
                 const Swz z = make_swz<D>(lane);
@@ -1045,7 +1047,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p) {
 // as sum_c |dO_c| * max |v| + |delta| (Hoelder), which holds for every key.
 
 // Partial max |v| over the cache: for q8_0 / q4_0 the block scale times 128 / 8, otherwise
-// every element. Grid-stride over V rows; partial per block.
+// every element (less the centre when V is centred). Grid-stride over V rows; partial per block.
 static __global__ __launch_bounds__(kThreads) void vmax_kernel(Params p) {
     float vm = 0.0f;
     const int64_t rows = (int64_t)p.M * p.Hkv;
@@ -1069,8 +1071,8 @@ static __global__ __launch_bounds__(kThreads) void vmax_kernel(Params p) {
             const int64_t row = e / p.D;
             const int c = (int)(e - row * p.D);
             const int hk = (int)(row / p.M), j = (int)(row - (int64_t)hk * p.M);
-            vm = fmaxf(vm, fabsf(load_scalar(p.v + (int64_t)hk * p.v_nb2 + (int64_t)j * p.v_nb1 + (int64_t)c * es,
-                                             p.v_type)));
+            const float x = load_scalar(p.v + (int64_t)hk * p.v_nb2 + (int64_t)j * p.v_nb1 + (int64_t)c * es, p.v_type);
+            vm = fmaxf(vm, fabsf(p.vcen ? x - p.vcen[(int64_t)hk * p.D + c] : x));
         }
     }
     __shared__ float red[kWaves];
@@ -1104,24 +1106,27 @@ static __global__ __launch_bounds__(kThreads) void saved_rows_kernel(Params p) {
             const int i = r / p.G, g = r - (r / p.G) * p.G;
             const int h = hk * p.G + g;
             const float lse = p.lse_in[(int64_t)h * p.N + i];
-            double dl = 0.0;
+            double dl = 0.0, dc = 0.0;   // dO . O, and dO . (O - c) for the products' delta
             float l1 = 0.0f;
             if (lse != neg_inf()) {
                 const float* orow = p.o_in + ((int64_t)h * p.N + i) * p.D;
+                const float* cen = p.vcen ? p.vcen + (int64_t)hk * p.D : nullptr;
                 for (int c = lane; c < p.D; c += 64) {
                     const float x = load_scalar(p.d + (int64_t)c * p.d_nb0 + (int64_t)h * p.d_nb1 + (int64_t)i * p.d_nb2,
                                                 p.d_type);
                     dl = fma((double)x, (double)orow[c], dl);
+                    dc = fma((double)x, (double)orow[c] - (cen ? (double)cen[c] : 0.0), dc);
                     l1 += fabsf(x);
                 }
                 // fixed-order wave sums
 #pragma unroll
                 for (int o = 32; o > 0; o >>= 1) {
                     dl += __shfl_xor(dl, o);
+                    dc += __shfl_xor(dc, o);
                     l1 += __shfl_xor(l1, o);
                 }
                 lse2 = (float)((double)lse * (1.0 / kLn2) - kPScaleLog2);
-                dlt = (float)ldexp(dl, edo);
+                dlt = (float)ldexp(dc, edo);
                 bound = fmaxf(bound, ldexpf(l1, edo) * vmax + fabsf(dlt));
             }
             if (lane == 0) {
@@ -1146,6 +1151,48 @@ static __global__ __launch_bounds__(kThreads) void saved_rows_kernel(Params p) {
 }
 
 // ----------------------------------------------------------------------------- dQ reduce
+
+// ----------------------------------------------------------------------------- centred V
+
+// The centre of each KV head's V columns: the fp64 mean of its first min(M, kCentreKeys) keys,
+// summed in key order. Any constant would leave the results unchanged in exact arithmetic; one
+// near the values keeps V - c small, so its fp16 rounding is small too. Grid: one block per
+// KV head.
+constexpr int kCentreKeys = 256;
+static __global__ __launch_bounds__(kThreads) void vcentre_kernel(Params p) {
+    const int hk = blockIdx.x;
+    const int n = p.M < kCentreKeys ? p.M : kCentreKeys;
+    const int es = p.v_type == FA_BACK_F32 ? 4 : 2;
+    const char* vh = p.v + (int64_t)hk * p.v_nb2;
+    for (int c = threadIdx.x; c < p.D; c += kThreads) {
+        double s = 0.0;
+#pragma unroll 8
+        for (int j = 0; j < n; ++j) s += (double)load_scalar(vh + (int64_t)j * p.v_nb1 + (int64_t)c * es, p.v_type);
+        p.vcen[(int64_t)hk * p.D + c] = n ? (float)(s / n) : 0.0f;
+    }
+}
+
+// The delta output of centred runs: the products give delta' = delta - dO . c; add dO . c back,
+// formed in fp64 with a fixed-order wave sum. One wave per row (h, i); rows whose LSE is -inf
+// (fully masked) keep delta = 0.
+static __global__ __launch_bounds__(kThreads) void vcentre_delta_kernel(Params p) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t rows = (int64_t)p.H * p.N;
+    for (int64_t r = (int64_t)blockIdx.x * kWaves + wave; r < rows; r += (int64_t)gridDim.x * kWaves) {
+        const int h = (int)(r / p.N), i = (int)(r - (int64_t)h * p.N);
+        if (p.lse[r] == neg_inf()) continue;   // wave-uniform
+        const float* cen = p.vcen + (int64_t)(h / p.G) * p.D;
+        double s = 0.0;
+        for (int c = lane; c < p.D; c += 64) {
+            const float x = load_scalar(p.d + (int64_t)c * p.d_nb0 + (int64_t)h * p.d_nb1 + (int64_t)i * p.d_nb2,
+                                        p.d_type);
+            s = fma((double)x, (double)cen[c], s);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+        if (lane == 0) p.delta[r] = (float)((double)p.delta[r] + s);
+    }
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void dqreduce_kernel(Params p) {
@@ -1259,7 +1306,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
             decode_tile<D, kQTileKeys, kKVThreads>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, sK,
                                                    threadIdx.x);
             decode_tile<D, kQTileKeys, kKVThreads>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV, sV,
-                                                   threadIdx.x);
+                                                   threadIdx.x, p.vcen ? p.vcen + (int64_t)hk * D : nullptr);
             __syncthreads();
             if ((kb >> 1) == half) {
                 const Swz z = make_swz<D>(lane);

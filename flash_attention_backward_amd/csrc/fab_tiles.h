@@ -203,21 +203,49 @@ FAB_DEV void dma_raw_tile(const char* base, int64_t nb1, int64_t nb2, int hk, in
     }
 }
 
+// The 8 values of cen (the row's centre, 32-byte aligned) that go with value group grp.
+FAB_DEV void centre8(const float* cen, int grp, float c[8]) {
+    const f32x4 x = *(const f32x4*)(cen + 8 * grp);
+    const f32x4 y = *(const f32x4*)(cen + 8 * grp + 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        c[t] = x[t];
+        c[4 + t] = y[t];
+    }
+}
+
 // 8 consecutive values of an F32, F16 or BF16 row (16-byte aligned), starting at value 8*grp,
-// rounded to fp16.
+// less the centre cen[8*grp + t] when cen is not NULL (F32, F16, BF16 only; the difference is
+// formed in fp32), rounded to fp16.
 template <int D>
-FAB_DEV f16x8 decode8(const char* rowp, int type, int grp, const unsigned char*, int) {
+FAB_DEV f16x8 decode8(const char* rowp, int type, int grp, const float* cen) {
     f16x8 r;
     if (type == FA_BACK_F32) {
         const f32x4 a = *(const f32x4*)(rowp + 32 * grp);
         const f32x4 b = *(const f32x4*)(rowp + 32 * grp + 16);
+        if (cen) {
+            float c[8];
+            centre8(cen, grp, c);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            r[t] = (_Float16)a[t];
-            r[4 + t] = (_Float16)b[t];
+            for (int t = 0; t < 4; ++t) {
+                r[t] = (_Float16)(a[t] - c[t]);
+                r[4 + t] = (_Float16)(b[t] - c[4 + t]);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                r[t] = (_Float16)a[t];
+                r[4 + t] = (_Float16)b[t];
+            }
         }
     } else if (type == FA_BACK_F16) {
         r = *(const f16x8*)(rowp + 16 * grp);
+        if (cen) {
+            float c[8];
+            centre8(cen, grp, c);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) r[t] = (_Float16)((float)r[t] - c[t]);
+        }
     } else if (type == FA_BACK_Q4_0) {
         // values 8*grp .. +7: block grp/4, elements 8*(grp%4) ..; elements t < 16 are the low
         // nibbles of bytes t, elements t >= 16 the high nibbles of bytes t - 16. The row is
@@ -235,10 +263,12 @@ FAB_DEV f16x8 decode8(const char* rowp, int type, int grp, const unsigned char*,
         }
     } else {   // BF16
         const u32x4 a = *(const u32x4*)(rowp + 16 * grp);
+        float c[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        if (cen) centre8(cen, grp, c);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            r[2 * t] = (_Float16)__uint_as_float(a[t] << 16);
-            r[2 * t + 1] = (_Float16)__uint_as_float(a[t] & 0xffff0000u);
+            r[2 * t] = (_Float16)(__uint_as_float(a[t] << 16) - c[2 * t]);
+            r[2 * t + 1] = (_Float16)(__uint_as_float(a[t] & 0xffff0000u) - c[2 * t + 1]);
         }
     }
     return r;
@@ -329,13 +359,16 @@ FAB_DEV void decode_block(int type, const unsigned char* slot, int off, int blk,
 }
 
 // Decode keys [j0, j0+KEYS) into the swizzled fp16 tile dst[key][D]. Keys >= M become 0.
+// cen: the head's centre (D floats) taken from every value before its rounding, or NULL
+// (F32, F16 and BF16 rows only).
 // NT threads take part, tid = 0 .. NT-1 being this thread's index among them.
 //   q8_0, q4_0: one item = one 32-value block of a key (from the staged raw bytes)
 //   F32/F16/BF16: one item = 8 values of a key, read from global memory; every load of the
 //   thread is issued before the first conversion
 template <int D, int KEYS, int NT>
 FAB_DEV void decode_tile(const char* base, int type, int64_t nb1, int64_t nb2, int hk, int j0,
-                         int M, const unsigned char* raw, _Float16* dst, int tid) {
+                         int M, const unsigned char* raw, _Float16* dst, int tid,
+                         const float* cen = nullptr) {
     const char* hbase = base + (int64_t)hk * nb2;
     if (is_block_type(type)) {
         constexpr int BPR = D / 32;                    // blocks per row
@@ -369,7 +402,7 @@ FAB_DEV void decode_tile(const char* base, int type, int64_t nb1, int64_t nb2, i
         const int j = j0 + key;
 #pragma unroll
         for (int t = 0; t < 8; ++t) vals[it][t] = (_Float16)0.0f;
-        if (item < ITEMS && j < M) vals[it] = decode8<D>(hbase + (int64_t)j * nb1, type, grp, nullptr, 0);
+        if (item < ITEMS && j < M) vals[it] = decode8<D>(hbase + (int64_t)j * nb1, type, grp, cen);
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {

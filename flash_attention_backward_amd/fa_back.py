@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libfa_back.so")
 
 NONE, F32, F16, BF16, Q8_0, Q4_0 = -1, 0, 1, 2, 8, 9
 CAUSAL_TAIL = 16   # mask type only: query i sees keys j <= M - N + i, nothing stored
+FLAG_CENTER_V = 1  # descriptor flag: centre V before its fp16 rounding
 TYPE_IDS = {"none": NONE, "f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0,
             "causal_tail": CAUSAL_TAIL}
 ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, Q8_0: 34, Q4_0: 18}
@@ -36,7 +37,7 @@ class Tensor(ctypes.Structure):
 
 class Desc(ctypes.Structure):
     _fields_ = [("q", Tensor), ("k", Tensor), ("v", Tensor), ("d", Tensor), ("mask", Tensor),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("flags", ctypes.c_uint32)]
 
 
 class Layout(ctypes.Structure):
@@ -207,6 +208,7 @@ def describe(p) -> Desc:
         ne, nb = _ggml(p.mask, p.mask_type, p.M)
         ds.mask = make_tensor(p.mask_type, ne, nb)
     ds.scale = float(p.scale)
+    ds.flags = int(getattr(p, "flags", 0))
     return ds
 
 

@@ -78,6 +78,21 @@ extern "C" {
 #define FA_BACK_Q4_0 9
 #define FA_BACK_CAUSAL_TAIL 16 /* mask only: query i sees keys j <= M - N + i; no storage */
 
+/* Flags (fa_back_desc.flags; 0 = the plain operator).
+ *
+ * FA_BACK_FLAG_CENTER_V: for caches whose V rows differ in their low bits only (near-constant
+ * V: the case the second review of "CambrianTech/llama.cpp PR #63" added to its oracle cases,
+ * "compensated products", and that its fused revision keeps under the 1e-5 bar). The products
+ * round V to fp16, which keeps about 11 significant bits; dS = P o (dP - delta) then cancels
+ * the part that all keys share, and what is left is mostly rounding. With the flag, a
+ * constant c[hk][c'] (the mean of the first 256 keys of each KV head and column) is taken from
+ * V before the rounding. For every row P sums to 1, so dP - delta, and with it dS, dQ, dK and
+ * dV, are unchanged in exact arithmetic; only the rounding now falls on V - c. The delta
+ * output is delta' + dO . c, with dO . c formed in fp64. V must be F32, F16 or BF16
+ * (FA_BACK_EUNSUPPORTED for q8_0 / q4_0); other bits are FA_BACK_EINVAL. Costs: one pass over
+ * 256 keys of V and one over dO, and one subtraction per decoded V value. */
+#define FA_BACK_FLAG_CENTER_V 1u
+
 /* status codes (no entry point aborts or exits) */
 #define FA_BACK_OK 0
 #define FA_BACK_EINVAL (-1)       /* null pointer, negative extent, non-finite scale        */
@@ -96,6 +111,7 @@ typedef struct {
 typedef struct {
     fa_back_tensor q, k, v, d, mask;   /* mask.type == FA_BACK_NONE: no mask */
     float scale;                        /* softmax scale, e.g. 1/sqrt(D) */
+    uint32_t flags;                     /* FA_BACK_FLAG_* bits, 0 for the plain operator */
 } fa_back_desc;
 
 typedef struct {

@@ -19,7 +19,8 @@ def say(msg):
 def run_gpu(p, device="cuda:0", poison=True):
     import torch
     say(f"[gpu] {p.name}: D={p.D} H={p.H} Hkv={p.Hkv} N={p.N} M={p.M} "
-        f"types q={p.q_type} k={p.k_type} v={p.v_type} d={p.d_type} mask={p.mask_type}")
+        f"types q={p.q_type} k={p.k_type} v={p.v_type} d={p.d_type} mask={p.mask_type} "
+        f"flags={getattr(p, 'flags', 0)}")
     dp = fab.DeviceProblem(p, device, poison=poison)
     dp.run()
     torch.cuda.synchronize()

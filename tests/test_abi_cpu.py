@@ -181,3 +181,21 @@ def test_implicit_causal_tail_descriptor():
     d.mask.ne[2] = 1
     d.mask.ne[0] = p.M + 1                             # extents must be {M, N, 1}
     assert lib.fa_back_layout_query(ctypes.byref(d), ctypes.byref(lay)) == B.ESHAPE
+
+
+def test_centre_v_flag_validation():
+    # the flag applies to F32 / F16 / BF16 V; block types and unknown bits are refused
+    _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_CENTER_V), "c1_f32kv")
+    _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_CENTER_V), "c3")
+    _expect(B.EUNSUPPORTED, lambda d: setattr(d, "flags", B.FLAG_CENTER_V), "c1")
+    _expect(B.EINVAL, lambda d: setattr(d, "flags", 2), "c1_f32kv")
+    # the centre takes Hkv * D floats of workspace
+    d0 = _desc("c1_f32kv")
+    d1 = _desc("c1_f32kv")
+    d1.flags = B.FLAG_CENTER_V
+    lib = fab.load_library()
+    l0, l1 = B.Layout(), B.Layout()
+    assert lib.fa_back_layout_query(ctypes.byref(d0), ctypes.byref(l0)) == B.OK
+    assert lib.fa_back_layout_query(ctypes.byref(d1), ctypes.byref(l1)) == B.OK
+    assert l1.workspace_bytes >= l0.workspace_bytes + 4 * 2 * 128
+    assert l1.out_bytes == l0.out_bytes
