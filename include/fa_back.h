@@ -95,7 +95,7 @@ extern "C" {
 
 /* status codes (no entry point aborts or exits) */
 #define FA_BACK_OK 0
-#define FA_BACK_EINVAL (-1)       /* null pointer, negative extent, non-finite scale        */
+#define FA_BACK_EINVAL (-1)       /* null pointer, negative extent, non-finite scale, unknown flag bit */
 #define FA_BACK_ESHAPE (-2)       /* extents disagree (D, Dv, N, M, H % Hkv, Hm, q8_0 width) */
 #define FA_BACK_ESTRIDE (-3)      /* nb[0] != element size, zero stride, misaligned stride  */
 #define FA_BACK_EUNSUPPORTED (-4) /* type combination, D/Dv, size limit, device not gfx950  */
