@@ -251,19 +251,35 @@ def make(name: str, seed: int = 0, mask_type: str = "f16") -> Problem:
     raise KeyError(name)
 
 
+def magnitude_class(N: int, H: int, classes: int) -> np.ndarray:
+    """(N, H) class c in 0..classes-1 of dO row (i, h): c = (i * H + h) % classes."""
+    return (np.arange(N)[:, None] * H + np.arange(H)[None, :]) % classes
+
+
 def make_custom(name="custom", *, D=64, H=2, Hkv=1, N=16, M=64, seed=0, q_type="f32",
                 k_type="f32", v_type="f32", d_type="f32", mask="tail", mask_type="f16",
-                Hm=1, scale=None, v_offset=0.0, v_spread=1.0, d_mult=1.0,
-                masked_rows=(), flags=0, **_ignored) -> Problem:
+                Hm=1, scale=None, v_offset=0.0, v_spread=1.0, k_offset=0.0, k_spread=1.0,
+                d_mult=1.0, d_decades=0, d_group_mult=None, masked_rows=(), flags=0,
+                **_ignored) -> Problem:
     """A parameterised case with the same draw order and distributions as the named configs.
 
     mask: 'none' | 'tail' | 'random' (iid -inf with prob 0.3) ; masked_rows: (hm, i) pairs
-    whose mask row is set to all -inf."""
+    whose mask row is set to all -inf. v = v_offset + v_spread * z (likewise k). d_decades = n > 0
+    scales dO row (i, h) by 10^-c, c = magnitude_class(N, H, n + 1)[i, h] (rows of n + 1 decades in
+    one tensor); d_group_mult = (hk, f) scales the dO rows of every head of KV head hk by f."""
     Dv = D
     rng = np.random.default_rng(seed)
     k, v, q, do = _draws(rng, H, Hkv, N, M, D, Dv)
     v = (np.float32(v_offset) + np.float32(v_spread) * v).astype(np.float32)
+    k = (np.float32(k_offset) + np.float32(k_spread) * k).astype(np.float32)
     do = (do * np.float32(d_mult)).astype(np.float32)
+    if d_decades:
+        cls = magnitude_class(N, H, d_decades + 1)
+        do = (do * (np.float32(10.0) ** -cls.astype(np.float32))[:, :, None]).astype(np.float32)
+    if d_group_mult is not None:
+        hk, f = d_group_mult
+        G = H // Hkv
+        do[:, hk * G:(hk + 1) * G, :] *= np.float32(f)
     m = None
     if mask == "tail":
         m = causal_tail_mask(N, M, Hm, mask_type)

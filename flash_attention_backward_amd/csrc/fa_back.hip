@@ -19,6 +19,30 @@ constexpr int kVmaxBlocks = 256;   // partial max |v| blocks of fa_back_run_save
 
 constexpr uint64_t kAlign = 256;
 
+// The layout's CU count: fa_back_layout_query plans for a whole MI355X (256 compute units).
+// The workspace holds the key side's split tail tiles for each CU count a gfx950 device (or
+// partition of one) has, so it is a function of the descriptor only; a device with another
+// count gets no tail split if its split would not fit.
+constexpr int kRefCUs = 256;
+constexpr int kLayoutCUs[] = {32, 64, 128, 256};
+
+// Key-side tail tiles: one workgroup per CU at a time (LDS), so the tiles past the last full
+// round of workgroups would run nearly alone; each of them is split into up to 4 row ranges.
+// Returns the number of split tiles and sets *split to the ranges per tile (1 if none).
+int tail_split(int T, int cus, int* split) {
+    const int tail = T > cus ? T % cus : 0;
+    const int sp = tail > 0 ? std::min(4, cus / tail) : 1;
+    if (tail > 0 && tail <= cus / 2 && sp >= 2) {
+        *split = sp;
+        return tail;
+    }
+    *split = 1;
+    return 0;
+}
+
+constexpr uint32_t kKnownFlags =
+    FA_BACK_FLAG_CENTER_V | FA_BACK_FLAG_WALK1_KEYS | FA_BACK_FLAG_WALK1_ROWS | FA_BACK_FLAG_CENTER_K;
+
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
 int64_t elem_size(int type) {
@@ -34,9 +58,11 @@ int64_t elem_size(int type) {
 
 // Everything derived from a valid descriptor: shapes, plan choices, offsets.
 struct Geometry {
+    int cus;               // compute units the work split is planned for
     int D, Dv, H, Hkv, G, N, M, Hm;
     int R, RB, RT, KT, splits, tiles_per_split, KVT;
     int kv_full, kv_tail, kv_split;   // key side: unsplit tiles, split tiles, parts per split tile
+    int64_t kv_parts_ws;              // split-tile parts the workspace holds (any planned CU count)
     bool w1keys;           // walk 1 by key tiles (else by row tiles)
     int KT1, RS1, w1_rbs;  // its 256-key tiles, row splits and row blocks per workgroup
     int nparts;            // walk-1 records per row
@@ -44,8 +70,9 @@ struct Geometry {
     fa_back_layout layout;
     // workspace offsets (bytes)
     uint64_t ws_absmax, ws_scal, ws_qr, ws_dr;
-    uint64_t ws_pm, ws_pl, ws_pd, ws_pb, ws_lse2, ws_dlt, ws_bound, ws_dqp, ws_mcls, ws_kvp, ws_vmax;
+    uint64_t ws_rec, ws_lse2, ws_dlt, ws_rks, ws_bound, ws_dqp, ws_mcls, ws_kvp, ws_vmax;
     uint64_t ws_vcen;      // [Hkv][D] V centre (FA_BACK_FLAG_CENTER_V only)
+    uint64_t ws_kcen;      // [Hkv][D] K centre (FA_BACK_FLAG_CENTER_K only)
 };
 
 bool tensor_nonneg(const fa_back_tensor& t) {
@@ -61,7 +88,8 @@ int check_strides(const fa_back_tensor& t, bool rows16) {
     return FA_BACK_OK;
 }
 
-int validate(const fa_back_desc* d, Geometry* g) {
+// Validates `d` and plans the work for a device with `cus` compute units.
+int validate(const fa_back_desc* d, int cus, Geometry* g) {
     if (!d) return FA_BACK_EINVAL;
     const fa_back_tensor &q = d->q, &k = d->k, &v = d->v, &dd = d->d, &m = d->mask;
     // types
@@ -73,8 +101,10 @@ int validate(const fa_back_desc* d, Geometry* g) {
     const bool causal = m.type == FA_BACK_CAUSAL_TAIL;   // implicit: no storage, no strides
     if (has_mask && !causal && m.type != FA_BACK_F32 && m.type != FA_BACK_F16) return FA_BACK_EUNSUPPORTED;
     if (!std::isfinite(d->scale)) return FA_BACK_EINVAL;
-    if (d->flags & ~FA_BACK_FLAG_CENTER_V) return FA_BACK_EINVAL;
+    if (d->flags & ~kKnownFlags) return FA_BACK_EINVAL;
+    if ((d->flags & FA_BACK_FLAG_WALK1_KEYS) && (d->flags & FA_BACK_FLAG_WALK1_ROWS)) return FA_BACK_EINVAL;
     if ((d->flags & FA_BACK_FLAG_CENTER_V) && is_blk(v.type)) return FA_BACK_EUNSUPPORTED;
+    if ((d->flags & FA_BACK_FLAG_CENTER_K) && is_blk(k.type)) return FA_BACK_EUNSUPPORTED;
     if (!tensor_nonneg(q) || !tensor_nonneg(k) || !tensor_nonneg(v) || !tensor_nonneg(dd) ||
         (has_mask && !tensor_nonneg(m)))
         return FA_BACK_EINVAL;
@@ -108,6 +138,7 @@ int validate(const fa_back_desc* d, Geometry* g) {
     if (N * H >= (int64_t)1 << 30 || M * Hkv >= (int64_t)1 << 30 || G * N >= (int64_t)1 << 30 || H > 65535)
         return FA_BACK_EUNSUPPORTED;
 
+    g->cus = cus;
     g->D = (int)D; g->Dv = (int)Dv; g->H = (int)H; g->Hkv = (int)Hkv; g->G = (int)G;
     g->N = (int)N; g->M = (int)M; g->Hm = (int)Hm;
     g->R = (int)(G * N);
@@ -115,20 +146,28 @@ int validate(const fa_back_desc* d, Geometry* g) {
     g->RT = (g->RB + kWaves - 1) / kWaves;
     g->KT = (g->M + kQTileKeys - 1) / kQTileKeys;
     g->KVT = (g->M + kKVKeys - 1) / kKVKeys;
-    // key side: one workgroup per CU at a time (LDS), so the tiles past the last full round of
-    // kCUs workgroups would run nearly alone; each of them is split into up to 4 row ranges.
-    // A workgroup lists at most KVLds::kMaxRB row blocks, so with more rows every tile is split
-    // into ranges of at most that many.
+    // key side: the tail tiles are split (tail_split); a workgroup lists at most KVLds::kMaxRB
+    // row blocks, so with more rows every tile is split into ranges of at most that many
     {
         const int T = g->KVT * (int)Hkv;
         const int pmin = (g->RB + KVLds<64>::kMaxRB - 1) / KVLds<64>::kMaxRB;
         if (pmin > 1) {
             g->kv_tail = T;
             g->kv_split = pmin;
+            g->kv_parts_ws = (int64_t)T * pmin;
         } else {
-            const int tail = T > kCUs ? T % kCUs : 0;
-            g->kv_tail = (tail > 0 && tail <= kCUs / 2) ? tail : 0;
-            g->kv_split = g->kv_tail ? std::min(4, kCUs / g->kv_tail) : 1;
+            int64_t most = 0;
+            for (int c : kLayoutCUs) {
+                int sp;
+                const int t = tail_split(T, c, &sp);
+                most = std::max<int64_t>(most, (int64_t)t * sp);
+            }
+            g->kv_parts_ws = most;
+            g->kv_tail = tail_split(T, cus, &g->kv_split);
+            if ((int64_t)g->kv_tail * g->kv_split > most) {   // a CU count the layout does not plan for
+                g->kv_tail = 0;
+                g->kv_split = 1;
+            }
         }
         g->kv_full = T - g->kv_tail;
     }
@@ -145,27 +184,24 @@ int validate(const fa_back_desc* d, Geometry* g) {
         g->splits = g->KT > 0 ? (g->KT + tps - 1) / tps : 1;
     }
     // walk 1 by key tiles when the cache is long next to the rows (each K/V tile is then
-    // decoded once per 256 keys instead of once per 128 rows); FA_BACK_WALK1=keys|rows
-    // overrides the choice
+    // decoded once per 256 keys instead of once per 128 rows), unless a flag picks the walk
     {
         g->KT1 = (g->M + kW1Keys - 1) / kW1Keys;
         bool keys = g->M >= 2 * (int64_t)g->R;
-        if (const char* e = std::getenv("FA_BACK_WALK1")) {
-            if (!std::strcmp(e, "keys")) keys = true;
-            if (!std::strcmp(e, "rows")) keys = false;
-        }
+        if (d->flags & FA_BACK_FLAG_WALK1_KEYS) keys = true;
+        if (d->flags & FA_BACK_FLAG_WALK1_ROWS) keys = false;
         g->w1keys = keys && g->M > 0 && g->R > 0;
         g->RS1 = 1;
         g->w1_rbs = g->RB;
         if (g->w1keys) {
-            // row splits: minimise rounds of kCUs workgroups x (setup + row blocks per workgroup),
-            // the setup (decoding 256 keys) counted as 8 row blocks
+            // row splits: minimise rounds of `cus` workgroups x (setup + row blocks per
+            // workgroup), the setup (decoding 256 keys) counted as 8 row blocks
             const int rs_min = (g->RB + W1Lds<64>::kMaxRB - 1) / W1Lds<64>::kMaxRB;
             int best = rs_min;
             double best_cost = 1e300;
             for (int rs = rs_min; rs <= 16; ++rs) {
                 const int rbs = (g->RB + rs - 1) / rs;
-                const double rounds = std::ceil((double)g->KT1 * g->Hkv * rs / (double)kCUs);
+                const double rounds = std::ceil((double)g->KT1 * g->Hkv * rs / (double)cus);
                 const double cost = rounds * (8.0 + rbs);
                 if (cost < best_cost - 1e-9) { best_cost = cost; best = rs; }
             }
@@ -176,7 +212,7 @@ int validate(const fa_back_desc* d, Geometry* g) {
     }
     g->npart = (int)std::min<int64_t>(512, std::max<int64_t>(1, N * H / 8));
     const int64_t total_rows = (int64_t)g->Hkv * g->RB * 32;
-    g->nbound = (int)std::min<int64_t>(kMergeMaxBlocks, std::max<int64_t>(1, (total_rows + kMergeRows - 1) / kMergeRows));
+    g->nbound = (int)std::min<int64_t>(kMergeMaxBlocks, std::max<int64_t>(1, (g->RB * 32 + kMergeRows - 1) / kMergeRows));
 
     // packed output
     fa_back_layout& L = g->layout;
@@ -195,22 +231,31 @@ int validate(const fa_back_desc* d, Geometry* g) {
     g->ws_scal = take(64);
     g->ws_qr = take(frag);
     g->ws_dr = take(frag);
-    g->ws_pm = take(4 * prow);
-    g->ws_pl = take(8 * prow);
-    g->ws_pd = take(8 * prow);
-    g->ws_pb = take(4 * prow);
+    g->ws_rec = take(16 * prow);
     g->ws_lse2 = take(4ull * total_rows);
     g->ws_dlt = take(4ull * total_rows);
-    g->ws_bound = take(4ull * g->nbound);
+    g->ws_rks = take(4ull * total_rows);
+    g->ws_bound = take(4ull * g->nbound * g->Hkv);
     g->ws_dqp = take(g->splits > 1 ? 4ull * g->splits * total_rows * D : 0);
     // mask classes: stored masks only (the causal-tail classes are computed where needed)
     const bool stored_mask = has_mask && d->mask.type != FA_BACK_CAUSAL_TAIL;
     g->ws_mcls = take(stored_mask ? (uint64_t)(Hm == 1 ? 1 : g->Hkv) * g->RB * g->KT : 0);
-    g->ws_kvp = take(4ull * g->kv_tail * g->kv_split * 2 * kKVKeys * D);
+    g->ws_kvp = take(4ull * g->kv_parts_ws * 2 * kKVKeys * D);
     g->ws_vmax = take(4ull * kVmaxBlocks);   // fa_back_run_saved only
     g->ws_vcen = take((d->flags & FA_BACK_FLAG_CENTER_V) ? 4ull * g->Hkv * D : 0);
+    g->ws_kcen = take((d->flags & FA_BACK_FLAG_CENTER_K) ? 4ull * g->Hkv * D : 0);
     L.workspace_bytes = std::max<uint64_t>(o, kAlign);
     return FA_BACK_OK;
+}
+
+// Static LDS of the largest tile kernel for head size D (the tile kernels use 1 workgroup
+// per CU; the small kernels use a few KB).
+template <int D>
+int max_lds_bytes_d() {
+    return std::max(std::max(QLds<D>::kBytes, W1Lds<D>::kBytes), KVLds<D>::kBytes);
+}
+int max_lds_bytes(int D) {
+    return D == 64 ? max_lds_bytes_d<64>() : D == 128 ? max_lds_bytes_d<128>() : max_lds_bytes_d<256>();
 }
 
 // Records an event after each phase when `ev` is non-NULL (ev[0] is recorded by the caller
@@ -222,6 +267,20 @@ struct PhaseMarks {
         if (ev) (void)hipEventRecord(ev[phase + 1], st);
     }
 };
+
+// The query-side walk, in the instantiation of the K/V decode the types need.
+template <int D, bool GRAD>
+void launch_qpass(const Geometry& g, const Params& P, hipStream_t st) {
+    const dim3 grid(g.RT * g.Hkv, g.splits), block(kQThreads);
+    const bool blk_k = P.k_type == FA_BACK_Q8_0 || P.k_type == FA_BACK_Q4_0;
+    const bool blk_v = P.v_type == FA_BACK_Q8_0 || P.v_type == FA_BACK_Q4_0;
+    if (P.k_type == FA_BACK_Q8_0 && P.v_type == FA_BACK_Q8_0)
+        hipLaunchKernelGGL((qpass_kernel<D, GRAD, kDecQ8>), grid, block, 0, st, P);
+    else if (blk_k && blk_v)
+        hipLaunchKernelGGL((qpass_kernel<D, GRAD, kDecBlk>), grid, block, 0, st, P);
+    else
+        hipLaunchKernelGGL((qpass_kernel<D, GRAD, kDecGen>), grid, block, 0, st, P);
+}
 
 template <int D>
 int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& pm) {
@@ -239,7 +298,8 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
         return hipGetLastError() == hipSuccess ? FA_BACK_OK : FA_BACK_EHIP;
     }
     hipLaunchKernelGGL(absmax_kernel, dim3(g.npart), dim3(kThreads), 0, st, P);
-    if (P.vcen) hipLaunchKernelGGL(vcentre_kernel, dim3(g.Hkv), dim3(kThreads), 0, st, P);
+    if (P.vcen) hipLaunchKernelGGL(centre_kernel<false>, dim3(g.Hkv), dim3(kThreads), 0, st, P);
+    if (P.kcen) hipLaunchKernelGGL(centre_kernel<true>, dim3(g.Hkv), dim3(kThreads), 0, st, P);
     pm.mark(0);
     hipLaunchKernelGGL(prep_kernel<D>, dim3(g.Hkv * g.RB), dim3(kThreads), 0, st, P);
     if (g.Hm > 0 && P.m_type != FA_BACK_CAUSAL_TAIL) {
@@ -254,24 +314,24 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
         // forward-saved LSE and O: the row statistics without walk 1 and the merge
         hipLaunchKernelGGL(vmax_kernel, dim3(kVmaxBlocks), dim3(kThreads), 0, st, P);
         pm.mark(2);
-        hipLaunchKernelGGL(saved_rows_kernel, dim3(g.nbound), dim3(kThreads), 0, st, P);
+        hipLaunchKernelGGL(saved_rows_kernel, dim3(g.nbound, g.Hkv), dim3(kThreads), 0, st, P);
         pm.mark(3);
     } else {
         if (g.w1keys)
             hipLaunchKernelGGL(walk1_keys_kernel<D>, dim3(g.KT1 * g.Hkv, g.RS1), dim3(kW1Threads), 0, st, P);
         else
-            hipLaunchKernelGGL((qpass_kernel<D, false>), dim3(g.RT * g.Hkv, g.splits), dim3(kQThreads), 0, st, P);
+            launch_qpass<D, false>(g, P, st);
         pm.mark(2);
-        hipLaunchKernelGGL(merge_kernel, dim3(g.nbound), dim3(kThreads), 0, st, P);
-        if (P.vcen) {
-            // the merge wrote delta - dO . c
+        hipLaunchKernelGGL(merge_kernel, dim3(g.nbound, g.Hkv), dim3(kThreads), 0, st, P);
+        if (P.vcen || P.kcen) {
+            // the merge wrote delta - dO . c (V centred) and lse - scale q . c (K centred)
             const int64_t rows = (int64_t)g.H * g.N;
             const int blocks = (int)std::min<int64_t>(4096, (rows + kWaves - 1) / kWaves);
-            hipLaunchKernelGGL(vcentre_delta_kernel, dim3(blocks), dim3(kThreads), 0, st, P);
+            hipLaunchKernelGGL(centre_out_kernel, dim3(blocks), dim3(kThreads), 0, st, P);
         }
         pm.mark(3);
     }
-    hipLaunchKernelGGL((qpass_kernel<D, true>), dim3(g.RT * g.Hkv, g.splits), dim3(kQThreads), 0, st, P);
+    launch_qpass<D, true>(g, P, st);
     pm.mark(4);
     if (g.splits > 1) {
         const int64_t n4 = (int64_t)g.Hkv * g.RB * 32 * (D / 4);
@@ -315,7 +375,7 @@ const char* fa_back_status_string(int s) {
 int fa_back_layout_query(const fa_back_desc* desc, fa_back_layout* layout) {
     if (!layout) return FA_BACK_EINVAL;
     Geometry g;
-    const int rc = validate(desc, &g);
+    const int rc = validate(desc, kRefCUs, &g);
     if (rc == FA_BACK_OK) *layout = g.layout;
     return rc;
 }
@@ -324,13 +384,17 @@ int fa_back_create(const fa_back_desc* desc, int device, fa_back_plan** plan, fa
     if (!plan) return FA_BACK_EINVAL;
     *plan = nullptr;
     Geometry g;
-    int rc = validate(desc, &g);
+    int rc = validate(desc, kRefCUs, &g);   // descriptor errors before any device call
     if (rc != FA_BACK_OK) return rc;
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return FA_BACK_EUNSUPPORTED;
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, device) != hipSuccess) return FA_BACK_EHIP;
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return FA_BACK_EUNSUPPORTED;
+    if ((size_t)max_lds_bytes(g.D) > prop.sharedMemPerBlock) return FA_BACK_EUNSUPPORTED;
+    if (prop.multiProcessorCount < 1) return FA_BACK_EUNSUPPORTED;
+    rc = validate(desc, prop.multiProcessorCount, &g);
+    if (rc != FA_BACK_OK) return rc;
     fa_back_plan* p = new (std::nothrow) fa_back_plan;
     if (!p) return FA_BACK_EINVAL;
     p->desc = *desc;
@@ -399,10 +463,8 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     P.scal = (int*)(w + g.ws_scal);
     P.qr = (_Float16*)(w + g.ws_qr);
     P.dr = (_Float16*)(w + g.ws_dr);
-    P.part_m = (float*)(w + g.ws_pm);
-    P.part_l = (double*)(w + g.ws_pl);
-    P.part_d = (double*)(w + g.ws_pd);
-    P.part_b = (float*)(w + g.ws_pb);
+    P.part_rec = (f32x4*)(w + g.ws_rec);
+    P.row_ks = (int*)(w + g.ws_rks);
     P.row_lse2 = (float*)(w + g.ws_lse2);
     P.row_dlt = (float*)(w + g.ws_dlt);
     P.bound_part = (float*)(w + g.ws_bound);
@@ -413,6 +475,7 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     P.kv_split = g.kv_split;
     P.kv_part = (float*)(w + g.ws_kvp);
     if (ds.flags & FA_BACK_FLAG_CENTER_V) P.vcen = (float*)(w + g.ws_vcen);
+    if (ds.flags & FA_BACK_FLAG_CENTER_K) P.kcen = (float*)(w + g.ws_kcen);
     if (saved && !q_empty) {
         P.lse_in = lse_in;
         P.o_in = o_in;

@@ -22,7 +22,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kRowBlock = 32;     // rows per MFMA block (the 32 of a 32x32x16 product)
 constexpr int kQTileKeys = 64;    // keys per tile in the query-side passes
-constexpr int kCUs = 256;         // compute units of an MI355X (workgroup rounds)
 constexpr int kKVKeys = 128;      // keys owned by one key-side workgroup (32 per wave)
 constexpr int kPScaleLog2 = 15;   // P is rounded to fp16 as p * 2^15 (p <= 1)
 constexpr int kNegInfBits = 0xff800000;
@@ -63,16 +62,15 @@ struct Params {
     int* scal;            // [0] = e_q, [1] = e_do (power-of-two exponents)
     _Float16* qr;         // [Hkv][RB*32][D]  q rows scaled by 2^e_q, fp16, row-major
     _Float16* dr;         // [Hkv][RB*32][D]  dO rows scaled by 2^e_do, fp16, row-major
-    float* part_m;        // [nparts][Hkv*RB*32]  running max (log2 units)
-    double* part_l;       // softmax sum at part_m
-    double* part_d;       // sum of e * dp at part_m (dp in 2^e_do units)
-    float* part_b;        // max |dp| over visible keys
+    f32x4* part_rec;      // [nparts][Hkv*RB*32] walk-1 records {max m (log2 units), softmax sum
+                          //   at m, sum of e * dp at m (dp in 2^e_do units), max |dp| over visible keys}
     float* row_lse2;      // [Hkv*RB*32]  lse in log2 units minus kPScaleLog2, so that exp2(s - row_lse2)
                           //   is the P image p * 2^15; +inf for dead or padding rows (the image is 0
                           //   for them with no test)
     float* row_dlt;       // [Hkv*RB*32]  delta in 2^e_do units
-    float* bound_part;    // [nbound] per-block max of max|dp| + |delta|
-    int nbound;
+    int* row_ks;          // [Hkv*RB*32]  the row's dS exponent: dS goes to fp16 as dS * 2^-ks (walk 2)
+    float* bound_part;    // [Hkv][nbound] per-block max of max|dp| + |delta| over a head's rows
+    int nbound;           // blocks per KV head
     float* dq_part;       // [splits][Hkv*RB*32][D] when splits > 1
     unsigned char* mcls;  // [Hc][RB][KT] mask class of (row block, 64-key tile); Hc = Hm==1 ? 1 : Hkv
     // key side: workgroups 0 .. kv_full-1 own one 128-key tile (tile = workgroup); each of the
@@ -85,6 +83,7 @@ struct Params {
     float* vmax_part;     // [nvpart] partial max |v| over the cache
     int nvpart;
     float* vcen;          // [Hkv][D] constant taken from V before its fp16 rounding; NULL: none
+    float* kcen;          // [Hkv][D] constant taken from K before its fp16 rounding; NULL: none
 };
 
 // Mask classes of a (32-row block, 64-key tile): no masking needed, every entry -inf, other.

@@ -134,12 +134,27 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
 
 // ----------------------------------------------------------------------------- helpers
 
-// dS exponent: every wave reduces the merge kernel's bound partials. It ends in a wave-wide
-// reduction, so every lane of the wave must call it (never from a lane-divergent branch).
-FAB_DEV int load_ds_exponent(const Params& p) {
+// dS exponent of KV head hk (for the key side, which sums dS over every row of the head):
+// every wave reduces the head's bound partials of the merge. It ends in a wave-wide reduction,
+// so every lane of the wave must call it (never from a lane-divergent branch).
+FAB_DEV int head_ds_exponent(const Params& p, int hk) {
     float b = 0.0f;
-    for (int t = threadIdx.x & 63; t < p.nbound; t += 64) b = fmaxf(b, p.bound_part[t]);
+    const float* bp = p.bound_part + (int64_t)hk * p.nbound;
+    for (int t = threadIdx.x & 63; t < p.nbound; t += 64) b = fmaxf(b, bp[t]);
     return ds_exponent(wave_max(b));
+}
+
+// q_i . c for query row i of head h (K centre c of its KV head), fp64, fixed-order wave sum;
+// every lane of the wave must call it and gets the sum.
+FAB_DEV double q_dot_kcen(const Params& p, int h, int i, int lane) {
+    const float* cen = p.kcen + (int64_t)(h / p.G) * p.D;
+    double s = 0.0;
+    for (int c = lane; c < p.D; c += 64)
+        s = fma((double)load_scalar(p.q + (int64_t)c * p.q_nb0 + (int64_t)i * p.q_nb1 + (int64_t)h * p.q_nb2, p.q_type),
+                (double)cen[c], s);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    return s;
 }
 
 // ----------------------------------------------------------------------------- mask classes
@@ -338,7 +353,14 @@ struct QLds {
     static constexpr int kBytes = kOffCls + 16;
 };
 
-template <int D, bool GRAD>
+// How the K waves decode a sub-tile: both K and V q8_0, both block types (q8_0 / q4_0), or
+// anything else (F32/F16/BF16 rows read from global memory, possibly centred). Each is a
+// kernel of its own, so that no decode holds registers in another's loop.
+constexpr int kDecQ8 = 0;
+constexpr int kDecBlk = 1;
+constexpr int kDecGen = 2;
+
+template <int D, bool GRAD, int DEC>
 __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     using L = QLds<D>;
     // The K waves decode whole sub-tiles. (Handing the V half to the S waves was measured: with
@@ -410,7 +432,7 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
                 lse2 = p.row_lse2[ridx];
                 dlt = p.row_dlt[ridx];
             }
-            lse2k = lse2 + (float)(load_ds_exponent(p) + kPScaleLog2);
+            lse2k = lse2 + (float)((row_ok ? p.row_ks[ridx] : 0) + kPScaleLog2);
         }
         const bool dead = (lse2 == pos_inf());
         const RowWalk<D> rw = make_row_walk<D>(lane);
@@ -543,13 +565,8 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
             const double lo = l64 + __shfl_xor(l64, 32);
             const double dd = d64 + __shfl_xor(d64, 32);
             const float bb = fmaxf(bmax, __shfl_xor(bmax, 32));
-            if (g == 0) {
-                const int64_t idx = (int64_t)split * p.Hkv * rowsHK + ridx;
-                p.part_m[idx] = m_run;
-                p.part_l[idx] = lo;
-                p.part_d[idx] = dd;
-                p.part_b[idx] = bb;
-            }
+            // the split's sums, carried in fp64, are rounded once to fp32 for the record
+            if (g == 0) p.part_rec[(int64_t)split * p.Hkv * rowsHK + ridx] = f32x4{m_run, (float)lo, (float)dd, bb};
         }
         return;
     }
@@ -559,27 +576,21 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     const int ktid = kw * 64 + lane;
     const char* kh = p.k + (int64_t)hk * p.k_nb2;
     const char* vh = p.v + (int64_t)hk * p.v_nb2;
-    const bool pairq8 = p.k_type == FA_BACK_Q8_0 && p.v_type == FA_BACK_Q8_0;
-    const bool pairblk = is_block_type(p.k_type) && is_block_type(p.v_type);
     auto kdecode = [&](int s) {
         _Float16* tk = (_Float16*)slot(s);
         _Float16* tv = (_Float16*)(slot(s) + L::kTile);
         constexpr int last = kSplitDecode ? Q8Pair<D>::UPT : Q8Pair<D>::U;
-        // the q8_0 pair decode is laid out as the fall-through path and the others away from
-        // it: with the q4_0 or generic decode in its place, the q8_0 loop ran 6% slower
-        if (__builtin_expect(pairq8, 1)) {
+        if constexpr (DEC == kDecQ8) {
             decode_blk_pair32<D, true>(kh, p.k_nb1, p.k_type, vh, p.v_nb1, p.v_type, s * kSubKeys, p.M,
                                        rawK(s), rawV(s), tk, tv, kw, last, lane);
-        } else if (__builtin_expect(pairblk, 0)) {
+        } else if constexpr (DEC == kDecBlk) {
             decode_blk_pair32<D, false>(kh, p.k_nb1, p.k_type, vh, p.v_nb1, p.v_type, s * kSubKeys, p.M,
                                         rawK(s), rawV(s), tk, tv, kw, last, lane);
         } else {
-            decode_tile<D, kSubKeys, 256>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, s * kSubKeys, p.M, rawK(s), tk, ktid);
+            decode_tile<D, kSubKeys, 256>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, s * kSubKeys, p.M, rawK(s), tk, ktid,
+                                          p.kcen ? p.kcen + (int64_t)hk * D : nullptr);
             decode_tile<D, kSubKeys, 256>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), tv, ktid,
                                           p.vcen ? p.vcen + (int64_t)hk * D : nullptr);
-            // nothing of this path stays in flight: where the two paths join, the compiler
-            // would otherwise make the block path wait for its loads, and with them the DMA
-            wait_all_mem();
         }
     };
     // prologue: the S waves stage sub-tile s_begin; its class is posted
@@ -614,9 +625,8 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         if (s == s_end) break;
         if (s + 1 < s_end) kdecode(s + 1);
     }
-    // (a wave-wide reduction: taken by every lane, before the per-row branch)
-    const int ksx = GRAD ? load_ds_exponent(p) : 0;
     if (GRAD && row_ok) {
+        const int ksx = p.row_ks[ridx];   // the row's dS exponent
         const bool direct = p.splits == 1;
         const float fac = direct ? p.scale * ldexpf(1.0f, ksx - edo) : 1.0f;
         float* dst = direct ? p.dq + ((int64_t)h * p.N + i) * D
@@ -714,7 +724,7 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
             __syncthreads();   // bytes of qt landed; the decoded tiles of qt-1 are read
             if (qt + 1 < L::kTiles) stage(qt + 1);
             decode_tile<D, kQTileKeys, kW1Threads>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK(qt), sK,
-                                                   threadIdx.x);
+                                                   threadIdx.x, p.kcen ? p.kcen + (int64_t)hk * D : nullptr);
             decode_tile<D, kQTileKeys, kW1Threads>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV(qt), sV,
                                                    threadIdx.x, p.vcen ? p.vcen + (int64_t)hk * D : nullptr);
             __syncthreads();
@@ -748,11 +758,7 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
     for (int idx = threadIdx.x; idx < 32 * nloc; idx += kW1Threads) {
         const int rbx = rb0 + idx / 32;
         if (needed(rbx)) continue;
-        const int64_t ri = rec0 + (int64_t)rb0 * 32 + idx;
-        p.part_m[ri] = neg_inf();
-        p.part_l[ri] = 0.0;
-        p.part_d[ri] = 0.0;
-        p.part_b[ri] = 0.0f;
+        p.part_rec[rec0 + (int64_t)rb0 * 32 + idx] = f32x4{neg_inf(), 0.0f, 0.0f, 0.0f};
     }
 
     if (wave == 0) {
@@ -818,11 +824,7 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
                 ds = fmaf(x[2], f, ds);
             }
         }
-        const int64_t ri = rec0 + (int64_t)rbx * 32 + l32;
-        p.part_m[ri] = mx;
-        p.part_l[ri] = (double)ls;
-        p.part_d[ri] = (double)ds;
-        p.part_b[ri] = bb;
+        p.part_rec[rec0 + (int64_t)rbx * 32 + l32] = f32x4{mx, ls, ds, bb};
     };
 
     const float sc2 = fabsf(p.scale) * ldexpf(1.0f, -p.scal[0]) * kLog2e;   // q carries the sign
@@ -964,27 +966,30 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
 // ----------------------------------------------------------------------------- merge
 
 // Merge of the walk-1 records of every row (one record per key-range split or key tile), then
-// LSE and delta. A block takes 64 consecutive rows; wave w takes records w, w+4, ... of each
-// row (loads coalesced across the rows), and the four partial results meet in LDS in wave
-// order. Each block also leaves max(max|dp| + |delta|) over its rows in bound_part.
+// LSE, delta and the row's dS exponent. Grid (blocks, Hkv): a block takes 64 consecutive rows of
+// one KV head at a time; wave w takes records w, w+4, ... of each row (16-byte loads coalesced
+// across the rows), and the four partial results meet in LDS in wave order. Each block also
+// leaves max(max|dp| + |delta|) over its rows in bound_part[hk][block], for the head's exponent.
 constexpr int kMergeRows = 64;
-constexpr int kMergeMaxBlocks = 4096;
+constexpr int kMergeMaxBlocks = 1024;   // blocks per KV head
 
 __global__ __launch_bounds__(kThreads) void merge_kernel(Params p) {
     __shared__ float smax[kWaves][kMergeRows];
     __shared__ double sl[kWaves][kMergeRows], sd[kWaves][kMergeRows];
     __shared__ float sb[kWaves][kMergeRows];
     const int rowsHK = p.RB * 32;
-    const int total = p.Hkv * rowsHK;
+    const int64_t total = (int64_t)p.Hkv * rowsHK;
+    const int hk = blockIdx.y;
     const int lr = threadIdx.x & 63, grp = threadIdx.x >> 6;
     float bound = 0.0f;
-    for (int base = blockIdx.x * kMergeRows; base < total; base += gridDim.x * kMergeRows) {
-        const int ridx = base + lr;
-        const bool ok = ridx < total;
+    for (int base = blockIdx.x * kMergeRows; base < rowsHK; base += gridDim.x * kMergeRows) {
+        const int r = base + lr;
+        const int64_t ridx = (int64_t)hk * rowsHK + r;
+        const bool ok = r < rowsHK;
         float mx = neg_inf();
         if (ok) {
 #pragma unroll 8
-            for (int s = grp; s < p.nparts; s += kWaves) mx = fmaxf(mx, p.part_m[(int64_t)s * total + ridx]);
+            for (int s = grp; s < p.nparts; s += kWaves) mx = fmaxf(mx, p.part_rec[s * total + ridx][0]);
         }
         smax[grp][lr] = mx;
         __syncthreads();
@@ -994,13 +999,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p) {
         if (ok && mx != neg_inf()) {
 #pragma unroll 4
             for (int s = grp; s < p.nparts; s += kWaves) {
-                const int64_t idx = (int64_t)s * total + ridx;
-                const float m = p.part_m[idx];
-                b = fmaxf(b, p.part_b[idx]);
-                if (m != neg_inf()) {
-                    const double f = (double)fast_exp2(m - mx);   // 1 for the record holding the max
-                    Ls = fma(p.part_l[idx], f, Ls);
-                    Ds = fma(p.part_d[idx], f, Ds);
+                const f32x4 rec = p.part_rec[s * total + ridx];
+                b = fmaxf(b, rec[3]);
+                if (rec[0] != neg_inf()) {
+                    const double f = (double)fast_exp2(rec[0] - mx);   // 1 for the record holding the max
+                    Ls = fma((double)rec[1], f, Ls);
+                    Ds = fma((double)rec[2], f, Ds);
                 }
             }
         }
@@ -1011,6 +1015,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p) {
         if (grp == 0 && ok) {
             float lse2 = pos_inf();   // dead or padding row
             double dl = 0.0, lnat = 0.0;
+            int ks = 0;
             if (mx != neg_inf()) {
                 const double L = ((sl[0][lr] + sl[1][lr]) + sl[2][lr]) + sl[3][lr];
                 const double Dd = ((sd[0][lr] + sd[1][lr]) + sd[2][lr]) + sd[3][lr];
@@ -1018,12 +1023,13 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p) {
                 lse2 = (float)(l2 - kPScaleLog2);   // stored less the P image exponent
                 lnat = l2 * kLn2;
                 dl = Dd / L;
-                bound = fmaxf(bound, fmaxf(fmaxf(sb[0][lr], sb[1][lr]), fmaxf(sb[2][lr], sb[3][lr])) +
-                                         fabsf((float)dl));
+                const float br = fmaxf(fmaxf(sb[0][lr], sb[1][lr]), fmaxf(sb[2][lr], sb[3][lr])) + fabsf((float)dl);
+                ks = ds_exponent(br);
+                bound = fmaxf(bound, br);
             }
             p.row_lse2[ridx] = lse2;
             p.row_dlt[ridx] = (float)dl;
-            const int hk = ridx / rowsHK, r = ridx - (ridx / rowsHK) * rowsHK;
+            p.row_ks[ridx] = ks;
             if (r < p.R) {
                 const int i = r / p.G, g = r - (r / p.G) * p.G;
                 const int h = hk * p.G + g;
@@ -1035,7 +1041,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p) {
     }
     if (grp != 0) return;
     bound = wave_max(bound);
-    if (lr == 0) p.bound_part[blockIdx.x] = bound;
+    if (lr == 0) p.bound_part[hk * gridDim.x + blockIdx.x] = bound;
 }
 
 // ----------------------------------------------------------------------------- saved statistics
@@ -1088,20 +1094,22 @@ static __global__ __launch_bounds__(kThreads) void vmax_kernel(Params p) {
 
 // Row statistics from the saved LSE and O, one wave per row (rows r = i*G + g of each KV head,
 // padding rows past R included): the log2-LSE less the P image exponent (+inf for a fully
-// masked or padding row), delta in the dO-scaled units of the products, the LSE and delta
-// outputs, and per block the max of the dS bound over its rows.
+// masked or padding row), delta in the dO-scaled units of the products, the row's dS exponent,
+// the LSE and delta outputs, and per block the max of the dS bound over its rows. Grid
+// (blocks, Hkv), like the merge.
 static __global__ __launch_bounds__(kThreads) void saved_rows_kernel(Params p) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int rowsHK = p.RB * 32;
-    const int total = p.Hkv * rowsHK;
+    const int hk = blockIdx.y;
     const int edo = p.scal[1];
     float vmax = 0.0f;
     for (int t = lane; t < p.nvpart; t += 64) vmax = fmaxf(vmax, p.vmax_part[t]);
     vmax = wave_max(vmax) * 1.001f;   // the fp16 rounding of the products' V values
     float bound = 0.0f;
-    for (int ridx = blockIdx.x * kWaves + wave; ridx < total; ridx += gridDim.x * kWaves) {
-        const int hk = ridx / rowsHK, r = ridx - hk * rowsHK;
+    for (int r = blockIdx.x * kWaves + wave; r < rowsHK; r += gridDim.x * kWaves) {
+        const int64_t ridx = (int64_t)hk * rowsHK + r;
         float lse2 = pos_inf(), dlt = 0.0f;
+        int ks = 0;
         if (r < p.R) {
             const int i = r / p.G, g = r - (r / p.G) * p.G;
             const int h = hk * p.G + g;
@@ -1125,9 +1133,14 @@ static __global__ __launch_bounds__(kThreads) void saved_rows_kernel(Params p) {
                     dc += __shfl_xor(dc, o);
                     l1 += __shfl_xor(l1, o);
                 }
-                lse2 = (float)((double)lse * (1.0 / kLn2) - kPScaleLog2);
+                // with K centred, the products see the centred scores: their LSE is the given
+                // one less scale * q . c
+                const double lc = p.kcen ? (double)lse - (double)p.scale * q_dot_kcen(p, h, i, lane) : (double)lse;
+                lse2 = (float)(lc * (1.0 / kLn2) - kPScaleLog2);
                 dlt = (float)ldexp(dc, edo);
-                bound = fmaxf(bound, ldexpf(l1, edo) * vmax + fabsf(dlt));
+                const float br = ldexpf(l1, edo) * vmax + fabsf(dlt);
+                ks = ds_exponent(br);
+                bound = fmaxf(bound, br);
             }
             if (lane == 0) {
                 p.lse[(int64_t)h * p.N + i] = lse;
@@ -1137,6 +1150,7 @@ static __global__ __launch_bounds__(kThreads) void saved_rows_kernel(Params p) {
         if (lane == 0) {
             p.row_lse2[ridx] = lse2;
             p.row_dlt[ridx] = dlt;
+            p.row_ks[ridx] = ks;
         }
     }
     __shared__ float red[kWaves];
@@ -1146,51 +1160,63 @@ static __global__ __launch_bounds__(kThreads) void saved_rows_kernel(Params p) {
     if (threadIdx.x == 0) {
         float a = red[0];
         for (int w = 1; w < kWaves; ++w) a = fmaxf(a, red[w]);
-        p.bound_part[blockIdx.x] = a;
+        p.bound_part[hk * gridDim.x + blockIdx.x] = a;
     }
 }
 
 // ----------------------------------------------------------------------------- dQ reduce
 
-// ----------------------------------------------------------------------------- centred V
+// ----------------------------------------------------------------------------- centred K and V
 
-// The centre of each KV head's V columns: the fp64 mean of its first min(M, kCentreKeys) keys,
-// summed in key order. Any constant would leave the results unchanged in exact arithmetic; one
-// near the values keeps V - c small, so its fp16 rounding is small too. Grid: one block per
-// KV head.
+// The centre of each KV head's K or V columns (ISK: K): the fp64 mean of its first
+// min(M, kCentreKeys) keys, summed in key order. Any constant would leave the results unchanged
+// in exact arithmetic; one near the values keeps the difference small, so its fp16 rounding is
+// small too. Grid: one block per KV head.
 constexpr int kCentreKeys = 256;
-static __global__ __launch_bounds__(kThreads) void vcentre_kernel(Params p) {
+template <bool ISK>
+static __global__ __launch_bounds__(kThreads) void centre_kernel(Params p) {
     const int hk = blockIdx.x;
     const int n = p.M < kCentreKeys ? p.M : kCentreKeys;
-    const int es = p.v_type == FA_BACK_F32 ? 4 : 2;
-    const char* vh = p.v + (int64_t)hk * p.v_nb2;
+    const int type = ISK ? p.k_type : p.v_type;
+    const int es = type == FA_BACK_F32 ? 4 : 2;
+    const char* th = (ISK ? p.k + (int64_t)hk * p.k_nb2 : p.v + (int64_t)hk * p.v_nb2);
+    const int64_t nb1 = ISK ? p.k_nb1 : p.v_nb1;
+    float* cen = ISK ? p.kcen : p.vcen;
     for (int c = threadIdx.x; c < p.D; c += kThreads) {
         double s = 0.0;
 #pragma unroll 8
-        for (int j = 0; j < n; ++j) s += (double)load_scalar(vh + (int64_t)j * p.v_nb1 + (int64_t)c * es, p.v_type);
-        p.vcen[(int64_t)hk * p.D + c] = n ? (float)(s / n) : 0.0f;
+        for (int j = 0; j < n; ++j) s += (double)load_scalar(th + (int64_t)j * nb1 + (int64_t)c * es, type);
+        cen[(int64_t)hk * p.D + c] = n ? (float)(s / n) : 0.0f;
     }
 }
 
-// The delta output of centred runs: the products give delta' = delta - dO . c; add dO . c back,
-// formed in fp64 with a fixed-order wave sum. One wave per row (h, i); rows whose LSE is -inf
-// (fully masked) keep delta = 0.
-static __global__ __launch_bounds__(kThreads) void vcentre_delta_kernel(Params p) {
+// The outputs of centred runs, one wave per row (h, i); rows whose LSE is -inf (fully masked)
+// keep LSE = -inf and delta = 0.
+//   V centred: the products give delta' = delta - dO . c; dO . c is added back.
+//   K centred: the products give the LSE of the centred scores, lse - scale * q . c; the shift
+//   is added back.
+static __global__ __launch_bounds__(kThreads) void centre_out_kernel(Params p) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t rows = (int64_t)p.H * p.N;
     for (int64_t r = (int64_t)blockIdx.x * kWaves + wave; r < rows; r += (int64_t)gridDim.x * kWaves) {
         const int h = (int)(r / p.N), i = (int)(r - (int64_t)h * p.N);
         if (p.lse[r] == neg_inf()) continue;   // wave-uniform
-        const float* cen = p.vcen + (int64_t)(h / p.G) * p.D;
-        double s = 0.0;
-        for (int c = lane; c < p.D; c += 64) {
-            const float x = load_scalar(p.d + (int64_t)c * p.d_nb0 + (int64_t)h * p.d_nb1 + (int64_t)i * p.d_nb2,
-                                        p.d_type);
-            s = fma((double)x, (double)cen[c], s);
-        }
+        if (p.vcen) {
+            const float* cen = p.vcen + (int64_t)(h / p.G) * p.D;
+            double s = 0.0;
+            for (int c = lane; c < p.D; c += 64) {
+                const float x = load_scalar(p.d + (int64_t)c * p.d_nb0 + (int64_t)h * p.d_nb1 + (int64_t)i * p.d_nb2,
+                                            p.d_type);
+                s = fma((double)x, (double)cen[c], s);
+            }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-        if (lane == 0) p.delta[r] = (float)((double)p.delta[r] + s);
+            for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+            if (lane == 0) p.delta[r] = (float)((double)p.delta[r] + s);
+        }
+        if (p.kcen) {
+            const double s = q_dot_kcen(p, h, i, lane);
+            if (lane == 0) p.lse[r] = (float)((double)p.lse[r] + (double)p.scale * s);
+        }
     }
 }
 
@@ -1198,8 +1224,6 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void dqreduce_kernel(Params p) {
     const int rowsHK = p.RB * 32;
     const int64_t total = (int64_t)p.Hkv * rowsHK;
-    const int ksx = load_ds_exponent(p);
-    const float fac = p.scale * ldexpf(1.0f, ksx - p.scal[1]);
     const int64_t n4 = total * (D / 4);
     for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n4; e += (int64_t)gridDim.x * kThreads) {
         const int64_t ridx = e / (D / 4);
@@ -1213,6 +1237,7 @@ __global__ __launch_bounds__(kThreads) void dqreduce_kernel(Params p) {
         }
         const int i = r / p.G, g = r - (r / p.G) * p.G;
         const int h = hk * p.G + g;
+        const float fac = p.scale * ldexpf(1.0f, p.row_ks[ridx] - p.scal[1]);   // the row's dS exponent
         *(f32x4*)(p.dq + ((int64_t)h * p.N + i) * D + 4 * c4) = acc * fac;
     }
 }
@@ -1304,7 +1329,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
             wait_all_mem();
             __syncthreads();
             decode_tile<D, kQTileKeys, kKVThreads>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rawK, sK,
-                                                   threadIdx.x);
+                                                   threadIdx.x, p.kcen ? p.kcen + (int64_t)hk * D : nullptr);
             decode_tile<D, kQTileKeys, kKVThreads>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, rawV, sV,
                                                    threadIdx.x, p.vcen ? p.vcen + (int64_t)hk * D : nullptr);
             __syncthreads();
@@ -1355,7 +1380,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     };
 
     const int eq = p.scal[0], edo = p.scal[1];
-    const int ksx = load_ds_exponent(p);
+    const int ksx = head_ds_exponent(p, hk);   // one dS exponent for every row of the head
 
     f32x16 acc[MD];
 #pragma unroll

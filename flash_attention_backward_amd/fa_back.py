@@ -16,7 +16,11 @@ LIB_PATH = os.path.join(_HERE, "libfa_back.so")
 
 NONE, F32, F16, BF16, Q8_0, Q4_0 = -1, 0, 1, 2, 8, 9
 CAUSAL_TAIL = 16   # mask type only: query i sees keys j <= M - N + i, nothing stored
-FLAG_CENTER_V = 1  # descriptor flag: centre V before its fp16 rounding
+# descriptor flags (include/fa_back.h)
+FLAG_CENTER_V = 1    # centre V before its fp16 rounding
+FLAG_WALK1_KEYS = 2  # LSE/delta walk owned by key tiles
+FLAG_WALK1_ROWS = 4  # LSE/delta walk owned by row tiles
+FLAG_CENTER_K = 8    # centre K before its fp16 rounding
 TYPE_IDS = {"none": NONE, "f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0,
             "causal_tail": CAUSAL_TAIL}
 ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, Q8_0: 34, Q4_0: 18}

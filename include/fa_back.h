@@ -89,9 +89,32 @@ extern "C" {
  * V before the rounding. For every row P sums to 1, so dP - delta, and with it dS, dQ, dK and
  * dV, are unchanged in exact arithmetic; only the rounding now falls on V - c. The delta
  * output is delta' + dO . c, with dO . c formed in fp64. V must be F32, F16 or BF16
- * (FA_BACK_EUNSUPPORTED for q8_0 / q4_0); other bits are FA_BACK_EINVAL. Costs: one pass over
- * 256 keys of V and one over dO, and one subtraction per decoded V value. */
+ * (FA_BACK_EUNSUPPORTED for q8_0 / q4_0). Costs: one pass over 256 keys of V and one over dO,
+ * and one subtraction per decoded V value. Bits other than the FA_BACK_FLAG_* below are
+ * FA_BACK_EINVAL. */
 #define FA_BACK_FLAG_CENTER_V 1u
+
+/* FA_BACK_FLAG_WALK1_KEYS, FA_BACK_FLAG_WALK1_ROWS: which way the pass that forms each row's
+ * LSE and delta walks the problem. Both give results that meet the same bar; they differ in
+ * speed only. With neither bit the plan takes the key-owned walk when the cache is long next to
+ * the rows (M >= 2 * G * N, G = H / Hkv) and the row-owned walk otherwise. WALK1_KEYS forces the
+ * key-owned walk (each K/V tile decoded once per 256 keys, one statistics record per row and
+ * 256-key tile), WALK1_ROWS the row-owned one (row tiles walk the keys, records per key-range
+ * split). Setting both is FA_BACK_EINVAL. The choice changes the workspace size: pass the same
+ * flags to fa_back_layout_query and fa_back_create. */
+#define FA_BACK_FLAG_WALK1_KEYS 2u
+#define FA_BACK_FLAG_WALK1_ROWS 4u
+
+/* FA_BACK_FLAG_CENTER_K: for caches whose K rows differ in their low bits only (near-constant
+ * K). A per-(KV head, column) constant c (the mean of the first 256 keys) is taken from K
+ * before its fp16 rounding. For query row i, every score then moves by the same amount
+ * scale * q_i . c, which the softmax does not see: P, dP, dS and dK are unchanged in exact
+ * arithmetic, and so is dQ = scale * sum_j dS_ij (k_j - c), because sum_j dS_ij = 0 on every
+ * row. The LSE output is the centred row's LSE plus scale * q_i . c, formed in fp64 (a fully
+ * masked row keeps -inf). K must be F32, F16 or BF16 (FA_BACK_EUNSUPPORTED for q8_0 / q4_0).
+ * Costs: one pass over 256 keys of K and one over q, and one subtraction per decoded K value.
+ * The fa_back_run_saved entry takes the uncentred LSE and removes the shift itself. */
+#define FA_BACK_FLAG_CENTER_K 8u
 
 /* status codes (no entry point aborts or exits) */
 #define FA_BACK_OK 0
@@ -123,14 +146,20 @@ typedef struct {
 typedef struct fa_back_plan fa_back_plan;
 
 /* Validate a descriptor and compute the output layout and workspace size. Touches no
- * device, so it runs on a host without a GPU. Returns FA_BACK_OK or an error code;
- * `layout` is written only on success. */
+ * device, so it runs on a host without a GPU. The layout is a function of the descriptor
+ * only (flags included), never of the device: fa_back_create returns the same one. Returns
+ * FA_BACK_OK or an error code; `layout` is written only on success. */
 int fa_back_layout_query(const fa_back_desc* desc, fa_back_layout* layout);
 
-/* Validate `desc` (before touching the device), check that `device` is a gfx950 GPU with
- * enough LDS, and build an immutable plan. On success *plan owns host memory only and
- * `layout` (if non-NULL) receives the same layout as fa_back_layout_query. On failure
- * *plan is set to NULL. */
+/* Validate `desc` (before touching the device), read the device's limits once, and build an
+ * immutable plan. `device` must be a gfx950 GPU whose per-workgroup LDS (sharedMemPerBlock)
+ * holds the largest tile buffer of the kernels for this head size (up to about 152 KiB at
+ * D = 256), else FA_BACK_EUNSUPPORTED. The device's compute-unit count sets how work is split
+ * over workgroups (the key-side tail split, the key-owned walk's row ranges); it never changes
+ * the layout or the results' bits beyond what the split orders fix (same device type, same
+ * bits). The plan is a pure function of the descriptor and these device limits; nothing in the
+ * library reads the environment. On success *plan owns host memory only and `layout` (if
+ * non-NULL) receives the same layout as fa_back_layout_query. On failure *plan is set to NULL. */
 int fa_back_create(const fa_back_desc* desc, int device, fa_back_plan** plan,
                    fa_back_layout* layout);
 

@@ -188,7 +188,7 @@ def test_centre_v_flag_validation():
     _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_CENTER_V), "c1_f32kv")
     _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_CENTER_V), "c3")
     _expect(B.EUNSUPPORTED, lambda d: setattr(d, "flags", B.FLAG_CENTER_V), "c1")
-    _expect(B.EINVAL, lambda d: setattr(d, "flags", 2), "c1_f32kv")
+    _expect(B.EINVAL, lambda d: setattr(d, "flags", 1 << 5), "c1_f32kv")
     # the centre takes Hkv * D floats of workspace
     d0 = _desc("c1_f32kv")
     d1 = _desc("c1_f32kv")
@@ -197,5 +197,43 @@ def test_centre_v_flag_validation():
     l0, l1 = B.Layout(), B.Layout()
     assert lib.fa_back_layout_query(ctypes.byref(d0), ctypes.byref(l0)) == B.OK
     assert lib.fa_back_layout_query(ctypes.byref(d1), ctypes.byref(l1)) == B.OK
+    assert l1.workspace_bytes >= l0.workspace_bytes + 4 * 2 * 128
+    assert l1.out_bytes == l0.out_bytes
+
+
+def test_walk1_and_centre_k_flags():
+    # the two walk-1 flags exclude each other; K centring applies to F32 / F16 / BF16 K only
+    _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_WALK1_KEYS))
+    _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_WALK1_ROWS))
+    _expect(B.EINVAL, lambda d: setattr(d, "flags", B.FLAG_WALK1_KEYS | B.FLAG_WALK1_ROWS))
+    _expect(B.EUNSUPPORTED, lambda d: setattr(d, "flags", B.FLAG_CENTER_K), "c1")
+    _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_CENTER_K), "c1_f32kv")
+    _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_CENTER_K | B.FLAG_CENTER_V), "c3")
+    _expect(B.EINVAL, lambda d: setattr(d, "flags", 16), "c1_f32kv")
+
+
+def _ws(p, flags):
+    d = B.describe(p)
+    d.flags = flags
+    return fab.fa_back_layout_query(d)
+
+
+def test_walk1_flag_sets_the_workspace():
+    """The key-owned walk keeps one record per row and 256-key tile, the row-owned walk one per
+    key-range split: the flags pick the walk (and with it the workspace); without a flag a long
+    cache (M >= 2 G N) takes the key-owned walk and a short one the row-owned walk."""
+    long_cache = fa_inputs.make_custom("long", D=64, H=24, Hkv=4, N=256, M=8192, mask="none")
+    short = fa_inputs.make_custom("short", D=64, H=4, Hkv=1, N=64, M=300, mask="none")
+    for p in (long_cache, short):
+        keys, rows = _ws(p, B.FLAG_WALK1_KEYS), _ws(p, B.FLAG_WALK1_ROWS)
+        assert keys.out_bytes == rows.out_bytes and keys.off_delta == rows.off_delta
+        assert keys.workspace_bytes != rows.workspace_bytes
+    assert _ws(long_cache, 0).workspace_bytes == _ws(long_cache, B.FLAG_WALK1_KEYS).workspace_bytes
+    assert _ws(short, 0).workspace_bytes == _ws(short, B.FLAG_WALK1_ROWS).workspace_bytes
+
+
+def test_centre_k_workspace():
+    l0 = _ws(fa_inputs.make("c1_f32kv"), 0)
+    l1 = _ws(fa_inputs.make("c1_f32kv"), B.FLAG_CENTER_K)
     assert l1.workspace_bytes >= l0.workspace_bytes + 4 * 2 * 128
     assert l1.out_bytes == l0.out_bytes

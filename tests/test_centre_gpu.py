@@ -1,9 +1,9 @@
-"""Centred V (FA_BACK_FLAG_CENTER_V) on the GPU, through the C ABI.
+"""Centred V and K (FA_BACK_FLAG_CENTER_V, FA_BACK_FLAG_CENTER_K) on the GPU, through the C ABI.
 
-F32 V whose rows differ only in their low bits (V = 1 + 1e-3 z) is the case the flag is for:
-with it every output meets the bar (NMSE <= 1e-5 per output) against the float64 oracle. The
-flag must not change what ordinary inputs give beyond the bar, under both walk-1 variants and
-through the saved-statistics entry."""
+F32 V (or K) whose rows differ only in their low bits (1 + 1e-3 z) is the case the flags are
+for: with them every output meets the bar (NMSE <= 1e-5 per output) against the float64
+oracle. The flags must not change what ordinary inputs give beyond the bar, under both walk-1
+variants and through the saved-statistics entry."""
 import dataclasses
 
 import numpy as np
@@ -12,7 +12,7 @@ import pytest
 import fa_inputs
 from flash_attention_backward_amd import fa_back as B
 from oracle import fa_back_oracle as O
-from tests.gpu_util import compare, run_gpu, say
+from tests.gpu_util import compare, run_gpu, say, walk1
 
 pytestmark = pytest.mark.gpu
 
@@ -38,9 +38,8 @@ def _centred(cfg, name):
 
 @pytest.mark.parametrize("mode", ["rows", "keys"])
 @pytest.mark.parametrize("name,cfg", CASES, ids=[c[0] for c in CASES])
-def test_centred_parity(name, cfg, mode, monkeypatch):
-    monkeypatch.setenv("FA_BACK_WALK1", mode)
-    p = _centred(cfg, name)
+def test_centred_parity(name, cfg, mode):
+    p = walk1(_centred(cfg, name), mode)
     got, _, _ = run_gpu(p)
     errs = compare(got, O.run_problem(p))
     say("   nmse " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
@@ -80,5 +79,73 @@ def test_centred_bitwise_repeat():
     p = _centred(CASES[1][1], "centred_repeat")
     a, _, _ = run_gpu(p)
     b, _, _ = run_gpu(p)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+
+
+# ----------------------------------------------------------------------------- centred K
+
+NEAR_CONST_K = dict(D=128, H=4, Hkv=1, N=64, M=256, mask="tail", k_offset=1.0, k_spread=1e-3,
+                    k_type="f32", v_type="f32")
+
+K_CASES = [
+    ("near_const_k_f32", NEAR_CONST_K),
+    ("near_const_k_d256_gqa", dict(D=256, H=6, Hkv=2, N=40, M=300, mask="random", k_offset=-2.0,
+                                   k_spread=2e-3, k_type="f32", v_type="q8_0", masked_rows=[(0, 3)])),
+    ("near_const_k_f16", dict(D=64, H=2, Hkv=1, N=50, M=130, mask="tail", k_offset=1.0, k_spread=1e-2,
+                              k_type="f16", v_type="f16")),
+    ("ordinary_k_f32", dict(D=128, H=8, Hkv=2, N=64, M=512, mask="none", k_type="f32", v_type="q8_0")),
+    ("near_const_k_and_v", dict(D=128, H=4, Hkv=2, N=33, M=200, mask="tail", k_offset=1.0,
+                                k_spread=1e-3, v_offset=-1.0, v_spread=1e-3, k_type="f32", v_type="f32")),
+]
+
+
+def _kcentred(cfg, name):
+    flags = B.FLAG_CENTER_K | (B.FLAG_CENTER_V if "v_offset" in cfg else 0)
+    return fa_inputs.make_custom(name=name, flags=flags, **cfg)
+
+
+@pytest.mark.parametrize("mode", ["rows", "keys"])
+@pytest.mark.parametrize("name,cfg", K_CASES, ids=[c[0] for c in K_CASES])
+def test_k_centred_parity(name, cfg, mode):
+    p = walk1(_kcentred(cfg, name), mode)
+    got, _, _ = run_gpu(p)
+    errs = compare(got, O.run_problem(p))
+    say("   nmse " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+def test_near_constant_k_needs_the_flag():
+    # without the flag the fp16 rounding of K = 1 + 1e-3 z keeps about one bit of z, and
+    # dQ = scale sum_j dS_ij k_j, whose shared part cancels (sum_j dS_ij = 0), is mostly
+    # rounding; with it dQ meets the bar
+    plain = fa_inputs.make_custom(name="near_const_k_plain", **NEAR_CONST_K)
+    ref = O.run_problem(plain)
+    a, _, _ = run_gpu(plain)
+    b, _, _ = run_gpu(dataclasses.replace(plain, name="near_const_k_centred", flags=B.FLAG_CENTER_K))
+    ea, eb = O.nmse(a["dq"], ref["dq"]), O.nmse(b["dq"], ref["dq"])
+    say(f"   dq nmse plain {ea:.2e}  centred {eb:.2e}")
+    assert eb <= 1e-5 and ea > 100 * eb
+
+
+def test_k_centred_saved_entry():
+    import torch
+    import flash_attention_backward_amd as fab
+    p = _kcentred(NEAR_CONST_K, "near_const_k_saved")
+    lse, o = O.forward_problem(p)
+    dp = fab.DeviceProblem(p, "cuda:0")
+    lse_t = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).to("cuda:0")
+    o_t = torch.from_numpy(np.ascontiguousarray(o, dtype=np.float32)).to("cuda:0")
+    dp.run_saved(lse_t, o_t)
+    torch.cuda.synchronize()
+    got = dp.outputs()
+    dp.close()
+    errs = compare(got, O.run_problem(p))
+    say("   nmse " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+def test_k_centred_bitwise_repeat():
+    p = _kcentred(K_CASES[1][1], "k_centred_repeat")
+    a, _, _ = run_gpu(p)
+    b, _, _ = run_gpu(p, fill=0x00)
     for k in a:
         assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k

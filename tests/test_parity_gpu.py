@@ -3,12 +3,15 @@
 Bar: NMSE <= 1e-5 on each of dQ, dK, dV, LSE and delta separately, -inf LSE entries equal,
 every defined output byte written (outputs are pre-filled with NaN bytes), bitwise
 reproducible runs."""
+import dataclasses
+
 import numpy as np
 import pytest
 
 import fa_inputs
+from flash_attention_backward_amd import fa_back as fab_flags
 from oracle import fa_back_oracle as O
-from tests.gpu_util import compare, run_gpu, say
+from tests.gpu_util import compare, run_gpu, say, walk1
 
 pytestmark = pytest.mark.gpu
 
@@ -117,11 +120,10 @@ def test_q8_0_equals_dequantised_f32_bitwise():
 
 
 @pytest.mark.parametrize("mode", ["rows", "keys"])
-def test_q4_0_equals_dequantised_f32_bitwise(mode, monkeypatch):
+def test_q4_0_equals_dequantised_f32_bitwise(mode):
     # every q4_0 value is exact in F32 and rounds once to fp16 on both paths
-    monkeypatch.setenv("FA_BACK_WALK1", mode)
-    p = fa_inputs.make_custom(name="q4_bits", D=128, H=4, Hkv=2, N=37, M=200, mask="tail",
-                              k_type="q4_0", v_type="q4_0")
+    p = walk1(fa_inputs.make_custom(name="q4_bits", D=128, H=4, Hkv=2, N=37, M=200, mask="tail",
+                                    k_type="q4_0", v_type="q4_0"), mode)
     f = fa_inputs.Problem(**{**p.__dict__})
     f.name = "q4_bits_f32"
     f.k = O.widen(p.k, "q4_0", p.D).astype(np.float32)
@@ -141,11 +143,10 @@ def test_strided_cache_equals_contiguous_bitwise():
 
 
 @pytest.mark.parametrize("mode", ["rows", "keys"])
-def test_gqa_equals_replicated_heads(mode, monkeypatch):
+def test_gqa_equals_replicated_heads(mode):
     # the same walk-1 variant for both runs: the shape-based choice could differ between them
-    monkeypatch.setenv("FA_BACK_WALK1", mode)
-    p = fa_inputs.make_custom("gqa", D=128, H=6, Hkv=2, N=33, M=150, mask="tail", k_type="q8_0",
-                              v_type="q8_0")
+    p = walk1(fa_inputs.make_custom("gqa", D=128, H=6, Hkv=2, N=33, M=150, mask="tail", k_type="q8_0",
+                                    v_type="q8_0"), mode)
     rep = fa_inputs.Problem(**{**p.__dict__})
     rep.name = "gqa_replicated"
     rep.Hkv = p.H
@@ -160,8 +161,8 @@ def test_gqa_equals_replicated_heads(mode, monkeypatch):
         assert O.nmse(a[k], summed) <= 1e-10, k
 
 
-# Walk 1 runs by row tiles or by key tiles (chosen from the shape; FA_BACK_WALK1 overrides the
-# choice when the plan is created). Both must meet the bar on the same inputs.
+# Walk 1 runs by row tiles or by key tiles (chosen from the shape unless a descriptor flag picks
+# one). Both must meet the bar on the same inputs.
 WALK1_CASES = ["c0", "c1_causal", "ragged_d128_headmask", "ragged_d64_q8", "ragged_d256_f32mask",
                "all_masked", "single_key", "dead_row_blocks", "kv_live_middle_blocks"]
 
@@ -174,10 +175,9 @@ def _walk1_problem(name):
 
 @pytest.mark.parametrize("mode", ["rows", "keys"])
 @pytest.mark.parametrize("name", WALK1_CASES)
-def test_walk1_variants(name, mode, monkeypatch):
-    monkeypatch.setenv("FA_BACK_WALK1", mode)
+def test_walk1_variants(name, mode):
     say(f"[walk1 {mode}]")
-    _parity(_walk1_problem(name))
+    _parity(walk1(_walk1_problem(name), mode))
 
 
 # The causal-tail mask without storage (FA_BACK_CAUSAL_TAIL): the library forms the mask from
@@ -199,9 +199,8 @@ def _implicit_problem(name, cfg):
 
 @pytest.mark.parametrize("mode", ["rows", "keys"])
 @pytest.mark.parametrize("name,cfg", IMPLICIT_CASES, ids=[c[0] for c in IMPLICIT_CASES])
-def test_implicit_causal_tail_bitwise(name, cfg, mode, monkeypatch):
-    monkeypatch.setenv("FA_BACK_WALK1", mode)
-    p = _implicit_problem(name, cfg)
+def test_implicit_causal_tail_bitwise(name, cfg, mode):
+    p = walk1(_implicit_problem(name, cfg), mode)
     a, _, _ = run_gpu(p)
     b, _, _ = run_gpu(fa_inputs.implicit_causal(p))
     for k in a:
@@ -210,3 +209,18 @@ def test_implicit_causal_tail_bitwise(name, cfg, mode, monkeypatch):
 
 def test_implicit_causal_tail_parity():
     _parity(fa_inputs.implicit_causal(fa_inputs.make_custom(name="impl_parity", **IMPLICIT_CASES[2][1])))
+
+
+@pytest.mark.parametrize("flags", [0, fab_flags.FLAG_WALK1_KEYS, fab_flags.FLAG_WALK1_ROWS],
+                         ids=["default", "walk1_keys", "walk1_rows"])
+def test_create_layout_equals_query(flags):
+    # the plan reads the device's CU count and LDS size; the layout stays that of the descriptor
+    import flash_attention_backward_amd as fab
+    for name in ("c0", "c1", "c2", "c3"):
+        p = dataclasses.replace(fa_inputs.make(name), flags=flags)
+        d = fab_flags.describe(p)
+        q = fab.fa_back_layout_query(d)
+        plan, lay = fab.fa_back_create(d, 0)
+        fab.fa_back_destroy(plan)
+        for f, _ in fab_flags.Layout._fields_:
+            assert getattr(q, f) == getattr(lay, f), (name, f)
