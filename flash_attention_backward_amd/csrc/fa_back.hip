@@ -2,10 +2,11 @@
 // workspace sizing, the plan, and the launch sequence. Device code is in fab_kernels.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "fa_back.h"
@@ -349,12 +350,40 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
     return hipGetLastError() == hipSuccess ? FA_BACK_OK : FA_BACK_EHIP;
 }
 
+// Workspace for fa_back_run_noalloc: a static device array, one copy per GPU the library runs
+// on, held until the process ends. In host code `scratch` only names the symbol; the device
+// address of each GPU's copy comes from hipGetSymbolAddress with that GPU current, and only
+// that address is handed to kernels.
+constexpr uint64_t kScratchBytes = 64ull << 20;
+static_assert(kScratchBytes == FA_BACK_NOALLOC_MAX_WORKSPACE, "header and library disagree");
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, once looked up
+
+// The address of this device's `scratch` (the device must be current). nullptr on failure.
+void* scratch_address(int device) {
+    if (device < 0 || device >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[device] = ptr;
+    }
+    return g_scratch_ptr[device];
+}
+
 }  // namespace
 
 struct fa_back_plan {
     fa_back_desc desc;
     Geometry geo;
     int device;
+    void* scratch;   // this device's static scratch (fa_back_run_noalloc), or nullptr
 };
 
 extern "C" {
@@ -368,6 +397,7 @@ const char* fa_back_status_string(int s) {
         case FA_BACK_EUNSUPPORTED: return "unsupported type, size or device";
         case FA_BACK_EHIP: return "HIP runtime error";
         case FA_BACK_EALIGN: return "misaligned device pointer";
+        case FA_BACK_ESCRATCH: return "workspace larger than the static scratch of fa_back_run_noalloc";
         default: return "unknown status";
     }
 }
@@ -395,11 +425,22 @@ int fa_back_create(const fa_back_desc* desc, int device, fa_back_plan** plan, fa
     if (prop.multiProcessorCount < 1) return FA_BACK_EUNSUPPORTED;
     rc = validate(desc, prop.multiProcessorCount, &g);
     if (rc != FA_BACK_OK) return rc;
+    // the device's copy of the static scratch (fa_back_run_noalloc), looked up with it current
+    void* scr = nullptr;
+    {
+        int old = -1;
+        if (hipGetDevice(&old) != hipSuccess) return FA_BACK_EHIP;
+        if (old != device && hipSetDevice(device) != hipSuccess) return FA_BACK_EHIP;
+        scr = scratch_address(device);
+        if (old != device) (void)hipSetDevice(old);
+        if (!scr) return FA_BACK_EHIP;
+    }
     fa_back_plan* p = new (std::nothrow) fa_back_plan;
     if (!p) return FA_BACK_EINVAL;
     p->desc = *desc;
     p->geo = g;
     p->device = device;
+    p->scratch = scr;
     *plan = p;
     if (layout) *layout = g.layout;
     return FA_BACK_OK;
@@ -528,6 +569,14 @@ int fa_back_run_saved(const fa_back_plan* plan, const void* q, const void* k, co
                       const void* mask, const float* lse, const float* o, void* out, void* workspace,
                       void* stream) {
     return run_impl(plan, q, k, v, d, mask, lse, o, true, out, workspace, stream, nullptr);
+}
+
+int fa_back_run_noalloc(const fa_back_plan* plan, const void* q, const void* k, const void* v,
+                        const void* d, const void* mask, void* out, void* stream) {
+    if (!plan) return FA_BACK_EINVAL;
+    if (plan->geo.layout.workspace_bytes > kScratchBytes) return FA_BACK_ESCRATCH;
+    if (!plan->scratch) return FA_BACK_EHIP;
+    return run_impl(plan, q, k, v, d, mask, nullptr, nullptr, false, out, plan->scratch, stream, nullptr);
 }
 
 int fa_back_run_saved_timed(const fa_back_plan* plan, const void* q, const void* k, const void* v,

@@ -25,7 +25,8 @@ TYPE_IDS = {"none": NONE, "f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "q
             "causal_tail": CAUSAL_TAIL}
 ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, Q8_0: 34, Q4_0: 18}
 
-OK, EINVAL, ESHAPE, ESTRIDE, EUNSUPPORTED, EHIP, EALIGN = 0, -1, -2, -3, -4, -5, -6
+OK, EINVAL, ESHAPE, ESTRIDE, EUNSUPPORTED, EHIP, EALIGN, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
+NOALLOC_MAX_WORKSPACE = 64 << 20   # bytes of the library's static scratch (fa_back_run_noalloc)
 
 
 class FaBackError(RuntimeError):
@@ -76,6 +77,8 @@ def load_library():
     lib.fa_back_run_saved_timed.argtypes = ([ctypes.c_void_p] + [ctypes.c_void_p] * 10 +
                                             [ctypes.POINTER(ctypes.c_float)])
     lib.fa_back_run_saved_timed.restype = ctypes.c_int
+    lib.fa_back_run_noalloc.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 7
+    lib.fa_back_run_noalloc.restype = ctypes.c_int
     lib.fa_back_destroy.argtypes = [ctypes.c_void_p]
     lib.fa_back_destroy.restype = None
     lib.fa_back_status_string.argtypes = [ctypes.c_int]
@@ -116,6 +119,14 @@ def fa_back_run(plan, q: int, k: int, v: int, d: int, mask: Optional[int], out: 
     rc = load_library().fa_back_run(plan, q, k, v, d, mask or None, out, workspace, stream or None)
     if rc != OK:
         raise FaBackError(rc, "fa_back_run")
+
+
+def fa_back_run_noalloc(plan, q: int, k: int, v: int, d: int, mask: Optional[int], out: int,
+                        stream: int = 0) -> None:
+    """fa_back_run with the library's static scratch as the workspace (no device allocation)."""
+    rc = load_library().fa_back_run_noalloc(plan, q, k, v, d, mask or None, out, stream or None)
+    if rc != OK:
+        raise FaBackError(rc, "fa_back_run_noalloc")
 
 
 NUM_PHASES = 7
@@ -252,6 +263,14 @@ class DeviceProblem:
                     self.bufs["v"].data_ptr(), self.bufs["d"].data_ptr(),
                     None if m is None else m.data_ptr(), self.out.data_ptr(), self.ws.data_ptr(),
                     s.cuda_stream)
+
+    def run_noalloc(self, stream=None):
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        m = self.bufs["mask"]
+        fa_back_run_noalloc(self.plan, self.bufs["q"].data_ptr(), self.bufs["k"].data_ptr(),
+                            self.bufs["v"].data_ptr(), self.bufs["d"].data_ptr(),
+                            None if m is None else m.data_ptr(), self.out.data_ptr(), s.cuda_stream)
 
     def run_timed(self, stream=None) -> list:
         import torch

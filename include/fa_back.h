@@ -124,6 +124,8 @@ extern "C" {
 #define FA_BACK_EUNSUPPORTED (-4) /* type combination, D/Dv, size limit, device not gfx950  */
 #define FA_BACK_EHIP (-5)         /* a HIP runtime call or kernel launch failed             */
 #define FA_BACK_EALIGN (-6)       /* a device pointer passed to fa_back_run is misaligned   */
+#define FA_BACK_ESCRATCH (-7)     /* fa_back_run_noalloc: the plan's workspace exceeds
+                                     FA_BACK_NOALLOC_MAX_WORKSPACE                        */
 
 typedef struct {
     int32_t type;    /* FA_BACK_* element type */
@@ -208,6 +210,23 @@ int fa_back_run_saved(const fa_back_plan* plan, const void* q, const void* k, co
 int fa_back_run_saved_timed(const fa_back_plan* plan, const void* q, const void* k, const void* v,
                             const void* d, const void* mask, const float* lse, const float* o,
                             void* out, void* workspace, void* stream, float* phase_ms);
+
+/* Largest workspace (layout.workspace_bytes) fa_back_run_noalloc accepts: 64 MiB. */
+#define FA_BACK_NOALLOC_MAX_WORKSPACE (64ull << 20)
+
+/* fa_back_run for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments, conventions and results
+ * as fa_back_run (the same kernels run), except that there is no workspace argument: the
+ * library's own static device array of FA_BACK_NOALLOC_MAX_WORKSPACE bytes serves as the
+ * workspace. Each GPU the library runs on holds one copy of it from the plan's creation until
+ * the process ends; fa_back_create looks up its address. The caller still passes the inputs
+ * and `out`. The call allocates and frees nothing (no hipMalloc, no allocating library call).
+ * Returns FA_BACK_ESCRATCH, enqueuing nothing, when the plan's workspace is larger than the
+ * array. Every call on one GPU uses that GPU's single array: calls whose work overlaps on one
+ * GPU (other streams, other threads, other plans) race, and the caller must order them, e.g.
+ * on one stream. The array keeps the last call's contents; no kernel relies on them. */
+int fa_back_run_noalloc(const fa_back_plan* plan, const void* q, const void* k, const void* v,
+                        const void* d, const void* mask, void* out, void* stream);
 
 /* Free a plan (NULL is allowed). */
 void fa_back_destroy(fa_back_plan* plan);

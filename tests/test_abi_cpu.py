@@ -237,3 +237,12 @@ def test_centre_k_workspace():
     l1 = _ws(fa_inputs.make("c1_f32kv"), B.FLAG_CENTER_K)
     assert l1.workspace_bytes >= l0.workspace_bytes + 4 * 2 * 128
     assert l1.out_bytes == l0.out_bytes
+
+
+def test_noalloc_status_and_limit():
+    assert "scratch" in fab.status_string(B.ESCRATCH)
+    txt = open(os.path.join(ROOT, "include", "fa_back.h")).read()
+    assert "#define FA_BACK_NOALLOC_MAX_WORKSPACE (64ull << 20)" in txt
+    assert B.NOALLOC_MAX_WORKSPACE == 64 << 20
+    lib = fab.load_library()
+    assert lib.fa_back_run_noalloc(None, *([None] * 7)) == B.EINVAL
