@@ -42,6 +42,24 @@ KERNEL_NAMES = {"walk1": "qpass_kernel<D, false>", "walk2": "qpass_kernel<D, tru
                 "kvpass": "kvpass_kernel<D>"}
 
 
+def phase_bytes(p, phase):
+    """Algorithmic HBM bytes of one launch of a phase's kernel: what it must read and write once.
+    Every phase reads the K/V cache (stored types) and the fp16 q and dO rows (2 bytes a value,
+    each row once); walk 1 and walk 2 also read the stored mask and write 8 bytes of statistics a
+    row, walk 2 writes dQ (F32), the key side reads 8 bytes of statistics a row and writes dK and
+    dV (F32)."""
+    import fa_inputs
+    kv = fa_inputs.storage_bytes(p.k) + fa_inputs.storage_bytes(p.v)
+    rows = p.N * p.H
+    qd = 2 * 2 * rows * p.D
+    mask = 0 if p.mask is None or p.mask_type == "causal_tail" else fa_inputs.storage_bytes(p.mask)
+    if phase == "kvpass":
+        return kv + qd + 8 * rows + 4 * 2 * p.Hkv * p.M * p.D
+    if phase == "walk2":
+        return kv + qd + mask + 8 * rows + 4 * rows * p.D
+    return kv + qd + mask + 8 * rows
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -197,15 +215,26 @@ def main():
     log("phase ms: " + " ".join(f"{k}={v:.3f}" for k, v in mean_phase.items()))
 
     dom = max(PHASE_FLOPS_PER_PAIR_PER_D, key=lambda n: mean_phase[n])
-    dom_flops = PHASE_FLOPS_PER_PAIR_PER_D[dom] * p.D * flops["visible"]
-    achieved = dom_flops / (mean_phase[dom] * 1e-3) / 1e12
     kname = KERNEL_NAMES[dom].replace("D", str(p.D), 1)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_F16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
-                "traffic": (measured_traffic(kname, args.workload)
-                            if args.mask == "stored" and not args.saved else None),
-                "kernel": kname, "phase": dom,
-                "flops_per_launch": dom_flops, "avg_launch_ms": round(mean_phase[dom], 4)}
+    nbytes = fa_inputs.min_bytes(p)
+    intensity = flops["full"] / nbytes["total"]
+    traffic = (measured_traffic(kname, args.workload) if args.mask == "stored" and not args.saved else None)
+    if intensity >= PEAK_MFMA_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        dom_flops = PHASE_FLOPS_PER_PAIR_PER_D[dom] * p.D * flops["visible"]
+        achieved = dom_flops / (mean_phase[dom] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_F16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4), "traffic": traffic,
+                    "kernel": kname, "phase": dom,
+                    "flops_per_launch": dom_flops, "avg_launch_ms": round(mean_phase[dom], 4)}
+    else:
+        dom_bytes = phase_bytes(p, dom)
+        achieved = dom_bytes / (mean_phase[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "kernel": kname, "phase": dom,
+                    "bytes_per_launch": dom_bytes, "avg_launch_ms": round(mean_phase[dom], 4),
+                    "call": {"min_bytes": nbytes["total"],
+                             "gbs": round(nbytes["total"] / (statistics.median(per_call) * 1e-3) / 1e9, 1)}}
     value = flops["full"] / (ms * 1e-3) / 1e12
     rec = {
         "metric": (METRIC if args.workload == "c4" and args.mask == "stored" and not args.saved

@@ -317,3 +317,17 @@ def flop_count(p: Problem) -> dict:
     five: the five backward products only = 2*V*(3D + 2Dv)."""
     V = visible_pairs(p)
     return {"visible": V, "full": 2 * V * (5 * p.D + 4 * p.Dv), "five": 2 * V * (3 * p.D + 2 * p.Dv)}
+
+
+def storage_bytes(x: np.ndarray) -> int:
+    """Bytes of the elements of a (possibly strided) stored tensor."""
+    return int(x.size * x.itemsize)
+
+
+def min_bytes(p: Problem) -> dict:
+    """HBM bytes a backward must move at least: every input read once (q, dO, K, V and the stored
+    mask, in their stored types) and every output written once (dQ, dK, dV F32, LSE and delta)."""
+    reads = (storage_bytes(p.q) + storage_bytes(p.d) + storage_bytes(p.k) + storage_bytes(p.v) +
+             (0 if p.mask is None or p.mask_type == "causal_tail" else storage_bytes(p.mask)))
+    writes = 4 * (p.D * p.N * p.H + p.D * p.M * p.Hkv + p.Dv * p.M * p.Hkv + 2 * p.N * p.H)
+    return {"read": reads, "write": writes, "total": reads + writes}

@@ -19,10 +19,10 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = OUT, defines=()) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = OUT + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(PKG, "csrc"), "-o", tmp, SRC]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -30,8 +30,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed building libfa_back.so")
     if verbose:
         sys.stderr.write("\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l))
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -1251,7 +1251,8 @@ __global__ __launch_bounds__(kThreads) void dqreduce_kernel(Params p) {
 //                        Y wave), then dV^T += dO^T P from its own fp16 image.
 //   Y wave (w = 4 + kb)  V fragments in registers. Per row block: dK^T += Q^T dS of the previous
 //                        block (its dS kept in registers, its q rows still in their buffer),
-//                        dP = dO V^T; then, with P from the X wave, dS = P (dP - delta) in fp32.
+//                        dP = dO V^T (kept in registers across the mid-block barrier); then,
+//                        with P from the X wave, dS = P (dP - delta) in fp32.
 // Two barriers per row block. Neither wave waits for the other's products: the X wave's
 // exponentials run beside the Y wave's dK and dP products, the Y wave's dS arithmetic beside
 // the X wave's dV products. The q and dO row blocks (fp16, row-major, with their lse/delta) are
@@ -1267,8 +1268,7 @@ struct KVLds {
     static constexpr int kBlk = 32 * D * 2;                              // bytes of a 32-row block
     static constexpr int kBuf = 2 * kBlk + 256;                          // q, dO, 32 lse, 32 delta
     static constexpr int kExF = 4 * 4096;                                // [kb][4][lane] P image, fp32
-    static constexpr int kExD = 4 * 4096;                                // [kb][4][lane] dP, fp32 (Y only)
-    static constexpr int kWork = 3 * kBuf + kExF + kExD;
+    static constexpr int kWork = 3 * kBuf + kExF;
     static constexpr int kRaw = RawTile<D, kQTileKeys>::kBytes;
     static constexpr int kSetup = 2 * kQTileKeys * D * 2 + 2 * kRaw;     // K, V half tiles + bytes
     static constexpr int kMaxRB = 2048;                                  // row blocks listed per workgroup
@@ -1285,7 +1285,6 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
     unsigned char* work = lds;                        // setup scratch, then buffers + exchange
     unsigned char* exF = work + 3 * L::kBuf;             // P images from the X to the Y waves
-    unsigned char* exD = exF + L::kExF;                  // dP parked by the Y waves across the barrier
     uint32_t* sched = (uint32_t*)(lds + L::kBytes - L::kTail);          // needed row blocks of a chunk
     unsigned char* clsA = (unsigned char*)(sched + L::kMaxRB);         // class of (row block, first 64 keys)
     unsigned char* clsB = clsA + L::kMaxRB;                             // class of (row block, last 64 keys)
@@ -1390,7 +1389,6 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     const RowWalkX rw0 = make_row_walk_x<D>(lane);
     const ColWalkX cw0 = make_col_walk_x<D>(lane);
     unsigned char* myF = exF + kb * 4096;             // the pair's P image in fp32 [4][lane] x 16 B
-    unsigned char* myD = exD + kb * 4096;             // the Y wave's dP [4][lane] x 16 B
 
     // ---- the needed row blocks (those with a 64-key half not fully masked) are listed in order
     // in LDS with both classes, entry = (rb - rb_lo) | class(first 64 keys) << 24 |
@@ -1539,25 +1537,17 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                 cols_acc_x<D>(work + bprev * L::kBuf, bs, acc, cw);
                 mfma_prio_lo();
             }
-            if (cls != kMaskDead) {
-                f32x16 pa;
+            // dP stays in registers across the barrier (0 for a dead block: its dS is formed
+            // too, and then not used)
+            f32x16 pa;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) pa[v] = 0.0f;
+            for (int v = 0; v < 16; ++v) pa[v] = 0.0f;
+            if (cls != kMaskDead) {
                 mfma_prio_hi();
                 rows_chain_x<D, 1>(tq + L::kBlk, bkv, pa, rw);
                 mfma_prio_lo();
-                // parked in LDS across the barrier and the copy (registers are short there)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const f32x4 o = {pa[4 * b], pa[4 * b + 1], pa[4 * b + 2], pa[4 * b + 3]};
-                    *(f32x4*)(myD + (b * 64 + lane) * 16) = o;
-                }
             }
             lds_barrier();     // Y: P of block rb published; the buffer of block k-1 is read
-            // the copy of the block two ahead, into the buffer of block k-1 (past the end of the
-            // list: block k again)
-            dma_block(k + 2 < n ? c0 + (int)(__builtin_amdgcn_readfirstlane(sched[k + 2]) & 0xffffffu) : rb,
-                      bi == 0 ? 2 : bi - 1, 4, kb);
             // dS is formed for a dead block too (and then not used): assigned on every path, the
             // previous block's dS is dead once its products are issued
             live = cls != kMaskDead;
@@ -1565,16 +1555,19 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                 const float* drow = (const float*)(tq + 2 * L::kBlk) + 32;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    const f32x4 dp4 = *(const f32x4*)(myD + (b * 64 + lane) * 16);
                     const f32x4 p4 = *(const f32x4*)(myF + (b * 64 + lane) * 16);
                     const f32x4 d4 = *(const f32x4*)(drow + 8 * b + 4 * g);
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int v = 4 * b + u;
-                        bs[v >> 3][v & 7] = (_Float16)(p4[u] * (dp4[u] - d4[u]) * dsf);
+                        bs[v >> 3][v & 7] = (_Float16)(p4[u] * (pa[v] - d4[u]) * dsf);
                     }
                 }
             }
+            // the copy of the block two ahead, into the buffer of block k-1 (past the end of the
+            // list: block k again)
+            dma_block(k + 2 < n ? c0 + (int)(__builtin_amdgcn_readfirstlane(sched[k + 2]) & 0xffffffu) : rb,
+                      bi == 0 ? 2 : bi - 1, 4, kb);
             bprev = bi;
             ent = __builtin_amdgcn_readfirstlane(nxt);
             bi = bi == 2 ? 0 : bi + 1;
@@ -1587,20 +1580,47 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     }
     } }   // rows listed
     wait_all_mem();   // no copy is left in flight when the wave ends
-    if (!key_ok) return;
+    __syncthreads();  // every wave is done with the row-block buffers: they stage the output
+    // Output: a lane holds 16-byte pieces of its key's row, so a direct store instruction would
+    // write 32 bytes of each of 32 rows. Each wave instead stages 8 of its 32 key rows at a time
+    // (fp32, scaled, padded rows) in an LDS area of its own and writes them back one whole row
+    // (D floats) per 64 lanes, so that every store instruction covers whole cache lines.
     const int outk = role == 0 ? 1 : 0;               // X waves hold dV, Y waves dK
     const float fac = outk == 0 ? fabsf(p.scale) * ldexpf(1.0f, ksx - eq - edo) : ldexpf(1.0f, -kPScaleLog2 - edo);
-    float* dst = split ? p.kv_part + ((((int64_t)(tile - p.kv_full) * p.kv_split + part) * 2 + outk) * kKVKeys +
-                                      32 * kb + l32) * D
-                       : (outk == 0 ? p.dk : p.dv) + ((int64_t)hk * p.M + myj) * D;
+    float* dst0 = split ? p.kv_part + ((((int64_t)(tile - p.kv_full) * p.kv_split + part) * 2 + outk) * kKVKeys +
+                                       32 * kb) * D
+                        : (outk == 0 ? p.dk : p.dv) + ((int64_t)hk * p.M + key0 + 32 * kb) * D;
+    constexpr int kRowB = D * 4 + 16;                 // staged row bytes (padded)
+    constexpr int kPass = 8;                          // rows per pass
+    static_assert(kKVWaves * kPass * kRowB <= L::kWork, "staging fits the row-block buffers");
+    unsigned char* stage = work + wave * kPass * kRowB;
+    constexpr int CPR = D / 4;                        // 16-byte chunks per row
+#pragma unroll 1
+    for (int r0 = 0; r0 < 32; r0 += kPass) {
+        if ((l32 & ~(kPass - 1)) == r0) {
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
+            for (int md = 0; md < MD; ++md)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            f32x4 o = {acc[md][4 * b] * fac, acc[md][4 * b + 1] * fac, acc[md][4 * b + 2] * fac,
-                       acc[md][4 * b + 3] * fac};
-            *(f32x4*)(dst + 32 * md + 8 * b + 4 * g) = o;
+                for (int b = 0; b < 4; ++b) {
+                    const f32x4 o = {acc[md][4 * b] * fac, acc[md][4 * b + 1] * fac, acc[md][4 * b + 2] * fac,
+                                     acc[md][4 * b + 3] * fac};
+                    *(f32x4*)(stage + (l32 - r0) * kRowB + 4 * (32 * md + 8 * b + 4 * g)) = o;
+                }
         }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the pass's rows are in LDS
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int t = 0; t < kPass * CPR / 64; ++t) {
+            const int rr = t * (64 / CPR) + lane / CPR, c = lane % CPR;
+            const int j = key0 + 32 * kb + r0 + rr;
+            if (split || j < p.M) {
+                const f32x4 o = *(const f32x4*)(stage + rr * kRowB + 16 * c);
+                *(f32x4*)(dst0 + (int64_t)(r0 + rr) * D + 4 * c) = o;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();   // the staged rows are read before the next pass
+    }
 }
 
 // ----------------------------------------------------------------------------- fills
