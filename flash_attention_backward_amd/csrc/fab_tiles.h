@@ -108,6 +108,14 @@ FAB_DEV void dma16(const void* gsrc, void* lds_wave_base) {
 // it explicitly (wait_all_mem) before any read of its destination, and never reads or writes
 // that destination while it is in flight. M0 is saved and restored around the copy.
 FAB_DEV void dma16_hidden(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
+    // the base and the LDS address are the same in every lane: taken from the first active lane
+    // so that they sit in scalar registers whatever the compiler could prove
+    // (readfirstlane returns a signed int: each half is taken back to uint32_t before widening)
+    const uint64_t a = (uint64_t)(uintptr_t)sbase;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    sbase = (const void*)(uintptr_t)((uint64_t)lo | ((uint64_t)hi << 32));
+    lds_wave_base = (uint32_t)__builtin_amdgcn_readfirstlane(lds_wave_base);
     int keep;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
