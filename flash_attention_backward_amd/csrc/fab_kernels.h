@@ -617,13 +617,15 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         cls_cur = cls_nx;                                            // class of sub-tile s+1
         if (lane == 0 && s + 1 < s_end) clsx[((s + 1) & 1) * 4 + kw] = (unsigned char)cls_cur;
         cls_nx = s + 2 < s_end ? wclass(s + 2) : kMaskDead;          // in flight during sub-tile s
+        // the decode (vector ALU work) first, beside the S waves' products; then the dQ products,
+        // beside the S waves' exponentials
+        if (s + 1 < s_end) kdecode(s + 1);
         if (GRAD && s > s_begin && cls_prev != kMaskDead) {
             const unsigned char* ex = exch(s - 1);
             const f16x8 bb[2] = {*(const f16x8*)(ex + lane * 16), *(const f16x8*)(ex + 1024 + lane * 16)};
             cols_acc<D>(slot(s - 1), bb, dqacc, cw);
         }
         if (s == s_end) break;
-        if (s + 1 < s_end) kdecode(s + 1);
     }
     if (GRAD && row_ok) {
         const int ksx = p.row_ks[ridx];   // the row's dS exponent
