@@ -112,9 +112,10 @@ def describe_workload(p):
             f"Q/dO {p.q_type} mask {mask}")
 
 
-def cpu_baseline(rows: int):
-    """Time the float64 oracle on a bounded sample of the same workload: the last `rows`
-    query rows of every head against the whole cache (same draws, same mask rows)."""
+def cpu_baseline(workload: str, rows: int):
+    """Time the float64 oracle on a bounded sample of the same workload: its last `rows`
+    query rows of every head (all of them when it has no more) against the whole cache (same
+    draws, same mask rows)."""
     import numpy as np
     import fa_inputs
     from oracle import fa_back_oracle as O
@@ -123,16 +124,13 @@ def cpu_baseline(rows: int):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    name = {8: "c4n8", 16: "c4n16"}.get(rows)
-    if name:
-        s = fa_inputs.make(name)
-    else:
-        full = fa_inputs.make("c4")
-        s = full
-        s.name = f"c4 last {rows} rows"
-        s.q = np.ascontiguousarray(full.q[:, full.N - rows:, :])
-        s.d = np.ascontiguousarray(full.d[full.N - rows:, :, :])
-        s.mask = np.ascontiguousarray(full.mask[:, full.N - rows:, :])
+    s = fa_inputs.make(workload)
+    if rows < s.N:
+        s.name = f"{workload} last {rows} rows"
+        s.q = np.ascontiguousarray(s.q[:, s.N - rows:, :])
+        s.d = np.ascontiguousarray(s.d[s.N - rows:, :, :])
+        if s.mask is not None:
+            s.mask = np.ascontiguousarray(s.mask[:, s.N - rows:, :])
         s.N = rows
     f = fa_inputs.flop_count(s)
     log(f"cpu baseline: oracle on {s.name} ({f['full'] / 1e9:.1f} GFLOP counted), {threads} BLAS threads")
@@ -142,7 +140,7 @@ def cpu_baseline(rows: int):
     log(f"cpu baseline: {dt:.2f} s")
     return {"value": f["full"] / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "seconds": dt,
-            "sample": f"float64 numpy oracle on the last {rows} query rows of all {s.H} heads against "
+            "sample": f"float64 numpy oracle on the last {s.N} query rows of all {s.H} heads against "
                       f"the full M={s.M} cache (same inputs and mask rows); value = that sample's "
                       f"counted FLOPs / oracle wall time"}
 
@@ -259,8 +257,8 @@ def main():
     torch.cuda.empty_cache()
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
-    if not args.no_cpu_baseline and args.workload == "c4" and args.mask == "stored" and not args.saved:
-        rec["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+    if not args.no_cpu_baseline and args.mask == "stored" and not args.saved:
+        rec["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_rows)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
