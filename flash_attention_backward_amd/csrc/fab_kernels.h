@@ -803,6 +803,31 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
             dma16((ten ? dbase : qbase) + blk + off, base + ten * L::kBlk + ii * 1024);
         }
     };
+    // The same copy by the late waves (wl = 0 .. 3 among them) in the loop. Instruction
+    // ins = wl + 4k moves 1 KB piece ii = ins % NI of tensor ins / NI; the swizzle repeats every
+    // IP = D/32 pieces, so a lane's source offset is that of ii % IP, one of the two computed
+    // here once, and the rest of the address is a uniform 16-row step on the base. The copies
+    // are hidden from the compiler (dma16_hidden); the block barrier waits for them.
+    constexpr int IP = D / 32;
+    const int wl = (wave - kW1Waves / 2) & 3;
+    uint32_t doff[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int P = ((wl + 4 * h) % IP) * 64 + lane;
+        const int row = P / (D / 8), pc = P - (P / (D / 8)) * (D / 8);
+        doff[h] = (uint32_t)((row * D + 8 * swz_chunk<D>(row, pc)) * 2);
+    }
+    auto dma_block_late = [&](int rbx, int b) {
+        const uint32_t base = lds_addr(work + b * L::kBuf);
+        const int64_t blk = (int64_t)rbx * L::kBlk;
+#pragma unroll
+        for (int k = 0; k < 2 * NI / 4; ++k) {
+            const int ins = wl + 4 * k;     // uniform
+            const int ten = ins / NI, ii = ins - (ins / NI) * NI;
+            const char* sb = (ten ? dbase : qbase) + blk + (int64_t)(ii / IP) * (16 * D * 2);
+            dma16_hidden(sb, doff[IP > 4 ? (k & 1) : 0], base + ten * L::kBlk + ii * 1024);
+        }
+    };
     // the 8 records of a row of a finished block are merged in wave order; waves 0..3 (which
     // finish their products first) take 8 rows each, one per lane
     auto merge_block = [&](int rbx, const unsigned char* rec, int l32) {
@@ -949,7 +974,7 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
             }
             // the next block's DMA is queued by the late waves after their products (queued by
             // all waves at the barrier, the later ones stall behind the earlier ones' copies)
-            if (c1 >= 0 && !early) dma_block(c1, (i + 1) & 1, kW1Waves / 2, wave - kW1Waves / 2);
+            if (c1 >= 0 && !early) dma_block_late(c1, (i + 1) & 1);
             if (early) {
                 ha = sa;
                 hp = pa;
