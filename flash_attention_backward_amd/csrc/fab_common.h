@@ -112,6 +112,26 @@ FAB_DEV float load_scalar(const char* p, int type) {
     return bf16_to_f32(*(const unsigned short*)p);
 }
 
+// A value of lane l combined with that of lane l ^ 32 without going through LDS: two copies of x
+// with their halves swapped (v_permlane32_swap) hold, in every lane, the value of lane l & 31
+// and that of lane (l & 31) + 32. Both operations are commutative, so every lane gets exactly
+// op(x[l], x[l ^ 32]).
+FAB_DEV void wave_halves(float x, float& lo, float& hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+}
+FAB_DEV float max_halves(float x) {
+    float lo, hi;
+    wave_halves(x, lo, hi);
+    return fmaxf(lo, hi);
+}
+FAB_DEV float sum_halves(float x) {
+    float lo, hi;
+    wave_halves(x, lo, hi);
+    return lo + hi;
+}
+
 FAB_DEV float wave_max(float x) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));

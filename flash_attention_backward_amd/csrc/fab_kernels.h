@@ -485,7 +485,7 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
                     float tm = sa[0];
 #pragma unroll
                     for (int v = 1; v < 16; ++v) tm = fmaxf(tm, sa[v]);
-                    tm = fmaxf(tm, __shfl_xor(tm, 32));
+                    tm = max_halves(tm);
                     const float mnew = fmaxf(m_run, tm * sc2);
                     const float alpha = fast_exp2(m_run - mnew);
                     float ls = 0.0f, ds = 0.0f, bm = 0.0f;
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
                         if (madd[v] != neg_inf()) tmax = fmaxf(tmax, fmaf(sa[v], sc2, madd[v]));
-                    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                    tmax = max_halves(tmax);
                     const float mnew = fmaxf(m_run, tmax);
                     if (mnew != neg_inf()) {
                         const float alpha = fast_exp2(m_run - mnew);
@@ -883,7 +883,7 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
             madd[v] = mv;
             if (mv != neg_inf()) tm = fmaxf(tm, fmaf(sa[v], sc2, mv));
         }
-        m = fmaxf(tm, __shfl_xor(tm, 32));
+        m = max_halves(tm);
         if (m != neg_inf()) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -894,9 +894,9 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
                 b = fmaxf(b, fabsf(pa[v]));
             }
         }
-        l += __shfl_xor(l, 32);
-        d += __shfl_xor(d, 32);
-        b = fmaxf(b, __shfl_xor(b, 32));
+        l = sum_halves(l);
+        d = sum_halves(d);
+        b = max_halves(b);
         return f32x4{m, l, d, b};
     };
     auto fast_ok = [&](int rbx, int c) { return c == kMaskZero && wkey0 + 32 <= p.M && (rbx + 1) * 32 <= p.R; };
@@ -906,7 +906,7 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
         float tm = neg_inf(), l = 0.0f, d = 0.0f, b = 0.0f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) tm = fmaxf(tm, sa[v]);
-        const float m = fmaxf(tm, __shfl_xor(tm, 32)) * sc2;
+        const float m = max_halves(tm) * sc2;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const float e = fast_exp2(fmaf(sa[v], sc2, -m));
@@ -914,9 +914,9 @@ __global__ __launch_bounds__(kW1Threads, 1) void walk1_keys_kernel(Params p) {
             d = fmaf(e, pa[v], d);
             b = fmaxf(b, fabsf(pa[v]));
         }
-        l += __shfl_xor(l, 32);
-        d += __shfl_xor(d, 32);
-        b = fmaxf(b, __shfl_xor(b, 32));
+        l = sum_halves(l);
+        d = sum_halves(d);
+        b = max_halves(b);
         return f32x4{m, l, d, b};
     };
     auto put_rec = [&](int bufx, const f32x4& rec) {
