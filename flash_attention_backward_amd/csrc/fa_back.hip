@@ -336,8 +336,8 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
     pm.mark(4);
     if (g.splits > 1) {
         const int64_t n4 = (int64_t)g.Hkv * g.RB * 32 * (D / 4);
-        const int blocks = (int)std::min<int64_t>(4096, (n4 + kThreads - 1) / kThreads);
-        hipLaunchKernelGGL(dqreduce_kernel<D>, dim3(blocks), dim3(kThreads), 0, st, P);
+        const int blocks = (int)std::min<int64_t>(65536, (n4 + kDqThreads - 1) / kDqThreads);
+        hipLaunchKernelGGL(dqreduce_kernel<D>, dim3(blocks), dim3(kDqThreads), 0, st, P);
     }
     pm.mark(5);
     hipLaunchKernelGGL(kvpass_kernel<D>, dim3(g.kv_full + g.kv_tail * g.kv_split), dim3(kKVThreads), 0, st, P);

@@ -1247,21 +1247,32 @@ static __global__ __launch_bounds__(kThreads) void centre_out_kernel(Params p) {
     }
 }
 
+// One lane per 16 bytes of output; launched with kDqThreads per block. The split partials are
+// added in split order; their loads go out eight at a time.
+constexpr int kDqThreads = 64;
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void dqreduce_kernel(Params p) {
+__global__ __launch_bounds__(kDqThreads) void dqreduce_kernel(Params p) {
     const int rowsHK = p.RB * 32;
     const int64_t total = (int64_t)p.Hkv * rowsHK;
     const int64_t n4 = total * (D / 4);
-    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n4; e += (int64_t)gridDim.x * kThreads) {
+    for (int64_t e = (int64_t)blockIdx.x * kDqThreads + threadIdx.x; e < n4; e += (int64_t)gridDim.x * kDqThreads) {
         const int64_t ridx = e / (D / 4);
         const int c4 = (int)(e - ridx * (D / 4));
         const int hk = (int)(ridx / rowsHK), r = (int)(ridx - (ridx / rowsHK) * rowsHK);
         if (r >= p.R) continue;
-        f32x4 acc = *(const f32x4*)(p.dq_part + ridx * D + 4 * c4);
-        for (int s = 1; s < p.splits; ++s) {
-            const f32x4 x = *(const f32x4*)(p.dq_part + ((int64_t)s * total + ridx) * D + 4 * c4);
-            acc += x;
+        const float* src = p.dq_part + ridx * D + 4 * c4;
+        const int64_t step = total * D;
+        f32x4 acc = *(const f32x4*)src;
+        int s = 1;
+        for (; s + 8 <= p.splits; s += 8) {
+            f32x4 x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = *(const f32x4*)(src + (int64_t)(s + u) * step);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += x[u];
         }
+        for (; s < p.splits; ++s) acc += *(const f32x4*)(src + (int64_t)s * step);
         const int i = r / p.G, g = r - (r / p.G) * p.G;
         const int h = hk * p.G + g;
         const float fac = p.scale * ldexpf(1.0f, p.row_ks[ridx] - p.scal[1]);   // the row's dS exponent
