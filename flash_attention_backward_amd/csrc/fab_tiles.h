@@ -287,6 +287,10 @@ FAB_DEV f16x8 decode8(const char* rowp, int type, int grp, const float* cen) {
 // exponent pattern 0x64 reads as 1024 + u; subtracting 1152 gives q exactly, and one fp16
 // product with the scale rounds q * d once (nearest even), which is the fp16 an F32 cache
 // holding d * q gives. Both steps run on packed fp16 pairs.
+// The scale is read with the int8 as the word before them: it is the high half of that word
+// when the int8 start on a word boundary, else the low half of the first word. (The word before
+// a slot's first block lies inside the staging buffer or right before it in the same LDS
+// allocation; it is used only when it holds the scale.)
 FAB_DEV void decode_q8_block(const unsigned char* slot, int off, int blk, f16x8 out[4]) {
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     const int base = off + 34 * blk;                  // fp16 scale (even offset)
@@ -294,9 +298,10 @@ FAB_DEV void decode_q8_block(const unsigned char* slot, int off, int blk, f16x8 
     const int sh = qb & 3;
     const unsigned int* wp = (const unsigned int*)(slot + (qb & ~3));
     unsigned int w[9];
+    const unsigned int wm = wp[-1];
 #pragma unroll
     for (int k = 0; k < 9; ++k) w[k] = wp[k];
-    const unsigned short sb = *(const unsigned short*)(slot + base);
+    const unsigned short sb = (unsigned short)(sh ? (w[0] & 0xffffu) : (wm >> 16));
     const _Float16 dh = __builtin_bit_cast(_Float16, sb);
     const h2 d2 = {dh, dh};
     const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
@@ -426,7 +431,24 @@ FAB_DEV void decode_tile(const char* base, int type, int64_t nb1, int64_t nb2, i
 // 0,1,4,5,8,9,12,13,2,3,6,7,10,11,14,15 (plus 16 for the second half) times min(4, D/32)
 // blocks, so that the 16-byte stores of 16 lanes land on 16 distinct bank groups of the
 // swizzled tile and the dword reads of the staged bytes hit each bank at most twice.
+//
+// At D = 256 the lanes are arranged for the 32 four-byte banks instead (a dword read serves 32
+// lanes at a time, a 16-byte store 8 lanes). A staged row takes an odd number of 16-byte
+// chunks, so the same dword of keys k and k' falls in the same bank exactly when k = k' mod 8,
+// and the int8 of block b start at dword (34b + 2) / 4 of the row, with residues 0 1 1 2 2 3 3 0
+// mod 4 for b = 0 .. 7. Lanes 32h + 8j + t take block quad[j] of the blocks {0, 1, 3, 5} or
+// {2, 4, 6, 7} (one per residue) and key K(h, t), where the 8 keys of a half have bit 3 equal
+// to bit 1 (h = 0) or to its complement (h = 1): distinct in bits 0-2, so each half-wave's
+// reads meet 32 distinct banks, and distinct in bits 0, 2 and 3, so each 8-lane group's stores
+// meet 8 distinct 16-byte columns of the swizzled tile.
 FAB_DEV int perm16(int t) { return (t & 1) | ((t & 6) << 1) | ((t & 8) >> 2); }
+
+// (key within 16, block) of lane `lane` in block-quad bq (0: {0, 1, 3, 5}, 1: {2, 4, 6, 7})
+FAB_DEV void item256(int lane, int bq, int& key, int& blk) {
+    const int h = lane >> 5, j = (lane >> 3) & 3, t = lane & 7;
+    key = (t & 1) | ((t & 2) << 1) | ((t & 4) >> 1) | ((((t >> 2) & 1) ^ h) << 3);
+    blk = bq == 0 ? (j == 0 ? 0 : 2 * j - 1) : (j == 3 ? 7 : 2 * j + 2);
+}
 
 template <int D>
 struct Q8Pair {
@@ -448,8 +470,14 @@ FAB_DEV void decode_blk_item(const char* kh, int64_t knb1, int ktype, const char
     using Q = Q8Pair<D>;
     const bool isv = u >= Q::UPT;
     const int uu = isv ? u - Q::UPT : u;
-    const int key = perm16(lane & 15) + 16 * ((lane >> 4) % Q::KG) + Q::KL * (uu % (32 / Q::KL));
-    const int blk = (lane >> 4) / Q::KG + Q::BL * (uu / (32 / Q::KL));
+    int key, blk;
+    if constexpr (D == 256) {
+        item256(lane, uu / 2, key, blk);
+        key += 16 * (uu % 2);
+    } else {
+        key = perm16(lane & 15) + 16 * ((lane >> 4) % Q::KG) + Q::KL * (uu % (32 / Q::KL));
+        blk = (lane >> 4) / Q::KG + Q::BL * (uu / (32 / Q::KL));
+    }
     const int j = j0 + key;
     f16x8 o[4];
     if (j < M) {
