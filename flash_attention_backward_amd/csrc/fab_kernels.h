@@ -576,13 +576,22 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     const int ktid = kw * 64 + lane;
     const char* kh = p.k + (int64_t)hk * p.k_nb2;
     const char* vh = p.v + (int64_t)hk * p.v_nb2;
+    // q8_0 with row strides that are multiples of 16 bytes: offsets formed once
+    const bool fixed16 = DEC == kDecQ8 && ((p.k_nb1 | p.v_nb1) & 15) == 0;
+    Q8Fixed<D> qf;
+    if constexpr (DEC == kDecQ8) {
+        if (fixed16) qf.init(kw, (int)((uintptr_t)kh & 15), (int)((uintptr_t)vh & 15), lane);
+    }
     auto kdecode = [&](int s) {
         _Float16* tk = (_Float16*)slot(s);
         _Float16* tv = (_Float16*)(slot(s) + L::kTile);
         constexpr int last = kSplitDecode ? Q8Pair<D>::UPT : Q8Pair<D>::U;
         if constexpr (DEC == kDecQ8) {
-            decode_blk_pair32<D, true>(kh, p.k_nb1, p.k_type, vh, p.v_nb1, p.v_type, s * kSubKeys, p.M,
-                                       rawK(s), rawV(s), tk, tv, kw, last, lane);
+            if (fixed16)
+                qf.decode(s * kSubKeys, p.M, rawK(s), rawV(s), (unsigned char*)tk, (unsigned char*)tv, kw, last);
+            else
+                decode_blk_pair32<D, true>(kh, p.k_nb1, p.k_type, vh, p.v_nb1, p.v_type, s * kSubKeys, p.M,
+                                           rawK(s), rawV(s), tk, tv, kw, last, lane);
         } else if constexpr (DEC == kDecBlk) {
             decode_blk_pair32<D, false>(kh, p.k_nb1, p.k_type, vh, p.v_nb1, p.v_type, s * kSubKeys, p.M,
                                         rawK(s), rawV(s), tk, tv, kw, last, lane);

@@ -500,6 +500,98 @@ FAB_DEV void decode_blk_item(const char* kh, int64_t knb1, int ktype, const char
     for (int c = 0; c < 4; ++c) *(f16x8*)(dst + tile_off<D>(key, 4 * blk + c)) = o[c];
 }
 
+// The q8_0 pair decode with fixed row strides (both multiples of 16 bytes, so a row's
+// misalignment is that of the head's base): this lane's read and store offsets are the same
+// for every sub-tile, so they are formed once (Q8Fixed::init) and each sub-tile adds only its
+// buffers' addresses. A sub-tile wholly inside [0, M) takes no per-key test. The conversion is
+// decode_q8_block's, instruction for instruction.
+template <int D>
+struct Q8Fixed {
+    static constexpr int NIT = (Q8Pair<D>::U + 3) / 4;     // items of a wave (K first, then V)
+    uint32_t rd[NIT];       // byte offset in the staged tile of the word before the item's int8
+    uint32_t wr[NIT][4];    // byte offsets in the fp16 tile of its 4 sixteen-byte pieces
+    int sh[NIT];            // byte offset of the int8 in their first word (0 or 2)
+    int key[NIT];
+
+    // first = this wave's index among the 4; offk / offv: the K / V heads' bases mod 16
+    FAB_DEV void init(int first, int offk, int offv, int lane) {
+        using Q = Q8Pair<D>;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int u = first + 4 * it;
+            const bool isv = u >= Q::UPT;
+            const int uu = isv ? u - Q::UPT : u;
+            int k, blk;
+            if constexpr (D == 256) {
+                item256(lane, uu / 2, k, blk);
+                k += 16 * (uu % 2);
+            } else {
+                k = perm16(lane & 15) + 16 * ((lane >> 4) % Q::KG) + Q::KL * (uu % (32 / Q::KL));
+                blk = (lane >> 4) / Q::KG + Q::BL * (uu / (32 / Q::KL));
+            }
+            const int qb = (isv ? offv : offk) + 34 * blk + 2;
+            key[it] = k;
+            sh[it] = qb & 3;
+            rd[it] = (uint32_t)(k * Q8Row<D>::kSlot + (qb & ~3) - 4);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) wr[it][c] = (uint32_t)(2 * tile_off<D>(k, 4 * blk + c));
+        }
+    }
+
+    template <bool TAIL>
+    FAB_DEV void decode_items(int j0, int M, const unsigned char* rawk, const unsigned char* rawv,
+                              unsigned char* dstk, unsigned char* dstv, int first, int last) const {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int u = first + 4 * it;
+            if (u >= Q8Pair<D>::U || u >= last) break;     // wave-uniform
+            const bool isv = u >= Q8Pair<D>::UPT;          // wave-uniform
+            const unsigned int* wp = (const unsigned int*)((isv ? rawv : rawk) + rd[it]);
+            unsigned int w[10];
+#pragma unroll
+            for (int k = 0; k < 10; ++k) w[k] = wp[k];
+            const unsigned short sb = (unsigned short)(sh[it] ? (w[1] & 0xffffu) : (w[0] >> 16));
+            const _Float16 dh = __builtin_bit_cast(_Float16, sb);
+            const h2 d2 = {dh, dh};
+            f16x8 o[4];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const unsigned int x = __builtin_amdgcn_alignbyte(w[k + 2], w[k + 1], sh[it]) ^ 0x80808080u;
+                const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u));
+                const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u));
+                const h2 a = (lo + bias) * d2;
+                const h2 c = (hi + bias) * d2;
+                const int b = 4 * (k & 1);
+                o[k >> 1][b + 0] = a.x;
+                o[k >> 1][b + 1] = a.y;
+                o[k >> 1][b + 2] = c.x;
+                o[k >> 1][b + 3] = c.y;
+            }
+            if constexpr (TAIL) {
+                if (j0 + key[it] >= M) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) o[c][e] = (_Float16)0.0f;
+                }
+            }
+            unsigned char* dst = isv ? dstv : dstk;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) *(f16x8*)(dst + wr[it][c]) = o[c];
+        }
+    }
+
+    FAB_DEV void decode(int j0, int M, const unsigned char* rawk, const unsigned char* rawv,
+                        unsigned char* dstk, unsigned char* dstv, int first, int last) const {
+        if (j0 + 32 <= M)                                   // uniform: no key past M
+            decode_items<false>(j0, M, rawk, rawv, dstk, dstv, first, last);
+        else
+            decode_items<true>(j0, M, rawk, rawv, dstk, dstv, first, last);
+    }
+};
+
 // The wave-instructions u = first, first + 4, ... below `last` for one of 4 waves.
 template <int D, bool Q8>
 FAB_DEV void decode_blk_pair32(const char* kh, int64_t knb1, int ktype, const char* vh, int64_t vnb1,
