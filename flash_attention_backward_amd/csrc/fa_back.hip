@@ -305,10 +305,17 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
     hipLaunchKernelGGL(prep_kernel<D>, dim3(g.Hkv * g.RB), dim3(kThreads), 0, st, P);
     if (g.Hm > 0 && P.m_type != FA_BACK_CAUSAL_TAIL) {
         const dim3 grid((g.Hm == 1 ? 1 : g.Hkv) * g.RB, (g.KT + kClassTilesPerBlock - 1) / kClassTilesPerBlock);
-        if (P.m_type == FA_BACK_F16)
+        if (g.Hm == 1) {
+            // one mask head: each distinct query row of a row block is read once
+            if (P.m_type == FA_BACK_F16)
+                hipLaunchKernelGGL(maskclass_rows_kernel<2>, grid, dim3(kThreads), 0, st, P);
+            else
+                hipLaunchKernelGGL(maskclass_rows_kernel<4>, grid, dim3(kThreads), 0, st, P);
+        } else if (P.m_type == FA_BACK_F16) {
             hipLaunchKernelGGL(maskclass_kernel<2>, grid, dim3(kThreads), 0, st, P);
-        else
+        } else {
             hipLaunchKernelGGL(maskclass_kernel<4>, grid, dim3(kThreads), 0, st, P);
+        }
     }
     pm.mark(1);
     if (P.lse_in) {

@@ -241,6 +241,75 @@ __global__ __launch_bounds__(kThreads) void maskclass_kernel(Params p) {
     }
 }
 
+// The same classes with one mask head, reading each distinct query row of a block once: the
+// rows r = i*G + g of a 32-row block share the mask row of query i. Wave w, lane l: key chunk
+// kc = l & 7 (8 keys), tile ts = (l >> 3) + 8 (w & 1) of the block's 16, row group w >> 1 (the
+// block's query rows i_lo, i_lo + 2, ... or i_lo + 1, i_lo + 3, ...). A tile's 8 chunk lanes
+// meet in a ballot, its two row groups in LDS. Rows past R and keys past M are ignored; a tile
+// with no row left is dead, as in maskclass_kernel.
+template <int ESZ>
+__global__ __launch_bounds__(kThreads) void maskclass_rows_kernel(Params p) {
+    __shared__ unsigned int red[kClassTilesPerBlock][2];
+    const int rb = blockIdx.x;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int kc = lane & 7, ts = (lane >> 3) + 8 * (wave & 1), rg = wave >> 1;
+    const int r0 = rb * 32, r1 = min(p.R, r0 + 32);
+    const int i_lo = r0 / p.G, i_hi = r1 > r0 ? (r1 - 1) / p.G : i_lo - 1;
+    const int t = blockIdx.y * kClassTilesPerBlock + ts;
+    const int j = t * kQTileKeys + 8 * kc;
+    const bool vec = (((uintptr_t)p.mask | (uintptr_t)p.m_nb1) & 15) == 0;
+    bool all0 = true, allinf = true;
+    if (t < p.KT) {
+#pragma unroll 4
+        for (int i = i_lo + rg; i <= i_hi; i += 2) {
+            const char* mrow = p.mask + (int64_t)i * p.m_nb1;
+            if (vec && j + 8 <= p.M) {
+                u32x4 raw[ESZ / 2];
+#pragma unroll
+                for (int h = 0; h < ESZ / 2; ++h) raw[h] = *(const u32x4*)(mrow + (int64_t)j * ESZ + 16 * h);
+                if constexpr (ESZ == 2) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const unsigned int x = raw[0][w];
+                        all0 = all0 && ((x & 0x7fff7fffu) == 0u);
+                        allinf = allinf && (x == 0xfc00fc00u);
+                    }
+                } else {
+#pragma unroll
+                    for (int w = 0; w < 8; ++w) {
+                        const unsigned int x = raw[w >> 2][w & 3];
+                        all0 = all0 && ((x & 0x7fffffffu) == 0u);
+                        allinf = allinf && (x == (unsigned int)kNegInfBits);
+                    }
+                }
+            } else {
+                for (int e = 0; e < 8; ++e) {
+                    if (j + e >= p.M) break;
+                    const float x = p.m_type == FA_BACK_F16 ? (float)*(const _Float16*)(mrow + 2 * (int64_t)(j + e))
+                                                             : *(const float*)(mrow + 4 * (int64_t)(j + e));
+                    all0 = all0 && (x == 0.0f);
+                    allinf = allinf && (x == neg_inf());
+                }
+            }
+        }
+    }
+    const unsigned long long m0 = __ballot(all0), mi = __ballot(allinf);
+    if (kc == 0) {
+        const int sh = lane & ~7;
+        const unsigned int g0 = ((m0 >> sh) & 0xffull) == 0xffull ? 1u : 0u;
+        const unsigned int gi = ((mi >> sh) & 0xffull) == 0xffull ? 2u : 0u;
+        red[ts][rg] = g0 | gi;
+    }
+    __syncthreads();
+    if (threadIdx.x < kClassTilesPerBlock) {
+        const int tt = blockIdx.y * kClassTilesPerBlock + (int)threadIdx.x;
+        if (tt < p.KT) {
+            const unsigned int f = red[threadIdx.x][0] & red[threadIdx.x][1];
+            p.mcls[(int64_t)rb * p.KT + tt] = (unsigned char)((f & 2u) ? kMaskDead : ((f & 1u) ? kMaskZero : kMaskMixed));
+        }
+    }
+}
+
 FAB_DEV int mask_class(const Params& p, int hk, int rb, int t) {
     if (p.m_type == FA_BACK_NONE) return kMaskZero;
     if (p.m_type == FA_BACK_CAUSAL_TAIL) {
