@@ -701,7 +701,10 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         if (GRAD && s > s_begin && cls_prev != kMaskDead) {
             const unsigned char* ex = exch(s - 1);
             const f16x8 bb[2] = {*(const f16x8*)(ex + lane * 16), *(const f16x8*)(ex + 1024 + lane * 16)};
+            // the K waves' products (the longer role of the pair) issue ahead of the S wave's work
+            mfma_prio_hi();
             cols_acc<D>(slot(s - 1), bb, dqacc, cw);
+            mfma_prio_lo();
         }
         if (s == s_end) break;
     }
