@@ -1574,9 +1574,9 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
                 f32x16 sa;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) sa[v] = 0.0f;
-                mfma_prio_hi();
+                // the X waves' products keep the default priority, so the Y wave of the pair
+                // (dK, dP and the dS arithmetic: the longer role) issues ahead of them
                 rows_chain_x<D, 1>(tq, bkv, sa, rw);
-                mfma_prio_lo();
                 if (cls == kMaskMixed) {
                     // mask terms staged through the wave's fp32 P slot by a rolled loop, so the
                     // masked case costs the loop below no registers; a fully masked row (and every
@@ -1620,9 +1620,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
             }
             lds_barrier();     // Y: P published for the Y wave (the copies in flight stay so)
             if (cls != kMaskDead) {
-                mfma_prio_hi();
                 cols_acc_pf<D>(tq + L::kBlk, bp, acc, cw);
-                mfma_prio_lo();
             }
             ent = __builtin_amdgcn_readfirstlane(nxt);
             bi = bi == 2 ? 0 : bi + 1;
