@@ -41,8 +41,8 @@ int tail_split(int T, int cus, int* split) {
     return 0;
 }
 
-constexpr uint32_t kKnownFlags =
-    FA_BACK_FLAG_CENTER_V | FA_BACK_FLAG_WALK1_KEYS | FA_BACK_FLAG_WALK1_ROWS | FA_BACK_FLAG_CENTER_K;
+constexpr uint32_t kKnownFlags = FA_BACK_FLAG_CENTER_V | FA_BACK_FLAG_WALK1_KEYS | FA_BACK_FLAG_WALK1_ROWS |
+                                  FA_BACK_FLAG_CENTER_K | FA_BACK_FLAG_KV_IMAGE | FA_BACK_FLAG_KV_INLINE;
 
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
@@ -67,6 +67,8 @@ struct Geometry {
     bool w1keys;           // walk 1 by key tiles (else by row tiles)
     int KT1, RS1, w1_rbs;  // its 256-key tiles, row splits and row blocks per workgroup
     int nparts;            // walk-1 records per row
+    bool img;              // the query-side walks copy K/V tiles from the decoded image
+    int img_ns;            // its 32-key sub-tiles per KV head
     int npart, nbound;
     fa_back_layout layout;
     // workspace offsets (bytes)
@@ -74,6 +76,7 @@ struct Geometry {
     uint64_t ws_rec, ws_lse2, ws_dlt, ws_rks, ws_bound, ws_dqp, ws_mcls, ws_kvp, ws_vmax;
     uint64_t ws_vcen;      // [Hkv][D] V centre (FA_BACK_FLAG_CENTER_V only)
     uint64_t ws_kcen;      // [Hkv][D] K centre (FA_BACK_FLAG_CENTER_K only)
+    uint64_t ws_img;       // [Hkv][img_ns][32-key slot] decoded K/V tiles (img only)
 };
 
 bool tensor_nonneg(const fa_back_tensor& t) {
@@ -104,6 +107,7 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
     if (!std::isfinite(d->scale)) return FA_BACK_EINVAL;
     if (d->flags & ~kKnownFlags) return FA_BACK_EINVAL;
     if ((d->flags & FA_BACK_FLAG_WALK1_KEYS) && (d->flags & FA_BACK_FLAG_WALK1_ROWS)) return FA_BACK_EINVAL;
+    if ((d->flags & FA_BACK_FLAG_KV_IMAGE) && (d->flags & FA_BACK_FLAG_KV_INLINE)) return FA_BACK_EINVAL;
     if ((d->flags & FA_BACK_FLAG_CENTER_V) && is_blk(v.type)) return FA_BACK_EUNSUPPORTED;
     if ((d->flags & FA_BACK_FLAG_CENTER_K) && is_blk(k.type)) return FA_BACK_EUNSUPPORTED;
     if (!tensor_nonneg(q) || !tensor_nonneg(k) || !tensor_nonneg(v) || !tensor_nonneg(dd) ||
@@ -211,6 +215,15 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
         }
         g->nparts = g->w1keys ? g->KT1 : g->splits;
     }
+    // the decoded image of the cache: when each sub-tile would be decoded by at least 4 row
+    // tiles of the query-side walks (a flag forces either way)
+    {
+        bool img = g->RT >= 4;
+        if (d->flags & FA_BACK_FLAG_KV_IMAGE) img = true;
+        if (d->flags & FA_BACK_FLAG_KV_INLINE) img = false;
+        g->img = img && g->M > 0 && g->R > 0;
+        g->img_ns = (g->M + kSubKeys - 1) / kSubKeys;
+    }
     g->npart = (int)std::min<int64_t>(512, std::max<int64_t>(1, N * H / 8));
     const int64_t total_rows = (int64_t)g->Hkv * g->RB * 32;
     g->nbound = (int)std::min<int64_t>(kMergeMaxBlocks, std::max<int64_t>(1, (g->RB * 32 + kMergeRows - 1) / kMergeRows));
@@ -245,6 +258,7 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
     g->ws_vmax = take(4ull * kVmaxBlocks);   // fa_back_run_saved only
     g->ws_vcen = take((d->flags & FA_BACK_FLAG_CENTER_V) ? 4ull * g->Hkv * D : 0);
     g->ws_kcen = take((d->flags & FA_BACK_FLAG_CENTER_K) ? 4ull * g->Hkv * D : 0);
+    g->ws_img = take(g->img ? (uint64_t)g->Hkv * g->img_ns * (uint64_t)(4 * kSubKeys * D) : 0);
     L.workspace_bytes = std::max<uint64_t>(o, kAlign);
     return FA_BACK_OK;
 }
@@ -253,7 +267,7 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
 // per CU; the small kernels use a few KB).
 template <int D>
 int max_lds_bytes_d() {
-    return std::max(std::max(QLds<D>::kBytes, W1Lds<D>::kBytes), KVLds<D>::kBytes);
+    return std::max(std::max(std::max(QLds<D>::kBytes, QLds<D, true>::kBytes), W1Lds<D>::kBytes), KVLds<D>::kBytes);
 }
 int max_lds_bytes(int D) {
     return D == 64 ? max_lds_bytes_d<64>() : D == 128 ? max_lds_bytes_d<128>() : max_lds_bytes_d<256>();
@@ -275,12 +289,28 @@ void launch_qpass(const Geometry& g, const Params& P, hipStream_t st) {
     const dim3 grid(g.RT * g.Hkv, g.splits), block(kQThreads);
     const bool blk_k = P.k_type == FA_BACK_Q8_0 || P.k_type == FA_BACK_Q4_0;
     const bool blk_v = P.v_type == FA_BACK_Q8_0 || P.v_type == FA_BACK_Q4_0;
-    if (P.k_type == FA_BACK_Q8_0 && P.v_type == FA_BACK_Q8_0)
+    if (P.kvimg)
+        hipLaunchKernelGGL((qpass_kernel<D, GRAD, kDecImg>), grid, block, 0, st, P);
+    else if (P.k_type == FA_BACK_Q8_0 && P.v_type == FA_BACK_Q8_0)
         hipLaunchKernelGGL((qpass_kernel<D, GRAD, kDecQ8>), grid, block, 0, st, P);
     else if (blk_k && blk_v)
         hipLaunchKernelGGL((qpass_kernel<D, GRAD, kDecBlk>), grid, block, 0, st, P);
     else
         hipLaunchKernelGGL((qpass_kernel<D, GRAD, kDecGen>), grid, block, 0, st, P);
+}
+
+// The decoded image of the cache, in the decode the types need.
+template <int D>
+void launch_kvimage(const Geometry& g, const Params& P, hipStream_t st) {
+    const dim3 grid(g.img_ns, g.Hkv), block(kImgThreads);
+    const bool blk_k = P.k_type == FA_BACK_Q8_0 || P.k_type == FA_BACK_Q4_0;
+    const bool blk_v = P.v_type == FA_BACK_Q8_0 || P.v_type == FA_BACK_Q4_0;
+    if (P.k_type == FA_BACK_Q8_0 && P.v_type == FA_BACK_Q8_0)
+        hipLaunchKernelGGL((kvimage_kernel<D, kDecQ8>), grid, block, 0, st, P);
+    else if (blk_k && blk_v)
+        hipLaunchKernelGGL((kvimage_kernel<D, kDecBlk>), grid, block, 0, st, P);
+    else
+        hipLaunchKernelGGL((kvimage_kernel<D, kDecGen>), grid, block, 0, st, P);
 }
 
 template <int D>
@@ -317,6 +347,7 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
             hipLaunchKernelGGL(maskclass_kernel<4>, grid, dim3(kThreads), 0, st, P);
         }
     }
+    if (P.kvimg) launch_kvimage<D>(g, P, st);
     pm.mark(1);
     if (P.lse_in) {
         // forward-saved LSE and O: the row statistics without walk 1 and the merge
@@ -524,6 +555,10 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     P.kv_part = (float*)(w + g.ws_kvp);
     if (ds.flags & FA_BACK_FLAG_CENTER_V) P.vcen = (float*)(w + g.ws_vcen);
     if (ds.flags & FA_BACK_FLAG_CENTER_K) P.kcen = (float*)(w + g.ws_kcen);
+    if (g.img) {
+        P.kvimg = (unsigned char*)(w + g.ws_img);
+        P.img_ns = g.img_ns;
+    }
     if (saved && !q_empty) {
         P.lse_in = lse_in;
         P.o_in = o_in;

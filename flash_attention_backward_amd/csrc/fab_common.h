@@ -84,6 +84,9 @@ struct Params {
     int nvpart;
     float* vcen;          // [Hkv][D] constant taken from V before its fp16 rounding; NULL: none
     float* kcen;          // [Hkv][D] constant taken from K before its fp16 rounding; NULL: none
+    unsigned char* kvimg; // [Hkv][img_ns][32-key slot] decoded K and V tiles of the query-side
+                          //   walks (kvimage_kernel); NULL: the walks decode for themselves
+    int img_ns;           // 32-key sub-tiles per head in kvimg
 };
 
 // Mask classes of a (32-row block, 64-key tile): no masking needed, every entry -inf, other.

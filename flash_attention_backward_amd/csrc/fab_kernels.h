@@ -410,28 +410,70 @@ constexpr int kQWaves = 8;
 constexpr int kQThreads = kQWaves * kWave;
 constexpr int kSubKeys = 32;
 
-template <int D>
+// With the decoded image of the cache (IMG), the S waves copy whole slots from it two sub-tiles
+// ahead: four slots rotate and nothing is staged.
+template <int D, bool IMG = false>
 struct QLds {
     static constexpr int kTile = kSubKeys * D * 2;                 // bytes of a K or V sub-tile
     static constexpr int kSlot = 2 * kTile;                        // K tile then V tile
     static constexpr int kRaw = RawTile<D, kSubKeys>::kBytes;      // block bytes of one sub-tile
-    static constexpr int kOffSlot = 0;                             // 3 slots
-    static constexpr int kOffRaw = kOffSlot + 3 * kSlot;           // [2][K, V] staged bytes
-    static constexpr int kOffEx = kOffRaw + 4 * kRaw;              // [2][4 row blocks] dS, 2 KB
+    static constexpr int kSlots = IMG ? 4 : 3;
+    static constexpr int kOffSlot = 0;
+    static constexpr int kOffRaw = kOffSlot + kSlots * kSlot;      // [2][K, V] staged bytes
+    static constexpr int kOffEx = kOffRaw + (IMG ? 0 : 4 * kRaw);  // [2][4 row blocks] dS, 2 KB
     static constexpr int kOffCls = kOffEx + 2 * 4 * 2048;          // [2][4 row blocks] mask class
     static constexpr int kBytes = kOffCls + 16;
 };
 
 // How the K waves decode a sub-tile: both K and V q8_0, both block types (q8_0 / q4_0), or
 // anything else (F32/F16/BF16 rows read from global memory, possibly centred). Each is a
-// kernel of its own, so that no decode holds registers in another's loop.
+// kernel of its own, so that no decode holds registers in another's loop. kDecImg decodes
+// nothing: the slots are copied from the image kvimage_kernel wrote (the same decode, done
+// once per sub-tile instead of once per workgroup).
 constexpr int kDecQ8 = 0;
 constexpr int kDecBlk = 1;
 constexpr int kDecGen = 2;
+constexpr int kDecImg = 3;
+
+// Byte offset of head hk's first row from a 16-byte boundary (q8_0 rows with fixed strides).
+FAB_DEV int q8_misalign(const char* base, int64_t nb2, int hk) {
+    return (int)((uintptr_t)(base + (int64_t)hk * nb2) & 15);
+}
+
+// Decode K and V of sub-tile s (keys 32s ..) of head hk into the swizzled fp16 tiles tk, tv:
+// from the bytes staged in rk, rv for the block types, from global memory for the others
+// (centred where a centre is given); keys >= M become 0. kw is this wave among the 4 decoding
+// waves and `last` the bound of its q8_0 items. The query-side walks and kvimage_kernel both
+// decode through here, so the image holds exactly the walks' own tiles.
+template <int D, int DEC>
+FAB_DEV void decode_sub(const Params& p, int hk, bool fixed16, const Q8Fixed<D>& qf, int s,
+                        const unsigned char* rk, const unsigned char* rv, _Float16* tk, _Float16* tv,
+                        int kw, int lane, int last) {
+    const char* kh = p.k + (int64_t)hk * p.k_nb2;
+    const char* vh = p.v + (int64_t)hk * p.v_nb2;
+    const int j0 = s * kSubKeys;
+    if constexpr (DEC == kDecQ8) {
+        if (fixed16)
+            qf.decode(j0, p.M, rk, rv, (unsigned char*)tk, (unsigned char*)tv, kw, last);
+        else
+            decode_blk_pair32<D, true>(kh, p.k_nb1, p.k_type, vh, p.v_nb1, p.v_type, j0, p.M,
+                                       rk, rv, tk, tv, kw, last, lane);
+    } else if constexpr (DEC == kDecBlk) {
+        decode_blk_pair32<D, false>(kh, p.k_nb1, p.k_type, vh, p.v_nb1, p.v_type, j0, p.M,
+                                    rk, rv, tk, tv, kw, last, lane);
+    } else {
+        const int ktid = kw * 64 + lane;
+        decode_tile<D, kSubKeys, 256>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, j0, p.M, rk, tk, ktid,
+                                      p.kcen ? p.kcen + (int64_t)hk * D : nullptr);
+        decode_tile<D, kSubKeys, 256>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, j0, p.M, rv, tv, ktid,
+                                      p.vcen ? p.vcen + (int64_t)hk * D : nullptr);
+    }
+}
 
 template <int D, bool GRAD, int DEC>
 __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
-    using L = QLds<D>;
+    constexpr bool IMG = DEC == kDecImg;
+    using L = QLds<D, IMG>;
     // The K waves decode whole sub-tiles. (Handing the V half to the S waves was measured: with
     // the DMA queued from the S waves, they are the busier role.)
     constexpr bool kSplitDecode = false;
@@ -458,7 +500,7 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     const int s_end = min(NS, 2 * min(p.KT, (split + 1) * p.tiles_per_split));
     const int eq = p.scal[0], edo = p.scal[1];
 
-    auto slot = [&](int s) { return lds + L::kOffSlot + (s % 3) * L::kSlot; };
+    auto slot = [&](int s) { return lds + L::kOffSlot + (s % L::kSlots) * L::kSlot; };
     auto rawK = [&](int s) { return lds + L::kOffRaw + ((s & 1) * 2 + 0) * L::kRaw; };
     auto rawV = [&](int s) { return lds + L::kOffRaw + ((s & 1) * 2 + 1) * L::kRaw; };
     auto exch = [&](int s) { return lds + L::kOffEx + ((s & 1) * 4 + w4) * 2048; };
@@ -519,22 +561,45 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         // plain loads, which the compiler does not hold back for the DMA in flight (it makes
         // transpose reads wait for it)
         RawDma<D, kSubKeys, 256> dk, dv;
-        dk.init(kh, p.k_nb1, block_row_bytes(p.k_type, D), s_begin * kSubKeys, w4 * 64 + lane);
-        dv.init(vh, p.v_nb1, block_row_bytes(p.v_type, D), s_begin * kSubKeys, w4 * 64 + lane);
+        if constexpr (!IMG) {
+            dk.init(kh, p.k_nb1, block_row_bytes(p.k_type, D), s_begin * kSubKeys, w4 * 64 + lane);
+            dv.init(vh, p.v_nb1, block_row_bytes(p.v_type, D), s_begin * kSubKeys, w4 * 64 + lane);
+        }
+        // image: the slot of sub-tile t is one contiguous run of kSlot bytes; each S wave copies
+        // a quarter of it in 1 KB pieces (hidden from the compiler: the copies stay in flight
+        // across the products, and the block barrier below waits for them by count)
+        constexpr int NI = L::kSlot / (4 * 1024);
+        const unsigned char* img = IMG ? p.kvimg + (int64_t)hk * p.img_ns * L::kSlot : nullptr;
         auto sdma = [&](int t) {
-            if (is_block_type(p.k_type)) dk.issue(rawK(t), p.M, w4);
-            if (is_block_type(p.v_type)) dv.issue(rawV(t), p.M, w4);
+            if constexpr (IMG) {
+                const unsigned char* src = img + (int64_t)t * L::kSlot + w4 * (NI * 1024);
+                const uint32_t dst = lds_addr(slot(t)) + (uint32_t)(w4 * (NI * 1024));
+#pragma unroll
+                for (int it = 0; it < NI; ++it) dma16_hidden(src + it * 1024, 16u * lane, dst + it * 1024);
+            } else {
+                if (is_block_type(p.k_type)) dk.issue(rawK(t), p.M, w4);
+                if (is_block_type(p.v_type)) dv.issue(rawV(t), p.M, w4);
+            }
         };
         // prologue: sub-tile s_begin staged and decoded (V half here, K half by the K waves),
-        // the bytes of s_begin+1 on their way
+        // the bytes of s_begin+1 on their way; from the image, the first two slots on their way
         if (s_begin < s_end) sdma(s_begin);
-        wait_all_mem();
-        __syncthreads();
-        if (s_begin + 1 < s_end) sdma(s_begin + 1);
+        if constexpr (IMG) {
+            if (s_begin + 1 < s_end) sdma(s_begin + 1);
+            lds_barrier();
+        } else {
+            wait_all_mem();
+            __syncthreads();
+            if (s_begin + 1 < s_end) sdma(s_begin + 1);
+        }
         if (sdec && s_begin < s_end) sdecode(s_begin);
         for (int s = s_begin; s <= s_end; ++s) {
-            wait_all_mem();
-            __syncthreads();   // sub-tile s decoded and its class posted; exchange slot s free
+            if (IMG && s + 1 < s_end) {
+                dma_barrier<NI>();   // slot s landed; the NI copies of slot s+1 stay in flight
+            } else {
+                wait_all_mem();
+                __syncthreads();   // sub-tile s decoded and its class posted; exchange slot s free
+            }
             if (s == s_end) break;
             if (s + 2 < s_end) sdma(s + 2);
             const int cls = __builtin_amdgcn_readfirstlane(clsx[(s & 1) * 4 + w4]);
@@ -642,34 +707,17 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
 
     // ================= K waves
     const int kw = wave - 4;                          // 0..3, uniform
-    const int ktid = kw * 64 + lane;
-    const char* kh = p.k + (int64_t)hk * p.k_nb2;
-    const char* vh = p.v + (int64_t)hk * p.v_nb2;
     // q8_0 with row strides that are multiples of 16 bytes: offsets formed once
     const bool fixed16 = DEC == kDecQ8 && ((p.k_nb1 | p.v_nb1) & 15) == 0;
     Q8Fixed<D> qf;
     if constexpr (DEC == kDecQ8) {
-        if (fixed16) qf.init(kw, (int)((uintptr_t)kh & 15), (int)((uintptr_t)vh & 15), lane);
+        if (fixed16) qf.init(kw, q8_misalign(p.k, p.k_nb2, hk), q8_misalign(p.v, p.v_nb2, hk), lane);
     }
     auto kdecode = [&](int s) {
-        _Float16* tk = (_Float16*)slot(s);
-        _Float16* tv = (_Float16*)(slot(s) + L::kTile);
         constexpr int last = kSplitDecode ? Q8Pair<D>::UPT : Q8Pair<D>::U;
-        if constexpr (DEC == kDecQ8) {
-            if (fixed16)
-                qf.decode(s * kSubKeys, p.M, rawK(s), rawV(s), (unsigned char*)tk, (unsigned char*)tv, kw, last);
-            else
-                decode_blk_pair32<D, true>(kh, p.k_nb1, p.k_type, vh, p.v_nb1, p.v_type, s * kSubKeys, p.M,
-                                           rawK(s), rawV(s), tk, tv, kw, last, lane);
-        } else if constexpr (DEC == kDecBlk) {
-            decode_blk_pair32<D, false>(kh, p.k_nb1, p.k_type, vh, p.v_nb1, p.v_type, s * kSubKeys, p.M,
-                                        rawK(s), rawV(s), tk, tv, kw, last, lane);
-        } else {
-            decode_tile<D, kSubKeys, 256>(p.k, p.k_type, p.k_nb1, p.k_nb2, hk, s * kSubKeys, p.M, rawK(s), tk, ktid,
-                                          p.kcen ? p.kcen + (int64_t)hk * D : nullptr);
-            decode_tile<D, kSubKeys, 256>(p.v, p.v_type, p.v_nb1, p.v_nb2, hk, s * kSubKeys, p.M, rawV(s), tv, ktid,
-                                          p.vcen ? p.vcen + (int64_t)hk * D : nullptr);
-        }
+        if constexpr (!IMG)
+            decode_sub<D, DEC>(p, hk, fixed16, qf, s, rawK(s), rawV(s), (_Float16*)slot(s),
+                               (_Float16*)(slot(s) + L::kTile), kw, lane, last);
     };
     // prologue: the S waves stage sub-tile s_begin; its class is posted
     int cls_cur = s_begin < s_end ? wclass(s_begin) : kMaskDead;    // class of sub-tile s
@@ -723,6 +771,46 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
                 *(f32x4*)(dst + 32 * md + 8 * b + 4 * g) = o;
             }
     }
+}
+
+// ----------------------------------------------------------------------------- cache image
+
+// The decoded cache for the query-side walks when several of their workgroups would decode each
+// sub-tile: for every KV head and 32-key sub-tile, the LDS slot a walk decodes (swizzled fp16 K
+// tile, then V tile, keys >= M zero), written out once to img [Hkv][img_ns][slot bytes]. A
+// workgroup of 4 waves stages one sub-tile, decodes it with the walks' own decode and copies
+// the slot out; the walks then copy slots instead of decoding (qpass_kernel<.., kDecImg>).
+constexpr int kImgThreads = 256;
+
+template <int D, int DEC>
+__global__ __launch_bounds__(kImgThreads) void kvimage_kernel(Params p) {
+    using L = QLds<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[L::kSlot + 2 * L::kRaw];
+    unsigned char* rk = lds + L::kSlot;
+    unsigned char* rv = rk + L::kRaw;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int s = blockIdx.x, hk = blockIdx.y;
+    const char* kh = p.k + (int64_t)hk * p.k_nb2;
+    const char* vh = p.v + (int64_t)hk * p.v_nb2;
+    RawDma<D, kSubKeys, kImgThreads> dk, dv;
+    dk.init(kh, p.k_nb1, block_row_bytes(p.k_type, D), s * kSubKeys, threadIdx.x);
+    dv.init(vh, p.v_nb1, block_row_bytes(p.v_type, D), s * kSubKeys, threadIdx.x);
+    if (is_block_type(p.k_type)) dk.issue(rk, p.M, wave);
+    if (is_block_type(p.v_type)) dv.issue(rv, p.M, wave);
+    const bool fixed16 = DEC == kDecQ8 && ((p.k_nb1 | p.v_nb1) & 15) == 0;
+    Q8Fixed<D> qf;
+    if constexpr (DEC == kDecQ8) {
+        if (fixed16) qf.init(wave, q8_misalign(p.k, p.k_nb2, hk), q8_misalign(p.v, p.v_nb2, hk), lane);
+    }
+    wait_all_mem();
+    __syncthreads();
+    decode_sub<D, DEC>(p, hk, fixed16, qf, s, rk, rv, (_Float16*)lds, (_Float16*)(lds + L::kTile),
+                       wave, lane, Q8Pair<D>::U);
+    __syncthreads();
+    unsigned char* dst = p.kvimg + ((int64_t)hk * p.img_ns + s) * L::kSlot;
+#pragma unroll
+    for (int o = 16 * (int)threadIdx.x; o < L::kSlot; o += 16 * kImgThreads)
+        *(uint4*)(dst + o) = *(const uint4*)(lds + o);
 }
 
 // ----------------------------------------------------------------------------- walk 1 by keys

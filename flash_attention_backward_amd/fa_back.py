@@ -21,6 +21,8 @@ FLAG_CENTER_V = 1    # centre V before its fp16 rounding
 FLAG_WALK1_KEYS = 2  # LSE/delta walk owned by key tiles
 FLAG_WALK1_ROWS = 4  # LSE/delta walk owned by row tiles
 FLAG_CENTER_K = 8    # centre K before its fp16 rounding
+FLAG_KV_IMAGE = 16   # decode the cache once into the workspace for the query-side walks
+FLAG_KV_INLINE = 32  # every query-side workgroup decodes the cache tiles it reads
 TYPE_IDS = {"none": NONE, "f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0,
             "causal_tail": CAUSAL_TAIL}
 ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, Q8_0: 34, Q4_0: 18}

@@ -116,6 +116,19 @@ extern "C" {
  * The fa_back_run_saved entry takes the uncentred LSE and removes the shift itself. */
 #define FA_BACK_FLAG_CENTER_K 8u
 
+/* FA_BACK_FLAG_KV_IMAGE, FA_BACK_FLAG_KV_INLINE: where the query-side walks get the fp16 K and
+ * V tiles their products read. With KV_IMAGE a first kernel decodes every 32-key sub-tile of
+ * the cache once into the workspace (128 * D bytes per sub-tile and KV head: the K and V tiles
+ * as the walks lay them out in LDS), and the walks copy those tiles instead of decoding them;
+ * with KV_INLINE every workgroup of the walks decodes the sub-tiles it reads. The results are
+ * bitwise the same. With neither bit the plan takes the image when at least 4 row tiles (of
+ * 128 query rows of one KV head) read each sub-tile. Setting both is FA_BACK_EINVAL. The choice
+ * changes the workspace size: pass the same flags to fa_back_layout_query and fa_back_create;
+ * KV_INLINE keeps the image out of a workspace that must stay within
+ * FA_BACK_NOALLOC_MAX_WORKSPACE. */
+#define FA_BACK_FLAG_KV_IMAGE 16u
+#define FA_BACK_FLAG_KV_INLINE 32u
+
 /* status codes (no entry point aborts or exits) */
 #define FA_BACK_OK 0
 #define FA_BACK_EINVAL (-1)       /* null pointer, negative extent, non-finite scale, unknown flag bit */

@@ -188,7 +188,7 @@ def test_centre_v_flag_validation():
     _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_CENTER_V), "c1_f32kv")
     _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_CENTER_V), "c3")
     _expect(B.EUNSUPPORTED, lambda d: setattr(d, "flags", B.FLAG_CENTER_V), "c1")
-    _expect(B.EINVAL, lambda d: setattr(d, "flags", 1 << 5), "c1_f32kv")
+    _expect(B.EINVAL, lambda d: setattr(d, "flags", 1 << 6), "c1_f32kv")
     # the centre takes Hkv * D floats of workspace
     d0 = _desc("c1_f32kv")
     d1 = _desc("c1_f32kv")
@@ -209,7 +209,7 @@ def test_walk1_and_centre_k_flags():
     _expect(B.EUNSUPPORTED, lambda d: setattr(d, "flags", B.FLAG_CENTER_K), "c1")
     _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_CENTER_K), "c1_f32kv")
     _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_CENTER_K | B.FLAG_CENTER_V), "c3")
-    _expect(B.EINVAL, lambda d: setattr(d, "flags", 16), "c1_f32kv")
+    _expect(B.EINVAL, lambda d: setattr(d, "flags", 64), "c1_f32kv")
 
 
 def _ws(p, flags):
@@ -230,6 +230,23 @@ def test_walk1_flag_sets_the_workspace():
         assert keys.workspace_bytes != rows.workspace_bytes
     assert _ws(long_cache, 0).workspace_bytes == _ws(long_cache, B.FLAG_WALK1_KEYS).workspace_bytes
     assert _ws(short, 0).workspace_bytes == _ws(short, B.FLAG_WALK1_ROWS).workspace_bytes
+
+
+def test_kv_image_flags_and_workspace():
+    """The decoded image of the cache takes Hkv * ceil(M / 32) * 128 * D bytes of workspace; the
+    two flags exclude each other; without a flag the plan takes the image when at least 4 row
+    tiles of 128 rows (per KV head) read each sub-tile: c3 (32 row tiles) yes, c1 (2) no."""
+    _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_KV_IMAGE))
+    _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_KV_INLINE))
+    _expect(B.EINVAL, lambda d: setattr(d, "flags", B.FLAG_KV_IMAGE | B.FLAG_KV_INLINE))
+    for name, default_image in (("c3", True), ("c1", False)):
+        p = fa_inputs.make(name)
+        img, inl, dflt = _ws(p, B.FLAG_KV_IMAGE), _ws(p, B.FLAG_KV_INLINE), _ws(p, 0)
+        image_bytes = p.Hkv * ((p.M + 31) // 32) * 128 * p.D
+        assert img.workspace_bytes - inl.workspace_bytes >= image_bytes
+        assert img.workspace_bytes - inl.workspace_bytes < image_bytes + 256
+        assert img.out_bytes == inl.out_bytes
+        assert dflt.workspace_bytes == (img if default_image else inl).workspace_bytes
 
 
 def test_centre_k_workspace():
