@@ -610,7 +610,11 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
             f32x16 sa, pa;
 #pragma unroll
             for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
+            // both roles' products at raised priority: whichever wave has products to issue goes
+            // ahead of the other's exponentials
+            mfma_prio_hi();
             pair_rows<D, 2>(slot(s), bq, bd, sa, pa, rw);
+            mfma_prio_lo();
             const int j0 = s * kSubKeys;
             const bool fast = full_rows && cls == kMaskZero && j0 + kSubKeys <= p.M;
             if (!GRAD) {
@@ -749,7 +753,6 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         if (GRAD && s > s_begin && cls_prev != kMaskDead) {
             const unsigned char* ex = exch(s - 1);
             const f16x8 bb[2] = {*(const f16x8*)(ex + lane * 16), *(const f16x8*)(ex + 1024 + lane * 16)};
-            // the K waves' products (the longer role of the pair) issue ahead of the S wave's work
             mfma_prio_hi();
             cols_acc<D>(slot(s - 1), bb, dqacc, cw);
             mfma_prio_lo();
