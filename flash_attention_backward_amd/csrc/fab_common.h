@@ -98,6 +98,16 @@ constexpr int kMaskMixed = 2;
 // the column is lane % 32.
 FAB_DEV int crow(int v, int g) { return 8 * (v >> 2) + 4 * g + (v & 3); }
 
+// dS = p (dp - delta) to fp16 as walk 2 forms it: the product rounded to fp32, then to fp16.
+// The product passes through an empty asm statement so that the compiler cannot fuse the
+// multiply into the conversion (v_fma_mix, one rounding instead of two) in some paths and not in
+// others: every path that forms walk 2's dS gives the same bits.
+FAB_DEV _Float16 ds_f16(float pv, float dp, float delta) {
+    float x = pv * (dp - delta);
+    asm volatile("" : "+v"(x));
+    return (_Float16)x;
+}
+
 FAB_DEV f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }

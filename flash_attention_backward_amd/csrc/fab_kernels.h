@@ -583,6 +583,11 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         };
         // prologue: sub-tile s_begin staged and decoded (V half here, K half by the K waves),
         // the bytes of s_begin+1 on their way; from the image, the first two slots on their way
+        if constexpr (IMG) {
+            // the q and dO fragments are in registers before the first copy is queued: a wait
+            // for them left inside the loop would wait for the copies in flight as well
+            wait_all_mem();
+        }
         if (s_begin < s_end) sdma(s_begin);
         if constexpr (IMG) {
             if (s_begin + 1 < s_end) sdma(s_begin + 1);
@@ -679,7 +684,7 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const float pv = fast_exp2(fmaf(sa[v], sc2, -lse2k));
-                        bs[v >> 3][v & 7] = (_Float16)(pv * (pa[v] - dlt));
+                        bs[v >> 3][v & 7] = ds_f16(pv, pa[v], dlt);
                     }
                 } else {
                     // masked or ragged sub-tile, same arithmetic as above for mask-0 entries
@@ -690,7 +695,7 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
                         if (!row_ok || key >= p.M) mv = neg_inf();
                         else if (cls == kMaskMixed) mv = mask_value(p, mrow, i, key) * kLog2e;
                         const float pv = (dead || mv == neg_inf()) ? 0.0f : fast_exp2(fmaf(sa[v], sc2, mv - lse2k));
-                        bs[v >> 3][v & 7] = (_Float16)(pv * (pa[v] - dlt));
+                        bs[v >> 3][v & 7] = ds_f16(pv, pa[v], dlt);
                     }
                 }
                 unsigned char* ex = exch(s);
