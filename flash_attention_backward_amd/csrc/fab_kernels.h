@@ -310,20 +310,37 @@ __global__ __launch_bounds__(kThreads) void maskclass_rows_kernel(Params p) {
     }
 }
 
-FAB_DEV int mask_class(const Params& p, int hk, int rb, int t) {
+// The class without a stored mask: no mask (kMaskZero), or the causal tail, where query row i
+// sees keys j <= M - N + i; the block's rows r < R hold query rows ilo..ihi and the tile keys
+// j0..j1 < M: the class the stored mask would get.
+FAB_DEV int mask_class_implicit(const Params& p, int rb, int t) {
     if (p.m_type == FA_BACK_NONE) return kMaskZero;
-    if (p.m_type == FA_BACK_CAUSAL_TAIL) {
-        // query row i sees keys j <= M - N + i; the block's rows r < R hold query rows ilo..ihi
-        // and the tile keys j0..j1 < M: the class the stored mask would get
-        const int ilo = (32 * rb) / p.G, ihi = min(32 * rb + 31, p.R - 1) / p.G;
-        const int j0 = t * kQTileKeys, j1 = min(j0 + kQTileKeys - 1, p.M - 1);
-        const int off = p.M - p.N;
-        if (j0 > off + ihi) return kMaskDead;
-        if (j1 <= off + ilo) return kMaskZero;
-        return kMaskMixed;
-    }
+    const int ilo = (32 * rb) / p.G, ihi = min(32 * rb + 31, p.R - 1) / p.G;
+    const int j0 = t * kQTileKeys, j1 = min(j0 + kQTileKeys - 1, p.M - 1);
+    const int off = p.M - p.N;
+    if (j0 > off + ihi) return kMaskDead;
+    if (j1 <= off + ilo) return kMaskZero;
+    return kMaskMixed;
+}
+
+// Class of (32-row block rb, 64-key tile t): none or causal-tail masks from the indices, stored
+// masks from the class table.
+FAB_DEV int mask_class(const Params& p, int hk, int rb, int t) {
+    if (p.m_type == FA_BACK_NONE || p.m_type == FA_BACK_CAUSAL_TAIL) return mask_class_implicit(p, rb, t);
     const int hc = p.Hm == 1 ? 0 : hk;
     return p.mcls[((int64_t)hc * p.RB + rb) * p.KT + t];
+}
+
+// mask_class for wave-uniform arguments: a stored class is read through the scalar cache (the
+// load counts on lgkmcnt, so waiting for it leaves the wave's vector loads and copies in flight).
+// The dword read may cover up to 3 bytes past the table, which the workspace still holds.
+FAB_DEV int mask_class_s(const Params& p, int hk, int rb, int t) {
+    if (p.m_type == FA_BACK_NONE || p.m_type == FA_BACK_CAUSAL_TAIL) return mask_class_implicit(p, rb, t);
+    const int hc = p.Hm == 1 ? 0 : hk;
+    const int64_t o = ((int64_t)hc * p.RB + rb) * p.KT + t;
+    typedef const __attribute__((address_space(4))) unsigned int cu32;
+    const unsigned int w = *(cu32*)(uintptr_t)(p.mcls + (o & ~(int64_t)3));
+    return (int)((w >> (8 * (int)(o & 3))) & 0xffu);
 }
 
 FAB_DEV float mask_at(const char* mrow, int type, int j) {
@@ -588,25 +605,21 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
             // for them left inside the loop would wait for the copies in flight as well
             wait_all_mem();
         }
-        if (s_begin < s_end) sdma(s_begin);
         if constexpr (IMG) {
-            if (s_begin + 1 < s_end) sdma(s_begin + 1);
+            // the K waves copy the slots from the image
             lds_barrier();
         } else {
+            if (s_begin < s_end) sdma(s_begin);
             wait_all_mem();
             __syncthreads();
             if (s_begin + 1 < s_end) sdma(s_begin + 1);
         }
         if (sdec && s_begin < s_end) sdecode(s_begin);
         for (int s = s_begin; s <= s_end; ++s) {
-            if (IMG && s + 1 < s_end) {
-                dma_barrier<NI>();   // slot s landed; the NI copies of slot s+1 stay in flight
-            } else {
-                wait_all_mem();
-                __syncthreads();   // sub-tile s decoded and its class posted; exchange slot s free
-            }
+            wait_all_mem();
+            __syncthreads();   // sub-tile s decoded or copied and its class posted; exchange slot s free
             if (s == s_end) break;
-            if (s + 2 < s_end) sdma(s + 2);
+            if (!IMG && s + 2 < s_end) sdma(s + 2);
             const int cls = __builtin_amdgcn_readfirstlane(clsx[(s & 1) * 4 + w4]);
             if (cls == kMaskDead) {
                 if (sdec && s + 1 < s_end) sdecode(s + 1);
@@ -728,10 +741,37 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
             decode_sub<D, DEC>(p, hk, fixed16, qf, s, rawK(s), rawV(s), (_Float16*)slot(s),
                                (_Float16*)(slot(s) + L::kTile), kw, lane, last);
     };
-    // prologue: the S waves stage sub-tile s_begin; its class is posted
-    int cls_cur = s_begin < s_end ? wclass(s_begin) : kMaskDead;    // class of sub-tile s
+    // image: the slot of sub-tile t is one contiguous run of kSlot bytes; each K wave copies a
+    // quarter of it in 1 KB pieces (hidden from the compiler: the copies stay in flight across
+    // the transpose reads, and the block barrier waits for them by count)
+    constexpr int NI = L::kSlot / (4 * 1024);
+    auto kdma = [&](int t) {
+        if constexpr (IMG) {
+            const unsigned char* src = p.kvimg + ((int64_t)hk * p.img_ns + t) * L::kSlot + kw * (NI * 1024);
+            const uint32_t dst = lds_addr(slot(t)) + (uint32_t)(kw * (NI * 1024));
+#pragma unroll
+            for (int it = 0; it < NI; ++it) dma16_hidden(src + it * 1024, 16u * lane, dst + it * 1024);
+        }
+    };
+    // the class of sub-tile s; with the image a scalar load, so that waiting for it leaves the
+    // copies in flight
+    auto kclass = [&](int s) {
+        if constexpr (IMG) return active ? mask_class_s(p, hk, rb, s >> 1) : kMaskDead;
+        else return wclass(s);
+    };
+    // prologue: the S waves stage sub-tile s_begin (or the K waves copy the first two slots);
+    // its class is posted
+    int cls_cur = s_begin < s_end ? kclass(s_begin) : kMaskDead;    // class of sub-tile s
     if (lane == 0) clsx[(s_begin & 1) * 4 + kw] = (unsigned char)cls_cur;
-    __syncthreads();
+    if constexpr (IMG) {
+        // the class loads are done before the first copy is queued
+        wait_all_mem();
+        if (s_begin < s_end) kdma(s_begin);
+        if (s_begin + 1 < s_end) kdma(s_begin + 1);
+        lds_barrier();   // the copies stay in flight: the first block barrier waits for them
+    } else {
+        __syncthreads();
+    }
     if (s_begin < s_end) kdecode(s_begin);
 
     f32x16 dqacc[GRAD ? MD : 1];
@@ -743,15 +783,20 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     }
     const ColWalk<D> cw = make_col_walk<D>(lane);
     int cls_last = kMaskDead;                                        // class of sub-tile s-1
-    int cls_nx = s_begin + 1 < s_end ? wclass(s_begin + 1) : kMaskDead;   // s+1, in flight
+    int cls_nx = s_begin + 1 < s_end ? kclass(s_begin + 1) : kMaskDead;   // s+1, in flight
     for (int s = s_begin; s <= s_end; ++s) {
-        wait_all_mem();
-        __syncthreads();   // sub-tile s decoded and dS of s-1 exchanged
+        if (IMG && s + 1 < s_end) {
+            dma_barrier<NI>();   // slot s+1 landed (needed next); the copies of s+2 stay in flight
+        } else {
+            wait_all_mem();
+            __syncthreads();   // sub-tile s decoded and dS of s-1 exchanged
+        }
         const int cls_prev = cls_last;
         cls_last = cls_cur;
         cls_cur = cls_nx;                                            // class of sub-tile s+1
         if (lane == 0 && s + 1 < s_end) clsx[((s + 1) & 1) * 4 + kw] = (unsigned char)cls_cur;
-        cls_nx = s + 2 < s_end ? wclass(s + 2) : kMaskDead;          // in flight during sub-tile s
+        cls_nx = s + 2 < s_end ? kclass(s + 2) : kMaskDead;          // in flight during sub-tile s
+        if (IMG && s + 2 < s_end) kdma(s + 2);
         // the decode (vector ALU work) first, beside the S waves' products; then the dQ products,
         // beside the S waves' exponentials
         if (s + 1 < s_end) kdecode(s + 1);

@@ -156,6 +156,16 @@ FAB_DEV void dma_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Wait until all but this wave's V most recent vector memory operations have completed (LDS
+// operations are not waited for).
+template <int V>
+FAB_DEV void wait_vm() {
+    static_assert(V >= 0 && V < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));   // vmcnt(V)
+    asm volatile("" ::: "memory");
+}
+
 // ----------------------------------------------------------------------------- block rows
 
 // q8_0 and q4_0 rows are staged raw in LDS and decoded from there.
