@@ -126,6 +126,71 @@ def encode_q4_0(x: np.ndarray) -> np.ndarray:
     return out.reshape(*x.shape[:-1], D // 32 * Q4_0_BLOCK_BYTES)
 
 
+def _pack_codes(code: np.ndarray) -> np.ndarray:
+    """16 bytes per block: byte t holds code t (low nibble) and code t + 16 (high nibble)."""
+    c = (code & 15).astype(np.uint8)
+    return c[..., :16] | (c[..., 16:] << 4)
+
+
+def _high_bits(code: np.ndarray) -> np.ndarray:
+    """The 32-bit word whose bit t is bit 4 of code t, as 4 little-endian bytes."""
+    h = np.zeros(code.shape[:-1], dtype=np.uint32)
+    for t in range(32):
+        h |= ((code[..., t].astype(np.uint32) >> 4) & 1) << t
+    return h[..., None].view(np.uint8).reshape(*h.shape, 4)
+
+
+def encode_min_step(x: np.ndarray, levels: int) -> tuple:
+    """Per block of 32: the minimum m, step d = (max - m) / levels (float32) and codes
+    round((x - m) / d) clamped to [0, levels] (0 for a constant block)."""
+    x = np.asarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    blk = x.reshape(*x.shape[:-1], D // 32, 32)
+    mn = blk.min(axis=-1)
+    d = ((blk.max(axis=-1) - mn) / np.float32(levels)).astype(np.float32)
+    safe = np.where(d > 0, d, np.float32(1.0))
+    code = np.where(d[..., None] > 0, np.floor((blk - mn[..., None]) / safe[..., None] + np.float32(0.5)), 0)
+    return mn, d, np.clip(code, 0, levels).astype(np.int64)
+
+
+def _f16_bytes(v: np.ndarray) -> np.ndarray:
+    return v.astype(np.float16).view(np.uint8).reshape(*v.shape, 2)
+
+
+def encode_q4_1(x: np.ndarray) -> np.ndarray:
+    """q4_1 blocks (20 bytes): fp16 step d, fp16 minimum m, then the 16 bytes of 4-bit codes;
+    d and codes from encode_min_step(x, 15). Returns uint8 (..., D/32*20)."""
+    mn, d, code = encode_min_step(x, 15)
+    out = np.concatenate([_f16_bytes(d), _f16_bytes(mn), _pack_codes(code)], axis=-1)
+    return out.reshape(*out.shape[:-2], -1)
+
+
+def encode_q5_1(x: np.ndarray) -> np.ndarray:
+    """q5_1 blocks (24 bytes): fp16 d, fp16 m, the word of code bits 4, the 16 bytes of low
+    nibbles; d and codes from encode_min_step(x, 31). Returns uint8 (..., D/32*24)."""
+    mn, d, code = encode_min_step(x, 31)
+    out = np.concatenate([_f16_bytes(d), _f16_bytes(mn), _high_bits(code), _pack_codes(code)], axis=-1)
+    return out.reshape(*out.shape[:-2], -1)
+
+
+def encode_q5_0(x: np.ndarray) -> np.ndarray:
+    """q5_0 blocks (22 bytes): fp16 step d, the word of code bits 4, the 16 bytes of low
+    nibbles. Per block: m = the value of largest magnitude (with its sign), d = m / -16 (float32),
+    code = floor(x/d + 16.5) clamped to [0, 31] (16 for an all-zero block); value d*(code-16).
+    Returns uint8 (..., D/32*22)."""
+    x = np.asarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    blk = x.reshape(*x.shape[:-1], D // 32, 32)
+    idx = np.abs(blk).argmax(axis=-1)[..., None]
+    m = np.take_along_axis(blk, idx, axis=-1)[..., 0]
+    d = (m / np.float32(-16.0)).astype(np.float32)
+    safe = np.where(d != 0, d, np.float32(1.0))
+    t = np.where(d[..., None] != 0, blk / safe[..., None], np.float32(0.0)).astype(np.float32)
+    code = np.clip(np.floor(t + np.float32(16.5)), 0, 31).astype(np.int64)
+    out = np.concatenate([_f16_bytes(d), _high_bits(code), _pack_codes(code)], axis=-1)
+    return out.reshape(*out.shape[:-2], -1)
+
+
 def encode(x: np.ndarray, typ: str) -> np.ndarray:
     if typ == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
@@ -137,6 +202,12 @@ def encode(x: np.ndarray, typ: str) -> np.ndarray:
         return encode_q8_0(x)
     if typ == "q4_0":
         return encode_q4_0(x)
+    if typ == "q4_1":
+        return encode_q4_1(x)
+    if typ == "q5_0":
+        return encode_q5_0(x)
+    if typ == "q5_1":
+        return encode_q5_1(x)
     raise ValueError(typ)
 
 

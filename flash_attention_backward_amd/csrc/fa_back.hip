@@ -53,8 +53,16 @@ int64_t elem_size(int type) {
         case FA_BACK_BF16: return 2;
         case FA_BACK_Q8_0: return 34;   // one 32-value block
         case FA_BACK_Q4_0: return 18;   // one 32-value block
+        case FA_BACK_Q4_1: return 20;
+        case FA_BACK_Q5_0: return 22;
+        case FA_BACK_Q5_1: return 24;
         default: return 0;
     }
+}
+
+bool is_block_kv(int type) {
+    return type == FA_BACK_Q8_0 || type == FA_BACK_Q4_0 || type == FA_BACK_Q4_1 || type == FA_BACK_Q5_0 ||
+           type == FA_BACK_Q5_1;
 }
 
 // Everything derived from a valid descriptor: shapes, plan choices, offsets.
@@ -87,7 +95,7 @@ int check_strides(const fa_back_tensor& t, bool rows16) {
     const int64_t es = elem_size(t.type);
     if (t.nb[0] != es) return FA_BACK_ESTRIDE;
     if (t.nb[1] <= 0 || t.nb[2] <= 0) return FA_BACK_ESTRIDE;
-    const int64_t a = rows16 ? 16 : (t.type == FA_BACK_Q8_0 || t.type == FA_BACK_Q4_0 ? 2 : es);
+    const int64_t a = rows16 ? 16 : (is_block_kv(t.type) ? 2 : es);
     if (t.nb[1] % a || t.nb[2] % a) return FA_BACK_ESTRIDE;
     return FA_BACK_OK;
 }
@@ -98,8 +106,8 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
     const fa_back_tensor &q = d->q, &k = d->k, &v = d->v, &dd = d->d, &m = d->mask;
     // types
     auto is_act = [](int t) { return t == FA_BACK_F32 || t == FA_BACK_F16 || t == FA_BACK_BF16; };
-    auto is_kv = [&](int t) { return is_act(t) || t == FA_BACK_Q8_0 || t == FA_BACK_Q4_0; };
-    auto is_blk = [](int t) { return t == FA_BACK_Q8_0 || t == FA_BACK_Q4_0; };
+    auto is_kv = [&](int t) { return is_act(t) || is_block_kv(t); };
+    auto is_blk = [](int t) { return is_block_kv(t); };
     if (!is_act(q.type) || !is_act(dd.type) || !is_kv(k.type) || !is_kv(v.type)) return FA_BACK_EUNSUPPORTED;
     const bool has_mask = m.type != FA_BACK_NONE;
     const bool causal = m.type == FA_BACK_CAUSAL_TAIL;   // implicit: no storage, no strides
@@ -287,6 +295,7 @@ struct PhaseMarks {
 template <int D, bool GRAD>
 void launch_qpass(const Geometry& g, const Params& P, hipStream_t st) {
     const dim3 grid(g.RT * g.Hkv, g.splits), block(kQThreads);
+    // the pair decode covers q8_0 and q4_0; the other block types take the general decode
     const bool blk_k = P.k_type == FA_BACK_Q8_0 || P.k_type == FA_BACK_Q4_0;
     const bool blk_v = P.v_type == FA_BACK_Q8_0 || P.v_type == FA_BACK_Q4_0;
     if (P.kvimg)
@@ -303,6 +312,7 @@ void launch_qpass(const Geometry& g, const Params& P, hipStream_t st) {
 template <int D>
 void launch_kvimage(const Geometry& g, const Params& P, hipStream_t st) {
     const dim3 grid(g.img_ns, g.Hkv), block(kImgThreads);
+    // the pair decode covers q8_0 and q4_0; the other block types take the general decode
     const bool blk_k = P.k_type == FA_BACK_Q8_0 || P.k_type == FA_BACK_Q4_0;
     const bool blk_v = P.v_type == FA_BACK_Q8_0 || P.v_type == FA_BACK_Q4_0;
     if (P.k_type == FA_BACK_Q8_0 && P.v_type == FA_BACK_Q8_0)
@@ -501,7 +511,7 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     if (!has_mask && mask) return FA_BACK_EINVAL;
     if (has_mask && !mask && (int64_t)g.M * g.N != 0) return FA_BACK_EINVAL;
     auto misaligned = [](const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) != 0; };
-    auto kv_align = [](int t) -> uintptr_t { return t == FA_BACK_Q8_0 || t == FA_BACK_Q4_0 ? 2 : 16; };
+    auto kv_align = [](int t) -> uintptr_t { return is_block_kv(t) ? 2 : 16; };
     if (misaligned(q, elem_size(ds.q.type)) || misaligned(d, elem_size(ds.d.type)) ||
         misaligned(k, kv_align(ds.k.type)) || misaligned(v, kv_align(ds.v.type)) ||
         (has_mask && misaligned(mask, elem_size(ds.mask.type))) || misaligned(out, kAlign) ||

@@ -1306,10 +1306,13 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p) {
 static __global__ __launch_bounds__(kThreads) void vmax_kernel(Params p) {
     float vm = 0.0f;
     const int64_t rows = (int64_t)p.M * p.Hkv;
-    if (p.v_type == FA_BACK_Q8_0 || p.v_type == FA_BACK_Q4_0) {
-        // block scale times the largest |q|: 128 (q8_0) or 8 (q4_0)
-        const int bsz = p.v_type == FA_BACK_Q8_0 ? 34 : 18;
-        const float qmax = p.v_type == FA_BACK_Q8_0 ? 128.0f : 8.0f;
+    if (is_block_type(p.v_type)) {
+        // |d| times the largest |code| (128 for q8_0, 8 for q4_0, 15 for q4_1, 16 for q5_0,
+        // 31 for q5_1), plus |m| for the types with a minimum
+        const int bsz = block_bytes(p.v_type);
+        const float qmax = p.v_type == FA_BACK_Q8_0 ? 128.0f : p.v_type == FA_BACK_Q4_0 ? 8.0f
+                         : p.v_type == FA_BACK_Q4_1 ? 15.0f : p.v_type == FA_BACK_Q5_0 ? 16.0f : 31.0f;
+        const bool has_m = p.v_type == FA_BACK_Q4_1 || p.v_type == FA_BACK_Q5_1;
         const int bpr = p.D / 32;
         const int64_t n = rows * bpr;
         for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += (int64_t)gridDim.x * kThreads) {
@@ -1317,7 +1320,9 @@ static __global__ __launch_bounds__(kThreads) void vmax_kernel(Params p) {
             const int b = (int)(e - row * bpr);
             const int hk = (int)(row / p.M), j = (int)(row - (int64_t)hk * p.M);
             const char* blk = p.v + (int64_t)hk * p.v_nb2 + (int64_t)j * p.v_nb1 + bsz * b;
-            vm = fmaxf(vm, fabsf((float)*(const _Float16*)blk) * qmax);
+            float bound = fabsf((float)*(const _Float16*)blk) * qmax;
+            if (has_m) bound += fabsf((float)*(const _Float16*)(blk + 2));
+            vm = fmaxf(vm, bound);
         }
     } else {
         const int64_t n = rows * p.D;

@@ -168,10 +168,23 @@ FAB_DEV void wait_vm() {
 
 // ----------------------------------------------------------------------------- block rows
 
-// q8_0 and q4_0 rows are staged raw in LDS and decoded from there.
-FAB_DEV bool is_block_type(int type) { return type == FA_BACK_Q8_0 || type == FA_BACK_Q4_0; }
-// bytes of one row of D values: D/32 blocks of 34 (q8_0) or 18 (q4_0) bytes
-FAB_DEV int block_row_bytes(int type, int D) { return D / 32 * (type == FA_BACK_Q8_0 ? 34 : 18); }
+// Rows of the ggml block types are staged raw in LDS and decoded from there.
+FAB_DEV bool is_block_type(int type) {
+    return type == FA_BACK_Q8_0 || type == FA_BACK_Q4_0 || type == FA_BACK_Q4_1 || type == FA_BACK_Q5_0 ||
+           type == FA_BACK_Q5_1;
+}
+// bytes of one 32-value block
+FAB_DEV int block_bytes(int type) {
+    switch (type) {
+        case FA_BACK_Q8_0: return 34;
+        case FA_BACK_Q4_0: return 18;
+        case FA_BACK_Q4_1: return 20;
+        case FA_BACK_Q5_0: return 22;
+        default: return 24;   // FA_BACK_Q5_1
+    }
+}
+// bytes of one row of D values (D/32 blocks)
+FAB_DEV int block_row_bytes(int type, int D) { return D / 32 * block_bytes(type); }
 
 // Staged row geometry, sized for q8_0 (the longer block row): a row's bytes are staged in LDS
 // as the 16-byte-aligned chunks that cover it (the row may start at any even address).
@@ -373,6 +386,46 @@ FAB_DEV void decode_q4_block(const unsigned char* slot, int off, int blk, f16x8 
     }
 }
 
+// Values 8c .. 8c+7 of a 32-value q4_1, q5_0 or q5_1 block of a staged row, decoded to fp16.
+// Fields are read as halfwords (the row is 2-byte aligned): fp16 d, [fp16 m], [the 32-bit word
+// h whose bit t is bit 4 of code t], then 16 bytes, byte b holding the low nibbles of codes b and
+// b + 16 (in its low and high half). So values 8c .. 8c+7 take bytes 8(c&1) .. +7, their low
+// nibbles when c < 2, else the high ones, and bits 8c .. 8c+7 of h. A value is formed in fp32,
+// d * (code - 16) for q5_0 and d * code + m otherwise (d * code is exact, so one fp32 rounding
+// at most), and rounded once to fp16, as an F32 cache holding that fp32 value would be.
+template <int TYPE>
+FAB_DEV f16x8 decode_qx_chunk(const unsigned char* slot, int off, int blk, int c) {
+    constexpr bool HAS_M = TYPE != FA_BACK_Q5_0;
+    constexpr bool HAS_H = TYPE != FA_BACK_Q4_1;
+    constexpr int NB = TYPE == FA_BACK_Q4_1 ? 20 : (TYPE == FA_BACK_Q5_0 ? 22 : 24);
+    constexpr int QS = 2 + (HAS_M ? 2 : 0) + (HAS_H ? 4 : 0);   // byte offset of the nibbles
+    const unsigned short* hw = (const unsigned short*)(slot + off + NB * blk);
+    const float d = (float)__builtin_bit_cast(_Float16, hw[0]);
+    const float m = HAS_M ? (float)__builtin_bit_cast(_Float16, hw[1]) : 0.0f;
+    unsigned int hb = 0;   // bits 8c .. 8c+7 of h
+    if constexpr (HAS_H) hb = ((unsigned int)hw[(HAS_M ? 2 : 1) + (c >> 1)] >> (8 * (c & 1))) & 0xffu;
+    unsigned int q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = hw[QS / 2 + 4 * (c & 1) + k];
+    const int sh = c < 2 ? 0 : 4;
+    f16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int code = (int)((q[i >> 1] >> (8 * (i & 1) + sh)) & 15u);
+        if constexpr (HAS_H) code += (int)((hb >> i) & 1u) << 4;
+        const float x = TYPE == FA_BACK_Q5_0 ? (float)(code - 16) * d : fmaf((float)code, d, m);
+        r[i] = (_Float16)x;
+    }
+    return r;
+}
+
+// Values 8c .. 8c+7 of block blk of a staged row of type q4_1, q5_0 or q5_1.
+FAB_DEV f16x8 decode_qx(int type, const unsigned char* slot, int off, int blk, int c) {
+    if (type == FA_BACK_Q4_1) return decode_qx_chunk<FA_BACK_Q4_1>(slot, off, blk, c);
+    if (type == FA_BACK_Q5_0) return decode_qx_chunk<FA_BACK_Q5_0>(slot, off, blk, c);
+    return decode_qx_chunk<FA_BACK_Q5_1>(slot, off, blk, c);
+}
+
 // Block blk of a staged q8_0 or q4_0 row.
 FAB_DEV void decode_block(int type, const unsigned char* slot, int off, int blk, f16x8 out[4]) {
     if (type == FA_BACK_Q8_0)
@@ -385,7 +438,7 @@ FAB_DEV void decode_block(int type, const unsigned char* slot, int off, int blk,
 // cen: the head's centre (D floats) taken from every value before its rounding, or NULL
 // (F32, F16 and BF16 rows only).
 // NT threads take part, tid = 0 .. NT-1 being this thread's index among them.
-//   q8_0, q4_0: one item = one 32-value block of a key (from the staged raw bytes)
+//   block types: one item = one 32-value block of a key (from the staged raw bytes)
 //   F32/F16/BF16: one item = 8 values of a key, read from global memory; every load of the
 //   thread is issued before the first conversion
 template <int D, int KEYS, int NT>
@@ -400,9 +453,16 @@ FAB_DEV void decode_tile(const char* base, int type, int64_t nb1, int64_t nb2, i
             const int key = item / BPR, blk = item - (item / BPR) * BPR;
             const int j = j0 + key;
             f16x8 out[4];
-            if (j < M) {
-                const int off = (int)((uintptr_t)(hbase + (int64_t)j * nb1) & 15);
-                decode_block(type, raw + key * Q8Row<D>::kSlot, off, blk, out);
+            const int off = (int)((uintptr_t)(hbase + (int64_t)j * nb1) & 15);
+            const unsigned char* slot = raw + key * Q8Row<D>::kSlot;
+            if (j < M && (type == FA_BACK_Q8_0 || type == FA_BACK_Q4_0)) {
+                decode_block(type, slot, off, blk, out);
+            } else if (j < M) {
+                // the other block types a chunk of 8 values at a time, each stored when formed
+#pragma unroll 1
+                for (int c = 0; c < 4; ++c)
+                    *(f16x8*)(dst + tile_off<D>(key, 4 * blk + c)) = decode_qx(type, slot, off, blk, c);
+                continue;
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)

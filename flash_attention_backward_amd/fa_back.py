@@ -14,7 +14,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa_back.so")
 
-NONE, F32, F16, BF16, Q8_0, Q4_0 = -1, 0, 1, 2, 8, 9
+NONE, F32, F16, BF16, Q8_0, Q4_0, Q4_1, Q5_0, Q5_1 = -1, 0, 1, 2, 8, 9, 10, 11, 12
 CAUSAL_TAIL = 16   # mask type only: query i sees keys j <= M - N + i, nothing stored
 # descriptor flags (include/fa_back.h)
 FLAG_CENTER_V = 1    # centre V before its fp16 rounding
@@ -24,8 +24,10 @@ FLAG_CENTER_K = 8    # centre K before its fp16 rounding
 FLAG_KV_IMAGE = 16   # decode the cache once into the workspace for the query-side walks
 FLAG_KV_INLINE = 32  # every query-side workgroup decodes the cache tiles it reads
 TYPE_IDS = {"none": NONE, "f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0,
-            "causal_tail": CAUSAL_TAIL}
-ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, Q8_0: 34, Q4_0: 18}
+            "q4_1": Q4_1, "q5_0": Q5_0, "q5_1": Q5_1, "causal_tail": CAUSAL_TAIL}
+# bytes of one element (one 32-value block for the ggml block types)
+ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, Q8_0: 34, Q4_0: 18, Q4_1: 20, Q5_0: 22, Q5_1: 24}
+BLOCK_TYPES = ("q8_0", "q4_0", "q4_1", "q5_0", "q5_1")
 
 OK, EINVAL, ESHAPE, ESTRIDE, EUNSUPPORTED, EHIP, EALIGN, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 NOALLOC_MAX_WORKSPACE = 64 << 20   # bytes of the library's static scratch (fa_back_run_noalloc)
@@ -198,7 +200,7 @@ def _ggml(x: np.ndarray, typ: str, ne0: int):
         s2 = x.itemsize
         s1 = max(c, 1) * s2
         s0 = max(b, 1) * s1
-    if typ in ("q8_0", "q4_0"):
+    if typ in BLOCK_TYPES:
         assert s2 == 1
     else:
         assert s2 == x.itemsize == nb0

@@ -18,8 +18,8 @@
  *
  * Tensors are described ggml-style: ne[] are extents innermost first, nb[] byte strides.
  *     q    ne = {D,  N, H  }   F32 | F16 | BF16
- *     k    ne = {D,  M, Hkv}   F32 | F16 | BF16 | Q8_0 | Q4_0   (K and V types independent)
- *     v    ne = {Dv, M, Hkv}   F32 | F16 | BF16 | Q8_0 | Q4_0
+ *     k    ne = {D,  M, Hkv}   F32 | F16 | BF16 | Q8_0 | Q4_0 | Q4_1 | Q5_0 | Q5_1
+ *     v    ne = {Dv, M, Hkv}   the same types (K and V types independent)
  *     d    ne = {Dv, H, N  }   F32 | F16 | BF16          (dO; note the H, N order, as the
  *                                                         operator's "Layout and shape" states)
  *     mask ne = {M,  N, Hm }   F32 | F16, Hm in {1, H}; type FA_BACK_NONE for no mask;
@@ -34,7 +34,14 @@
  * its value is scale * int8. A Q4_0 block (18 bytes, nb[0] = 18) is a little-endian fp16
  * scale followed by 16 bytes; byte t holds element t in its low nibble and element t + 16 in
  * its high nibble, and an element's value is scale * (nibble - 8) (the ggml q4_0 block, the
- * format of the served cache on the "torad-labs/llama.cpp PR #71" page).
+ * format of the served cache on the "torad-labs/llama.cpp PR #71" page). The other ggml block
+ * types (the pages name none of them; every field little-endian, 16 bytes of nibbles laid
+ * out as in Q4_0, code t = nibble t plus 16 times bit t of the word h where there is one):
+ *     Q4_1 (20 bytes): fp16 d, fp16 m, nibbles;           value = d * nibble + m
+ *     Q5_0 (22 bytes): fp16 d, 32-bit h, nibbles;         value = d * (code - 16)
+ *     Q5_1 (24 bytes): fp16 d, fp16 m, 32-bit h, nibbles; value = d * code + m
+ * A block value is formed in fp32 and rounded once to fp16, as an F32 cache holding that fp32
+ * value would be.
  *
  * Output: one packed F32 buffer, laid out as the operator's packed result (first review,
  * "Layout and shape"; second review, output index):
@@ -57,7 +64,7 @@
  *
  * Supported: D == Dv in {64, 128, 256}; H % Hkv == 0; N, M >= 0 (N == 0: dK = dV = 0;
  * M == 0: every row is fully masked); F32/F16/BF16 K or V rows 16-byte aligned (base and
- * strides); Q8_0 and Q4_0 rows 2-byte aligned; K and V row strides (nb[1]) below 2^32 bytes.
+ * strides); block-type rows 2-byte aligned; K and V row strides (nb[1]) below 2^32 bytes.
  */
 #ifndef FA_BACK_H
 #define FA_BACK_H
@@ -76,6 +83,9 @@ extern "C" {
 #define FA_BACK_BF16 2
 #define FA_BACK_Q8_0 8
 #define FA_BACK_Q4_0 9
+#define FA_BACK_Q4_1 10
+#define FA_BACK_Q5_0 11
+#define FA_BACK_Q5_1 12
 #define FA_BACK_CAUSAL_TAIL 16 /* mask only: query i sees keys j <= M - N + i; no storage */
 
 /* Flags (fa_back_desc.flags; 0 = the plain operator).

@@ -26,6 +26,12 @@ Readings where the pages are silent or ambiguous:
   - q4_0 (the served cache's type on the "torad-labs/llama.cpp PR #71" page; the pages do not
     spell out its block): the ggml block, fp16 scale then 16 bytes, byte t holding element t
     in its low nibble and element t + 16 in its high one; value = float64(scale) * (nibble - 8).
+  - q4_1, q5_0, q5_1 (ggml block types that the pages do not name; their blocks are read as
+    ggml lays them out, with every field little-endian):
+    q4_1 = fp16 scale d, fp16 minimum m, 16 bytes of nibbles as in q4_0; value = d * n + m.
+    q5_0 = fp16 d, a 32-bit word h, 16 bytes of nibbles; element t's code is its nibble plus 16
+    times bit t of h, value = d * (code - 16). q5_1 = fp16 d, fp16 m, the word h, 16 bytes;
+    value = d * code + m. (float64 throughout: every value is exact.)
 Every function here is pinned by tests/test_oracle_*.py (finite differences, a hand-worked
 example, closed forms, invariants and an independent pure-Python loop implementation).
 """
@@ -72,7 +78,38 @@ def widen(x: np.ndarray, typ: str, width: int | None = None) -> np.ndarray:
         qs = blocks[..., 2:18].astype(np.int64)
         nib = np.concatenate([qs & 15, qs >> 4], axis=-1).astype(np.float64) - 8.0
         return (step[..., None] * nib).reshape(*raw.shape[:-1], nblk * 32)
+    if typ in ("q4_1", "q5_0", "q5_1"):
+        # 20 / 22 / 24-byte blocks: fp16 d, [fp16 m], [32-bit word h], 16 bytes of nibbles,
+        # byte t holding element t (low nibble) and element t + 16 (high nibble)
+        nbytes = BLOCK_BYTES[typ]
+        raw = np.asarray(x, dtype=np.uint8)
+        nblk = raw.shape[-1] // nbytes
+        if width is not None and nblk * 32 != width:
+            raise ValueError(f"{typ} row width mismatch")
+        blocks = np.ascontiguousarray(raw).reshape(*raw.shape[:-1], nblk, nbytes)
+        d = np.ascontiguousarray(blocks[..., 0:2]).view(np.float16)[..., 0].astype(np.float64)
+        at = 2
+        m = np.zeros_like(d)
+        if typ != "q5_0":
+            m = np.ascontiguousarray(blocks[..., 2:4]).view(np.float16)[..., 0].astype(np.float64)
+            at = 4
+        code = np.zeros((*blocks.shape[:-1], 32), dtype=np.int64)
+        if typ != "q4_1":
+            h = np.ascontiguousarray(blocks[..., at:at + 4]).view("<u4")[..., 0].astype(np.int64)
+            code += ((h[..., None] >> np.arange(32)) & 1) << 4
+            at += 4
+        qs = blocks[..., at:at + 16].astype(np.int64)
+        code += np.concatenate([qs & 15, qs >> 4], axis=-1)
+        if typ == "q5_0":
+            val = d[..., None] * (code.astype(np.float64) - 16.0)
+        else:
+            val = d[..., None] * code.astype(np.float64) + m[..., None]
+        return val.reshape(*raw.shape[:-1], nblk * 32)
     raise ValueError(f"unknown type {typ}")
+
+
+# bytes of one 32-value block of the ggml block types
+BLOCK_BYTES = {"q8_0": 34, "q4_0": 18, "q4_1": 20, "q5_0": 22, "q5_1": 24}
 
 
 def problem_arrays(p):

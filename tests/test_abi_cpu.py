@@ -263,3 +263,23 @@ def test_noalloc_status_and_limit():
     assert B.NOALLOC_MAX_WORKSPACE == 64 << 20
     lib = fab.load_library()
     assert lib.fa_back_run_noalloc(None, *([None] * 7)) == B.EINVAL
+
+
+@pytest.mark.parametrize("typ,nbytes", [("q4_1", 20), ("q5_0", 22), ("q5_1", 24)])
+def test_other_block_types_accepted_as_cache_only(typ, nbytes):
+    # K and V may be any of the ggml block types (2-byte aligned rows of D/32 blocks of nbytes);
+    # Q, dO and the mask may not
+    p = fa_inputs.make_custom(name=typ, D=128, H=4, Hkv=2, N=20, M=70, mask="tail", k_type=typ,
+                              v_type=typ)
+    assert p.k.shape[-1] == 128 // 32 * nbytes
+    d = B.describe(p)
+    assert d.k.type == B.TYPE_IDS[typ] and d.k.nb[0] == nbytes
+    lay = fab.fa_back_layout_query(d)
+    assert lay.off_dv >= lay.off_dk + 4 * p.D * p.M * p.Hkv
+    for field in ("q", "d", "mask"):
+        _expect(B.EUNSUPPORTED, lambda dd, f=field: setattr(getattr(dd, f), "type", B.TYPE_IDS[typ]))
+    # a row pitch that is odd breaks the 2-byte alignment of the fp16 fields
+    d.k.nb[1] += 1
+    d.k.nb[2] = d.k.nb[1] * p.M
+    lay = B.Layout()
+    assert fab.load_library().fa_back_layout_query(ctypes.byref(d), ctypes.byref(lay)) == B.ESTRIDE

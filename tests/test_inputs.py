@@ -1,5 +1,6 @@
 """The seeded input generators (CPU only)."""
 import numpy as np
+import pytest
 
 import fa_inputs
 from oracle import fa_back_oracle as O
@@ -89,3 +90,19 @@ def test_q4_0_encoding_round_trip_error():
     err = np.abs(dec - x.reshape(3, 5, 2, 32).astype(np.float64))
     assert np.all(err <= np.abs(step)[..., None] * (1 + 1e-3) + 1e-6)
     assert np.all(dec[0, 0, 0] == 0.0)
+
+
+@pytest.mark.parametrize("typ,nbytes", [("q4_1", 20), ("q5_0", 22), ("q5_1", 24)])
+def test_other_block_encodings_round_trip_error(typ, nbytes):
+    # the decoded values lie within one step of the drawn ones (half a step where no code clips),
+    # and a constant block (zero for q5_0) decodes exactly
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((3, 5, 64)).astype(np.float32)
+    x[0, 0, :32] = 0.0 if typ == "q5_0" else 0.75
+    raw = fa_inputs.encode(x, typ)
+    assert raw.shape == (3, 5, 2 * nbytes) and raw.dtype == np.uint8
+    dec = O.widen(raw, typ, 64).reshape(3, 5, 2, 32)
+    step = np.abs(raw.reshape(3, 5, 2, nbytes)[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64))
+    err = np.abs(dec - x.reshape(3, 5, 2, 32).astype(np.float64))
+    assert np.all(err <= step[..., None] * (1 + 2e-3) + 2e-3)
+    assert np.all(dec[0, 0, 0] == x[0, 0, 0])

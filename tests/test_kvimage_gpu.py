@@ -2,7 +2,7 @@
 workspace, the query-side walks copy tiles from it) against per-workgroup decoding
 (FA_BACK_FLAG_KV_INLINE): bitwise the same outputs. The cases cover every decode the walks
 have (q8_0 pairs with 16-byte and other row strides, q4_0 / q8_0 mixes, a block type beside an
-F16 row type, F32 / BF16 rows, centred F16 rows), the three head sizes, ragged caches, stored
+F16 row type, the q4_1 / q5_0 / q5_1 blocks, F32 / BF16 rows, centred F16 rows), the three head sizes, ragged caches, stored
 and dead mask rows, key-range splits (the walks start mid-cache) and both directions of the
 walk that forms LSE and delta (the row-owned one reads the image too)."""
 import dataclasses
@@ -27,6 +27,9 @@ CASES = [
          v_type="f16", k_offset=3.0, k_spread=0.01, v_offset=2.0, v_spread=0.01,
          flags=B.FLAG_CENTER_K | B.FLAG_CENTER_V),
     dict(name="img_split_128", D=128, H=4, Hkv=1, N=64, M=2048, mask="tail", k_type="q8_0", v_type="q8_0"),
+    dict(name="img_q5_1q4_1_256", D=256, H=8, Hkv=2, N=70, M=300, mask="tail", k_type="q5_1", v_type="q4_1"),
+    dict(name="img_q5_0f16_64", D=64, H=4, Hkv=2, N=50, M=130, mask="random", Hm=4, k_type="q5_0",
+         v_type="f16"),
 ]
 
 

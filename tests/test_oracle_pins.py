@@ -237,6 +237,53 @@ def test_q4_0_decoding_of_hand_built_blocks(golden_dir):
     np.testing.assert_array_equal(got.ravel(), np.array(expect))
 
 
+@pytest.mark.parametrize("typ", ["q4_1", "q5_0", "q5_1"])
+def test_other_block_types_decoding_of_hand_built_blocks(golden_dir, typ):
+    g = json.load(open(os.path.join(golden_dir, f"{typ}_blocks.json")))
+    raw = bytearray()
+    expect = []
+    for b in g["blocks"]:
+        raw += bytes(b["bytes"])
+        expect += b["values"]
+    assert len(raw) == O.BLOCK_BYTES[typ] * len(g["blocks"])
+    arr = np.frombuffer(bytes(raw), dtype=np.uint8).reshape(1, 1, -1)
+    got = O.widen(arr, typ, 32 * len(g["blocks"]))
+    np.testing.assert_array_equal(got.ravel(), np.array(expect))
+
+
+@pytest.mark.parametrize("typ", ["q4_1", "q5_0", "q5_1"])
+def test_other_block_types_run_equals_dequantised_f32_run(typ):
+    p = fa_inputs.make_custom(name=typ, D=64, H=4, Hkv=2, N=9, M=40, mask="tail", k_type=typ, v_type=typ)
+    nb = O.BLOCK_BYTES[typ]
+
+    # hand decode by integer arithmetic on the bytes (not the oracle's decoder)
+    def dec(raw):
+        raw = np.asarray(raw).astype(np.int64)
+        out = np.empty(raw.shape[:-1] + (raw.shape[-1] // nb * 32,))
+        for b in range(raw.shape[-1] // nb):
+            blk = raw[..., nb * b:nb * (b + 1)]
+            half = lambda i: (blk[..., i] | (blk[..., i + 1] << 8)).astype(np.uint16).view(np.float16).astype(np.float64)
+            d = half(0)
+            m = half(2) if typ != "q5_0" else 0.0
+            at = 2 if typ == "q5_0" else 4
+            h = 0
+            if typ != "q4_1":
+                h = blk[..., at] | (blk[..., at + 1] << 8) | (blk[..., at + 2] << 16) | (blk[..., at + 3] << 24)
+                at += 4
+            for t in range(32):
+                byte = blk[..., at + (t % 16)]
+                code = (byte % 16 if t < 16 else byte // 16) + 16 * ((h >> t) & 1)
+                val = d * (code - 16) if typ == "q5_0" else d * code + m
+                out[..., 32 * b + t] = val
+        return out
+    kf, vf = dec(p.k), dec(p.v)
+    a = O.run_problem(p)
+    q, _, _, do, mask = O.problem_arrays(p)
+    b = O.flash_attn_back(q, kf, vf, do, mask, p.scale)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+
+
 def test_q4_0_run_equals_dequantised_f32_run():
     p = fa_inputs.make_custom(name="q4", D=64, H=4, Hkv=2, N=9, M=40, mask="tail",
                               k_type="q4_0", v_type="q4_0")

@@ -60,6 +60,14 @@ RAGGED = [
     dict(name="q4_0_d256_tail", D=256, H=6, Hkv=1, N=40, M=333, mask="tail", k_type="q4_0", v_type="q4_0"),
     dict(name="q4_0_k_q8_0_v", D=64, H=4, Hkv=2, N=33, M=150, mask="tail", k_type="q4_0", v_type="q8_0"),
     dict(name="f16_k_q4_0_v", D=128, H=2, Hkv=1, N=20, M=100, mask="random", k_type="f16", v_type="q4_0"),
+    # the other ggml block types: q4_1, q5_0, q5_1, alone, mixed and beside a row type
+    dict(name="q4_1_kv", D=128, H=8, Hkv=2, N=64, M=300, mask="none", k_type="q4_1", v_type="q4_1"),
+    dict(name="q5_0_d256_tail", D=256, H=6, Hkv=1, N=40, M=333, mask="tail", k_type="q5_0", v_type="q5_0"),
+    dict(name="q5_1_d64_random", D=64, H=4, Hkv=2, N=33, M=150, mask="random", Hm=4, k_type="q5_1",
+         v_type="q5_1"),
+    dict(name="q5_1_k_q4_1_v", D=256, H=4, Hkv=2, N=37, M=210, mask="tail", k_type="q5_1", v_type="q4_1"),
+    dict(name="q8_0_k_q5_0_v", D=128, H=4, Hkv=1, N=70, M=129, mask="tail", k_type="q8_0", v_type="q5_0"),
+    dict(name="f16_k_q5_1_v", D=128, H=2, Hkv=1, N=20, M=100, mask="random", k_type="f16", v_type="q5_1"),
     # two row blocks per KV head at D=256: the key side's list holds exactly two entries
     dict(name="kv_two_blocks", D=256, H=2, Hkv=1, N=32, M=200, mask="tail", k_type="q8_0", v_type="f16"),
     # four row blocks, the first and the last fully masked: only the middle two are listed
@@ -128,6 +136,24 @@ def test_q4_0_equals_dequantised_f32_bitwise(mode):
     f.name = "q4_bits_f32"
     f.k = O.widen(p.k, "q4_0", p.D).astype(np.float32)
     f.v = O.widen(p.v, "q4_0", p.Dv).astype(np.float32)
+    f.k_type = f.v_type = "f32"
+    a, _, _ = run_gpu(p)
+    b, _, _ = run_gpu(f)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+
+
+@pytest.mark.parametrize("mode", ["rows", "keys"])
+@pytest.mark.parametrize("typ,D", [("q4_1", 128), ("q5_0", 256), ("q5_1", 64)])
+def test_block_types_equal_dequantised_f32_bitwise(typ, D, mode):
+    # each value of these types is one fp32 rounding of d * code (+ m); an F32 cache holding
+    # that value goes through the same fp16 rounding
+    p = walk1(fa_inputs.make_custom(name=f"{typ}_bits", D=D, H=4, Hkv=2, N=37, M=200, mask="tail",
+                                    k_type=typ, v_type=typ), mode)
+    f = fa_inputs.Problem(**{**p.__dict__})
+    f.name = f"{typ}_bits_f32"
+    f.k = O.widen(p.k, typ, p.D).astype(np.float32)
+    f.v = O.widen(p.v, typ, p.Dv).astype(np.float32)
     f.k_type = f.v_type = "f32"
     a, _, _ = run_gpu(p)
     b, _, _ = run_gpu(f)
