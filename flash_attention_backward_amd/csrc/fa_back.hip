@@ -26,6 +26,7 @@ constexpr uint64_t kAlign = 256;
 // count gets no tail split if its split would not fit.
 constexpr int kRefCUs = 256;
 constexpr int kLayoutCUs[] = {32, 64, 128, 256};
+constexpr int kMaxW1Splits = 32;   // key-range splits of walk 1 by row tiles, at most
 
 // Key-side tail tiles: one workgroup per CU at a time (LDS), so the tiles past the last full
 // round of workgroups would run nearly alone; each of them is split into up to 4 row ranges.
@@ -74,7 +75,9 @@ struct Geometry {
     int64_t kv_parts_ws;              // split-tile parts the workspace holds (any planned CU count)
     bool w1keys;           // walk 1 by key tiles (else by row tiles)
     int KT1, RS1, w1_rbs;  // its 256-key tiles, row splits and row blocks per workgroup
+    int w1_splits, w1_tps; // walk 1 by row tiles: key-range splits, 64-key tiles per split
     int nparts;            // walk-1 records per row
+    int nparts_ws;         // walk-1 records per row the workspace holds (any planned CU count)
     bool img;              // the query-side walks copy K/V tiles from the decoded image
     int img_ns;            // its 32-key sub-tiles per KV head
     int npart, nbound;
@@ -196,11 +199,21 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
         g->tiles_per_split = tps;
         g->splits = g->KT > 0 ? (g->KT + tps - 1) / tps : 1;
     }
-    // walk 1 by key tiles when the cache is long next to the rows (each K/V tile is then
-    // decoded once per 256 keys instead of once per 128 rows), unless a flag picks the walk
+    // the decoded image of the cache: when each sub-tile would be decoded by at least 4 row
+    // tiles of the query-side walks (a flag forces either way)
+    {
+        bool img = g->RT >= 4;
+        if (d->flags & FA_BACK_FLAG_KV_IMAGE) img = true;
+        if (d->flags & FA_BACK_FLAG_KV_INLINE) img = false;
+        g->img = img && g->M > 0 && g->R > 0;
+        g->img_ns = (g->M + kSubKeys - 1) / kSubKeys;
+    }
+    // walk 1 by key tiles when the cache is long next to the rows and not in the image (each
+    // K/V tile is then decoded once per 256 keys instead of once per 128 rows); over the image
+    // by row tiles of 256 rows, where all 8 waves form products; a flag picks the walk
     {
         g->KT1 = (g->M + kW1Keys - 1) / kW1Keys;
-        bool keys = g->M >= 2 * (int64_t)g->R;
+        bool keys = g->M >= 2 * (int64_t)g->R && !g->img;
         if (d->flags & FA_BACK_FLAG_WALK1_KEYS) keys = true;
         if (d->flags & FA_BACK_FLAG_WALK1_ROWS) keys = false;
         g->w1keys = keys && g->M > 0 && g->R > 0;
@@ -221,16 +234,25 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
             g->w1_rbs = (g->RB + best - 1) / best;
             g->RS1 = (g->RB + g->w1_rbs - 1) / g->w1_rbs;
         }
-        g->nparts = g->w1keys ? g->KT1 : g->splits;
-    }
-    // the decoded image of the cache: when each sub-tile would be decoded by at least 4 row
-    // tiles of the query-side walks (a flag forces either way)
-    {
-        bool img = g->RT >= 4;
-        if (d->flags & FA_BACK_FLAG_KV_IMAGE) img = true;
-        if (d->flags & FA_BACK_FLAG_KV_INLINE) img = false;
-        g->img = img && g->M > 0 && g->R > 0;
-        g->img_ns = (g->M + kSubKeys - 1) / kSubKeys;
+        // walk 1 by row tiles: its own key-range splits, chosen for its workgroups (256 rows
+        // each over the image, else 128): minimise rounds of `cus` workgroups x (64-key tiles
+        // per split + 1)
+        const int rows_wg = g->img ? 8 : kWaves;
+        const int wgs = ((g->RB + rows_wg - 1) / rows_wg) * g->Hkv;
+        const int kt = std::max(g->KT, 1);
+        const int sp_max = std::min(kMaxW1Splits, kt);
+        double best_cost = 1e300;
+        g->w1_splits = 1;
+        g->w1_tps = kt;
+        for (int sp = 1; sp <= sp_max; ++sp) {
+            const int tps = (kt + sp - 1) / sp;
+            const int n = (kt + tps - 1) / tps;
+            const double cost = std::ceil((double)wgs * n / (double)cus) * (tps + 1.0);
+            if (cost < best_cost - 1e-9) { best_cost = cost; g->w1_splits = n; g->w1_tps = tps; }
+        }
+        g->nparts = g->w1keys ? g->KT1 : g->w1_splits;
+        // the records the workspace holds do not depend on the CU count (the most splits allowed)
+        g->nparts_ws = g->w1keys ? g->KT1 : sp_max;
     }
     g->npart = (int)std::min<int64_t>(512, std::max<int64_t>(1, N * H / 8));
     const int64_t total_rows = (int64_t)g->Hkv * g->RB * 32;
@@ -248,7 +270,7 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
     uint64_t o = 0;
     auto take = [&](uint64_t bytes) { const uint64_t at = o; o = align_up(o + bytes, kAlign); return at; };
     const uint64_t frag = 2ull * total_rows * D;
-    const uint64_t prow = (uint64_t)std::max(g->splits, g->nparts) * total_rows;
+    const uint64_t prow = (uint64_t)std::max(g->nparts, g->nparts_ws) * total_rows;
     g->ws_absmax = take(8ull * g->npart);
     g->ws_scal = take(64);
     g->ws_qr = take(frag);
@@ -275,7 +297,8 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
 // per CU; the small kernels use a few KB).
 template <int D>
 int max_lds_bytes_d() {
-    return std::max(std::max(std::max(QLds<D>::kBytes, QLds<D, true>::kBytes), W1Lds<D>::kBytes), KVLds<D>::kBytes);
+    return std::max(std::max(std::max(QLds<D>::kBytes, QLds<D, true>::kBytes), W1Lds<D>::kBytes),
+                    std::max(KVLds<D>::kBytes, R1Lds<D>::kBytes));
 }
 int max_lds_bytes(int D) {
     return D == 64 ? max_lds_bytes_d<64>() : D == 128 ? max_lds_bytes_d<128>() : max_lds_bytes_d<256>();
@@ -294,12 +317,18 @@ struct PhaseMarks {
 // The query-side walk, in the instantiation of the K/V decode the types need.
 template <int D, bool GRAD>
 void launch_qpass(const Geometry& g, const Params& P, hipStream_t st) {
-    const dim3 grid(g.RT * g.Hkv, g.splits), block(kQThreads);
+    if (!GRAD && P.kvimg) {
+        // walk 1 over the image: every wave owns rows
+        const dim3 grid1((g.RB + kR1Waves - 1) / kR1Waves * g.Hkv, g.w1_splits);
+        hipLaunchKernelGGL(walk1_rows_kernel<D>, grid1, dim3(kR1Threads), 0, st, P);
+        return;
+    }
+    const dim3 grid(g.RT * g.Hkv, GRAD ? g.splits : g.w1_splits), block(kQThreads);
     // the pair decode covers q8_0 and q4_0; the other block types take the general decode
     const bool blk_k = P.k_type == FA_BACK_Q8_0 || P.k_type == FA_BACK_Q4_0;
     const bool blk_v = P.v_type == FA_BACK_Q8_0 || P.v_type == FA_BACK_Q4_0;
-    if (P.kvimg)
-        hipLaunchKernelGGL((qpass_kernel<D, GRAD, kDecImg>), grid, block, 0, st, P);
+    if (GRAD && P.kvimg)
+        hipLaunchKernelGGL((qpass_kernel<D, true, kDecImg>), grid, block, 0, st, P);
     else if (P.k_type == FA_BACK_Q8_0 && P.v_type == FA_BACK_Q8_0)
         hipLaunchKernelGGL((qpass_kernel<D, GRAD, kDecQ8>), grid, block, 0, st, P);
     else if (blk_k && blk_v)
@@ -538,7 +567,7 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     P.D = g.D; P.H = g.H; P.Hkv = g.Hkv; P.G = g.G; P.N = g.N; P.M = g.M; P.Hm = g.Hm;
     P.R = g.R; P.RB = g.RB; P.RT = g.RT; P.KT = g.KT; P.splits = g.splits;
     P.tiles_per_split = g.tiles_per_split; P.KVT = g.KVT;
-    P.w1_rbs = g.w1_rbs; P.nparts = g.nparts;
+    P.w1_rbs = g.w1_rbs; P.w1_tps = g.w1_tps; P.nparts = g.nparts;
     P.scale = ds.scale;
     char* o = (char*)out;
     P.dq = (float*)(o + g.layout.off_dq);

@@ -48,6 +48,7 @@ struct Params {
     int tiles_per_split;
     int KVT;          // 128-key tiles of the key-side pass
     int w1_rbs;       // walk 1 by key tiles: row blocks per workgroup
+    int w1_tps;       // walk 1 by row tiles: 64-key tiles per key-range split
     int nparts;       // walk-1 records per row that the merge combines (splits or key tiles)
     float scale;
     // outputs (packed)

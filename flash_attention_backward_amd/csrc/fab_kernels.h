@@ -487,6 +487,94 @@ FAB_DEV void decode_sub(const Params& p, int hk, bool fixed16, const Q8Fixed<D>&
     }
 }
 
+// Walk-1 statistics of one query row over the keys seen so far (the lane's half of the row's
+// entries): running max m of the scaled scores (log2 units), l = sum exp2(s - m) and
+// d' = sum exp2(s - m) dp carried in fp64, and max |dp|.
+struct W1Row {
+    float m;
+    double l, d;
+    float b;
+};
+
+FAB_DEV void w1_init(W1Row& w) {
+    w.m = neg_inf();
+    w.l = 0.0;
+    w.d = 0.0;
+    w.b = 0.0f;
+}
+
+// Folds the 32 keys j0 .. j0+31 of one 32-row block into the row's statistics: sa holds the
+// products q.k (prescaled; sc2 takes them to log2 units), pa the products dO.v, in the lane's
+// 16 entries of the 32 x 32 result. fast: every entry visible (no mask term, no ragged edge);
+// otherwise the mask (class cls) and the bounds decide per entry, and an entry with mask 0 gets
+// exactly the arithmetic of the fast path.
+FAB_DEV void w1_fold(const Params& p, W1Row& w, const f32x16& sa, const f32x16& pa, bool fast, int cls,
+                     bool row_ok, const char* mrow, int i, int j0, int g, float sc2) {
+    if (fast) {
+        // every entry visible: the scale is positive, so max(s) = sc2 * max(sa)
+        float tm = sa[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) tm = fmaxf(tm, sa[v]);
+        tm = max_halves(tm);
+        const float mnew = fmaxf(w.m, tm * sc2);
+        const float alpha = fast_exp2(w.m - mnew);
+        float ls = 0.0f, ds = 0.0f, bm = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float e = fast_exp2(fmaf(sa[v], sc2, -mnew));
+            ls += e;
+            ds = fmaf(e, pa[v], ds);
+            bm = fmaxf(bm, fabsf(pa[v]));
+        }
+        w.l = fma(w.l, (double)alpha, (double)ls);
+        w.d = fma(w.d, (double)alpha, (double)ds);
+        w.m = mnew;
+        w.b = fmaxf(w.b, bm);
+        return;
+    }
+    float madd[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int key = j0 + crow(v, g);
+        float mv = 0.0f;
+        if (!row_ok || key >= p.M) mv = neg_inf();
+        else if (cls == kMaskMixed) mv = mask_value(p, mrow, i, key) * kLog2e;
+        madd[v] = mv;
+    }
+    float tmax = neg_inf();
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+        if (madd[v] != neg_inf()) tmax = fmaxf(tmax, fmaf(sa[v], sc2, madd[v]));
+    tmax = max_halves(tmax);
+    const float mnew = fmaxf(w.m, tmax);
+    if (mnew != neg_inf()) {
+        const float alpha = fast_exp2(w.m - mnew);
+        float ls = 0.0f, ds = 0.0f, bm = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            if (madd[v] == neg_inf()) continue;
+            const float e = fast_exp2(fmaf(sa[v], sc2, madd[v] - mnew));
+            ls += e;
+            ds = fmaf(e, pa[v], ds);
+            bm = fmaxf(bm, fabsf(pa[v]));
+        }
+        w.l = fma(w.l, (double)alpha, (double)ls);
+        w.d = fma(w.d, (double)alpha, (double)ds);
+        w.m = mnew;
+        w.b = fmaxf(w.b, bm);
+    }
+}
+
+// The row's record for key-range split `split`: the two lane halves' sums, carried in fp64,
+// rounded once to fp32.
+FAB_DEV void w1_record(const Params& p, const W1Row& w, int split, int ridx, int g) {
+    const double lo = w.l + __shfl_xor(w.l, 32);
+    const double dd = w.d + __shfl_xor(w.d, 32);
+    const float bb = fmaxf(w.b, __shfl_xor(w.b, 32));
+    if (g == 0)
+        p.part_rec[(int64_t)split * p.Hkv * p.RB * 32 + ridx] = f32x4{w.m, (float)lo, (float)dd, bb};
+}
+
 template <int D, bool GRAD, int DEC>
 __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     constexpr bool IMG = DEC == kDecImg;
@@ -513,8 +601,9 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
     const bool row_ok = active && r < p.R;
     const int ridx = hk * rowsHK + r;
     const int NS = (p.M + kSubKeys - 1) / kSubKeys;
-    const int s_begin = 2 * split * p.tiles_per_split;
-    const int s_end = min(NS, 2 * min(p.KT, (split + 1) * p.tiles_per_split));
+    const int tps = GRAD ? p.tiles_per_split : p.w1_tps;    // walk 1 has key ranges of its own
+    const int s_begin = 2 * split * tps;
+    const int s_end = min(NS, 2 * min(p.KT, (split + 1) * tps));
     const int eq = p.scal[0], edo = p.scal[1];
 
     auto slot = [&](int s) { return lds + L::kOffSlot + (s % L::kSlots) * L::kSlot; };
@@ -549,10 +638,8 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
         // q rows carry the sign of the scale (prep), so the score scale is positive here
         const float sc2 = fabsf(p.scale) * ldexpf(1.0f, -eq) * kLog2e;
         const bool full_rows = active && (rb + 1) * 32 <= p.R;
-        // walk 1 state
-        float m_run = neg_inf();
-        double l64 = 0.0, d64 = 0.0;
-        float bmax = 0.0f;
+        W1Row w1;   // walk 1 state
+        w1_init(w1);
         // walk 2 state: p * 2^-ks = exp2(s2 - lse2 - ks), lse2 stored less the image exponent
         float lse2 = pos_inf(), dlt = 0.0f, lse2k = 0.0f;
         if (GRAD) {
@@ -636,61 +723,7 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
             const int j0 = s * kSubKeys;
             const bool fast = full_rows && cls == kMaskZero && j0 + kSubKeys <= p.M;
             if (!GRAD) {
-                if (fast) {
-                    // every entry visible: the scale is positive, so max(s) = sc2 * max(sa)
-                    float tm = sa[0];
-#pragma unroll
-                    for (int v = 1; v < 16; ++v) tm = fmaxf(tm, sa[v]);
-                    tm = max_halves(tm);
-                    const float mnew = fmaxf(m_run, tm * sc2);
-                    const float alpha = fast_exp2(m_run - mnew);
-                    float ls = 0.0f, ds = 0.0f, bm = 0.0f;
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const float e = fast_exp2(fmaf(sa[v], sc2, -mnew));
-                        ls += e;
-                        ds = fmaf(e, pa[v], ds);
-                        bm = fmaxf(bm, fabsf(pa[v]));
-                    }
-                    l64 = fma(l64, (double)alpha, (double)ls);
-                    d64 = fma(d64, (double)alpha, (double)ds);
-                    m_run = mnew;
-                    bmax = fmaxf(bmax, bm);
-                } else {
-                    // masked or ragged sub-tile; an entry with mask 0 gets exactly the
-                    // arithmetic of the path above
-                    float madd[16];
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int key = j0 + crow(v, g);
-                        float mv = 0.0f;
-                        if (!row_ok || key >= p.M) mv = neg_inf();
-                        else if (cls == kMaskMixed) mv = mask_value(p, mrow, i, key) * kLog2e;
-                        madd[v] = mv;
-                    }
-                    float tmax = neg_inf();
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        if (madd[v] != neg_inf()) tmax = fmaxf(tmax, fmaf(sa[v], sc2, madd[v]));
-                    tmax = max_halves(tmax);
-                    const float mnew = fmaxf(m_run, tmax);
-                    if (mnew != neg_inf()) {
-                        const float alpha = fast_exp2(m_run - mnew);
-                        float ls = 0.0f, ds = 0.0f, bm = 0.0f;
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            if (madd[v] == neg_inf()) continue;
-                            const float e = fast_exp2(fmaf(sa[v], sc2, madd[v] - mnew));
-                            ls += e;
-                            ds = fmaf(e, pa[v], ds);
-                            bm = fmaxf(bm, fabsf(pa[v]));
-                        }
-                        l64 = fma(l64, (double)alpha, (double)ls);
-                        d64 = fma(d64, (double)alpha, (double)ds);
-                        m_run = mnew;
-                        bmax = fmaxf(bmax, bm);
-                    }
-                }
+                w1_fold(p, w1, sa, pa, fast, cls, row_ok, mrow, i, j0, g, sc2);
             } else {
                 f16x8 bs[2];
                 if (fast) {
@@ -717,13 +750,7 @@ __global__ __launch_bounds__(kQThreads, 1) void qpass_kernel(Params p) {
             }
             if (sdec && s + 1 < s_end) sdecode(s + 1);
         }
-        if (!GRAD && active) {
-            const double lo = l64 + __shfl_xor(l64, 32);
-            const double dd = d64 + __shfl_xor(d64, 32);
-            const float bb = fmaxf(bmax, __shfl_xor(bmax, 32));
-            // the split's sums, carried in fp64, are rounded once to fp32 for the record
-            if (g == 0) p.part_rec[(int64_t)split * p.Hkv * rowsHK + ridx] = f32x4{m_run, (float)lo, (float)dd, bb};
-        }
+        if (!GRAD && active) w1_record(p, w1, split, ridx, g);
         return;
     }
 
@@ -864,6 +891,116 @@ __global__ __launch_bounds__(kImgThreads) void kvimage_kernel(Params p) {
 #pragma unroll
     for (int o = 16 * (int)threadIdx.x; o < L::kSlot; o += 16 * kImgThreads)
         *(uint4*)(dst + o) = *(const uint4*)(lds + o);
+}
+
+// ----------------------------------------------------------------------------- walk 1 by rows over the image
+
+// Walk 1 with the rows owned, reading K and V from the decoded image: a workgroup takes one KV
+// head, 8 row blocks of 32 rows (one per wave, its q and dO fragments in registers) and a key
+// range. Each 32-key slot is copied from the image into LDS by all 8 waves (an eighth each,
+// two slots ahead, three slots in turn), and every wave forms S and dP of its rows against it
+// and folds them into its rows' statistics. So all 8 waves issue products, two per SIMD, where
+// the query-side kernel's walk 1 leaves half of its waves to the tile copies. The per-row
+// arithmetic (w1_fold, w1_record) and the key ranges are those of the query-side kernel's
+// walk 1, so both give the same records.
+constexpr int kR1Waves = 8;
+constexpr int kR1Threads = kR1Waves * kWave;
+
+template <int D>
+struct R1Lds {
+    static constexpr int kSlot = 2 * kSubKeys * D * 2;   // K sub-tile, then V sub-tile (the image's slot)
+    static constexpr int kSlots = 3;
+    static constexpr int kBytes = kSlots * kSlot;
+};
+
+template <int D>
+__global__ __launch_bounds__(kR1Threads, 1) void walk1_rows_kernel(Params p) {
+    using L = R1Lds<D>;
+    constexpr int KS = D / 16;
+    constexpr int NI = L::kSlot / (kR1Waves * 1024);  // 1 KB copies per wave per slot
+    static_assert(NI >= 1 && L::kSlot == NI * kR1Waves * 1024, "a slot splits into 1 KB copies per wave");
+    __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int l32 = lane & 31, g = lane >> 5;
+    const int hk = blockIdx.x % p.Hkv;
+    const int rt = blockIdx.x / p.Hkv;
+    const int split = blockIdx.y;
+    const int rb = rt * kR1Waves + wave;
+    const bool active = rb < p.RB;
+    const int rowsHK = p.RB * 32;
+    const int r = rb * 32 + l32;
+    const int i = r / p.G, gh = r - (r / p.G) * p.G;
+    const int h = hk * p.G + gh;
+    const bool row_ok = active && r < p.R;
+    const int ridx = hk * rowsHK + r;
+    const int NS = (p.M + kSubKeys - 1) / kSubKeys;
+    const int s_begin = 2 * split * p.w1_tps;
+    const int s_end = min(NS, 2 * min(p.KT, (split + 1) * p.w1_tps));
+
+    f16x8 bq[KS], bd[KS];
+    if (active) {
+        const _Float16* rq = p.qr + ((int64_t)hk * rowsHK + r) * D;
+        const _Float16* rd = p.dr + ((int64_t)hk * rowsHK + r) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bq[ks] = *(const f16x8*)(rq + 16 * ks + 8 * g);
+            bd[ks] = *(const f16x8*)(rd + 16 * ks + 8 * g);
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) bq[ks][t] = bd[ks][t] = (_Float16)0.0f;
+    }
+    const bool has_mask = p.m_type != FA_BACK_NONE;
+    const char* mrow = (has_mask && row_ok)
+        ? p.mask + (int64_t)i * p.m_nb1 + (int64_t)(p.Hm == 1 ? 0 : h) * p.m_nb2 : nullptr;
+    // q rows carry the sign of the scale (prep), so the score scale is positive here
+    const float sc2 = fabsf(p.scale) * ldexpf(1.0f, -p.scal[0]) * kLog2e;
+    const bool full_rows = active && (rb + 1) * 32 <= p.R;
+    const RowWalk<D> rw = make_row_walk<D>(lane);
+
+    auto slot = [&](int s) { return lds + (s % L::kSlots) * L::kSlot; };
+    const unsigned char* img = p.kvimg + (int64_t)hk * p.img_ns * L::kSlot;
+    // the copies are hidden from the compiler (dma16_hidden): they stay in flight across the
+    // products, and the slot barrier waits for them by count
+    auto copy = [&](int t) {
+        const unsigned char* src = img + (int64_t)t * L::kSlot + wave * (NI * 1024);
+        const uint32_t dst = lds_addr(slot(t)) + (uint32_t)(wave * (NI * 1024));
+#pragma unroll
+        for (int it = 0; it < NI; ++it) dma16_hidden(src + it * 1024, 16u * lane, dst + it * 1024);
+    };
+
+    // All 8 waves form their products right after the slot barrier and fold them right after.
+    // (Measured and not kept: the two waves of a SIMD half a slot apart, and a slot's fold
+    // spread over the next slot's product steps; both slower.)
+    W1Row w1;
+    w1_init(w1);
+    wait_all_mem();   // the fragments are in registers before the first copy is queued
+    if (s_begin < s_end) copy(s_begin);
+    if (s_begin + 1 < s_end) copy(s_begin + 1);
+    for (int s = s_begin; s < s_end; ++s) {
+        // slot s has landed for every wave (the copies of s+1 stay in flight); the slot of s-1,
+        // which slot s+2 reuses, is read by no wave any more
+        if (s + 1 < s_end) dma_barrier<NI>();
+        else dma_barrier<0>();
+        if (s + 2 < s_end) copy(s + 2);
+        // a scalar load: waiting for it leaves the copies in flight
+        const int cls = active ? mask_class_s(p, hk, rb, s >> 1) : kMaskDead;
+        if (cls == kMaskDead) continue;
+        f32x16 sa, pa;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
+        mfma_prio_hi();
+        pair_rows<D, 2>(slot(s), bq, bd, sa, pa, rw);
+        mfma_prio_lo();
+        const int j0 = s * kSubKeys;
+        const bool fast = full_rows && cls == kMaskZero && j0 + kSubKeys <= p.M;
+        w1_fold(p, w1, sa, pa, fast, cls, row_ok, mrow, i, j0, g, sc2);
+    }
+    wait_all_mem();   // no copy is left in flight when the wave ends
+    if (active) w1_record(p, w1, split, ridx, g);
 }
 
 // ----------------------------------------------------------------------------- walk 1 by keys

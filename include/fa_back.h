@@ -99,18 +99,20 @@ extern "C" {
  * V before the rounding. For every row P sums to 1, so dP - delta, and with it dS, dQ, dK and
  * dV, are unchanged in exact arithmetic; only the rounding now falls on V - c. The delta
  * output is delta' + dO . c, with dO . c formed in fp64. V must be F32, F16 or BF16
- * (FA_BACK_EUNSUPPORTED for q8_0 / q4_0). Costs: one pass over 256 keys of V and one over dO,
+ * (FA_BACK_EUNSUPPORTED for the block types). Costs: one pass over 256 keys of V and one over dO,
  * and one subtraction per decoded V value. Bits other than the FA_BACK_FLAG_* below are
  * FA_BACK_EINVAL. */
 #define FA_BACK_FLAG_CENTER_V 1u
 
 /* FA_BACK_FLAG_WALK1_KEYS, FA_BACK_FLAG_WALK1_ROWS: which way the pass that forms each row's
  * LSE and delta walks the problem. Both give results that meet the same bar; they differ in
- * speed only. With neither bit the plan takes the key-owned walk when the cache is long next to
- * the rows (M >= 2 * G * N, G = H / Hkv) and the row-owned walk otherwise. WALK1_KEYS forces the
+ * speed only. With neither bit the plan takes the row-owned walk when the cache is decoded into
+ * the image (FA_BACK_FLAG_KV_IMAGE below), else the key-owned walk when the cache is long next
+ * to the rows (M >= 2 * G * N, G = H / Hkv), else the row-owned walk. WALK1_KEYS forces the
  * key-owned walk (each K/V tile decoded once per 256 keys, one statistics record per row and
- * 256-key tile), WALK1_ROWS the row-owned one (row tiles walk the keys, records per key-range
- * split). Setting both is FA_BACK_EINVAL. The choice changes the workspace size: pass the same
+ * 256-key tile), WALK1_ROWS the row-owned one (row tiles walk the keys, one record per row and
+ * key-range split, at most 32 splits; over the image, tiles of 256 rows copy each 32-key tile
+ * once). Setting both is FA_BACK_EINVAL. The choice changes the workspace size: pass the same
  * flags to fa_back_layout_query and fa_back_create. */
 #define FA_BACK_FLAG_WALK1_KEYS 2u
 #define FA_BACK_FLAG_WALK1_ROWS 4u
@@ -121,7 +123,7 @@ extern "C" {
  * scale * q_i . c, which the softmax does not see: P, dP, dS and dK are unchanged in exact
  * arithmetic, and so is dQ = scale * sum_j dS_ij (k_j - c), because sum_j dS_ij = 0 on every
  * row. The LSE output is the centred row's LSE plus scale * q_i . c, formed in fp64 (a fully
- * masked row keeps -inf). K must be F32, F16 or BF16 (FA_BACK_EUNSUPPORTED for q8_0 / q4_0).
+ * masked row keeps -inf). K must be F32, F16 or BF16 (FA_BACK_EUNSUPPORTED for the block types).
  * Costs: one pass over 256 keys of K and one over q, and one subtraction per decoded K value.
  * The fa_back_run_saved entry takes the uncentred LSE and removes the shift itself. */
 #define FA_BACK_FLAG_CENTER_K 8u

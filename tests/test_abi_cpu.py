@@ -220,15 +220,25 @@ def _ws(p, flags):
 
 def test_walk1_flag_sets_the_workspace():
     """The key-owned walk keeps one record per row and 256-key tile, the row-owned walk one per
-    key-range split: the flags pick the walk (and with it the workspace); without a flag a long
-    cache (M >= 2 G N) takes the key-owned walk and a short one the row-owned walk."""
+    key-range split, of which the workspace holds the most it may take: min(32, 64-key tiles).
+    The flags pick the walk (and with it the workspace); without a flag the row-owned walk is
+    taken when the cache is decoded into the image, else the key-owned walk for a long cache
+    (M >= 2 G N) and the row-owned walk for a short one."""
     long_cache = fa_inputs.make_custom("long", D=64, H=24, Hkv=4, N=256, M=8192, mask="none")
     short = fa_inputs.make_custom("short", D=64, H=4, Hkv=1, N=64, M=300, mask="none")
     for p in (long_cache, short):
         keys, rows = _ws(p, B.FLAG_WALK1_KEYS), _ws(p, B.FLAG_WALK1_ROWS)
         assert keys.out_bytes == rows.out_bytes and keys.off_delta == rows.off_delta
-        assert keys.workspace_bytes != rows.workspace_bytes
-    assert _ws(long_cache, 0).workspace_bytes == _ws(long_cache, B.FLAG_WALK1_KEYS).workspace_bytes
+        rows_total = p.Hkv * (-(-(p.H // p.Hkv) * p.N // 32)) * 32
+        rec_keys = -(-p.M // 256)
+        rec_rows = min(32, -(-p.M // 64))
+        want = (rec_keys - rec_rows) * 16 * rows_total
+        assert abs((keys.workspace_bytes - rows.workspace_bytes) - want) < 256
+    # long_cache has 12 row tiles of 128 rows per KV head, so the image by default
+    assert _ws(long_cache, 0).workspace_bytes == _ws(long_cache, B.FLAG_WALK1_ROWS).workspace_bytes
+    inline = B.FLAG_KV_INLINE
+    assert (_ws(long_cache, inline).workspace_bytes ==
+            _ws(long_cache, inline | B.FLAG_WALK1_KEYS).workspace_bytes)
     assert _ws(short, 0).workspace_bytes == _ws(short, B.FLAG_WALK1_ROWS).workspace_bytes
 
 
@@ -241,7 +251,8 @@ def test_kv_image_flags_and_workspace():
     _expect(B.EINVAL, lambda d: setattr(d, "flags", B.FLAG_KV_IMAGE | B.FLAG_KV_INLINE))
     for name, default_image in (("c3", True), ("c1", False)):
         p = fa_inputs.make(name)
-        img, inl, dflt = _ws(p, B.FLAG_KV_IMAGE), _ws(p, B.FLAG_KV_INLINE), _ws(p, 0)
+        rows = B.FLAG_WALK1_ROWS   # the walk-1 direction held fixed: the image alone differs
+        img, inl, dflt = _ws(p, B.FLAG_KV_IMAGE | rows), _ws(p, B.FLAG_KV_INLINE | rows), _ws(p, rows)
         image_bytes = p.Hkv * ((p.M + 31) // 32) * 128 * p.D
         assert img.workspace_bytes - inl.workspace_bytes >= image_bytes
         assert img.workspace_bytes - inl.workspace_bytes < image_bytes + 256
