@@ -897,8 +897,8 @@ __global__ __launch_bounds__(kImgThreads) void kvimage_kernel(Params p) {
 
 // Walk 1 with the rows owned, reading K and V from the decoded image: a workgroup takes one KV
 // head, 8 row blocks of 32 rows (one per wave, its q and dO fragments in registers) and a key
-// range. Each 32-key slot is copied from the image into LDS by all 8 waves (an eighth each,
-// two slots ahead, three slots in turn), and every wave forms S and dP of its rows against it
+// range. The image slots (32 keys each) are copied into LDS two at a time by all 8 waves (an
+// eighth each, one pair ahead), and every wave forms S and dP of its rows against each slot
 // and folds them into its rows' statistics. So all 8 waves issue products, two per SIMD, where
 // the query-side kernel's walk 1 leaves half of its waves to the tile copies. The per-row
 // arithmetic (w1_fold, w1_record) and the key ranges are those of the query-side kernel's
@@ -909,8 +909,12 @@ constexpr int kR1Threads = kR1Waves * kWave;
 template <int D>
 struct R1Lds {
     static constexpr int kSlot = 2 * kSubKeys * D * 2;   // K sub-tile, then V sub-tile (the image's slot)
-    static constexpr int kSlots = 3;
-    static constexpr int kBytes = kSlots * kSlot;
+    // two image slots per step (one barrier each; against one per step with three steps held:
+    // 3.30 against 3.44 ms at N2048/M75520/D256), the next step copied during this one
+    static constexpr int kSub = 2;                       // image slots per step
+    static constexpr int kSteps = 2;                     // steps held in LDS
+    static constexpr int kAhead = kSteps - 1;            // steps copied ahead of the one in use
+    static constexpr int kBytes = kSteps * kSub * kSlot;
 };
 
 template <int D>
@@ -961,43 +965,59 @@ __global__ __launch_bounds__(kR1Threads, 1) void walk1_rows_kernel(Params p) {
     const bool full_rows = active && (rb + 1) * 32 <= p.R;
     const RowWalk<D> rw = make_row_walk<D>(lane);
 
-    auto slot = [&](int s) { return lds + (s % L::kSlots) * L::kSlot; };
+    // step t covers image slots s_begin + kSub*t .. + kSub - 1 (those below s_end)
+    const int nsteps = (s_end - s_begin + L::kSub - 1) / L::kSub;
+    auto ring = [&](int t) { return lds + (t % L::kSteps) * (L::kSub * L::kSlot); };
     const unsigned char* img = p.kvimg + (int64_t)hk * p.img_ns * L::kSlot;
     // the copies are hidden from the compiler (dma16_hidden): they stay in flight across the
-    // products, and the slot barrier waits for them by count
+    // products, and the step barrier waits for them by count. Every step copies kSub slots, so
+    // that the counts are the same for every step: past s_end the last slot is copied again.
     auto copy = [&](int t) {
-        const unsigned char* src = img + (int64_t)t * L::kSlot + wave * (NI * 1024);
-        const uint32_t dst = lds_addr(slot(t)) + (uint32_t)(wave * (NI * 1024));
 #pragma unroll
-        for (int it = 0; it < NI; ++it) dma16_hidden(src + it * 1024, 16u * lane, dst + it * 1024);
+        for (int u = 0; u < L::kSub; ++u) {
+            const int sl = min(s_begin + L::kSub * t + u, s_end - 1);
+            const unsigned char* src = img + (int64_t)sl * L::kSlot + wave * (NI * 1024);
+            const uint32_t dst = lds_addr(ring(t) + u * L::kSlot) + (uint32_t)(wave * (NI * 1024));
+#pragma unroll
+            for (int it = 0; it < NI; ++it) dma16_hidden(src + it * 1024, 16u * lane, dst + it * 1024);
+        }
     };
+    constexpr int NS1 = L::kSub * NI;                 // copies per wave per step
 
-    // All 8 waves form their products right after the slot barrier and fold them right after.
+    // All 8 waves form their products right after the step barrier and fold them right after.
     // (Measured and not kept: the two waves of a SIMD half a slot apart, and a slot's fold
     // spread over the next slot's product steps; both slower.)
     W1Row w1;
     w1_init(w1);
     wait_all_mem();   // the fragments are in registers before the first copy is queued
-    if (s_begin < s_end) copy(s_begin);
-    if (s_begin + 1 < s_end) copy(s_begin + 1);
-    for (int s = s_begin; s < s_end; ++s) {
-        // slot s has landed for every wave (the copies of s+1 stay in flight); the slot of s-1,
-        // which slot s+2 reuses, is read by no wave any more
-        if (s + 1 < s_end) dma_barrier<NI>();
-        else dma_barrier<0>();
-        if (s + 2 < s_end) copy(s + 2);
-        // a scalar load: waiting for it leaves the copies in flight
-        const int cls = active ? mask_class_s(p, hk, rb, s >> 1) : kMaskDead;
-        if (cls == kMaskDead) continue;
-        f32x16 sa, pa;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
-        mfma_prio_hi();
-        pair_rows<D, 2>(slot(s), bq, bd, sa, pa, rw);
-        mfma_prio_lo();
-        const int j0 = s * kSubKeys;
-        const bool fast = full_rows && cls == kMaskZero && j0 + kSubKeys <= p.M;
-        w1_fold(p, w1, sa, pa, fast, cls, row_ok, mrow, i, j0, g, sc2);
+    for (int t = 0; t < L::kAhead; ++t)
+        if (t < nsteps) copy(t);
+    for (int t = 0; t < nsteps; ++t) {
+        // step t has landed for every wave (the copies of later steps stay in flight); the
+        // slots of step t-1, which step t+kAhead reuses, are read by no wave any more
+        const int later = min(L::kAhead - 1, nsteps - 1 - t);
+        if (later >= 2) dma_barrier<(L::kAhead >= 3 ? 2 : 0) * NS1>();
+        else if (later == 1) dma_barrier<(L::kAhead >= 2 ? 1 : 0) * NS1>();
+        else dma_barrier<0>();
+        if (t + L::kAhead < nsteps) copy(t + L::kAhead);
+#pragma unroll
+        for (int u = 0; u < L::kSub; ++u) {
+            const int s = s_begin + L::kSub * t + u;
+            if (s >= s_end) break;
+            // a scalar load: waiting for it leaves the copies in flight
+            const int cls = active ? mask_class_s(p, hk, rb, s >> 1) : kMaskDead;
+            if (cls == kMaskDead) continue;
+            f32x16 sa, pa;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sa[v] = pa[v] = 0.0f;
+            mfma_prio_hi();
+            pair_rows<D, 2>(ring(t) + u * L::kSlot, bq, bd, sa, pa, rw);
+            mfma_prio_lo();
+            const int j0 = s * kSubKeys;
+            const bool fast = full_rows && cls == kMaskZero && j0 + kSubKeys <= p.M;
+            w1_fold(p, w1, sa, pa, fast, cls, row_ok, mrow, i, j0, g, sc2);
+        }
     }
     wait_all_mem();   // no copy is left in flight when the wave ends
     if (active) w1_record(p, w1, split, ridx, g);
