@@ -38,8 +38,9 @@ PEAK_HBM_GBS = 8000.0
 
 # matrix-product work per visible (row, key, head) triple, per phase (D = Dv)
 PHASE_FLOPS_PER_PAIR_PER_D = {"walk1": 4, "walk2": 6, "kvpass": 8}
-KERNEL_NAMES = {"walk1": "qpass_kernel<D, false>", "walk2": "qpass_kernel<D, true>",
-                "kvpass": "kvpass_kernel<D>"}
+# the kernels a phase may run (the plan picks one), as name prefixes of their instantiations
+KERNEL_PREFIXES = {"walk1": ("walk1_rows_kernel<D>", "walk1_keys_kernel<D>", "qpass_kernel<D, false"),
+                   "walk2": ("qpass_kernel<D, true",), "kvpass": ("kvpass_kernel<D>",)}
 
 
 def phase_bytes(p, phase):
@@ -76,19 +77,22 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE summary, or
-    None when that summary was taken on other kernel sources (or is absent)."""
+def measured_traffic(prefixes, workload):
+    """(kernel name, HBM bytes per launch) of the kernel whose name starts with one of `prefixes`
+    in the committed FETCH_SIZE / WRITE_SIZE summary of `workload`, or (None, None) when that
+    summary was taken on other kernel sources (or is absent)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, None
     if rec.get("source_sha256") != kernel_source_hash():
-        return None
-    k = rec.get("kernels", {}).get(workload, {}).get(kernel)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+        return None, None
+    for name, k in rec.get("kernels", {}).get(workload, {}).items():
+        if name.startswith(prefixes):
+            return name, k.get("hbm_bytes_per_launch")
+    return None, None
 
 
 def copy_calibration(mib: int, reps: int = 3):
@@ -235,10 +239,13 @@ def main():
     log("phase ms: " + " ".join(f"{k}={v:.3f}" for k, v in mean_phase.items()))
 
     dom = max(PHASE_FLOPS_PER_PAIR_PER_D, key=lambda n: mean_phase[n])
-    kname = KERNEL_NAMES[dom].replace("D", str(p.D), 1)
+    prefixes = tuple(k.replace("D", str(p.D), 1) for k in KERNEL_PREFIXES[dom])
     nbytes = fa_inputs.min_bytes(p)
     intensity = flops["full"] / nbytes["total"]
-    traffic = (measured_traffic(kname, args.workload) if args.mask == "stored" and not args.saved else None)
+    kname, traffic = (measured_traffic(prefixes, args.workload) if args.mask == "stored" and not args.saved
+                      else (None, None))
+    if kname is None:
+        kname = " | ".join(prefixes)   # the phase's kernel, as far as the record can tell
     if intensity >= PEAK_MFMA_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
         dom_flops = PHASE_FLOPS_PER_PAIR_PER_D[dom] * p.D * flops["visible"]
         achieved = dom_flops / (mean_phase[dom] * 1e-3) / 1e12
