@@ -101,6 +101,10 @@ def compare(got, ref, keys=KEYS, tol=TOL, local=True):
 
 
 def walk1(p, mode):
-    """The same problem with the LSE/delta walk forced by its descriptor flag ('rows' or 'keys')."""
-    bit = {"keys": fab.fa_back.FLAG_WALK1_KEYS, "rows": fab.fa_back.FLAG_WALK1_ROWS}[mode]
-    return dataclasses.replace(p, flags=(p.flags & ~(fab.fa_back.FLAG_WALK1_KEYS | fab.fa_back.FLAG_WALK1_ROWS)) | bit)
+    """The same problem with the LSE/delta walk forced by its descriptor flag: 'rows', 'keys', or
+    'rows_image' (rows, with the cache decoded into the image: the row walk's own kernel)."""
+    F = fab.fa_back
+    bit = {"keys": F.FLAG_WALK1_KEYS, "rows": F.FLAG_WALK1_ROWS,
+           "rows_image": F.FLAG_WALK1_ROWS | F.FLAG_KV_IMAGE}[mode]
+    clear = F.FLAG_WALK1_KEYS | F.FLAG_WALK1_ROWS | (F.FLAG_KV_IMAGE | F.FLAG_KV_INLINE if mode == "rows_image" else 0)
+    return dataclasses.replace(p, flags=(p.flags & ~clear) | bit)

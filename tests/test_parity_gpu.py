@@ -188,7 +188,8 @@ def test_gqa_equals_replicated_heads(mode):
 
 
 # Walk 1 runs by row tiles or by key tiles (chosen from the shape unless a descriptor flag picks
-# one). Both must meet the bar on the same inputs.
+# one), and by row tiles in a kernel of its own when the cache is decoded into the image. Each
+# must meet the bar on the same inputs.
 WALK1_CASES = ["c0", "c1_causal", "ragged_d128_headmask", "ragged_d64_q8", "ragged_d256_f32mask",
                "all_masked", "single_key", "dead_row_blocks", "kv_live_middle_blocks"]
 
@@ -199,7 +200,7 @@ def _walk1_problem(name):
     return fa_inputs.make_custom(**next(c for c in RAGGED if c["name"] == name))
 
 
-@pytest.mark.parametrize("mode", ["rows", "keys"])
+@pytest.mark.parametrize("mode", ["rows", "keys", "rows_image"])
 @pytest.mark.parametrize("name", WALK1_CASES)
 def test_walk1_variants(name, mode):
     say(f"[walk1 {mode}]")
@@ -223,7 +224,7 @@ def _implicit_problem(name, cfg):
     return fa_inputs.make(name) if cfg is None else fa_inputs.make_custom(name=name, **cfg)
 
 
-@pytest.mark.parametrize("mode", ["rows", "keys"])
+@pytest.mark.parametrize("mode", ["rows", "keys", "rows_image"])
 @pytest.mark.parametrize("name,cfg", IMPLICIT_CASES, ids=[c[0] for c in IMPLICIT_CASES])
 def test_implicit_causal_tail_bitwise(name, cfg, mode):
     p = walk1(_implicit_problem(name, cfg), mode)
