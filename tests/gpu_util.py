@@ -44,8 +44,11 @@ def run_gpu(p, device="cuda:0", poison=True, fill=0xFF):
 # * m_rms. tol is LOCAL_TOL_VEC for vector rows and LOCAL_TOL_SCA for scalars. A row's fp16
 # operand rounding gives it an error of a few 1e-4 of its terms; a wrong tile gives errors of
 # order 1. A row whose gradient cancels (e.g. one that sees three keys, whose dS sums to 0) keeps
-# an absolute error set by its terms, not by its result: hence the floor.
-LOCAL_TOL_VEC, LOCAL_TOL_SCA, LOCAL_FLOOR = 1e-2, 5e-2, 1e-1
+# an absolute error set by its terms, not by its result: hence the floor. A key row that one
+# query row alone reaches (G * N = 1) is a single term dS_j q, and dS_j = P_j (dP_j - delta)
+# cancels inside: with fp16 operands (emulated on the CPU) one such row of a D = 256 case comes
+# to 1.2e-2 of the floored bound. So 2e-2, which still leaves a wrong tile 50 times over.
+LOCAL_TOL_VEC, LOCAL_TOL_SCA, LOCAL_FLOOR = 2e-2, 5e-2, 1e-1
 VECTOR_KEYS = ("dq", "dk", "dv")
 
 

@@ -1,0 +1,56 @@
+"""A seeded sweep of random problems against the float64 oracle, through the C ABI (GPU only).
+
+Each case draws a head size (64, 128, 256), a GQA shape, ragged N and M (so tiles of every
+kind end part-full), K and V types from all eight, a mask (none, stored causal-tail, stored
+random with one or per-head mask rows, or the implicit causal tail) and one of the walk-1 /
+cache-image plans, and must meet the parity bar of every fixed case (tests.gpu_util.compare).
+Sizes are capped so that the oracle finishes each case in a few seconds."""
+import numpy as np
+import pytest
+
+import fa_inputs
+from flash_attention_backward_amd import fa_back as B
+from oracle import fa_back_oracle as O
+from tests.gpu_util import compare, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+KV_TYPES = ["f32", "f16", "bf16", "q8_0", "q4_0", "q4_1", "q5_0", "q5_1"]
+PLANS = [0, B.FLAG_WALK1_ROWS, B.FLAG_WALK1_KEYS, B.FLAG_WALK1_ROWS | B.FLAG_KV_IMAGE,
+         B.FLAG_WALK1_KEYS | B.FLAG_KV_IMAGE, B.FLAG_WALK1_ROWS | B.FLAG_KV_INLINE]
+
+
+def _cases(n=96, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        D = int(rng.choice([64, 128, 256]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        H = Hkv * int(rng.choice([1, 2, 3, 6]))
+        N = int(rng.integers(1, 600))
+        cap = max(1, int(6e8 // (H * D * N)))            # oracle work ~ N * M * H * D
+        M = int(min(rng.integers(1, 5000), cap))
+        mask = str(rng.choice(["none", "tail", "random", "implicit"]))
+        Hm = int(rng.choice([1, H])) if mask == "random" else 1
+        kt, vt = (str(x) for x in rng.choice(KV_TYPES, 2))
+        out.append(dict(name=f"sweep{c}", D=D, H=H, Hkv=Hkv, N=N, M=M, Hm=Hm, k_type=kt, v_type=vt,
+                        mask=mask, flags=int(PLANS[c % len(PLANS)]), seed=100 + c))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=[c["name"] for c in CASES])
+def test_sweep_against_oracle(cfg):
+    cfg = dict(cfg)
+    implicit = cfg["mask"] == "implicit"
+    if implicit:
+        cfg["mask"] = "tail"
+    p = fa_inputs.make_custom(**cfg)
+    if implicit:
+        p = fa_inputs.implicit_causal(p)
+    got, _, _ = run_gpu(p)
+    ref = O.run_problem(p)
+    errs = compare(got, ref)
+    say("   nmse " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
