@@ -4,6 +4,8 @@ Each case draws a head size (64, 128, 256), a GQA shape, ragged N and M (so tile
 kind end part-full), K and V types from all eight, a mask (none, stored causal-tail, stored
 random with one or per-head mask rows, or the implicit causal tail) and one of the walk-1 /
 cache-image plans, and must meet the parity bar of every fixed case (tests.gpu_util.compare).
+A second set takes F32 / F16 / BF16 caches whose K or V values share a large common part,
+centred by the descriptor flags, with dO rows spread over up to four decades.
 Sizes are capped so that the oracle finishes each case in a few seconds."""
 import numpy as np
 import pytest
@@ -38,7 +40,31 @@ def _cases(n=96, seed=2024):
     return out
 
 
-CASES = _cases()
+def _cases_centred(n=32, seed=77):
+    """Row-type caches whose values share a large common part (near-constant K or V), centred by
+    the descriptor flags, with dO rows over several decades of magnitude."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        D = int(rng.choice([64, 128, 256]))
+        Hkv = int(rng.choice([1, 2]))
+        H = Hkv * int(rng.choice([1, 3, 6]))
+        N = int(rng.integers(1, 400))
+        cap = max(1, int(4e8 // (H * D * N)))
+        M = int(min(rng.integers(1, 3000), cap))
+        kt, vt = (str(x) for x in rng.choice(["f32", "f16", "bf16"], 2))
+        near_k, near_v = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+        flags = (B.FLAG_CENTER_K if near_k else 0) | (B.FLAG_CENTER_V if near_v else 0)
+        flags |= int(PLANS[c % len(PLANS)])
+        out.append(dict(name=f"centred{c}", D=D, H=H, Hkv=Hkv, N=N, M=M, k_type=kt, v_type=vt,
+                        mask=str(rng.choice(["none", "tail", "implicit"])), flags=flags, seed=300 + c,
+                        k_offset=2.0 if near_k else 0.0, k_spread=0.02 if near_k else 1.0,
+                        v_offset=1.5 if near_v else 0.0, v_spread=0.02 if near_v else 1.0,
+                        d_decades=int(rng.integers(0, 4))))
+    return out
+
+
+CASES = _cases() + _cases_centred()
 
 
 @pytest.mark.parametrize("cfg", CASES, ids=[c["name"] for c in CASES])
