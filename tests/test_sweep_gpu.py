@@ -14,6 +14,7 @@ import fa_inputs
 from flash_attention_backward_amd import fa_back as B
 from oracle import fa_back_oracle as O
 from tests.gpu_util import compare, run_gpu, say
+from tests.test_saved_gpu import _run_saved
 
 pytestmark = pytest.mark.gpu
 
@@ -67,16 +68,33 @@ def _cases_centred(n=32, seed=77):
 CASES = _cases() + _cases_centred()
 
 
-@pytest.mark.parametrize("cfg", CASES, ids=[c["name"] for c in CASES])
-def test_sweep_against_oracle(cfg):
+def _problem(cfg):
     cfg = dict(cfg)
     implicit = cfg["mask"] == "implicit"
     if implicit:
         cfg["mask"] = "tail"
     p = fa_inputs.make_custom(**cfg)
-    if implicit:
-        p = fa_inputs.implicit_causal(p)
+    return fa_inputs.implicit_causal(p) if implicit else p
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=[c["name"] for c in CASES])
+def test_sweep_against_oracle(cfg):
+    p = _problem(cfg)
     got, _, _ = run_gpu(p)
+    ref = O.run_problem(p)
+    errs = compare(got, ref)
+    say("   nmse " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+# every fourth case of the first set through the saved-statistics entry (the forward's LSE and
+# O from the oracle)
+SAVED = CASES[:96:4]
+
+
+@pytest.mark.parametrize("cfg", SAVED, ids=[c["name"] + "_saved" for c in SAVED])
+def test_sweep_saved_entry(cfg):
+    p = _problem(cfg)
+    got = _run_saved(p)[0]
     ref = O.run_problem(p)
     errs = compare(got, ref)
     say("   nmse " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
