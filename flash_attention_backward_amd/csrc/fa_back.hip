@@ -43,7 +43,10 @@ int tail_split(int T, int cus, int* split) {
 }
 
 constexpr uint32_t kKnownFlags = FA_BACK_FLAG_CENTER_V | FA_BACK_FLAG_WALK1_KEYS | FA_BACK_FLAG_WALK1_ROWS |
-                                  FA_BACK_FLAG_CENTER_K | FA_BACK_FLAG_KV_IMAGE | FA_BACK_FLAG_KV_INLINE;
+                                  FA_BACK_FLAG_CENTER_K | FA_BACK_FLAG_KV_IMAGE | FA_BACK_FLAG_KV_INLINE |
+                                  FA_BACK_FLAG_DS_STORE | FA_BACK_FLAG_DS_RECOMPUTE;
+constexpr int kMaxDqSplits = 8;     // key-range splits of the dQ pass from stored dS, at most
+constexpr uint64_t kMaxDsBytes = 16ull << 30;   // stored dS the plan takes without a flag, at most
 
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
@@ -80,6 +83,9 @@ struct Geometry {
     int nparts_ws;         // walk-1 records per row the workspace holds (any planned CU count)
     bool img;              // the query-side walks copy K/V tiles from the decoded image
     int img_ns;            // its 32-key sub-tiles per KV head
+    bool dss;              // dQ from the dS the key side stores (else walk 2 recomputes it)
+    int ds_kb;             // 32-key blocks per row block and head in the stored dS
+    int dq_splits_ws;      // dQ split partials the workspace holds
     int npart, nbound;
     fa_back_layout layout;
     // workspace offsets (bytes)
@@ -88,6 +94,7 @@ struct Geometry {
     uint64_t ws_vcen;      // [Hkv][D] V centre (FA_BACK_FLAG_CENTER_V only)
     uint64_t ws_kcen;      // [Hkv][D] K centre (FA_BACK_FLAG_CENTER_K only)
     uint64_t ws_img;       // [Hkv][img_ns][32-key slot] decoded K/V tiles (img only)
+    uint64_t ws_ds;        // [Hkv][RB][ds_kb][2048 bytes] stored dS tiles (dss only)
 };
 
 bool tensor_nonneg(const fa_back_tensor& t) {
@@ -119,6 +126,8 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
     if (d->flags & ~kKnownFlags) return FA_BACK_EINVAL;
     if ((d->flags & FA_BACK_FLAG_WALK1_KEYS) && (d->flags & FA_BACK_FLAG_WALK1_ROWS)) return FA_BACK_EINVAL;
     if ((d->flags & FA_BACK_FLAG_KV_IMAGE) && (d->flags & FA_BACK_FLAG_KV_INLINE)) return FA_BACK_EINVAL;
+    if ((d->flags & FA_BACK_FLAG_DS_STORE) && (d->flags & FA_BACK_FLAG_DS_RECOMPUTE)) return FA_BACK_EINVAL;
+    if ((d->flags & FA_BACK_FLAG_DS_STORE) && (d->flags & FA_BACK_FLAG_KV_INLINE)) return FA_BACK_EINVAL;
     if ((d->flags & FA_BACK_FLAG_CENTER_V) && is_blk(v.type)) return FA_BACK_EUNSUPPORTED;
     if ((d->flags & FA_BACK_FLAG_CENTER_K) && is_blk(k.type)) return FA_BACK_EUNSUPPORTED;
     if (!tensor_nonneg(q) || !tensor_nonneg(k) || !tensor_nonneg(v) || !tensor_nonneg(dd) ||
@@ -205,8 +214,33 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
         bool img = g->RT >= 4;
         if (d->flags & FA_BACK_FLAG_KV_IMAGE) img = true;
         if (d->flags & FA_BACK_FLAG_KV_INLINE) img = false;
+        // dQ from stored dS (it reads K from the image): by default whenever the image is used
+        // and the tiles fit kMaxDsBytes; a flag forces either way
+        const uint64_t ds_bytes = (uint64_t)Hkv * g->RB * (4ull * g->KVT) * 2048ull;
+        bool dss = img && ds_bytes <= kMaxDsBytes;
+        if (d->flags & FA_BACK_FLAG_DS_STORE) dss = true;
+        if (d->flags & FA_BACK_FLAG_DS_RECOMPUTE) dss = false;
+        g->dss = dss && g->M > 0 && g->R > 0;
+        if (g->dss) img = true;
         g->img = img && g->M > 0 && g->R > 0;
         g->img_ns = (g->M + kSubKeys - 1) / kSubKeys;
+        g->ds_kb = 4 * g->KVT;
+        g->dq_splits_ws = g->splits;
+        if (g->dss) {
+            // the dQ pass's own key-range splits, for its workgroups of 256 rows: minimise rounds
+            // of `cus` workgroups x (64-key tiles per split + 1), at most kMaxDqSplits
+            const int kt = std::max(g->KT, 1);
+            const int wgs = (g->RB + kQsWaves - 1) / kQsWaves * g->Hkv;
+            const int sp_max = std::min(kMaxDqSplits, kt);
+            double best_cost = 1e300;
+            for (int sp = 1; sp <= sp_max; ++sp) {
+                const int tps = (kt + sp - 1) / sp;
+                const int n = (kt + tps - 1) / tps;
+                const double cost = std::ceil((double)wgs * n / (double)cus) * (tps + 1.0);
+                if (cost < best_cost - 1e-9) { best_cost = cost; g->splits = n; g->tiles_per_split = tps; }
+            }
+            g->dq_splits_ws = sp_max;   // the workspace does not depend on the CU count
+        }
     }
     // walk 1 by key tiles when the cache is long next to the rows and not in the image (each
     // K/V tile is then decoded once per 256 keys instead of once per 128 rows); over the image
@@ -280,7 +314,7 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
     g->ws_dlt = take(4ull * total_rows);
     g->ws_rks = take(4ull * total_rows);
     g->ws_bound = take(4ull * g->nbound * g->Hkv);
-    g->ws_dqp = take(g->splits > 1 ? 4ull * g->splits * total_rows * D : 0);
+    g->ws_dqp = take(g->dq_splits_ws > 1 ? 4ull * g->dq_splits_ws * total_rows * D : 0);
     // mask classes: stored masks only (the causal-tail classes are computed where needed)
     const bool stored_mask = has_mask && d->mask.type != FA_BACK_CAUSAL_TAIL;
     g->ws_mcls = take(stored_mask ? (uint64_t)(Hm == 1 ? 1 : g->Hkv) * g->RB * g->KT : 0);
@@ -289,6 +323,7 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
     g->ws_vcen = take((d->flags & FA_BACK_FLAG_CENTER_V) ? 4ull * g->Hkv * D : 0);
     g->ws_kcen = take((d->flags & FA_BACK_FLAG_CENTER_K) ? 4ull * g->Hkv * D : 0);
     g->ws_img = take(g->img ? (uint64_t)g->Hkv * g->img_ns * (uint64_t)(4 * kSubKeys * D) : 0);
+    g->ws_ds = take(g->dss ? (uint64_t)g->Hkv * g->RB * g->ds_kb * 2048ull : 0);
     L.workspace_bytes = std::max<uint64_t>(o, kAlign);
     return FA_BACK_OK;
 }
@@ -298,7 +333,7 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
 template <int D>
 int max_lds_bytes_d() {
     return std::max(std::max(std::max(QLds<D>::kBytes, QLds<D, true>::kBytes), W1Lds<D>::kBytes),
-                    std::max(KVLds<D>::kBytes, R1Lds<D>::kBytes));
+                    std::max(std::max(KVLds<D>::kBytes, R1Lds<D>::kBytes), QsLds<D>::kBytes));
 }
 int max_lds_bytes(int D) {
     return D == 64 ? max_lds_bytes_d<64>() : D == 128 ? max_lds_bytes_d<128>() : max_lds_bytes_d<256>();
@@ -307,10 +342,13 @@ int max_lds_bytes(int D) {
 // Records an event after each phase when `ev` is non-NULL (ev[0] is recorded by the caller
 // before the first phase). Phases: absmax, prep, walk 1, merge, walk 2, dQ reduce, key side.
 struct PhaseMarks {
-    hipEvent_t* ev;
+    hipEvent_t* ev;        // 2 per phase: its start and its end
     hipStream_t st;
-    void mark(int phase) const {
-        if (ev) (void)hipEventRecord(ev[phase + 1], st);
+    void begin(int phase) const {
+        if (ev) (void)hipEventRecord(ev[2 * phase], st);
+    }
+    void end(int phase) const {
+        if (ev) (void)hipEventRecord(ev[2 * phase + 1], st);
     }
 };
 
@@ -356,6 +394,7 @@ template <int D>
 int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& pm) {
     if (g.N == 0 || g.M == 0) {
         // degenerate: zero dK, dV (N == 0) or every row fully masked (M == 0)
+        pm.begin(0);
         const int64_t nk = (int64_t)g.D * g.M * g.Hkv;
         if (nk) hipLaunchKernelGGL(fill_kernel, dim3(256), dim3(kThreads), 0, st, P.dk, nk, 0.0f);
         if (nk) hipLaunchKernelGGL(fill_kernel, dim3(256), dim3(kThreads), 0, st, P.dv, nk, 0.0f);
@@ -364,13 +403,19 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
         const int64_t nr = (int64_t)g.N * g.H;
         if (nr) hipLaunchKernelGGL(fill_kernel, dim3(64), dim3(kThreads), 0, st, P.lse, nr, -INFINITY);
         if (nr) hipLaunchKernelGGL(fill_kernel, dim3(64), dim3(kThreads), 0, st, P.delta, nr, 0.0f);
-        for (int ph = 0; ph < FA_BACK_NUM_PHASES; ++ph) pm.mark(ph);
+        pm.end(0);
+        for (int ph = 1; ph < FA_BACK_NUM_PHASES; ++ph) {
+            pm.begin(ph);
+            pm.end(ph);
+        }
         return hipGetLastError() == hipSuccess ? FA_BACK_OK : FA_BACK_EHIP;
     }
+    pm.begin(0);
     hipLaunchKernelGGL(absmax_kernel, dim3(g.npart), dim3(kThreads), 0, st, P);
     if (P.vcen) hipLaunchKernelGGL(centre_kernel<false>, dim3(g.Hkv), dim3(kThreads), 0, st, P);
     if (P.kcen) hipLaunchKernelGGL(centre_kernel<true>, dim3(g.Hkv), dim3(kThreads), 0, st, P);
-    pm.mark(0);
+    pm.end(0);
+    pm.begin(1);
     hipLaunchKernelGGL(prep_kernel<D>, dim3(g.Hkv * g.RB), dim3(kThreads), 0, st, P);
     if (g.Hm > 0 && P.m_type != FA_BACK_CAUSAL_TAIL) {
         const dim3 grid((g.Hm == 1 ? 1 : g.Hkv) * g.RB, (g.KT + kClassTilesPerBlock - 1) / kClassTilesPerBlock);
@@ -387,19 +432,23 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
         }
     }
     if (P.kvimg) launch_kvimage<D>(g, P, st);
-    pm.mark(1);
+    pm.end(1);
     if (P.lse_in) {
         // forward-saved LSE and O: the row statistics without walk 1 and the merge
+        pm.begin(2);
         hipLaunchKernelGGL(vmax_kernel, dim3(kVmaxBlocks), dim3(kThreads), 0, st, P);
-        pm.mark(2);
+        pm.end(2);
+        pm.begin(3);
         hipLaunchKernelGGL(saved_rows_kernel, dim3(g.nbound, g.Hkv), dim3(kThreads), 0, st, P);
-        pm.mark(3);
+        pm.end(3);
     } else {
+        pm.begin(2);
         if (g.w1keys)
             hipLaunchKernelGGL(walk1_keys_kernel<D>, dim3(g.KT1 * g.Hkv, g.RS1), dim3(kW1Threads), 0, st, P);
         else
             launch_qpass<D, false>(g, P, st);
-        pm.mark(2);
+        pm.end(2);
+        pm.begin(3);
         hipLaunchKernelGGL(merge_kernel, dim3(g.nbound, g.Hkv), dim3(kThreads), 0, st, P);
         if (P.vcen || P.kcen) {
             // the merge wrote delta - dO . c (V centred) and lse - scale q . c (K centred)
@@ -407,23 +456,43 @@ int launch_all(const Geometry& g, Params& P, hipStream_t st, const PhaseMarks& p
             const int blocks = (int)std::min<int64_t>(4096, (rows + kWaves - 1) / kWaves);
             hipLaunchKernelGGL(centre_out_kernel, dim3(blocks), dim3(kThreads), 0, st, P);
         }
-        pm.mark(3);
+        pm.end(3);
     }
-    launch_qpass<D, true>(g, P, st);
-    pm.mark(4);
-    if (g.splits > 1) {
-        const int64_t n4 = (int64_t)g.Hkv * g.RB * 32 * (D / 4);
-        const int blocks = (int)std::min<int64_t>(65536, (n4 + kDqThreads - 1) / kDqThreads);
-        hipLaunchKernelGGL(dqreduce_kernel<D>, dim3(blocks), dim3(kDqThreads), 0, st, P);
+    auto dq_reduce = [&]() {
+        pm.begin(5);
+        if (g.splits > 1) {
+            const int64_t n4 = (int64_t)g.Hkv * g.RB * 32 * (D / 4);
+            const int blocks = (int)std::min<int64_t>(65536, (n4 + kDqThreads - 1) / kDqThreads);
+            hipLaunchKernelGGL(dqreduce_kernel<D>, dim3(blocks), dim3(kDqThreads), 0, st, P);
+        }
+        pm.end(5);
+    };
+    if (!g.dss) {
+        pm.begin(4);
+        launch_qpass<D, true>(g, P, st);
+        pm.end(4);
+        dq_reduce();
     }
-    pm.mark(5);
-    hipLaunchKernelGGL(kvpass_kernel<D>, dim3(g.kv_full + g.kv_tail * g.kv_split), dim3(kKVThreads), 0, st, P);
+    pm.begin(6);
+    const dim3 kvgrid(g.kv_full + g.kv_tail * g.kv_split);
+    if (g.dss)
+        hipLaunchKernelGGL((kvpass_kernel<D, true>), kvgrid, dim3(kKVThreads), 0, st, P);
+    else
+        hipLaunchKernelGGL((kvpass_kernel<D, false>), kvgrid, dim3(kKVThreads), 0, st, P);
     if (g.kv_tail) {
         const int64_t n4 = (int64_t)g.kv_tail * 2 * kKVKeys * (D / 4);
         const int blocks = (int)std::min<int64_t>(2048, (n4 + kThreads - 1) / kThreads);
         hipLaunchKernelGGL(kvreduce_kernel<D>, dim3(blocks), dim3(kThreads), 0, st, P, g.kv_tail);
     }
-    pm.mark(6);
+    pm.end(6);
+    if (g.dss) {
+        // dQ from the dS tiles the key side stored
+        pm.begin(4);
+        const dim3 grid((g.RB + kQsWaves - 1) / kQsWaves * g.Hkv, g.splits);
+        hipLaunchKernelGGL(dq_stored_kernel<D>, grid, dim3(kQsThreads), 0, st, P);
+        pm.end(4);
+        dq_reduce();
+    }
     return hipGetLastError() == hipSuccess ? FA_BACK_OK : FA_BACK_EHIP;
 }
 
@@ -598,6 +667,10 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
         P.kvimg = (unsigned char*)(w + g.ws_img);
         P.img_ns = g.img_ns;
     }
+    if (g.dss) {
+        P.dsbuf = (_Float16*)(w + g.ws_ds);
+        P.ds_kb = g.ds_kb;
+    }
     if (saved && !q_empty) {
         P.lse_in = lse_in;
         P.o_in = o_in;
@@ -606,14 +679,13 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
     }
 
     hipStream_t st = (hipStream_t)stream;
-    hipEvent_t ev[FA_BACK_NUM_PHASES + 1];
+    hipEvent_t ev[2 * FA_BACK_NUM_PHASES];
     int nev = 0;
     PhaseMarks pm{nullptr, st};
     int rc = FA_BACK_OK;
     if (phase_ms) {
-        for (; nev <= FA_BACK_NUM_PHASES; ++nev)
+        for (; nev < 2 * FA_BACK_NUM_PHASES; ++nev)
             if (hipEventCreate(&ev[nev]) != hipSuccess) { rc = FA_BACK_EHIP; break; }
-        if (rc == FA_BACK_OK && hipEventRecord(ev[0], st) != hipSuccess) rc = FA_BACK_EHIP;
         pm.ev = ev;
     }
     if (rc == FA_BACK_OK) {
@@ -625,9 +697,11 @@ static int run_impl(const fa_back_plan* plan, const void* q, const void* k, cons
         }
     }
     if (phase_ms && rc == FA_BACK_OK) {
-        if (hipEventSynchronize(ev[FA_BACK_NUM_PHASES]) != hipSuccess) rc = FA_BACK_EHIP;
+        // every phase recorded its start and end events on the stream
+        for (int e = 0; rc == FA_BACK_OK && e < 2 * FA_BACK_NUM_PHASES; ++e)
+            if (hipEventSynchronize(ev[e]) != hipSuccess) rc = FA_BACK_EHIP;
         for (int ph = 0; rc == FA_BACK_OK && ph < FA_BACK_NUM_PHASES; ++ph)
-            if (hipEventElapsedTime(&phase_ms[ph], ev[ph], ev[ph + 1]) != hipSuccess) rc = FA_BACK_EHIP;
+            if (hipEventElapsedTime(&phase_ms[ph], ev[2 * ph], ev[2 * ph + 1]) != hipSuccess) rc = FA_BACK_EHIP;
     }
     for (int e = 0; e < nev; ++e) (void)hipEventDestroy(ev[e]);
     if (old != plan->device) (void)hipSetDevice(old);

@@ -88,6 +88,9 @@ struct Params {
     unsigned char* kvimg; // [Hkv][img_ns][32-key slot] decoded K and V tiles of the query-side
                           //   walks (kvimage_kernel); NULL: the walks decode for themselves
     int img_ns;           // 32-key sub-tiles per head in kvimg
+    _Float16* dsbuf;      // [Hkv][RB][ds_kb][32 x 32] dS tiles the key side stores for the dQ
+                          // pass from stored dS (NULL when walk 2 forms dQ)
+    int ds_kb;            // 32-key blocks per row block and head in dsbuf (4 per 128-key tile)
 };
 
 // Mask classes of a (32-row block, 64-key tile): no masking needed, every entry -inf, other.

@@ -1664,6 +1664,159 @@ __global__ __launch_bounds__(kDqThreads) void dqreduce_kernel(Params p) {
     }
 }
 
+// ----------------------------------------------------------------------------- dQ from stored dS
+
+// dQ = scale dS K from the dS tiles the key side stored (Params::dsbuf), instead of walk 2's
+// recomputation of S and dP. A workgroup takes one KV head, 8 row blocks of 32 rows (one per
+// wave, its dQ accumulators in registers) and a key range. Per step of two 32-key sub-tiles the
+// 8 waves copy the two K tiles from the image into LDS (an eighth each) and every wave copies
+// its own row block's two dS tiles; after the step barrier each wave forms dQ^T += K^T dS^T
+// with both operands read from LDS by transpose reads: K^T as walk 2 reads it, dS^T from the
+// tile as the key side's registers held it (lane = key, 16 rows), so that each lane gets its
+// row's 8 keys in the order of the K^T operand. The next step is copied during this one.
+// Position of lane l's 16 bytes in half hh of a stored dS tile: lanes 32..63 rotated by 4 and
+// the second half by 8, so that the dQ pass's transpose reads of a tile meet no bank twice.
+FAB_DEV int ds_pos(int hh, int l) {
+    const int p0 = l < 32 ? l : 32 + ((l - 28) & 31);
+    return (8 * hh + p0) & 63;
+}
+
+constexpr int kQsWaves = 8;
+constexpr int kQsThreads = kQsWaves * kWave;
+
+template <int D>
+struct QsLds {
+    static constexpr int kKTile = kSubKeys * D * 2;           // a K sub-tile: the first half of an image slot
+    static constexpr int kSlot = 2 * kKTile;                  // an image slot
+    static constexpr int kDsTile = 2048;                      // a stored 32 x 32 dS tile
+    static constexpr int kSub = 2;                            // sub-tiles per step
+    static constexpr int kStepK = kSub * kKTile;
+    static constexpr int kStepDs = kQsWaves * kSub * kDsTile;
+    static constexpr int kSteps = 2;
+    static constexpr int kBytes = kSteps * (kStepK + kStepDs);
+};
+
+// The B operand dS^T of one 16-key step (keys kstep*16 ..) of the stored tile at t: lane l gets
+// row l%32 and the keys 16*kstep + crow(j, l/32), j = 0..7, from two transpose reads. In each
+// 16-lane group, lane 4a+b takes element b of the 8-byte reads of lanes a, a+4, a+8, a+12: so
+// reading lane r = a' + 4i reads key k0 + i of the rows 4a'..4a'+3 of its group's half, where
+// the row n of the stored layout sits in half n/16, lane-half (n/4)%2, elements 4((n/8)%2) ...
+FAB_DEV f16x8 ds_frag(const unsigned char* t, int kstep, int lane) {
+    const int q16 = lane >> 4, r = lane & 15, a = r & 3, i = r >> 2;
+    const int hh = q16 & 1, g = q16 >> 1;
+    f16x8 out;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int k0 = 16 * kstep + 8 * jj + 4 * g;
+        const unsigned char* pa = t + hh * 1024 + 16 * ds_pos(hh, k0 + i + 32 * (a & 1)) + 8 * (a >> 1);
+        const f16x4 h = tr_read(pa);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[4 * jj + e] = h[e];
+    }
+    return out;
+}
+
+template <int D>
+__global__ __launch_bounds__(kQsThreads, 1) void dq_stored_kernel(Params p) {
+    using L = QsLds<D>;
+    constexpr int MD = D / 32;
+    constexpr int NKW = L::kStepK / (kQsWaves * 1024);       // K copies per wave per step
+    static_assert(NKW >= 1 && L::kStepK == NKW * kQsWaves * 1024, "a step's K tiles split into 1 KB copies per wave");
+    __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int l32 = lane & 31, g = lane >> 5;
+    const int hk = blockIdx.x % p.Hkv;
+    const int rt = blockIdx.x / p.Hkv;
+    const int split = blockIdx.y;
+    const int rb = rt * kQsWaves + wave;
+    const bool active = rb < p.RB;
+    const int rbc = active ? rb : p.RB - 1;                   // an existing row block's tiles for the idle copies
+    const int rowsHK = p.RB * 32;
+    const int r = rb * 32 + l32;
+    const int i = r / p.G, gh = r - (r / p.G) * p.G;
+    const int h = hk * p.G + gh;
+    const bool row_ok = active && r < p.R;
+    const int ridx = hk * rowsHK + r;
+    const int NS = (p.M + kSubKeys - 1) / kSubKeys;
+    const int s_begin = 2 * split * p.tiles_per_split;
+    const int s_end = min(NS, 2 * min(p.KT, (split + 1) * p.tiles_per_split));
+    const int nsteps = (s_end - s_begin + L::kSub - 1) / L::kSub;
+
+    auto ringK = [&](int t) { return lds + (t % L::kSteps) * (L::kStepK + L::kStepDs); };
+    auto ringDs = [&](int t) { return ringK(t) + L::kStepK + wave * (L::kSub * L::kDsTile); };
+    const unsigned char* img = p.kvimg + (int64_t)hk * p.img_ns * L::kSlot;
+    const unsigned char* dsb = (const unsigned char*)p.dsbuf + ((int64_t)hk * p.RB + rbc) * p.ds_kb * L::kDsTile;
+    // copies hidden from the compiler (dma16_hidden), waited for by count at the step barrier;
+    // the same number in every step (past s_end the last sub-tile again)
+    auto copy = [&](int t) {
+#pragma unroll
+        for (int c = 0; c < NKW; ++c) {
+            const int piece = wave + kQsWaves * c;                    // 1 KB piece of the step's K tiles
+            const int u = piece / (L::kKTile / 1024), o = piece - u * (L::kKTile / 1024);
+            const int sl = min(s_begin + L::kSub * t + u, s_end - 1);
+            dma16_hidden(img + (int64_t)sl * L::kSlot + o * 1024, 16u * lane,
+                         lds_addr(ringK(t)) + (uint32_t)(u * L::kKTile + o * 1024));
+        }
+#pragma unroll
+        for (int u = 0; u < L::kSub; ++u) {
+            const int sl = min(s_begin + L::kSub * t + u, s_end - 1);
+#pragma unroll
+            for (int o = 0; o < L::kDsTile / 1024; ++o)
+                dma16_hidden(dsb + (int64_t)sl * L::kDsTile + o * 1024, 16u * lane,
+                             lds_addr(ringDs(t)) + (uint32_t)(u * L::kDsTile + o * 1024));
+        }
+    };
+
+    f32x16 dqacc[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dqacc[md][v] = 0.0f;
+    const ColWalk<D> cw = make_col_walk<D>(lane);
+
+    if (nsteps > 0) copy(0);
+    for (int t = 0; t < nsteps; ++t) {
+        // step t has landed for every wave; the slots of step t-1, which step t+1 reuses, are
+        // read by no wave any more
+        dma_barrier<0>();
+        if (t + 1 < nsteps) copy(t + 1);
+#pragma unroll
+        for (int u = 0; u < L::kSub; ++u) {
+            const int s = s_begin + L::kSub * t + u;
+            if (s >= s_end) break;
+            // a scalar load: waiting for it leaves the copies in flight
+            const int cls = active ? mask_class_s(p, hk, rb, s >> 1) : kMaskDead;
+            if (cls == kMaskDead) continue;
+            const unsigned char* dt = ringDs(t) + u * L::kDsTile;
+            const f16x8 bb[2] = {ds_frag(dt, 0, lane), ds_frag(dt, 1, lane)};
+            mfma_prio_hi();
+            cols_acc<D>(ringK(t) + u * L::kKTile, bb, dqacc, cw);
+            mfma_prio_lo();
+        }
+    }
+    wait_all_mem();   // no copy is left in flight when the wave ends
+    // the key side's dS carries the head's exponent (a reduction over the wave: every lane takes
+    // part, before the branch on the lane's row)
+    const int ksx = head_ds_exponent(p, hk);
+    if (row_ok) {
+        // a split's partial is taken to the row's exponent, which the reduction applies (an exact
+        // power-of-two factor)
+        const bool direct = p.splits == 1;
+        const float fac = direct ? p.scale * ldexpf(1.0f, ksx - p.scal[1]) : ldexpf(1.0f, ksx - p.row_ks[ridx]);
+        float* dst = direct ? p.dq + ((int64_t)h * p.N + i) * D
+                            : p.dq_part + ((int64_t)split * p.Hkv * rowsHK + ridx) * D;
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                f32x4 o = {dqacc[md][4 * b] * fac, dqacc[md][4 * b + 1] * fac,
+                           dqacc[md][4 * b + 2] * fac, dqacc[md][4 * b + 3] * fac};
+                *(f32x4*)(dst + 32 * md + 8 * b + 4 * g) = o;
+            }
+    }
+}
+
 // ----------------------------------------------------------------------------- key side
 
 // Workgroup: one KV head, 128 keys in 4 blocks of 32, and 8 waves: one pair per key block kb,
@@ -1698,7 +1851,7 @@ struct KVLds {
     static constexpr int kBytes = (kSetup > kWork ? kSetup : kWork) + kTail;
 };
 
-template <int D>
+template <int D, bool DSOUT>
 __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
     using L = KVLds<D>;
     constexpr int KS = D / 16;
@@ -1939,7 +2092,9 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
         for (int k = 0; k < n; ++k) {
             const int rb = c0 + (int)(ent & 0xffffffu);
             const int cls = (int)(ent >> (24 + 4 * (kb >> 1))) & 0xf;
-            dma_barrier<D / 32>();   // X: block rb landed; the copy of block k+1 stays in flight
+            // X: block rb landed; the copy of block k+1 stays in flight (and with DSOUT the two
+            // dS stores issued after it)
+            dma_barrier<D / 32 + (DSOUT ? 2 : 0)>();
             const uint32_t nxt = sched[k + 1 < n ? k + 1 : k];   // next entry, used after the products
             const unsigned char* tq = work + bi * L::kBuf;
             // the walks pass through an opaque move here, so that the per-step offsets are formed
@@ -1988,6 +2143,18 @@ __global__ __launch_bounds__(kKVThreads, 1) void kvpass_kernel(Params p) {
             // list: block k again)
             dma_block(k + 2 < n ? c0 + (int)(__builtin_amdgcn_readfirstlane(sched[k + 2]) & 0xffffffu) : rb,
                       bi == 0 ? 2 : bi - 1, 4, kb);
+            if constexpr (DSOUT) {
+                // this block's dS for the dQ pass, as the registers hold it: two streaming stores
+                // in every iteration (a dead block's tile is never read), after the copies, so the
+                // copy wait above counts them. The lane offsets are formed here from an opaque lane
+                // index rather than held across the loop (the registers are short). (Stored after
+                // the next block barrier instead, beside the dK products, a walk offset spills
+                // into the loop.)
+                _Float16* t = p.dsbuf + ((((int64_t)hk * p.RB + rb) * p.ds_kb + 4 * kvt + kb) << 10);
+                const int ol = opaque(lane);
+                __builtin_nontemporal_store(bs[0], (f16x8*)(t + 8 * ds_pos(0, ol)));
+                __builtin_nontemporal_store(bs[1], (f16x8*)(t + 512 + 8 * ds_pos(1, ol)));
+            }
             bprev = bi;
             ent = __builtin_amdgcn_readfirstlane(nxt);
             bi = bi == 2 ? 0 : bi + 1;

@@ -23,6 +23,8 @@ FLAG_WALK1_ROWS = 4  # LSE/delta walk owned by row tiles
 FLAG_CENTER_K = 8    # centre K before its fp16 rounding
 FLAG_KV_IMAGE = 16   # decode the cache once into the workspace for the query-side walks
 FLAG_KV_INLINE = 32  # every query-side workgroup decodes the cache tiles it reads
+FLAG_DS_STORE = 64   # the key side stores dS; dQ is formed from it (no second query-side walk)
+FLAG_DS_RECOMPUTE = 128  # walk 2 recomputes S and dP for dQ
 TYPE_IDS = {"none": NONE, "f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0,
             "q4_1": Q4_1, "q5_0": Q5_0, "q5_1": Q5_1, "causal_tail": CAUSAL_TAIL}
 # bytes of one element (one 32-value block for the ggml block types)

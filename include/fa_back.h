@@ -141,6 +141,22 @@ extern "C" {
 #define FA_BACK_FLAG_KV_IMAGE 16u
 #define FA_BACK_FLAG_KV_INLINE 32u
 
+/* FA_BACK_FLAG_DS_STORE, FA_BACK_FLAG_DS_RECOMPUTE: how dQ = scale * dS K is formed. The pages'
+ * structure ("CambrianTech/llama.cpp PR #63", third review) forms it in the query-side kernel,
+ * which walks the keys a second time and recomputes S and dP for it (DS_RECOMPUTE). With
+ * DS_STORE the key-side pass, which forms dS anyway, stores it in the workspace as fp16 tiles
+ * (2 bytes per visible-or-not (row, key) pair of every listed 32-row block: Hkv * ceil(G*N/32)
+ * * 4 * ceil(M/128) * 2048 bytes), and a dQ pass forms dS K from them; the query-side walk over
+ * the keys for dQ is not run. It takes the decoded image of the cache (FA_BACK_FLAG_KV_INLINE
+ * with DS_STORE is FA_BACK_EINVAL). The results meet the same bar, not bitwise the same: dS is
+ * rounded with one exponent per KV head instead of one per row. With neither bit the plan
+ * stores dS whenever it takes the image and the tiles need at most 16 GiB, and recomputes
+ * otherwise. Setting both is FA_BACK_EINVAL. The choice changes the workspace size;
+ * DS_RECOMPUTE keeps the tiles out of a workspace that must stay within
+ * FA_BACK_NOALLOC_MAX_WORKSPACE. */
+#define FA_BACK_FLAG_DS_STORE 64u
+#define FA_BACK_FLAG_DS_RECOMPUTE 128u
+
 /* status codes (no entry point aborts or exits) */
 #define FA_BACK_OK 0
 #define FA_BACK_EINVAL (-1)       /* null pointer, negative extent, non-finite scale, unknown flag bit */
@@ -200,15 +216,17 @@ int fa_back_create(const fa_back_desc* desc, int device, fa_back_plan** plan,
 int fa_back_run(const fa_back_plan* plan, const void* q, const void* k, const void* v,
                 const void* d, const void* mask, void* out, void* workspace, void* stream);
 
-/* Number of kernel phases reported by fa_back_run_timed, in launch order:
+/* Number of kernel phases reported by fa_back_run_timed:
  * 0 absmax of q and dO, 1 q/dO to fp16 fragments, 2 query-side walk 1 (LSE and delta
  * statistics), 3 merge of key-range splits (writes LSE and delta), 4 query-side walk 2 (dQ),
- * 5 dQ split reduction (empty when the keys were not split), 6 key-side pass (dK, dV). */
+ * or with FA_BACK_FLAG_DS_STORE the dQ pass from the stored dS, 5 dQ split reduction (empty
+ * when the keys were not split), 6 key-side pass (dK, dV). They run in this order, except
+ * that with FA_BACK_FLAG_DS_STORE phases 4 and 5 run after phase 6. */
 #define FA_BACK_NUM_PHASES 7
 
-/* fa_back_run plus timing, for profiling: records a HIP event on `stream` before the first
- * kernel and after each phase, waits for the last one, and writes each phase's elapsed
- * milliseconds to phase_ms[0 .. FA_BACK_NUM_PHASES-1]. Unlike fa_back_run it blocks the
+/* fa_back_run plus timing, for profiling: records a HIP event on `stream` before and after
+ * each phase, waits for the last one, and writes each phase's elapsed milliseconds to
+ * phase_ms[0 .. FA_BACK_NUM_PHASES-1]. Unlike fa_back_run it blocks the
  * host until the run has finished; it creates and destroys its own events. */
 int fa_back_run_timed(const fa_back_plan* plan, const void* q, const void* k, const void* v,
                       const void* d, const void* mask, void* out, void* workspace, void* stream,

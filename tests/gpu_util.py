@@ -104,10 +104,14 @@ def compare(got, ref, keys=KEYS, tol=TOL, local=True):
 
 
 def walk1(p, mode):
-    """The same problem with the LSE/delta walk forced by its descriptor flag: 'rows', 'keys', or
-    'rows_image' (rows, with the cache decoded into the image: the row walk's own kernel)."""
+    """The same problem with the LSE/delta walk forced by its descriptor flag: 'rows', 'keys',
+    'rows_image' (rows, with the cache decoded into the image: the row walk's own kernel, and dQ
+    by walk 2), or 'rows_ds' (rows, with dQ from the dS the key side stores)."""
     F = fab.fa_back
     bit = {"keys": F.FLAG_WALK1_KEYS, "rows": F.FLAG_WALK1_ROWS,
-           "rows_image": F.FLAG_WALK1_ROWS | F.FLAG_KV_IMAGE}[mode]
-    clear = F.FLAG_WALK1_KEYS | F.FLAG_WALK1_ROWS | (F.FLAG_KV_IMAGE | F.FLAG_KV_INLINE if mode == "rows_image" else 0)
+           "rows_image": F.FLAG_WALK1_ROWS | F.FLAG_KV_IMAGE | F.FLAG_DS_RECOMPUTE,
+           "rows_ds": F.FLAG_WALK1_ROWS | F.FLAG_DS_STORE}[mode]
+    clear = F.FLAG_WALK1_KEYS | F.FLAG_WALK1_ROWS
+    if mode in ("rows_image", "rows_ds"):
+        clear |= F.FLAG_KV_IMAGE | F.FLAG_KV_INLINE | F.FLAG_DS_STORE | F.FLAG_DS_RECOMPUTE
     return dataclasses.replace(p, flags=(p.flags & ~clear) | bit)

@@ -188,7 +188,7 @@ def test_centre_v_flag_validation():
     _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_CENTER_V), "c1_f32kv")
     _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_CENTER_V), "c3")
     _expect(B.EUNSUPPORTED, lambda d: setattr(d, "flags", B.FLAG_CENTER_V), "c1")
-    _expect(B.EINVAL, lambda d: setattr(d, "flags", 1 << 6), "c1_f32kv")
+    _expect(B.EINVAL, lambda d: setattr(d, "flags", 1 << 8), "c1_f32kv")
     # the centre takes Hkv * D floats of workspace
     d0 = _desc("c1_f32kv")
     d1 = _desc("c1_f32kv")
@@ -209,7 +209,7 @@ def test_walk1_and_centre_k_flags():
     _expect(B.EUNSUPPORTED, lambda d: setattr(d, "flags", B.FLAG_CENTER_K), "c1")
     _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_CENTER_K), "c1_f32kv")
     _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_CENTER_K | B.FLAG_CENTER_V), "c3")
-    _expect(B.EINVAL, lambda d: setattr(d, "flags", 64), "c1_f32kv")
+    _expect(B.EINVAL, lambda d: setattr(d, "flags", 256), "c1_f32kv")
 
 
 def _ws(p, flags):
@@ -251,7 +251,8 @@ def test_kv_image_flags_and_workspace():
     _expect(B.EINVAL, lambda d: setattr(d, "flags", B.FLAG_KV_IMAGE | B.FLAG_KV_INLINE))
     for name, default_image in (("c3", True), ("c1", False)):
         p = fa_inputs.make(name)
-        rows = B.FLAG_WALK1_ROWS   # the walk-1 direction held fixed: the image alone differs
+        # the walk-1 direction and the dS choice held fixed: the image alone differs
+        rows = B.FLAG_WALK1_ROWS | B.FLAG_DS_RECOMPUTE
         img, inl, dflt = _ws(p, B.FLAG_KV_IMAGE | rows), _ws(p, B.FLAG_KV_INLINE | rows), _ws(p, rows)
         image_bytes = p.Hkv * ((p.M + 31) // 32) * 128 * p.D
         assert img.workspace_bytes - inl.workspace_bytes >= image_bytes
@@ -294,3 +295,22 @@ def test_other_block_types_accepted_as_cache_only(typ, nbytes):
     d.k.nb[2] = d.k.nb[1] * p.M
     lay = B.Layout()
     assert fab.load_library().fa_back_layout_query(ctypes.byref(d), ctypes.byref(lay)) == B.ESTRIDE
+
+
+def test_stored_ds_flags_and_workspace():
+    """DS_STORE stores 2 bytes of dS per (row, key) pair of every 32-row block and 128-key tile
+    (Hkv * ceil(G*N/32) * 4 * ceil(M/128) * 2048 bytes) and takes the image of the cache; it
+    excludes DS_RECOMPUTE and KV_INLINE. Without a flag the plan stores dS when it takes the
+    image."""
+    _expect(B.EINVAL, lambda d: setattr(d, "flags", B.FLAG_DS_STORE | B.FLAG_DS_RECOMPUTE))
+    _expect(B.EINVAL, lambda d: setattr(d, "flags", B.FLAG_DS_STORE | B.FLAG_KV_INLINE))
+    _expect(B.OK, lambda d: setattr(d, "flags", B.FLAG_DS_RECOMPUTE | B.FLAG_KV_INLINE))
+    p = fa_inputs.make("c3")   # 32 row tiles of 128 rows: the image by default
+    rows = B.FLAG_WALK1_ROWS
+    st, rc = _ws(p, B.FLAG_DS_STORE | rows), _ws(p, B.FLAG_DS_RECOMPUTE | rows)
+    assert _ws(p, rows).workspace_bytes == st.workspace_bytes   # stored by default with the image
+    c1 = fa_inputs.make("c1")   # 2 row tiles: no image, so recompute by default
+    assert _ws(c1, 0).workspace_bytes == _ws(c1, B.FLAG_DS_RECOMPUTE).workspace_bytes
+    ds_bytes = p.Hkv * (-(-(p.H // p.Hkv) * p.N // 32)) * 4 * (-(-p.M // 128)) * 2048
+    assert st.workspace_bytes - rc.workspace_bytes >= ds_bytes
+    assert st.out_bytes == rc.out_bytes

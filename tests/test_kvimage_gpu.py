@@ -34,8 +34,10 @@ CASES = [
 
 
 def _with(p, bit):
-    both = B.FLAG_KV_IMAGE | B.FLAG_KV_INLINE
-    return dataclasses.replace(p, flags=(p.flags & ~both) | bit)
+    # dQ by walk 2 in both runs (stored dS, which the plan takes with the image, rounds dS with
+    # another exponent and is checked against the oracle elsewhere)
+    both = B.FLAG_KV_IMAGE | B.FLAG_KV_INLINE | B.FLAG_DS_STORE
+    return dataclasses.replace(p, flags=(p.flags & ~both) | bit | B.FLAG_DS_RECOMPUTE)
 
 
 @pytest.mark.gpu

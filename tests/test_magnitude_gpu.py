@@ -22,7 +22,7 @@ DECADES = [
 ]
 
 
-@pytest.mark.parametrize("mode", ["rows", "keys"])
+@pytest.mark.parametrize("mode", ["rows", "keys", "rows_ds"])
 @pytest.mark.parametrize("cfg", DECADES, ids=[c["name"] for c in DECADES])
 def test_every_magnitude_class(cfg, mode):
     p = walk1(fa_inputs.make_custom(**cfg), mode)
@@ -37,7 +37,7 @@ def test_every_magnitude_class(cfg, mode):
         say(f"   rows x 1e-{c}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
-@pytest.mark.parametrize("mode", ["rows", "keys"])
+@pytest.mark.parametrize("mode", ["rows", "keys", "rows_ds"])
 def test_tiny_kv_group(mode):
     # every dO row of KV head 1's query heads is 1e-4 of the others: its dK and dV, and its rows'
     # dQ and delta, meet the bar on their own

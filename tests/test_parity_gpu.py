@@ -200,7 +200,7 @@ def _walk1_problem(name):
     return fa_inputs.make_custom(**next(c for c in RAGGED if c["name"] == name))
 
 
-@pytest.mark.parametrize("mode", ["rows", "keys", "rows_image"])
+@pytest.mark.parametrize("mode", ["rows", "keys", "rows_image", "rows_ds"])
 @pytest.mark.parametrize("name", WALK1_CASES)
 def test_walk1_variants(name, mode):
     say(f"[walk1 {mode}]")
@@ -224,7 +224,7 @@ def _implicit_problem(name, cfg):
     return fa_inputs.make(name) if cfg is None else fa_inputs.make_custom(name=name, **cfg)
 
 
-@pytest.mark.parametrize("mode", ["rows", "keys", "rows_image"])
+@pytest.mark.parametrize("mode", ["rows", "keys", "rows_image", "rows_ds"])
 @pytest.mark.parametrize("name,cfg", IMPLICIT_CASES, ids=[c[0] for c in IMPLICIT_CASES])
 def test_implicit_causal_tail_bitwise(name, cfg, mode):
     p = walk1(_implicit_problem(name, cfg), mode)
