@@ -39,8 +39,11 @@ PEAK_HBM_GBS = 8000.0
 # matrix-product work per visible (row, key, head) triple, per phase (D = Dv)
 PHASE_FLOPS_PER_PAIR_PER_D = {"walk1": 4, "walk2": 6, "kvpass": 8}
 # the kernels a phase may run (the plan picks one), as name prefixes of their instantiations
+# ("walk2" is the dQ phase: walk 2, or the dQ pass from the key side's stored dS)
 KERNEL_PREFIXES = {"walk1": ("walk1_rows_kernel<D>", "walk1_keys_kernel<D>", "qpass_kernel<D, false"),
-                   "walk2": ("qpass_kernel<D, true",), "kvpass": ("kvpass_kernel<D>",)}
+                   "walk2": ("qpass_kernel<D, true", "dq_stored_kernel<D>"), "kvpass": ("kvpass_kernel<D",)}
+# the dQ phase with stored dS forms only dS K: 2 * D flops per visible triple
+DQ_STORED_FLOPS_PER_PAIR_PER_D = 2
 
 
 def phase_bytes(p, phase):
@@ -204,6 +207,15 @@ def main():
     dev = torch.device("cuda:0")
     dp = fab.DeviceProblem(p, dev, poison=False)
     stream = torch.cuda.current_stream(dev)
+    F = fab.fa_back
+    pf = dict(PHASE_FLOPS_PER_PAIR_PER_D)
+    stored_ds = bool(dp.layout.plan_flags & F.FLAG_DS_STORE)
+    if stored_ds:
+        pf["walk2"] = DQ_STORED_FLOPS_PER_PAIR_PER_D
+    plan = [n for n, b in (("walk1_keys", F.FLAG_WALK1_KEYS), ("walk1_rows", F.FLAG_WALK1_ROWS),
+                            ("kv_image", F.FLAG_KV_IMAGE), ("kv_inline", F.FLAG_KV_INLINE),
+                            ("ds_store", F.FLAG_DS_STORE), ("ds_recompute", F.FLAG_DS_RECOMPUTE))
+            if dp.layout.plan_flags & b]
     if args.saved:
         # the LSE of the full operator on the same inputs, and a synthetic O
         dp.run()
@@ -238,7 +250,7 @@ def main():
                   "source": "HIP events on the launch stream, per call"}
     log("phase ms: " + " ".join(f"{k}={v:.3f}" for k, v in mean_phase.items()))
 
-    dom = max(PHASE_FLOPS_PER_PAIR_PER_D, key=lambda n: mean_phase[n])
+    dom = max(pf, key=lambda n: mean_phase[n])
     prefixes = tuple(k.replace("D", str(p.D), 1) for k in KERNEL_PREFIXES[dom])
     nbytes = fa_inputs.min_bytes(p)
     intensity = flops["full"] / nbytes["total"]
@@ -247,7 +259,7 @@ def main():
     if kname is None:
         kname = " | ".join(prefixes)   # the phase's kernel, as far as the record can tell
     if intensity >= PEAK_MFMA_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        dom_flops = PHASE_FLOPS_PER_PAIR_PER_D[dom] * p.D * flops["visible"]
+        dom_flops = pf[dom] * p.D * flops["visible"]
         achieved = dom_flops / (mean_phase[dom] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_F16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4), "traffic": traffic,
@@ -269,6 +281,7 @@ def main():
         roofline["copy_reference"] = {"gbs": round(copy, 1), "frac_of_copy": round(achieved / copy, 4),
                                       "what": "plain 1 GiB device copy, read + write bytes / time"}
     value = flops["full"] / (ms * 1e-3) / 1e12
+    executed = sum(pf[k] for k in pf if not (args.saved and k == "walk1")) * p.D * flops["visible"]
     rec = {
         "metric": (METRIC if args.workload == "c4" and args.mask == "stored" and not args.saved
                    else f"attn-backward TFLOP/s + ms/call, {args.workload} mask {args.mask}"
@@ -283,7 +296,11 @@ def main():
         "flops": {"count": ("2*V*(3D+4Dv)" if args.saved else "2*V*(5D+4Dv)") +
                            ", V = visible (row, key, head) triples",
                   "visible": flops["visible"], "full": flops["full"], "five_gemm": flops["five"],
-                  "tflops_five_gemm": round(flops["five"] / (ms * 1e-3) / 1e12, 3)},
+                  "tflops_five_gemm": round(flops["five"] / (ms * 1e-3) / 1e12, 3),
+                  "executed": executed, "tflops_executed": round(executed / (ms * 1e-3) / 1e12, 3),
+                  "executed_note": "matrix flops this plan runs (walk 1 skipped by the saved entry; "
+                                   "dQ from stored dS runs 2*D*V instead of walk 2's 6*D*V)"},
+        "plan": plan,
         "phase_ms": {k: round(v, 4) for k, v in mean_phase.items()},
         "roofline": roofline,
     }

@@ -325,6 +325,12 @@ int validate(const fa_back_desc* d, int cus, Geometry* g) {
     g->ws_img = take(g->img ? (uint64_t)g->Hkv * g->img_ns * (uint64_t)(4 * kSubKeys * D) : 0);
     g->ws_ds = take(g->dss ? (uint64_t)g->Hkv * g->RB * g->ds_kb * 2048ull : 0);
     L.workspace_bytes = std::max<uint64_t>(o, kAlign);
+    L.plan_flags = d->flags & (FA_BACK_FLAG_CENTER_V | FA_BACK_FLAG_CENTER_K);
+    if (g->M > 0 && g->R > 0) {
+        L.plan_flags |= g->w1keys ? FA_BACK_FLAG_WALK1_KEYS : FA_BACK_FLAG_WALK1_ROWS;
+        L.plan_flags |= g->img ? FA_BACK_FLAG_KV_IMAGE : FA_BACK_FLAG_KV_INLINE;
+        L.plan_flags |= g->dss ? FA_BACK_FLAG_DS_STORE : FA_BACK_FLAG_DS_RECOMPUTE;
+    }
     return FA_BACK_OK;
 }
 

@@ -54,7 +54,8 @@ class Desc(ctypes.Structure):
 class Layout(ctypes.Structure):
     _fields_ = [("off_dq", ctypes.c_uint64), ("off_dk", ctypes.c_uint64), ("off_dv", ctypes.c_uint64),
                 ("off_lse", ctypes.c_uint64), ("off_delta", ctypes.c_uint64),
-                ("out_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
+                ("out_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64),
+                ("plan_flags", ctypes.c_uint32)]
 
 
 _lib = None

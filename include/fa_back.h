@@ -184,6 +184,10 @@ typedef struct {
     uint64_t off_dq, off_dk, off_dv, off_lse, off_delta;  /* byte offsets in `out` */
     uint64_t out_bytes;        /* size the caller allocates for `out` */
     uint64_t workspace_bytes;  /* device scratch the caller allocates for `workspace` */
+    uint32_t plan_flags;       /* the plan's choices as FA_BACK_FLAG_* bits: one of WALK1_KEYS /
+                                  WALK1_ROWS, one of KV_IMAGE / KV_INLINE, one of DS_STORE /
+                                  DS_RECOMPUTE (and the CENTER bits of the descriptor); a
+                                  degenerate shape (N or M zero) reports none of the six */
 } fa_back_layout;
 
 typedef struct fa_back_plan fa_back_plan;

@@ -314,3 +314,19 @@ def test_stored_ds_flags_and_workspace():
     ds_bytes = p.Hkv * (-(-(p.H // p.Hkv) * p.N // 32)) * 4 * (-(-p.M // 128)) * 2048
     assert st.workspace_bytes - rc.workspace_bytes >= ds_bytes
     assert st.out_bytes == rc.out_bytes
+
+
+def test_layout_reports_the_plan():
+    """plan_flags names the plan's choices: c1 (M = 2 G N, 2 row tiles) walks keys, decodes
+    inline and recomputes dS; c3 (32 row tiles) walks rows over the image and stores dS; the
+    flags override either, and a degenerate shape reports none."""
+    F = B
+    c1 = fab.fa_back_layout_query(B.describe(fa_inputs.make("c1"))).plan_flags
+    assert c1 == F.FLAG_WALK1_KEYS | F.FLAG_KV_INLINE | F.FLAG_DS_RECOMPUTE
+    c3 = fab.fa_back_layout_query(B.describe(fa_inputs.make("c3"))).plan_flags
+    assert c3 == F.FLAG_WALK1_ROWS | F.FLAG_KV_IMAGE | F.FLAG_DS_STORE
+    assert _ws(fa_inputs.make("c3"), F.FLAG_DS_RECOMPUTE).plan_flags & F.FLAG_DS_RECOMPUTE
+    assert _ws(fa_inputs.make("c1"), F.FLAG_DS_STORE).plan_flags == (
+        F.FLAG_WALK1_ROWS | F.FLAG_KV_IMAGE | F.FLAG_DS_STORE)
+    empty = fa_inputs.make_custom(name="e", D=64, H=2, Hkv=1, N=4, M=0, mask="none")
+    assert fab.fa_back_layout_query(B.describe(empty)).plan_flags == 0
