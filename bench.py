@@ -51,15 +51,21 @@ def phase_bytes(p, phase):
     Every phase reads the K/V cache (stored types) and the fp16 q and dO rows (2 bytes a value,
     each row once); walk 1 and walk 2 also read the stored mask and write 8 bytes of statistics a
     row, walk 2 writes dQ (F32), the key side reads 8 bytes of statistics a row and writes dK and
-    dV (F32)."""
+    dV (F32). When the plan stores dS (2 bytes per (row, key, head)), the key side also writes
+    it, and the dQ phase reads it, K, the statistics, and writes dQ."""
     import fa_inputs
+    import flash_attention_backward_amd as fab
+    stored = bool(fab.fa_back_layout_query(fab.fa_back.describe(p)).plan_flags & fab.fa_back.FLAG_DS_STORE)
+    ds = 2 * p.N * p.H * p.M if stored else 0
     kv = fa_inputs.storage_bytes(p.k) + fa_inputs.storage_bytes(p.v)
     rows = p.N * p.H
     qd = 2 * 2 * rows * p.D
     mask = 0 if p.mask is None or p.mask_type == "causal_tail" else fa_inputs.storage_bytes(p.mask)
     if phase == "kvpass":
-        return kv + qd + 8 * rows + 4 * 2 * p.Hkv * p.M * p.D
+        return kv + qd + 8 * rows + 4 * 2 * p.Hkv * p.M * p.D + ds
     if phase == "walk2":
+        if stored:
+            return fa_inputs.storage_bytes(p.k) + ds + 8 * rows + 4 * rows * p.D
         return kv + qd + mask + 8 * rows + 4 * rows * p.D
     return kv + qd + mask + 8 * rows
 
