@@ -19,8 +19,11 @@ from tests.test_saved_gpu import _run_saved
 pytestmark = pytest.mark.gpu
 
 KV_TYPES = ["f32", "f16", "bf16", "q8_0", "q4_0", "q4_1", "q5_0", "q5_1"]
+# with the image the plan forms dQ from the key side's stored dS unless DS_RECOMPUTE says
+# otherwise, so the image plans cover both dQ paths
 PLANS = [0, B.FLAG_WALK1_ROWS, B.FLAG_WALK1_KEYS, B.FLAG_WALK1_ROWS | B.FLAG_KV_IMAGE,
-         B.FLAG_WALK1_KEYS | B.FLAG_KV_IMAGE, B.FLAG_WALK1_ROWS | B.FLAG_KV_INLINE]
+         B.FLAG_WALK1_KEYS | B.FLAG_KV_IMAGE | B.FLAG_DS_RECOMPUTE, B.FLAG_WALK1_ROWS | B.FLAG_KV_INLINE,
+         B.FLAG_WALK1_KEYS | B.FLAG_DS_STORE]
 
 
 def _cases(n=96, seed=2024):
