@@ -1674,6 +1674,7 @@ __global__ __launch_bounds__(kDqThreads) void dqreduce_kernel(Params p) {
 // with both operands read from LDS by transpose reads: K^T as walk 2 reads it, dS^T from the
 // tile as the key side's registers held it (lane = key, 16 rows), so that each lane gets its
 // row's 8 keys in the order of the K^T operand. The next step is copied during this one.
+
 // Position of lane l's 16 bytes in half hh of a stored dS tile: lanes 32..63 rotated by 4 and
 // the second half by 8, so that the dQ pass's transpose reads of a tile meet no bank twice.
 FAB_DEV int ds_pos(int hh, int l) {
@@ -1835,6 +1836,8 @@ __global__ __launch_bounds__(kQsThreads, 1) void dq_stored_kernel(Params p) {
 // Every wave stays within 256 registers.
 // S = Q K^T puts one key per lane column and 16 rows per lane: the layout of the second
 // operand of the dK/dV products, whose first operands are transpose reads of the row blocks.
+// With DSOUT the Y waves also store each block's dS tile (fp16, as their registers hold it) for
+// the dQ pass from stored dS.
 constexpr int kKVWaves = 8;
 constexpr int kKVThreads = kKVWaves * kWave;
 
